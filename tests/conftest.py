@@ -1,0 +1,25 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: long-running CPU test")
+
+
+@pytest.fixture(scope="session")
+def tiny_weights():
+    from seeded_inputs import generate_weights, get_config
+    return generate_weights(get_config("tiny"))
+
+
+@pytest.fixture(scope="session")
+def tiny_model(tiny_weights):
+    from oracle import Fp64Model
+    return Fp64Model(tiny_weights)
