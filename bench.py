@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Verified tokens/s of greedy block verification on one MI355X.
+
+Workload (default): the Qwen3-8B-shaped random-init target (36 layers,
+d 4096, 32/8 heads x 128, FFN 12288, vocab 151936, bf16), 50 prompts of 128
+random ids, 64 generated tokens each, K = 4 drafts per verify.  Each draft
+position is the target's true greedy token with probability 0.66, else a
+random wrong id (the first wrong one ends acceptance).  The true continuation
+comes from a plain one-token decode pass run first (also reported as the
+decode baseline).
+
+A timed *step* is one ``sv_verify`` call (the whole hot path: embed, 36
+layers, LM head + argmax, acceptance, truncate) on one prompt's window; the
+loop walks the prompts' speculative loops in order.  ``value`` = committed
+(verified) tokens / wall seconds of the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified tokens/s at K=4/8/16 (1 GPU); HBM GB/s vs peak; verify/decode mismatches"
+PEAK_HBM_GBS = 8000.0
+ROLE_GATE_UP = 2
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_step_bytes(cfg, m, kv_len):
+    """Bytes one verify of m rows at kv_len must move: weights once, KV read
+    once and written once, embedding rows."""
+    kvb = cfg.kv_bytes_per_token()
+    return cfg.weight_bytes_per_forward() + (kv_len + m) * kvb + m * kvb + 2 * m * cfg.d_model
+
+
+def gate_up_bytes(cfg, m):
+    """Algorithmic bytes of one gate/up GEMM launch: packed weights, the fp32
+    residual rows and gains it normalises, and the m x 2F fp32 outputs."""
+    n, k = 2 * cfg.d_ff, cfg.d_model
+    w = n * k * 2 if cfg.weight_fmt == "bf16" else n * k // 2 + n * (k // 64) * 2
+    return w + m * k * 4 + k * 2 + m * n * 4
+
+
+def load_traffic(kernel_src_sha):
+    path = os.path.join(ROOT, "profiles", "gate_up_q8b_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha256") != kernel_src_sha:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def run_spec(sessions, truth, prompt_len, gen, k, srcs, n_steps, profile_mask=0):
+    """Walk the prompts' speculative loops for exactly n_steps verify calls."""
+    from greedy_block_verification_amd import binding as B
+    import torch
+    st = {"tokens": 0, "accepted": 0, "proposed": 0, "mism": 0, "matched": 0, "finished": 0,
+          "rows": 0, "bytes": 0, "gu_bytes": 0, "steps": []}
+    p = 0
+    done = [0] * len(sessions)
+    for s in sessions:
+        B.sv_set_profile(s.ctx, profile_mask)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_steps):
+        s, c = sessions[p], done[p]
+        k_eff = min(k, gen - c - 1)
+        window = truth[p][c + 1: c + 1 + k_eff]
+        drafts = srcs[p].window(window, k_eff) if k_eff > 0 else []
+        cur = s.next_id
+        kv = s.kv_len
+        n, _ = B.sv_verify(s.ctx, kv, drafts)
+        new = [cur] + drafts[:n]
+        st["mism"] += sum(int(a != b) for a, b in zip(new, truth[p][c: c + n + 1]))
+        st["tokens"] += n + 1
+        st["accepted"] += n
+        st["proposed"] += k_eff
+        st["rows"] += k_eff + 1
+        st["steps"].append((k_eff, n, kv))
+        done[p] = c + n + 1
+        if done[p] >= gen:
+            st["finished"] += 1
+            st["matched"] += int(done[p] == gen)
+            s.truncate(prompt_len)
+            done[p] = 0
+            p = (p + 1) % len(sessions)
+    torch.cuda.synchronize()
+    st["seconds"] = time.perf_counter() - t0
+    for s in sessions:
+        B.sv_set_profile(s.ctx, 0)
+    # leave every session at its prompt for the next run
+    for i, s in enumerate(sessions):
+        if s.kv_len != prompt_len:
+            s.truncate(prompt_len)
+    return st
+
+
+def cpu_baseline(weights, ids, n_tokens, steps):
+    """The fp64 oracle's per-token decoder on this host (bounded sample)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import Fp64Model, TokenDecoder
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    m = Fp64Model(weights, cache=False)
+    dec = TokenDecoder(m)
+    t0 = time.perf_counter()
+    for t in ids[:n_tokens]:
+        dec.decode(int(t))
+    s_per_decode = (time.perf_counter() - t0) / n_tokens
+    # the oracle verifies a window of k_eff drafts with k_eff + 1 per-token decodes
+    tok = sum(n + 1 for _, n, _ in steps)
+    decodes = sum(k + 1 for k, _, _ in steps)
+    return {"value": tok / (decodes * s_per_decode), "unit": "verified tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n_tokens} fp64 per-token decode(s) of the full model at positions 0..{n_tokens - 1} "
+                      f"({s_per_decode:.2f} s each); verified tokens/s = committed tokens / ((k+1) decodes per "
+                      f"verify x s per decode) over the GPU run's own windows",
+            "s_per_decode": s_per_decode, "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300, help="timed verify steps at the headline K")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="q8b")
+    ap.add_argument("--k", type=int, default=4)
+    ap.add_argument("--k-sweep", default="8,16", help="extra K values timed after the headline (empty: none)")
+    ap.add_argument("--sweep-steps", type=int, default=150)
+    ap.add_argument("--prompts", type=int, default=50)
+    ap.add_argument("--prompt-len", type=int, default=128)
+    ap.add_argument("--gen-tokens", type=int, default=64)
+    ap.add_argument("--p-correct", type=float, default=0.66)
+    ap.add_argument("--cpu-tokens", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU sharding)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from greedy_block_verification_amd import binding as B
+    from greedy_block_verification_amd.session import DeviceModel, Session
+    from greedy_block_verification_amd import metrics
+    from seeded_inputs import DraftSource, generate_weights, get_config, prompt_ids
+
+    cfg = get_config(args.config)
+    t = time.perf_counter()
+    weights = generate_weights(cfg, threads=min(16, len(os.sched_getaffinity(0))))
+    log(f"[bench] weights generated in {time.perf_counter() - t:.1f} s")
+    t = time.perf_counter()
+    dm = DeviceModel(weights)
+    log(f"[bench] weights uploaded and packed in {time.perf_counter() - t:.1f} s")
+
+    P, L, G = args.prompts, args.prompt_len, args.gen_tokens
+    sessions, truth, prompts = [], [], []
+    t_prefill = t_decode = 0.0
+    for p in range(P):
+        s = Session(dm)
+        ids = prompt_ids(cfg.seed, p, L, cfg.vocab).tolist()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        nx = s.prefill(ids)
+        t_prefill += time.perf_counter() - t
+        seq = [nx]
+        t = time.perf_counter()
+        for _ in range(G):
+            seq.append(s.decode_step(seq[-1]))
+        t_decode += time.perf_counter() - t
+        s.truncate(L)
+        assert s.next_id == nx
+        sessions.append(s)
+        truth.append(seq)
+        prompts.append(ids)
+    decode_tpot_ms = 1000.0 * t_decode / (P * G)
+    log(f"[bench] {P} prompts prefetched; baseline decode {decode_tpot_ms:.3f} ms/token")
+
+    srcs = [DraftSource(cfg.seed, p, cfg.vocab, p_correct=args.p_correct) for p in range(P)]
+    run_spec(sessions[:1], truth[:1], L, G, args.k, [DraftSource(cfg.seed, 10_000, cfg.vocab, p_correct=args.p_correct)],
+             args.warmup)
+    st = run_spec(sessions, truth, L, G, args.k, srcs, args.steps, profile_mask=1 << ROLE_GATE_UP)
+    gu_ms = sum(B.sv_profile_read(s.ctx, ROLE_GATE_UP)[0] for s in sessions)
+    gu_n = sum(B.sv_profile_read(s.ctx, ROLE_GATE_UP)[1] for s in sessions)
+    value = metrics.verified_tok_s(st["tokens"], st["seconds"])
+    ms_step = 1000.0 * st["seconds"] / args.steps
+    log(f"[bench] K={args.k}: {value:.1f} verified tok/s, {ms_step:.3f} ms/step, "
+        f"acceptance {metrics.acceptance_rate(st['accepted'], st['proposed']):.4f}")
+
+    # roofline of the dominant kernel (gate/up GEMM): algorithmic bytes per
+    # launch over its mean event-timed duration in the timed region
+    gu_bytes = sum(gate_up_bytes(cfg, k_eff + 1) for k_eff, _, _ in st["steps"]) * cfg.n_layers
+    achieved = gu_bytes / (gu_ms / 1000.0) / 1e9 if gu_ms > 0 else 0.0
+    ksrc = open(os.path.join(ROOT, "greedy_block_verification_amd", "csrc", "sv_kernels.hip"), "rb").read()
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": load_traffic(hashlib.sha256(ksrc).hexdigest()),
+                "kernel": "k_gemm_bf16<1,kBNorm,kOutPartial,kRoleGateUp> (gate/up GEMM, 8B shape)",
+                "launches": gu_n, "mean_launch_us": round(1000.0 * gu_ms / max(1, gu_n), 2),
+                "bytes_per_launch": int(gu_bytes / max(1, gu_n))}
+    step_bytes = sum(algorithmic_step_bytes(cfg, k_eff + 1, kv) for k_eff, _, kv in st["steps"])
+    extra = {
+        "acceptance_rate": round(metrics.acceptance_rate(st["accepted"], st["proposed"]), 4),
+        "tokens_per_verify": round(st["tokens"] / args.steps, 4),
+        "rows_scored_per_s": round(st["rows"] / st["seconds"], 1),
+        "step_hbm_gbs": round(step_bytes / st["seconds"] / 1e9, 1),
+        "step_hbm_frac": round(step_bytes / st["seconds"] / 1e9 / PEAK_HBM_GBS, 4),
+        "verify_decode_mismatches": st["mism"],
+        "prompts_finished": st["finished"], "prompts_matched": st["matched"],
+        "baseline_decode_tpot_ms": round(decode_tpot_ms, 4),
+        "baseline_decode_tok_s": round(1000.0 / decode_tpot_ms, 2),
+        "speedup_vs_decode": round(value / (1000.0 / decode_tpot_ms), 4),
+        "prefill_ms_per_prompt": round(1000.0 * t_prefill / P, 3),
+    }
+    sweep = {}
+    for k in [int(x) for x in args.k_sweep.split(",") if x.strip()]:
+        if k > cfg.max_k:
+            continue
+        sk = run_spec(sessions, truth, L, G, k, [DraftSource(cfg.seed, 20_000 + p, cfg.vocab, p_correct=args.p_correct)
+                                                 for p in range(P)], args.sweep_steps)
+        sb = sum(algorithmic_step_bytes(cfg, ke + 1, kv) for ke, _, kv in sk["steps"])
+        sweep[f"K={k}"] = {"verified_tok_s": round(metrics.verified_tok_s(sk["tokens"], sk["seconds"]), 1),
+                           "ms_per_step": round(1000.0 * sk["seconds"] / args.sweep_steps, 4),
+                           "acceptance_rate": round(metrics.acceptance_rate(sk["accepted"], sk["proposed"]), 4),
+                           "step_hbm_gbs": round(sb / sk["seconds"] / 1e9, 1),
+                           "verify_decode_mismatches": sk["mism"]}
+        log(f"[bench] K={k}: {sweep[f'K={k}']}")
+    extra["k_sweep"] = sweep
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t = time.perf_counter()
+        cpu = cpu_baseline(weights, prompts[0], args.cpu_tokens, st["steps"])
+        log(f"[bench] cpu baseline {cpu['value']:.4f} tok/s in {time.perf_counter() - t:.1f} s")
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "verified tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights and random-id prompts)",
+        "config": {"workload": f"{cfg.name}: Qwen3-8B-shaped target, {cfg.n_layers} layers, d {cfg.d_model}, "
+                               f"{cfg.n_q_heads}/{cfg.n_kv_heads} heads x {cfg.head_dim}, FFN {cfg.d_ff}, "
+                               f"vocab {cfg.vocab}; {P} prompts x {L} ids, {G} generated, K={args.k}, "
+                               f"per-position draft accuracy {args.p_correct}",
+                   "k": args.k, "prompts": P, "prompt_len": L, "gen_tokens": G, "p_correct": args.p_correct,
+                   "kv_capacity": cfg.max_ctx},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

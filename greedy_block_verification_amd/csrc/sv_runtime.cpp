@@ -1,0 +1,505 @@
+// Host runtime behind the sv_* C ABI: argument checks, context state
+// (kv_len, next_id, per-position greedy history), workspace layout, and the
+// launch sequence of one forward.  All arithmetic runs in sv_kernels.hip.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/sv.h"
+#include "sv_internal.h"
+
+using namespace sv;
+
+namespace {
+
+struct GemmPlan {
+  int N = 0, K = 0, S = 1, fmt = 0;
+};
+
+struct Layout {
+  size_t params = 0, x = 0, ss = 0, q = 0, attn_part = 0, attn_out = 0, act = 0, partial = 0, best = 0,
+         result = 0, logits = 0, rope = 0, total = 0;
+  int max_split = 1;
+};
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Split-K count of one weight matrix.  It depends only on the matrix shape,
+// never on the number of rows, so every row count shares one summation order.
+int choose_split(int N, int K, int unit) {
+  const int groups = N / kColGroup;
+  const int kc = K / unit;
+  int best = 1;
+  for (int s = 1; s * 4 <= kc; ++s) {
+    if (kc % (s * 4) != 0) continue;
+    if (kc / (s * 4) < 2 && s > 1) break;
+    best = s;
+    if (groups * s >= 768) break;
+  }
+  return best;
+}
+
+bool valid_config(const sv_config& c) {
+  if (c.n_layers < 1 || c.d_model < 256 || c.n_q_heads < 1 || c.n_kv_heads < 1 || c.d_ff < 256 || c.vocab < 64)
+    return false;
+  if (c.head_dim != 64 && c.head_dim != 128) return false;
+  if (c.n_q_heads % c.n_kv_heads != 0) return false;
+  if (c.d_model % 256 || (c.n_q_heads * c.head_dim) % 256 || c.d_ff % 256 || c.vocab % kColGroup) return false;
+  if ((c.n_kv_heads * c.head_dim) % 64) return false;
+  if (c.act != 0 && c.act != 1) return false;
+  if (c.weight_fmt != 0 && c.weight_fmt != 1) return false;
+  if (c.weight_fmt == 1 && (c.d_model % 512 || (c.n_q_heads * c.head_dim) % 512 || c.d_ff % 512)) return false;
+  if (c.page_size != kPage || c.max_ctx < kPage || c.max_ctx % kPage) return false;
+  if (c.max_k < 0 || c.max_k > kMaxRows - 1) return false;
+  if (!(c.rms_eps > 0.f) || !(c.rope_theta > 1.f)) return false;
+  return true;
+}
+
+struct Plans {
+  GemmPlan qkv, o, gu, d, lm;
+};
+
+Plans make_plans(const sv_config& c) {
+  const int qd = c.n_q_heads * c.head_dim, kd = c.n_kv_heads * c.head_dim;
+  const int unit = c.weight_fmt == 1 ? 128 : 32;
+  Plans p;
+  p.qkv = {qd + 2 * kd, c.d_model, choose_split(qd + 2 * kd, c.d_model, unit), c.weight_fmt};
+  p.o = {c.d_model, qd, choose_split(c.d_model, qd, unit), c.weight_fmt};
+  p.gu = {2 * c.d_ff, c.d_model, choose_split(2 * c.d_ff, c.d_model, unit), c.weight_fmt};
+  p.d = {c.d_model, c.d_ff, choose_split(c.d_model, c.d_ff, unit), c.weight_fmt};
+  p.lm = {c.vocab, c.d_model, 1, 0};
+  return p;
+}
+
+Layout make_layout(const sv_config& c, const Plans& p) {
+  Layout L;
+  const size_t R = kMaxRows;
+  const int qd = c.n_q_heads * c.head_dim;
+  L.max_split = (c.max_ctx + kAttnSplit - 1) / kAttnSplit;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  L.params = take(sizeof(int) * kParamInts);
+  L.x = take(R * c.d_model * 4);
+  L.ss = take(R * (c.d_model / 256) * 4);
+  L.q = take(R * qd * 4);
+  L.attn_part = take(R * c.n_q_heads * (size_t)L.max_split * (c.head_dim + 2) * 4);
+  L.attn_out = take(R * qd * 2);
+  L.act = take(R * c.d_ff * 2);
+  size_t part = 0;
+  for (const GemmPlan* g : {&p.qkv, &p.o, &p.gu, &p.d}) part = std::max(part, (size_t)g->S * g->N);
+  L.partial = take(part * R * 4);
+  L.best = take(R * (c.vocab / kColGroup) * 8);
+  L.result = take(sizeof(int) * (2 + kMaxRows));
+  L.logits = take(R * (size_t)c.vocab * 4);
+  L.rope = take((size_t)c.max_ctx * (c.head_dim / 2) * 8);
+  L.total = off;
+  return L;
+}
+
+size_t kv_pool_bytes_for(const sv_config& c, int n_pages) {
+  return (size_t)c.n_layers * n_pages * 2 * c.n_kv_heads * kPage * c.head_dim * 2;
+}
+
+}  // namespace
+
+struct sv_ctx {
+  sv_config cfg{};
+  sv_weights w{};
+  std::vector<sv_layer_weights> layers;
+  sv_buffers buf{};
+  hipStream_t stream = nullptr;
+  Plans plans;
+  Layout lay;
+  char* ws = nullptr;
+  int* h_params = nullptr;   // pinned
+  int* h_result = nullptr;   // pinned
+  int kv_len = 0;
+  int next_id = -1;
+  std::vector<int> hist;     // hist[p] = greedy id after positions 0..p
+  int store_logits = 0;
+  int last_rows = 0;
+  int last_stored_logits = 0;
+  int last_argmax[kMaxRows] = {};
+  // profiling: events around enabled kernel roles
+  static constexpr int kRoles = 6;
+  int prof_mask = 0;
+  std::vector<hipEvent_t> ev;          // pool, reused every forward
+  std::vector<std::pair<int, int>> ev_used;   // (role, index of start event)
+  size_t ev_next = 0;
+  double prof_ms[kRoles] = {};
+  int64_t prof_n[kRoles] = {};
+
+  template <class T>
+  T* at(size_t off) { return reinterpret_cast<T*>(ws + off); }
+};
+
+namespace {
+
+constexpr int kRoleAttn = 5;
+
+hipError_t prof_mark(sv_ctx* c, int role, bool start) {
+  if (!(c->prof_mask & (1 << role))) return hipSuccess;
+  if (c->ev_next >= c->ev.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return hipErrorOutOfMemory;
+    c->ev.push_back(e);
+  }
+  if (start) c->ev_used.push_back({role, (int)c->ev_next});
+  return hipEventRecord(c->ev[c->ev_next++], c->stream);
+}
+
+void prof_collect(sv_ctx* c) {
+  for (const auto& u : c->ev_used) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, c->ev[u.second], c->ev[u.second + 1]) == hipSuccess) {
+      c->prof_ms[u.first] += ms;
+      c->prof_n[u.first] += 1;
+    }
+  }
+  c->ev_used.clear();
+  c->ev_next = 0;
+}
+
+hipError_t gemm_timed(sv_ctx* c, const GemmArgs& g, int role) {
+  hipError_t e = prof_mark(c, role, true);
+  if (e == hipSuccess) e = launch_gemm(g, role, c->stream);
+  if (e == hipSuccess) e = prof_mark(c, role, false);
+  return e;
+}
+
+sv_status forward(sv_ctx* c, int M, const int* ids, int verify) {
+  const sv_config& cfg = c->cfg;
+  hipStream_t st = c->stream;
+  const int qd = cfg.n_q_heads * cfg.head_dim;
+  int* d_params = c->at<int>(c->lay.params);
+  c->h_params[0] = c->kv_len;
+  c->h_params[1] = M;
+  std::memcpy(c->h_params + 2, ids, sizeof(int) * M);
+  if (hipMemcpyAsync(d_params, c->h_params, sizeof(int) * (2 + M), hipMemcpyHostToDevice, st) != hipSuccess)
+    return SV_EDEVICE;
+
+  float* x = c->at<float>(c->lay.x);
+  float* ss = c->at<float>(c->lay.ss);
+  float* q = c->at<float>(c->lay.q);
+  float* partial = c->at<float>(c->lay.partial);
+  uint16_t* attn_out = c->at<uint16_t>(c->lay.attn_out);
+  uint16_t* act = c->at<uint16_t>(c->lay.act);
+  const float2* rope = c->at<const float2>(c->lay.rope);
+  uint16_t* kv = static_cast<uint16_t*>(c->buf.kv_pool);
+
+  hipError_t e = launch_embed(d_params, M, c->w.embed, cfg.vocab, cfg.d_model, x, ss, st);
+  if (e != hipSuccess) return SV_EDEVICE;
+
+  const int n_split = (c->kv_len + M + kAttnSplit - 1) / kAttnSplit;
+  for (int l = 0; l < cfg.n_layers && e == hipSuccess; ++l) {
+    const sv_layer_weights& L = c->layers[l];
+    GemmArgs g{};
+    g.M = M;
+    g.eps = cfg.rms_eps;
+    g.partial = partial;
+
+    // attention block
+    g.W = L.wqkv; g.Wscale = L.wqkv_scales; g.N = c->plans.qkv.N; g.K = c->plans.qkv.K; g.S = c->plans.qkv.S;
+    g.fmt = c->plans.qkv.fmt;
+    g.xf = x; g.ss = ss; g.gain = static_cast<const uint16_t*>(L.g_attn);
+    if ((e = gemm_timed(c, g, kRoleQkv)) != hipSuccess) break;
+    EpiArgs ep{};
+    ep.partial = partial; ep.S = g.S; ep.M = M; ep.N = g.N; ep.kind = kEpiQkv; ep.params = d_params;
+    ep.q_out = q; ep.kv_pool = kv; ep.page_table = c->buf.page_table; ep.n_pages = c->buf.n_pages; ep.layer = l;
+    ep.nq = cfg.n_q_heads; ep.nkv = cfg.n_kv_heads; ep.dh = cfg.head_dim; ep.rope = rope;
+    if ((e = launch_epilogue(ep, st)) != hipSuccess) break;
+    AttnArgs at{};
+    at.params = d_params; at.q = q; at.kv_pool = kv; at.page_table = c->buf.page_table; at.n_pages = c->buf.n_pages;
+    at.layer = l; at.nq = cfg.n_q_heads; at.nkv = cfg.n_kv_heads; at.dh = cfg.head_dim; at.M = M;
+    at.n_split = n_split; at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cfg.head_dim));
+    at.part = c->at<float>(c->lay.attn_part); at.out = attn_out;
+    if ((e = prof_mark(c, kRoleAttn, true)) != hipSuccess) break;
+    if ((e = launch_attention(at, st)) != hipSuccess) break;
+    if ((e = prof_mark(c, kRoleAttn, false)) != hipSuccess) break;
+    g.W = L.wo; g.Wscale = L.wo_scales; g.N = c->plans.o.N; g.K = c->plans.o.K; g.S = c->plans.o.S;
+    g.xb = attn_out;
+    if ((e = gemm_timed(c, g, kRoleO)) != hipSuccess) break;
+    ep = EpiArgs{};
+    ep.partial = partial; ep.S = g.S; ep.M = M; ep.N = g.N; ep.kind = kEpiResid; ep.params = d_params;
+    ep.x = x; ep.ss = ss;
+    if ((e = launch_epilogue(ep, st)) != hipSuccess) break;
+
+    // MLP block
+    g.W = L.wgu; g.Wscale = L.wgu_scales; g.N = c->plans.gu.N; g.K = c->plans.gu.K; g.S = c->plans.gu.S;
+    g.xf = x; g.ss = ss; g.gain = static_cast<const uint16_t*>(L.g_mlp);
+    if ((e = gemm_timed(c, g, kRoleGateUp)) != hipSuccess) break;
+    ep = EpiArgs{};
+    ep.partial = partial; ep.S = g.S; ep.M = M; ep.N = g.N; ep.kind = kEpiGlu; ep.params = d_params;
+    ep.act_out = act; ep.act = cfg.act;
+    if ((e = launch_epilogue(ep, st)) != hipSuccess) break;
+    g.W = L.wd; g.Wscale = L.wd_scales; g.N = c->plans.d.N; g.K = c->plans.d.K; g.S = c->plans.d.S;
+    g.xb = act;
+    if ((e = gemm_timed(c, g, kRoleDown)) != hipSuccess) break;
+    ep = EpiArgs{};
+    ep.partial = partial; ep.S = g.S; ep.M = M; ep.N = g.N; ep.kind = kEpiResid; ep.params = d_params;
+    ep.x = x; ep.ss = ss;
+    if ((e = launch_epilogue(ep, st)) != hipSuccess) break;
+  }
+  if (e != hipSuccess) return SV_EDEVICE;
+
+  // final norm + LM head + per-64-column argmax, then acceptance
+  GemmArgs g{};
+  g.M = M; g.eps = cfg.rms_eps; g.fmt = 0;
+  g.W = c->w.lm_head; g.N = c->plans.lm.N; g.K = c->plans.lm.K; g.S = 1;
+  g.xf = x; g.ss = ss; g.gain = static_cast<const uint16_t*>(c->w.g_final);
+  g.best = c->at<uint64_t>(c->lay.best);
+  g.logits = c->store_logits ? c->at<float>(c->lay.logits) : nullptr;
+  if (gemm_timed(c, g, kRoleLmHead) != hipSuccess) return SV_EDEVICE;
+  int* d_result = c->at<int>(c->lay.result);
+  if (launch_accept(d_params, M, verify, g.best, cfg.vocab / kColGroup, d_result, st) != hipSuccess)
+    return SV_EDEVICE;
+  if (hipMemcpyAsync(c->h_result, d_result, sizeof(int) * (2 + M), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return SV_EDEVICE;
+  if (hipStreamSynchronize(st) != hipSuccess) return SV_EDEVICE;
+  if (!c->ev_used.empty()) prof_collect(c);
+  c->last_rows = M;
+  c->last_stored_logits = c->store_logits;
+  for (int r = 0; r < M; ++r) c->last_argmax[r] = c->h_result[2 + r];
+  return SV_OK;
+}
+
+bool ids_ok(const sv_ctx* c, const int32_t* ids, int n) {
+  for (int i = 0; i < n; ++i)
+    if (ids[i] < 0 || ids[i] >= c->cfg.vocab) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sv_status_str(sv_status s) {
+  switch (s) {
+    case SV_OK: return "ok";
+    case SV_EINVAL: return "invalid argument";
+    case SV_ESTATE: return "call does not match context state";
+    case SV_ENOSPACE: return "KV capacity exceeded";
+    case SV_EDEVICE: return "HIP device error";
+    case SV_EUNSUPPORTED: return "unsupported configuration";
+  }
+  return "unknown status";
+}
+
+sv_status sv_query_sizes(const sv_config* cfg, int64_t* kv_pool_bytes, int64_t* workspace_bytes) {
+  if (!cfg || !valid_config(*cfg)) return SV_EINVAL;
+  const Plans p = make_plans(*cfg);
+  const Layout L = make_layout(*cfg, p);
+  if (kv_pool_bytes) *kv_pool_bytes = (int64_t)kv_pool_bytes_for(*cfg, cfg->max_ctx / kPage);
+  if (workspace_bytes) *workspace_bytes = (int64_t)L.total;
+  return SV_OK;
+}
+
+sv_status sv_packed_linear_bytes(int32_t fmt, int32_t n, int32_t k, int64_t* bytes, int64_t* scale_bytes) {
+  if (n <= 0 || k <= 0 || n % 16) return SV_EINVAL;
+  if (fmt == 0) {
+    if (k % 32) return SV_EINVAL;
+    if (bytes) *bytes = (int64_t)n * k * 2;
+    if (scale_bytes) *scale_bytes = 0;
+    return SV_OK;
+  }
+  if (fmt == 1) {
+    if (k % 128) return SV_EINVAL;
+    if (bytes) *bytes = (int64_t)n * k / 2;
+    if (scale_bytes) *scale_bytes = (int64_t)n * (k / 64) * 2;
+    return SV_OK;
+  }
+  return SV_EINVAL;
+}
+
+sv_status sv_pack_linear(int32_t fmt, const void* src0, const void* src0_scales, const void* src1,
+                         const void* src1_scales, int32_t n, int32_t k, void* dst, void* dst_scales, void* stream) {
+  if (!src0 || !dst) return SV_EINVAL;
+  if (sv_packed_linear_bytes(fmt, n, k, nullptr, nullptr) != SV_OK) return SV_EINVAL;
+  if (fmt == 1 && (!src0_scales || !dst_scales || (src1 && !src1_scales))) return SV_EINVAL;
+  if (launch_pack(fmt, src0, src0_scales, src1, src1_scales, n, k, dst, dst_scales, (hipStream_t)stream) !=
+      hipSuccess)
+    return SV_EDEVICE;
+  return SV_OK;
+}
+
+sv_status sv_create(const sv_config* cfg, const sv_weights* w, const sv_buffers* buf, void* stream, sv_ctx** out) {
+  if (!out) return SV_EINVAL;
+  *out = nullptr;
+  if (!cfg || !w || !buf || !valid_config(*cfg)) return SV_EINVAL;
+  if (!w->embed || !w->lm_head || !w->g_final || !w->layers) return SV_EINVAL;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const sv_layer_weights& L = w->layers[l];
+    if (!L.wqkv || !L.wo || !L.wgu || !L.wd || !L.g_attn || !L.g_mlp) return SV_EINVAL;
+    if (cfg->weight_fmt == 1 && (!L.wqkv_scales || !L.wo_scales || !L.wgu_scales || !L.wd_scales)) return SV_EINVAL;
+  }
+  const Plans p = make_plans(*cfg);
+  const Layout lay = make_layout(*cfg, p);
+  if (!buf->kv_pool || !buf->page_table || !buf->workspace) return SV_EINVAL;
+  if (buf->n_pages < 1 || buf->kv_pool_bytes < (int64_t)kv_pool_bytes_for(*cfg, buf->n_pages)) return SV_EINVAL;
+  if (buf->workspace_bytes < (int64_t)lay.total) return SV_EINVAL;
+  // Every logical page must map into the pool: a bad entry would address
+  // memory outside it.
+  const int n_logical = cfg->max_ctx / kPage;
+  std::vector<int32_t> pt(n_logical);
+  if (hipMemcpy(pt.data(), buf->page_table, sizeof(int32_t) * n_logical, hipMemcpyDeviceToHost) != hipSuccess)
+    return SV_EDEVICE;
+  for (int32_t v : pt)
+    if (v < 0 || v >= buf->n_pages) return SV_EINVAL;
+
+  sv_ctx* c = new (std::nothrow) sv_ctx();
+  if (!c) return SV_EDEVICE;
+  c->cfg = *cfg;
+  c->layers.assign(w->layers, w->layers + cfg->n_layers);
+  c->w = *w;
+  c->w.layers = c->layers.data();
+  c->buf = *buf;
+  c->stream = (hipStream_t)stream;
+  c->plans = p;
+  c->lay = lay;
+  c->ws = static_cast<char*>(buf->workspace);
+  c->hist.assign(cfg->max_ctx, -1);
+  if (hipHostMalloc((void**)&c->h_params, sizeof(int) * kParamInts, hipHostMallocDefault) != hipSuccess ||
+      hipHostMalloc((void**)&c->h_result, sizeof(int) * (2 + kMaxRows), hipHostMallocDefault) != hipSuccess) {
+    sv_destroy(c);
+    return SV_EDEVICE;
+  }
+  // RoPE table: angle pos * theta^(-2i/dh) in double, cos/sin rounded once to float.
+  const int half = cfg->head_dim / 2;
+  std::vector<float> tab((size_t)cfg->max_ctx * half * 2);
+  for (int pos = 0; pos < cfg->max_ctx; ++pos)
+    for (int i = 0; i < half; ++i) {
+      const double ang = (double)pos * std::pow((double)cfg->rope_theta, -2.0 * i / cfg->head_dim);
+      tab[((size_t)pos * half + i) * 2 + 0] = (float)std::cos(ang);
+      tab[((size_t)pos * half + i) * 2 + 1] = (float)std::sin(ang);
+    }
+  if (hipMemcpyAsync(c->ws + lay.rope, tab.data(), tab.size() * 4, hipMemcpyHostToDevice, c->stream) != hipSuccess ||
+      hipStreamSynchronize(c->stream) != hipSuccess) {
+    sv_destroy(c);
+    return SV_EDEVICE;
+  }
+  *out = c;
+  return SV_OK;
+}
+
+void sv_destroy(sv_ctx* c) {
+  if (!c) return;
+  for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
+  if (c->h_params) (void)hipHostFree(c->h_params);
+  if (c->h_result) (void)hipHostFree(c->h_result);
+  delete c;
+}
+
+int32_t sv_kv_len(const sv_ctx* c) { return c ? c->kv_len : -1; }
+int32_t sv_next_id(const sv_ctx* c) { return c ? c->next_id : -1; }
+
+sv_status sv_prefill(sv_ctx* c, const int32_t* ids, int32_t n, int32_t* next_id) {
+  if (!c || !ids || n < 1) return SV_EINVAL;
+  if (!ids_ok(c, ids, n)) return SV_EINVAL;
+  if ((int64_t)c->kv_len + n > c->cfg.max_ctx) return SV_ENOSPACE;
+  for (int off = 0; off < n; off += kMaxRows) {
+    const int m = std::min(kMaxRows, n - off);
+    const sv_status s = forward(c, m, ids + off, 0);
+    if (s != SV_OK) return s;
+    for (int r = 0; r < m; ++r) c->hist[c->kv_len + r] = c->h_result[2 + r];
+    c->kv_len += m;
+    c->next_id = c->h_result[1];
+  }
+  if (next_id) *next_id = c->next_id;
+  return SV_OK;
+}
+
+sv_status sv_decode_step(sv_ctx* c, int32_t token, int32_t* next_id) {
+  if (!c) return SV_EINVAL;
+  if (!ids_ok(c, &token, 1)) return SV_EINVAL;
+  if (c->kv_len + 1 > c->cfg.max_ctx) return SV_ENOSPACE;
+  const sv_status s = forward(c, 1, &token, 1);
+  if (s != SV_OK) return s;
+  c->hist[c->kv_len] = c->h_result[2];
+  c->kv_len += 1;
+  c->next_id = c->h_result[1];
+  if (next_id) *next_id = c->next_id;
+  return SV_OK;
+}
+
+sv_status sv_verify(sv_ctx* c, int32_t prefix_len, const int32_t* draft_ids, int32_t k, int32_t* n_accepted,
+                    int32_t* next_id) {
+  if (!c) return SV_EINVAL;
+  if (k < 0 || k > c->cfg.max_k || (k > 0 && !draft_ids)) return SV_EINVAL;
+  if (prefix_len != c->kv_len || c->next_id < 0) return SV_ESTATE;
+  if (k > 0 && !ids_ok(c, draft_ids, k)) return SV_EINVAL;
+  if ((int64_t)c->kv_len + k + 1 > c->cfg.max_ctx) return SV_ENOSPACE;
+  int rows[kMaxRows];
+  rows[0] = c->next_id;
+  for (int i = 0; i < k; ++i) rows[1 + i] = draft_ids[i];
+  const sv_status s = forward(c, k + 1, rows, 1);
+  if (s != SV_OK) return s;
+  const int n = c->h_result[0];
+  for (int r = 0; r <= n; ++r) c->hist[c->kv_len + r] = c->h_result[2 + r];
+  c->kv_len += n + 1;
+  c->next_id = c->h_result[1];
+  if (n_accepted) *n_accepted = n;
+  if (next_id) *next_id = c->next_id;
+  return SV_OK;
+}
+
+sv_status sv_kv_truncate(sv_ctx* c, int32_t new_len) {
+  if (!c) return SV_EINVAL;
+  if (new_len < 1 || new_len > c->kv_len) return SV_EINVAL;
+  c->kv_len = new_len;
+  c->next_id = c->hist[new_len - 1];
+  return SV_OK;
+}
+
+sv_status sv_set_debug(sv_ctx* c, int32_t store_logits) {
+  if (!c || (store_logits != 0 && store_logits != 1)) return SV_EINVAL;
+  c->store_logits = store_logits;
+  return SV_OK;
+}
+
+sv_status sv_get_logits(sv_ctx* c, int32_t row, float* host_dst, int32_t vocab) {
+  if (!c || !host_dst || vocab != c->cfg.vocab) return SV_EINVAL;
+  if (!c->last_stored_logits || c->last_rows == 0) return SV_ESTATE;
+  if (row < 0 || row >= c->last_rows) return SV_EINVAL;
+  const float* src = c->at<float>(c->lay.logits) + (size_t)row * vocab;
+  if (hipMemcpyAsync(host_dst, src, sizeof(float) * vocab, hipMemcpyDeviceToHost, c->stream) != hipSuccess ||
+      hipStreamSynchronize(c->stream) != hipSuccess)
+    return SV_EDEVICE;
+  return SV_OK;
+}
+
+sv_status sv_set_profile(sv_ctx* c, int32_t mask) {
+  if (!c || mask < 0 || mask >= (1 << sv_ctx::kRoles)) return SV_EINVAL;
+  c->prof_mask = mask;
+  return SV_OK;
+}
+
+sv_status sv_profile_read(const sv_ctx* c, int32_t role, double* total_ms, int64_t* launches) {
+  if (!c || role < 0 || role >= sv_ctx::kRoles) return SV_EINVAL;
+  if (total_ms) *total_ms = c->prof_ms[role];
+  if (launches) *launches = c->prof_n[role];
+  return SV_OK;
+}
+
+sv_status sv_profile_reset(sv_ctx* c) {
+  if (!c) return SV_EINVAL;
+  for (int r = 0; r < sv_ctx::kRoles; ++r) { c->prof_ms[r] = 0.0; c->prof_n[r] = 0; }
+  return SV_OK;
+}
+
+sv_status sv_last_argmax(const sv_ctx* c, int32_t* dst, int32_t* m) {
+  if (!c || !dst || !m) return SV_EINVAL;
+  if (c->last_rows == 0) return SV_ESTATE;
+  *m = c->last_rows;
+  for (int r = 0; r < c->last_rows; ++r) dst[r] = c->last_argmax[r];
+  return SV_OK;
+}
+
+}  // extern "C"

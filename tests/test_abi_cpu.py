@@ -1,0 +1,59 @@
+"""The C-ABI library loads and exports every symbol include/*.h declares (no GPU calls)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for h in os.listdir(os.path.join(ROOT, "include")):
+        if h.endswith(".h"):
+            txt = open(os.path.join(ROOT, "include", h)).read()
+            txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+            names |= set(re.findall(r"\b(sv_[a-z_0-9]+)\s*\(", txt))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    from greedy_block_verification_amd import binding as B
+    L = B.lib()
+    names = _declared()
+    assert len(names) >= 15
+    for n in sorted(names):
+        assert hasattr(L, n), n
+        assert n in B.SIGNATURES, f"binding lacks {n}"
+
+
+def test_host_only_entry_points():
+    from greedy_block_verification_amd import binding as B
+    from seeded_inputs import get_config
+    cfg = B.make_config(get_config("q8b"))
+    kv, ws = B.sv_query_sizes(cfg)
+    assert kv == 36 * 128 * 2 * 8 * 16 * 128 * 2          # 2048 positions of K and V, bf16
+    assert ws > 0
+    assert B.sv_packed_linear_bytes(0, 6144, 4096) == (6144 * 4096 * 2, 0)
+    assert B.sv_packed_linear_bytes(1, 2048, 1536) == (2048 * 1536 // 2, 2048 * 24 * 2)
+    bad = B.make_config(get_config("q8b"))
+    bad.page_size = 32
+    with pytest.raises(B.SvError) as e:
+        B.sv_query_sizes(bad)
+    assert e.value.status == B.SV_EINVAL
+    with pytest.raises(B.SvError):
+        B.sv_packed_linear_bytes(0, 10, 4096)
+    assert B.sv_status_str(B.SV_ENOSPACE) == "KV capacity exceeded"
+    # create rejects a bad config before touching the device
+    st = B.lib().sv_create(C.byref(bad), None, None, None, C.byref(C.c_void_p()))
+    assert st == B.SV_EINVAL
+
+
+def test_no_oracle_import_in_product_code():
+    pkg = os.path.join(ROOT, "greedy_block_verification_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in txt and "from oracle" not in txt, f

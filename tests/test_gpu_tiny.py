@@ -1,0 +1,286 @@
+"""GPU parity on the tiny 2-layer config, through the C ABI.
+
+* GPU vs oracle: per-row |dlogit| <= 3e-2 and equal argmax except where the
+  oracle's top-2 margin is under 3e-2 (flagged near-ties, counted).
+* GPU verify vs GPU decode: bit-identical logits and argmax for every row.
+* Cache histories (one-token commits, 9-row block commits, one prefill): equal
+  KV bits and equal verify logits.
+* Rollback at every index, observer mode, NaN-poisoned pool, permuted pages,
+  and argument errors.
+"""
+import copy
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+TOL = 3e-2
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    from greedy_block_verification_amd.session import DeviceModel
+    from seeded_inputs import generate_weights, get_config
+    assert torch.cuda.is_available()
+    w = generate_weights(get_config("tiny"))
+    return DeviceModel(w), w
+
+
+@pytest.fixture(scope="module")
+def orc(dev):
+    from oracle import Fp64Model
+    return Fp64Model(dev[1])
+
+
+def _sess(dev, **kw):
+    from greedy_block_verification_amd.session import Session
+    return Session(dev[0], **kw)
+
+
+def _bits(a):
+    return np.asarray(a, dtype=np.float32).view(np.uint32)
+
+
+def _prompt(n=32, idx=0):
+    from seeded_inputs import prompt_ids
+    return prompt_ids(1, idx, n, 2048).tolist()
+
+
+def test_prefill_rows_match_oracle(dev, orc):
+    from oracle import forward_cacheless
+    from oracle.spec import greedy_id, top2_margin
+    ids = _prompt(32)
+    s = _sess(dev)
+    s.set_debug(True)
+    nx = s.prefill(ids)
+    ref = forward_cacheless(orc, ids)
+    flips = 0
+    worst = 0.0
+    for r in range(32):
+        lg = s.logits(r).astype(np.float64)
+        worst = max(worst, float(np.max(np.abs(lg - ref[r]))))
+        if int(np.argmax(lg)) != greedy_id(ref[r]):
+            assert top2_margin(ref[r]) < TOL
+            flips += 1
+    print(f"tiny prefill: max|dlogit| = {worst:.3e}, flips at flagged near-ties = {flips}")
+    assert worst <= TOL
+    assert nx == s.last_argmax()[-1]
+
+
+@pytest.mark.parametrize("k", [0, 1, 2, 3, 4, 7, 8])
+def test_verify_rows_bitwise_equal_decode(dev, k):
+    rng = np.random.default_rng(100 + k)
+    ids = _prompt(31, 1)
+    a = _sess(dev)
+    b = _sess(dev)
+    a.set_debug(True)
+    b.set_debug(True)
+    nx = a.prefill(ids)
+    assert b.prefill(ids) == nx
+    drafts = rng.integers(0, 2048, k).tolist()
+    rows = [nx] + drafts
+    dec_logits, dec_arg = [], []
+    for t in rows:
+        dec_arg.append(a.decode_step(t))
+        dec_logits.append(a.logits(0))
+    n, nx2 = b.verify(drafts)
+    ver_arg = b.last_argmax()
+    assert ver_arg == dec_arg
+    for r in range(k + 1):
+        np.testing.assert_array_equal(_bits(b.logits(r)), _bits(dec_logits[r]))
+    # acceptance is the longest prefix of drafts equal to the row argmax
+    exp_n = 0
+    while exp_n < k and drafts[exp_n] == dec_arg[exp_n]:
+        exp_n += 1
+    assert n == exp_n and nx2 == dec_arg[exp_n]
+    assert b.kv_len == len(ids) + n + 1
+
+
+@pytest.mark.parametrize("pattern", ["all_accept", "mismatch_at_2", "mismatch_at_0"])
+def test_spec_loop_against_oracle(dev, orc, pattern):
+    from oracle import TokenDecoder
+    from oracle.spec import greedy_id, prefill, top2_margin
+    from seeded_inputs import DraftSource
+    ids = _prompt(32)
+    s = _sess(dev)
+    s.prefill(ids)
+    od = TokenDecoder(orc)            # mirrors the GPU's committed ids
+    prefill(od, ids)
+    src = DraftSource(1, 0, 2048, pattern=pattern)
+    planted = {"all_accept": 4, "mismatch_at_2": 2, "mismatch_at_0": 0}[pattern]
+    committed, off_plan = [], 0
+    while len(committed) < 64:
+        k_eff = min(4, 64 - len(committed) - 1)
+        cur = s.next_id
+        # drafts: the oracle's greedy continuation of the GPU's prefix + cur
+        probe = copy.deepcopy(od)
+        truth, t = [], cur
+        for _ in range(k_eff):
+            t = greedy_id(probe.decode(t))
+            truth.append(t)
+        drafts = src.window(truth, k_eff) if k_eff > 0 else []
+        n, _ = s.verify(drafts)
+        off_plan += n != min(planted, k_eff)
+        new = [cur] + drafts[:n]
+        for tok in new:
+            od.decode(tok)
+        committed += new
+    assert len(committed) == 64
+    # teacher-forced: each committed id is the oracle's greedy id after the
+    # GPU's own prefix, unless the oracle's top-2 margin there is under TOL
+    od2 = TokenDecoder(orc)
+    prefill_logits = None
+    for t in ids:
+        prefill_logits = od2.decode(t)
+    prev, flips = prefill_logits, 0
+    for tok in committed:
+        if tok != greedy_id(prev):
+            assert top2_margin(prev) < TOL
+            flips += 1
+        prev = od2.decode(tok)
+    print(f"{pattern}: 64 committed, flagged flips {flips}, windows off the planted index {off_plan}")
+    assert off_plan <= flips
+
+
+def test_cache_histories_bitwise(dev):
+    ids = _prompt(87, 2)
+    s1, s2, s3 = _sess(dev), _sess(dev), _sess(dev)
+    nx1 = None
+    for t in ids:
+        nx1 = s1.decode_step(t)
+    nx2 = None
+    for i in range(0, 87, 9):
+        nx2 = s2.prefill(ids[i:i + 9])
+    nx3 = s3.prefill(ids)
+    assert nx1 == nx2 == nx3
+    kv1, kv2, kv3 = s1.kv_positions(87), s2.kv_positions(87), s3.kv_positions(87)
+    np.testing.assert_array_equal(kv1, kv2)
+    np.testing.assert_array_equal(kv1, kv3)
+    rng = np.random.default_rng(7)
+    for k in (8,):
+        drafts = rng.integers(0, 2048, k).tolist()
+        outs = []
+        for s in (s1, s2, s3):
+            s.set_debug(True)
+            s.verify(drafts)
+            outs.append([_bits(s.logits(r)) for r in range(k + 1)])
+        for r in range(k + 1):
+            np.testing.assert_array_equal(outs[0][r], outs[1][r])
+            np.testing.assert_array_equal(outs[0][r], outs[2][r])
+
+
+@pytest.mark.parametrize("reject_at", range(8))
+def test_rollback_at_every_index_then_reverify(dev, reject_at):
+    ids = _prompt(40, 3)
+    ref = _sess(dev)
+    nx = ref.prefill(ids)
+    truth = [nx]
+    for _ in range(14):
+        truth.append(ref.decode_step(truth[-1]))
+    # truth[i + 1] is the greedy id after ids + truth[0..i]
+    s = _sess(dev)
+    s.prefill(ids)
+    drafts = truth[1:9]
+    drafts[reject_at] = (truth[reject_at + 1] + 1) % 2048
+    n, nxt = s.verify(drafts)
+    assert n == reject_at and nxt == truth[reject_at + 1]
+    assert s.kv_len == 40 + reject_at + 1
+    # re-verify with correct drafts: rows must equal a one-token-built session bit for bit
+    s.set_debug(True)
+    k2 = 4
+    dr2 = truth[reject_at + 2: reject_at + 2 + k2]
+    assert len(dr2) == k2
+    n2, _ = s.verify(dr2)
+    assert n2 == k2
+    chk = _sess(dev)
+    chk.set_debug(True)
+    chk.prefill(ids)
+    for t in truth[:reject_at + 1]:
+        chk.decode_step(t)
+    for r, t in enumerate([truth[reject_at + 1]] + dr2):
+        chk.decode_step(t)
+        np.testing.assert_array_equal(_bits(chk.logits(0)), _bits(s.logits(r)))
+    np.testing.assert_array_equal(chk.kv_positions(chk.kv_len), s.kv_positions(s.kv_len))
+
+
+def test_truncate_restores_next_id_and_abort_retry(dev):
+    ids = _prompt(20, 4)
+    s = _sess(dev)
+    s.prefill(ids)
+    hist = [s.next_id]
+    for _ in range(6):
+        hist.append(s.decode_step(hist[-1]))
+    for new_len in (26, 23, 20, 1):
+        s.truncate(new_len)
+        assert s.kv_len == new_len
+        if new_len >= 20:
+            assert s.next_id == hist[new_len - 20]
+    # retry from the shortest prefix gives a fresh-cache result
+    fresh = _sess(dev)
+    assert fresh.prefill(ids[:1]) == s.next_id
+
+
+def test_observer_mode_does_not_change_argmax(dev):
+    rng = np.random.default_rng(11)
+    ids = _prompt(33, 5)
+    drafts = rng.integers(0, 2048, 8).tolist()
+    a, b = _sess(dev), _sess(dev)
+    b.set_debug(True)
+    a.prefill(ids)
+    b.prefill(ids)
+    ra, rb = a.verify(drafts), b.verify(drafts)
+    assert ra == rb and a.last_argmax() == b.last_argmax()
+
+
+def test_poisoned_pool_and_permuted_pages(dev):
+    rng = np.random.default_rng(12)
+    ids = _prompt(50, 6)
+    n_pages = 256 // 16
+    perm = rng.permutation(n_pages)
+    a = _sess(dev)
+    b = _sess(dev, page_perm=perm, poison=True)
+    a.set_debug(True)
+    b.set_debug(True)
+    assert a.prefill(ids) == b.prefill(ids)
+    for _ in range(3):
+        drafts = rng.integers(0, 2048, 5).tolist()
+        assert a.verify(drafts) == b.verify(drafts)
+        for r in range(a.m.cfg.max_k):
+            try:
+                la = a.logits(r)
+            except Exception:
+                break
+            lb = b.logits(r)
+            assert np.all(np.isfinite(lb))
+            np.testing.assert_array_equal(_bits(la), _bits(lb))
+        assert a.kv_len == b.kv_len
+    np.testing.assert_array_equal(a.kv_positions(a.kv_len), b.kv_positions(b.kv_len))
+
+
+def test_argument_errors_leave_state_untouched(dev):
+    from greedy_block_verification_amd import binding as B
+    s = _sess(dev)
+    ids = _prompt(10, 7)
+    s.prefill(ids)
+    kv, nx = s.kv_len, s.next_id
+    with pytest.raises(B.SvError) as e:
+        B.sv_verify(s.ctx, kv - 1, [1, 2])
+    assert e.value.status == B.SV_ESTATE
+    with pytest.raises(B.SvError) as e:
+        s.verify([1, 2048])
+    assert e.value.status == B.SV_EINVAL
+    with pytest.raises(B.SvError) as e:
+        s.verify([0] * 9)
+    assert e.value.status == B.SV_EINVAL
+    with pytest.raises(B.SvError) as e:
+        s.truncate(0)
+    assert e.value.status == B.SV_EINVAL
+    with pytest.raises(B.SvError) as e:
+        s.prefill([0] * 300)
+    assert e.value.status == B.SV_ENOSPACE
+    with pytest.raises(B.SvError) as e:
+        s.decode_step(-1)
+    assert e.value.status == B.SV_EINVAL
+    assert s.kv_len == kv and s.next_id == nx
