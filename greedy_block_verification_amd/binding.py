@@ -52,8 +52,8 @@ SIGNATURES = {
     "sv_query_sizes": (C.c_int, [C.POINTER(sv_config), C.POINTER(C.c_int64), C.POINTER(C.c_int64)]),
     "sv_packed_linear_bytes": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int64),
                                          C.POINTER(C.c_int64)]),
-    "sv_pack_linear": (C.c_int, [C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
-                                 C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "sv_pack_linear": (C.c_int, [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                 C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
     "sv_create": (C.c_int, [C.POINTER(sv_config), C.POINTER(sv_weights), C.POINTER(sv_buffers), C.c_void_p,
                             C.POINTER(C.c_void_p)]),
     "sv_destroy": (None, [C.c_void_p]),
@@ -122,9 +122,9 @@ def sv_packed_linear_bytes(fmt: int, n: int, k: int):
     return b.value, s.value
 
 
-def sv_pack_linear(fmt, src0, src0_scales, src1, src1_scales, n, k, dst, dst_scales, stream):
-    _check(lib().sv_pack_linear(fmt, src0, src0_scales, src1, src1_scales, n, k, dst, dst_scales, stream),
-           "sv_pack_linear")
+def sv_pack_linear(fmt, layout, src0, src0_scales, src1, src1_scales, n, k, head_dim, dst, dst_scales, stream):
+    _check(lib().sv_pack_linear(fmt, layout, src0, src0_scales, src1, src1_scales, n, k, head_dim, dst, dst_scales,
+                                stream), "sv_pack_linear")
 
 
 def sv_create(cfg: sv_config, weights: sv_weights, buffers: sv_buffers, stream) -> int:

@@ -86,10 +86,10 @@ __device__ __forceinline__ float block_sum256(float v, float* lds4) {
 }
 
 // ------------------------------------------------------------ packed weights
-// bf16 tile: 16 outputs x 32 inputs = 1 KiB, stored in MFMA operand order:
-// lane l = g*16 + i holds outputs (tile*16 + i), inputs (chunk*32 + 8g .. +7)
-// as one 16-byte vector at byte 16*l.  Tiles are [n_tile][k_chunk], so one
-// wave streaming a tile row reads contiguous KiBs.
+// bf16 tile chunk: 16 outputs x 32 inputs = 1 KiB, stored in MFMA operand
+// order: lane l = g*16 + i holds outputs (tile*16 + i), inputs (chunk*32 +
+// 8g .. +7) as one 16-byte vector at byte 16*l.  Chunks are stored
+// tile-major ([n_tile][k_chunk]).
 //
 // int4 tile: 16 outputs x 128 inputs (two scale groups of 64) = 1 KiB of
 // codes; lane l's 16 bytes hold 32 nibbles c = 0..31 for input
@@ -97,12 +97,22 @@ __device__ __forceinline__ float block_sum256(float v, float* lds4) {
 // byte b).  Scales: per tile 64 B = [group 0..1][16 outputs] bf16.
 
 // ------------------------------------------------------------ skinny GEMM
-// Y[r][n] = sum_k B[r][k] * W[n][k] for r < M.  Workgroup = 4 waves on one
-// 64-output group (4 tiles); the S*4 (split, wave) slices of K are fixed per
-// matrix.  Each wave runs its chunks in ascending order through one MFMA
-// accumulator chain per (row tile, output tile); the 4 wave partials are added
-// in wave order; split partials are added in split order by the epilogue.
-// The row count only sets how many row tiles are computed.
+// Y[r][n] = sum_k B[r][k] * W[n][k] for r < M.  An *item* is one packed
+// output tile (16 outputs) over the whole K.  A workgroup of NW waves takes
+// items blockIdx.x, blockIdx.x + gridDim.x, ...; its waves split K into NW
+// contiguous slices (fixed per matrix).  Each wave runs its chunks in
+// ascending order through one MFMA accumulator chain per row tile; the NW
+// wave partials are added in wave order through LDS.  The row count only
+// sets how many row tiles are computed, and no value crosses workgroups, so a
+// row's result never depends on M.  Weights are requested before anything
+// else, the normalised activations of a wave's K slice are built once per
+// workgroup (kept in registers), and the next item's weights are in flight
+// while the current item is reduced and finished.  Epilogue per role:
+//   QKV      tile = 8 dims + their RoPE partners (+ dh/2): RoPE, K/V into the
+//            paged cache (bf16), q (bf16) to the workspace
+//   O, down  residual add, per-16-column sum of squares for RMSNorm
+//   gate/up  tile = 8 gate + 8 up outputs of the same features: act(g) * u
+//   LM head  per-16-column (max logit, lowest id), optional fp32 logits
 
 template <int BM>
 __device__ __forceinline__ uint4 load_b(const GemmArgs& a, int r, int k0, float inv) {
@@ -138,408 +148,529 @@ __device__ __forceinline__ uint4 codes8(uint32_t w) {
                     pack2(code_bf16((w >> 24) & 15u), code_bf16((w >> 28) & 15u)));
 }
 
-template <int TM, int BM, int OUT, int TAG>
-__global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
-  __shared__ f32x4 red[4][4][64];
-  __shared__ uint64_t bestw[4][16];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int ng = blockIdx.x, s = blockIdx.y;
-  const int KC = a.K >> 5;
-  const int cpw = KC / (a.S * 4);
-  const int kc0 = (s * 4 + wave) * cpw;
-  const int j = lane & 15, g = lane >> 4;
-
-  float inv[TM];
-#pragma unroll
-  for (int rt = 0; rt < TM; ++rt) {
-    inv[rt] = 0.f;
-    if (BM == kBNorm) {
-      const int r = rt * 16 + j;
-      if (r < a.M) {
-        const int nsl = a.K >> 8;
-        float sum = a.ss[(size_t)r * nsl];
-        for (int c = 1; c < nsl; ++c) sum = sum + a.ss[(size_t)r * nsl + c];
-        inv[rt] = 1.0f / sqrtf(sum / (float)a.K + a.eps);
-      }
-    }
-  }
-
-  f32x4 acc[TM][4];
-#pragma unroll
-  for (int rt = 0; rt < TM; ++rt)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) acc[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const uint4* Wt = reinterpret_cast<const uint4*>(a.W) + (size_t)(ng * 4) * KC * 64 + lane;
-#pragma unroll 2
-  for (int c = 0; c < cpw; ++c) {
-    const int kc = kc0 + c;
-    uint4 A[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) A[t] = ld_stream(Wt + ((size_t)t * KC + kc) * 64);
-#pragma unroll
-    for (int rt = 0; rt < TM; ++rt) {
-      const int r = rt * 16 + j;
-      uint4 B = make_uint4(0u, 0u, 0u, 0u);
-      if (r < a.M) B = load_b<BM>(a, r, kc * 32 + g * 8, inv[rt]);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc[rt][t] = mfma16x16x32(A[t], B, acc[rt][t]);
-    }
-  }
-
-#pragma unroll
-  for (int rt = 0; rt < TM; ++rt) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) red[wave][t][lane] = acc[rt][t];
-    __syncthreads();
-    // Thread (wave w, lane) finishes output tile w: wave partials in order.
-    f32x4 v = red[0][wave][lane];
-    const f32x4 v1 = red[1][wave][lane], v2 = red[2][wave][lane], v3 = red[3][wave][lane];
-    v.x = v.x + v1.x; v.y = v.y + v1.y; v.z = v.z + v1.z; v.w = v.w + v1.w;
-    v.x = v.x + v2.x; v.y = v.y + v2.y; v.z = v.z + v2.z; v.w = v.w + v2.w;
-    v.x = v.x + v3.x; v.y = v.y + v3.y; v.z = v.z + v3.z; v.w = v.w + v3.w;
-    // v[i] = Y[r = rt*16 + j][n = (ng*4 + wave)*16 + 4g + i]
-    const int r = rt * 16 + j;
-    const int n0 = (ng * 4 + wave) * 16 + 4 * g;
-    if (OUT == kOutPartial) {
-      if (r < a.M)
-        *reinterpret_cast<float4*>(a.partial + ((size_t)s * a.M + r) * a.N + n0) = make_float4(v.x, v.y, v.z, v.w);
-    } else {
-      if (a.logits != nullptr && r < a.M)
-        *reinterpret_cast<float4*>(a.logits + (size_t)r * a.N + n0) = make_float4(v.x, v.y, v.z, v.w);
-      uint64_t b = argmax_key(v.x, n0);
-      b = umax64(b, argmax_key(v.y, n0 + 1));
-      b = umax64(b, argmax_key(v.z, n0 + 2));
-      b = umax64(b, argmax_key(v.w, n0 + 3));
-      b = umax64(b, __shfl_xor(b, 16));
-      b = umax64(b, __shfl_xor(b, 32));
-      if (g == 0) bestw[wave][j] = b;
-      __syncthreads();
-      if (threadIdx.x < 16) {
-        const int rr = rt * 16 + threadIdx.x;
-        const uint64_t bb = umax64(umax64(bestw[0][threadIdx.x], bestw[1][threadIdx.x]),
-                                   umax64(bestw[2][threadIdx.x], bestw[3][threadIdx.x]));
-        if (rr < a.M) a.best[(size_t)rr * (a.N >> 6) + ng] = bb;
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// int4 weights: per (row tile, output tile) and per scale group, two MFMAs
-// over the group's 64 inputs start from zero; the group sum is then scaled
-// by the fp32 group scale and added to the running fp32 sum in group order.
-template <int TM, int BM, int OUT, int TAG>
-__global__ __launch_bounds__(256) void k_gemm_int4(GemmArgs a) {
-  __shared__ f32x4 red[4][4][64];
-  __shared__ uint64_t bestw[4][16];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int ng = blockIdx.x, s = blockIdx.y;
-  const int KT = a.K >> 7;                 // 128-input tiles
-  const int tpw = KT / (a.S * 4);
-  const int kt0 = (s * 4 + wave) * tpw;
-  const int j = lane & 15, g = lane >> 4;
-
-  float inv[TM];
-#pragma unroll
-  for (int rt = 0; rt < TM; ++rt) {
-    inv[rt] = 0.f;
-    if (BM == kBNorm) {
-      const int r = rt * 16 + j;
-      if (r < a.M) {
-        const int nsl = a.K >> 8;
-        float sum = a.ss[(size_t)r * nsl];
-        for (int c = 1; c < nsl; ++c) sum = sum + a.ss[(size_t)r * nsl + c];
-        inv[rt] = 1.0f / sqrtf(sum / (float)a.K + a.eps);
-      }
-    }
-  }
-
-  f32x4 acc[TM][4];
-#pragma unroll
-  for (int rt = 0; rt < TM; ++rt)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) acc[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const uint4* Wt = reinterpret_cast<const uint4*>(a.W) + (size_t)(ng * 4) * KT * 64 + lane;
-  const uint2* St = reinterpret_cast<const uint2*>(a.Wscale) + (size_t)(ng * 4) * KT * 8 + g;
-  for (int c = 0; c < tpw; ++c) {
-    const int kt = kt0 + c;
-    uint4 Q[4];
-    uint2 SC[4][2];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      Q[t] = ld_stream(Wt + ((size_t)t * KT + kt) * 64);
-      const uint2* sp = St + ((size_t)t * KT + kt) * 8;
-      SC[t][0] = sp[0];
-      SC[t][1] = sp[4];
-    }
-#pragma unroll
-    for (int gq = 0; gq < 2; ++gq) {
-      uint4 Bv[TM][2];
-#pragma unroll
-      for (int rt = 0; rt < TM; ++rt) {
-        const int r = rt * 16 + j;
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch) {
-          Bv[rt][ch] = make_uint4(0u, 0u, 0u, 0u);
-          if (r < a.M) Bv[rt][ch] = load_b<BM>(a, r, kt * 128 + gq * 64 + ch * 32 + g * 8, inv[rt]);
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint32_t w0 = gq == 0 ? Q[t].x : Q[t].z;
-        const uint32_t w1 = gq == 0 ? Q[t].y : Q[t].w;
-        const uint4 A0 = codes8(w0), A1 = codes8(w1);
-        const float s0 = bf2f((uint16_t)(SC[t][gq].x & 0xffffu)), s1 = bf2f((uint16_t)(SC[t][gq].x >> 16));
-        const float s2 = bf2f((uint16_t)(SC[t][gq].y & 0xffffu)), s3 = bf2f((uint16_t)(SC[t][gq].y >> 16));
-#pragma unroll
-        for (int rt = 0; rt < TM; ++rt) {
-          f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
-          p = mfma16x16x32(A0, Bv[rt][0], p);
-          p = mfma16x16x32(A1, Bv[rt][1], p);
-          acc[rt][t].x = fmaf(s0, p.x, acc[rt][t].x);
-          acc[rt][t].y = fmaf(s1, p.y, acc[rt][t].y);
-          acc[rt][t].z = fmaf(s2, p.z, acc[rt][t].z);
-          acc[rt][t].w = fmaf(s3, p.w, acc[rt][t].w);
-        }
-      }
-    }
-  }
-
-#pragma unroll
-  for (int rt = 0; rt < TM; ++rt) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) red[wave][t][lane] = acc[rt][t];
-    __syncthreads();
-    f32x4 v = red[0][wave][lane];
-    const f32x4 v1 = red[1][wave][lane], v2 = red[2][wave][lane], v3 = red[3][wave][lane];
-    v.x = v.x + v1.x; v.y = v.y + v1.y; v.z = v.z + v1.z; v.w = v.w + v1.w;
-    v.x = v.x + v2.x; v.y = v.y + v2.y; v.z = v.z + v2.z; v.w = v.w + v2.w;
-    v.x = v.x + v3.x; v.y = v.y + v3.y; v.z = v.z + v3.z; v.w = v.w + v3.w;
-    const int r = rt * 16 + j;
-    const int n0 = (ng * 4 + wave) * 16 + 4 * g;
-    if (OUT == kOutPartial) {
-      if (r < a.M)
-        *reinterpret_cast<float4*>(a.partial + ((size_t)s * a.M + r) * a.N + n0) = make_float4(v.x, v.y, v.z, v.w);
-    }
-    __syncthreads();
-  }
-}
-
-// TAG only names the weight matrix (qkv, o, gate/up, down, LM head) so each
-// role is a separate kernel symbol in profiles; the code is the same.
-template <int BM, int OUT, int TAG>
-static hipError_t gemm_dispatch(const GemmArgs& a, hipStream_t st) {
-  const dim3 grid(a.N / kColGroup, a.S), block(256);
-  const int tm = (a.M + 15) / 16;
-  if (a.fmt == 1) {
-    if (OUT != kOutPartial) return hipErrorInvalidValue;
-    switch (tm) {
-      case 1: hipLaunchKernelGGL((k_gemm_int4<1, BM, OUT, TAG>), grid, block, 0, st, a); break;
-      case 2: hipLaunchKernelGGL((k_gemm_int4<2, BM, OUT, TAG>), grid, block, 0, st, a); break;
-      case 3: hipLaunchKernelGGL((k_gemm_int4<3, BM, OUT, TAG>), grid, block, 0, st, a); break;
-      case 4: hipLaunchKernelGGL((k_gemm_int4<4, BM, OUT, TAG>), grid, block, 0, st, a); break;
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    switch (tm) {
-      case 1: hipLaunchKernelGGL((k_gemm_bf16<1, BM, OUT, TAG>), grid, block, 0, st, a); break;
-      case 2: hipLaunchKernelGGL((k_gemm_bf16<2, BM, OUT, TAG>), grid, block, 0, st, a); break;
-      case 3: hipLaunchKernelGGL((k_gemm_bf16<3, BM, OUT, TAG>), grid, block, 0, st, a); break;
-      case 4: hipLaunchKernelGGL((k_gemm_bf16<4, BM, OUT, TAG>), grid, block, 0, st, a); break;
-      default: return hipErrorInvalidValue;
-    }
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_gemm(const GemmArgs& a, int role, hipStream_t st) {
-  if (a.M < 1 || a.M > kMaxRows || a.N % kColGroup != 0) return hipErrorInvalidValue;
-  switch (role) {
-    case kRoleQkv: return gemm_dispatch<kBNorm, kOutPartial, kRoleQkv>(a, st);
-    case kRoleO: return gemm_dispatch<kBBf16, kOutPartial, kRoleO>(a, st);
-    case kRoleGateUp: return gemm_dispatch<kBNorm, kOutPartial, kRoleGateUp>(a, st);
-    case kRoleDown: return gemm_dispatch<kBBf16, kOutPartial, kRoleDown>(a, st);
-    case kRoleLmHead: return gemm_dispatch<kBNorm, kOutArgmax, kRoleLmHead>(a, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-// ------------------------------------------------------------ split-K epilogues
-// One workgroup owns 256 consecutive outputs (whole heads; whole gate/up tile
-// pairs) and walks the rows.  Split partials are summed in split order.
 __device__ __forceinline__ float act_fn(float x, int act) {
   if (act == 0) return x / (1.0f + expf(-x));
   const float c = 0.7978845608028654f;  // sqrt(2/pi)
   return 0.5f * x * (1.0f + tanhf(c * (x + 0.044715f * (x * x * x))));
 }
 
-__global__ __launch_bounds__(256) void k_epilogue(EpiArgs a) {
-  __shared__ float y[kEpiCols];
-  __shared__ float red4[4];
-  const int t = threadIdx.x;
-  const int n = blockIdx.x * kEpiCols + t;
-  const bool live = n < a.N;
-  const int kv_len = a.params[0];
-  for (int r = 0; r < a.M; ++r) {
+constexpr int kMaxWaves = 16;
+constexpr int kBatch = 8;       // chunks (1 KiB of weights each) one wave keeps in flight
+constexpr int kCacheB = 8;      // most chunks per wave whose activations stay in registers
+
+struct GemmShared {
+  f32x4 red[kMaxWaves][64];   // wave partials of one row tile
+  float y[kMaxRows][16];      // finished outputs of the item
+  float inv[kMaxRows];        // 1 / rms of each row (kBNorm)
+};
+
+// 1 / sqrt(mean(x^2) + eps) per row from the per-16-column sums of squares:
+// one wave per row, each lane adds its slices in order, then a butterfly.
+template <int BM>
+__device__ __forceinline__ void rows_inv_rms(const GemmArgs& a, GemmShared& sh, int wave, int lane, int nw) {
+  if (BM != kBNorm) return;
+  const int nsl = a.K >> 4;
+  for (int r = wave; r < a.M; r += nw) {
+    const float* p = a.ss + (size_t)r * nsl;
     float v = 0.f;
-    if (live) {
-      v = a.partial[(size_t)r * a.N + n];
-      for (int s = 1; s < a.S; ++s) v = v + a.partial[((size_t)s * a.M + r) * a.N + n];
-    }
-    if (a.kind == kEpiResid) {
-      float xn = 0.f;
-      if (live) {
-        xn = a.x[(size_t)r * a.N + n] + v;
-        a.x[(size_t)r * a.N + n] = xn;
+    for (int i = lane; i < nsl; i += 64) v = v + p[i];
+    v = wave_sum(v);
+    if (lane == 0) sh.inv[r] = 1.0f / sqrtf(v / (float)a.K + a.eps);
+  }
+  __syncthreads();
+}
+
+// Epilogue on the finished 16 columns of item (tile) T.
+template <int ROLE>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, GemmShared& sh, int T) {
+  for (int idx = threadIdx.x; idx < a.M * 16; idx += blockDim.x) {
+    const int r = idx >> 4, c = idx & 15;
+    const float y = sh.y[r][c];
+    if (ROLE == kRoleO || ROLE == kRoleDown) {
+      const int n = T * 16 + c;
+      const size_t xi = (size_t)r * a.N + n;
+      const float xn = a.x[xi] + y;
+      a.x[xi] = xn;
+      float sq = xn * xn;
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) sq += __shfl_xor(sq, o);
+      if (c == 0) a.ss_out[(size_t)r * (a.N >> 4) + T] = sq;
+    } else if (ROLE == kRoleGateUp) {               // [gate 8 | up 8] of features 8T..8T+7
+      if (c < 8) a.act_out[(size_t)r * (a.N >> 1) + T * 8 + c] = f2bf(act_fn(y, a.act) * sh.y[r][c + 8]);
+    } else if (ROLE == kRoleQkv) {                  // [dims 8s+i | half + 8s + i], i < 8
+      const int half = a.dh >> 1;
+      const int gph = half >> 3;
+      const int hh = T / gph, sb = T % gph;
+      const bool lo = c < 8;
+      const int i = 8 * sb + (c & 7);
+      const int d = lo ? i : half + i;
+      const int pos = a.params[0] + r;
+      float out = y;
+      if (hh < a.nq + a.nkv) {
+        const float2 cs = a.rope[(size_t)pos * half + i];
+        const float partner = sh.y[r][c ^ 8];
+        out = lo ? (y * cs.x - partner * cs.y) : (y * cs.x + partner * cs.y);
       }
-      const float sq = block_sum256(xn * xn, red4);
-      if (t == 0) a.ss[(size_t)r * (a.N >> 8) + blockIdx.x] = sq;
-    } else if (a.kind == kEpiGlu) {
-      y[t] = v;
-      __syncthreads();
-      if (t < kEpiCols / 2) {
-        const int b = t >> 4, i = t & 15;
-        const int f = blockIdx.x * (kEpiCols / 2) + t;
-        if (f < (a.N >> 1)) {
-          const float gate = y[32 * b + i], up = y[32 * b + 16 + i];
-          a.act_out[(size_t)r * (a.N >> 1) + f] = f2bf(act_fn(gate, a.act) * up);
-        }
+      if (hh < a.nq) {
+        a.q_out[((size_t)r * a.nq + hh) * a.dh + d] = f2bf(out);
+      } else {
+        const int kv = hh < a.nq + a.nkv ? 0 : 1;
+        const int head = hh - a.nq - kv * a.nkv;
+        const int page = a.page_table[pos / kPage];
+        const size_t off = ((((size_t)a.layer * a.n_pages + page) * 2 + kv) * a.nkv + head) * kPage + (pos % kPage);
+        a.kv_pool[off * a.dh + d] = f2bf(out);
       }
-      __syncthreads();
-    } else {  // kEpiQkv
-      y[t] = v;
-      __syncthreads();
-      if (live) {
-        const int qd = a.nq * a.dh, kd = a.nkv * a.dh;
-        const int half = a.dh >> 1;
-        const int pos = kv_len + r;
-        const int d = n % a.dh;
-        const int i = d % half;
-        float out = v;
-        if (n < qd + kd) {
-          const float2 cs = a.rope[(size_t)pos * half + i];
-          const float partner = (d < half) ? y[t + half] : y[t - half];
-          out = (d < half) ? (v * cs.x - partner * cs.y) : (v * cs.x + partner * cs.y);
-        }
-        if (n < qd) {
-          a.q_out[(size_t)r * qd + n] = out;
-        } else {
-          const int kv = (n < qd + kd) ? 0 : 1;
-          const int h = (n - qd - kv * kd) / a.dh;
-          const int page = a.page_table[pos / kPage];
-          const size_t off = ((((size_t)a.layer * a.n_pages + page) * 2 + kv) * a.nkv + h) * kPage + (pos % kPage);
-          a.kv_pool[off * a.dh + d] = f2bf(out);
-        }
-      }
-      __syncthreads();
+    } else {                                        // kRoleLmHead
+      const int n = T * 16 + c;
+      if (a.logits != nullptr) a.logits[(size_t)r * a.N + n] = y;
+      uint64_t b = argmax_key(y, (uint32_t)n);
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) b = umax64(b, __shfl_xor(b, o));
+      if (c == 0) a.best[(size_t)r * (a.N >> 4) + T] = b;
     }
   }
 }
 
-hipError_t launch_epilogue(const EpiArgs& a, hipStream_t st) {
-  const int blocks = (a.N + kEpiCols - 1) / kEpiCols;
-  hipLaunchKernelGGL(k_epilogue, dim3(blocks), dim3(256), 0, st, a);
+// Wave partials of one item -> LDS -> summed in wave order -> sh.y -> epilogue.
+template <int TM, int ROLE>
+__device__ __forceinline__ void gemm_finish(const GemmArgs& a, GemmShared& sh, f32x4 (&acc)[TM], int T, int wave,
+                                            int lane, int nw) {
+#pragma unroll
+  for (int rt = 0; rt < TM; ++rt) {
+    sh.red[wave][lane] = acc[rt];
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      const int l = threadIdx.x;
+      f32x4 v = sh.red[0][l];
+      for (int w = 1; w < nw; ++w) {
+        const f32x4 u = sh.red[w][l];
+        v.x = v.x + u.x; v.y = v.y + u.y; v.z = v.z + u.z; v.w = v.w + u.w;
+      }
+      // v[i] = Y[r = rt*16 + (l & 15)][column 4 (l >> 4) + i]
+      const int r = rt * 16 + (l & 15);
+      const int c0 = 4 * (l >> 4);
+      if (r < a.M) { sh.y[r][c0] = v.x; sh.y[r][c0 + 1] = v.y; sh.y[r][c0 + 2] = v.z; sh.y[r][c0 + 3] = v.w; }
+    }
+    __syncthreads();
+  }
+  gemm_epilogue<ROLE>(a, sh, T);
+  __syncthreads();
+}
+
+template <int TM, int BM, int ROLE>
+__global__ __launch_bounds__(1024) void k_gemm_bf16(GemmArgs a) {
+  __shared__ GemmShared sh;
+  const int nw = blockDim.x >> 6;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = lane & 15, g = lane >> 4;
+  const int KC = a.K >> 5;
+  const int cpw = KC / nw;
+  const int kc0 = wave * cpw;
+  const int n_items = a.N >> 4;
+  int T = blockIdx.x;
+  const uint4* W4 = reinterpret_cast<const uint4*>(a.W) + lane;
+  // packed weights are tile-major: chunk kc of tile T is the KiB at (T * KC + kc)
+  auto wptr = [&](int t, int kc) { return W4 + ((size_t)t * KC + kc) * 64; };
+
+  // weights of the first batch of the first item: requested before anything else
+  uint4 A[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u)
+    if (u < cpw) A[u] = ld_stream(wptr(T, kc0 + u));
+
+  // normalised activations of this wave's K slice, built once
+  rows_inv_rms<BM>(a, sh, wave, lane, nw);
+  constexpr bool CACHE = (BM == kBNorm);
+  uint4 Bc[CACHE ? kCacheB : 1][TM];
+  if (CACHE) {
+#pragma unroll
+    for (int rt = 0; rt < TM; ++rt) {
+      const int r = rt * 16 + j;
+      const float inv = r < a.M ? sh.inv[r] : 0.f;
+#pragma unroll
+      for (int u = 0; u < kCacheB; ++u) {
+        Bc[CACHE ? u : 0][rt] = make_uint4(0u, 0u, 0u, 0u);
+        if (u < cpw && r < a.M) Bc[CACHE ? u : 0][rt] = load_b<BM>(a, r, (kc0 + u) * 32 + g * 8, inv);
+      }
+    }
+  }
+
+  for (;;) {
+    f32x4 acc[TM];
+#pragma unroll
+    for (int rt = 0; rt < TM; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b0 = 0; b0 < cpw; b0 += kBatch) {
+      if (b0 > 0) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+          if (b0 + u < cpw) A[u] = ld_stream(wptr(T, kc0 + b0 + u));
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (b0 + u < cpw) {
+#pragma unroll
+          for (int rt = 0; rt < TM; ++rt) {
+            uint4 B;
+            if (CACHE) {
+              B = Bc[CACHE ? u : 0][rt];
+            } else {
+              const int r = rt * 16 + j;
+              B = make_uint4(0u, 0u, 0u, 0u);
+              if (r < a.M) B = load_b<BM>(a, r, (kc0 + b0 + u) * 32 + g * 8, 0.f);
+            }
+            acc[rt] = mfma16x16x32(A[u], B, acc[rt]);
+          }
+        }
+      }
+    }
+    const int Tn = T + gridDim.x;
+    if (Tn < n_items) {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (u < cpw) A[u] = ld_stream(wptr(Tn, kc0 + u));
+    }
+    gemm_finish<TM, ROLE>(a, sh, acc, T, wave, lane, nw);
+    if (Tn >= n_items) break;
+    T = Tn;
+  }
+}
+
+// int4 weights: per row tile and per scale group, two MFMAs over the group's
+// 64 inputs start from zero; the group sum is then scaled by the fp32 group
+// scale and added to the running fp32 sum in group order.
+template <int TM, int BM, int ROLE>
+__global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
+  __shared__ GemmShared sh;
+  const int nw = blockDim.x >> 6;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = lane & 15, g = lane >> 4;
+  const int KT = a.K >> 7;                 // 128-input tiles
+  const int tpw = KT / nw;
+  const int kt0 = wave * tpw;
+  const int n_items = a.N >> 4;
+  rows_inv_rms<BM>(a, sh, wave, lane, nw);
+  float inv[TM];
+#pragma unroll
+  for (int rt = 0; rt < TM; ++rt) {
+    const int r = rt * 16 + j;
+    inv[rt] = (BM == kBNorm && r < a.M) ? sh.inv[r] : 0.f;
+  }
+  for (int T = blockIdx.x; T < n_items; T += gridDim.x) {
+    f32x4 acc[TM];
+#pragma unroll
+    for (int rt = 0; rt < TM; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint4* Wt = reinterpret_cast<const uint4*>(a.W) + (size_t)T * KT * 64 + lane;
+    const uint2* St = reinterpret_cast<const uint2*>(a.Wscale) + (size_t)T * KT * 8 + g;
+    for (int c = 0; c < tpw; ++c) {
+      const int kt = kt0 + c;
+      const uint4 Q = ld_stream(Wt + (size_t)kt * 64);
+      const uint2 SC0 = St[(size_t)kt * 8], SC1 = St[(size_t)kt * 8 + 4];
+#pragma unroll
+      for (int gq = 0; gq < 2; ++gq) {
+        const uint2 SC = gq == 0 ? SC0 : SC1;
+        const uint4 A0 = codes8(gq == 0 ? Q.x : Q.z), A1 = codes8(gq == 0 ? Q.y : Q.w);
+        const float s0 = bf2f((uint16_t)(SC.x & 0xffffu)), s1 = bf2f((uint16_t)(SC.x >> 16));
+        const float s2 = bf2f((uint16_t)(SC.y & 0xffffu)), s3 = bf2f((uint16_t)(SC.y >> 16));
+#pragma unroll
+        for (int rt = 0; rt < TM; ++rt) {
+          const int r = rt * 16 + j;
+          uint4 B0 = make_uint4(0u, 0u, 0u, 0u), B1 = B0;
+          if (r < a.M) {
+            B0 = load_b<BM>(a, r, kt * 128 + gq * 64 + g * 8, inv[rt]);
+            B1 = load_b<BM>(a, r, kt * 128 + gq * 64 + 32 + g * 8, inv[rt]);
+          }
+          f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
+          p = mfma16x16x32(A0, B0, p);
+          p = mfma16x16x32(A1, B1, p);
+          acc[rt].x = fmaf(s0, p.x, acc[rt].x);
+          acc[rt].y = fmaf(s1, p.y, acc[rt].y);
+          acc[rt].z = fmaf(s2, p.z, acc[rt].z);
+          acc[rt].w = fmaf(s3, p.w, acc[rt].w);
+        }
+      }
+    }
+    gemm_finish<TM, ROLE>(a, sh, acc, T, wave, lane, nw);
+  }
+}
+
+template <int BM, int ROLE, bool INT4>
+static hipError_t gemm_dispatch(const GemmArgs& a, int grid, hipStream_t st) {
+  const dim3 block(64 * a.S);
+  const int tm = (a.M + 15) / 16;
+  if constexpr (INT4) {
+    switch (tm) {
+      case 1: hipLaunchKernelGGL((k_gemm_int4<1, BM, ROLE>), dim3(grid), block, 0, st, a); break;
+      case 2: hipLaunchKernelGGL((k_gemm_int4<2, BM, ROLE>), dim3(grid), block, 0, st, a); break;
+      case 3: hipLaunchKernelGGL((k_gemm_int4<3, BM, ROLE>), dim3(grid), block, 0, st, a); break;
+      case 4: hipLaunchKernelGGL((k_gemm_int4<4, BM, ROLE>), dim3(grid), block, 0, st, a); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (tm) {
+      case 1: hipLaunchKernelGGL((k_gemm_bf16<1, BM, ROLE>), dim3(grid), block, 0, st, a); break;
+      case 2: hipLaunchKernelGGL((k_gemm_bf16<2, BM, ROLE>), dim3(grid), block, 0, st, a); break;
+      case 3: hipLaunchKernelGGL((k_gemm_bf16<3, BM, ROLE>), dim3(grid), block, 0, st, a); break;
+      case 4: hipLaunchKernelGGL((k_gemm_bf16<4, BM, ROLE>), dim3(grid), block, 0, st, a); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
   return hipGetLastError();
 }
 
+// a.S: waves splitting K inside one workgroup (fixed per matrix, 1..16);
+// grid: workgroups (each loops over items); any grid gives the same bits.
+hipError_t launch_gemm(const GemmArgs& a, int role, int grid, hipStream_t st) {
+  if (a.M < 1 || a.M > kMaxRows || a.S < 1 || a.S > kMaxWaves || a.N % 16 || grid < 1) return hipErrorInvalidValue;
+  if (a.fmt == 1 ? (a.K % (128 * a.S)) : (a.K % (32 * a.S))) return hipErrorInvalidValue;
+  if (a.fmt == 0 && (role == kRoleQkv || role == kRoleGateUp || role == kRoleLmHead) && a.K / 32 / a.S > kCacheB)
+    return hipErrorInvalidValue;
+  grid = grid > (a.N >> 4) ? (a.N >> 4) : grid;
+  const bool i4 = a.fmt == 1;
+  switch (role) {
+    case kRoleQkv: return i4 ? gemm_dispatch<kBNorm, kRoleQkv, true>(a, grid, st) : gemm_dispatch<kBNorm, kRoleQkv, false>(a, grid, st);
+    case kRoleO: return i4 ? gemm_dispatch<kBBf16, kRoleO, true>(a, grid, st) : gemm_dispatch<kBBf16, kRoleO, false>(a, grid, st);
+    case kRoleGateUp:
+      return i4 ? gemm_dispatch<kBNorm, kRoleGateUp, true>(a, grid, st) : gemm_dispatch<kBNorm, kRoleGateUp, false>(a, grid, st);
+    case kRoleDown:
+      return i4 ? gemm_dispatch<kBBf16, kRoleDown, true>(a, grid, st) : gemm_dispatch<kBBf16, kRoleDown, false>(a, grid, st);
+    case kRoleLmHead:
+      if (i4) return hipErrorInvalidValue;
+      return gemm_dispatch<kBNorm, kRoleLmHead, false>(a, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 // ------------------------------------------------------------ attention
-// One wave per (split, q head, row).  Row r attends to ctx = kv_len + r + 1
-// positions; split i covers [512 i, min(512 (i+1), ctx)), walked in blocks of
-// 64 absolute positions (one per lane).  Scores are sequential fp32 dot
-// products; masked lanes take -inf by select and are skipped in P.V, so a
-// position past ctx (stale or poisoned KV) never enters the arithmetic.
+// Split plan of one row, a function of its own ctx only: nb = ceil(ctx/64)
+// blocks of 64 absolute positions, bps = ceil(nb / 32) blocks per split,
+// ns = ceil(nb / bps) splits; split i covers positions
+// [64 i bps, min(64 (i+1) bps, ctx)).  Short contexts get one block per
+// split (many workgroups), long ones at most 32 splits (little partial data).
+__host__ __device__ __forceinline__ int attn_bps(int ctx) {
+  const int nb = (ctx + kAttnBlock - 1) / kAttnBlock;
+  return (nb + kAttnMaxSplits - 1) / kAttnMaxSplits;
+}
+__host__ __device__ __forceinline__ int attn_ns(int ctx) {
+  const int nb = (ctx + kAttnBlock - 1) / kAttnBlock;
+  const int bps = (nb + kAttnMaxSplits - 1) / kAttnMaxSplits;
+  return (nb + bps - 1) / bps;
+}
+int attn_splits(int ctx) { return attn_ns(ctx); }
+
+// One workgroup (8 waves) per (split index, KV head) holds every (row, q
+// head) pair of that KV head as MFMA columns: q-row qr = r*G + jj for query
+// head h*G + jj.  Row r works on its own split range of its ctx_r = kv_len +
+// r + 1 positions; the workgroup walks the union of the rows' ranges in
+// blocks of 64 absolute positions staged in LDS (K row-major, V transposed).
+// Per block and q-row:
+//   s_t = (K_t . q) * log2(e)/sqrt(dh)        one MFMA chain over d
+//   positions outside the row's range -> -inf by select; block max;
+//   p_t = bf16(2^(s_t - m_new)) (0 when masked), l = l * 2^(m - m_new) + sum p,
+//   o   = o * 2^(m - m_new) + V^T p             one MFMA chain over t.
+// A block with no valid position leaves (m, l, o) exactly as they were (the
+// rescale factor is 1 while the running max is still -inf).  Every reduction
+// runs in the same order for every q-row slot, so a row's result does not
+// depend on which other rows share the launch.  Positions at or past
+// kv_len + M are zero-filled in LDS, so stale or poisoned KV never enters the
+// arithmetic; positions between a row's own ctx and kv_len + M hold this
+// launch's finite K/V and meet p = 0 exactly.
 template <int DH>
-__global__ __launch_bounds__(64) void k_attn_split(AttnArgs a) {
-  constexpr int PER = DH / 64;
-  __shared__ float qs[DH];
-  const int split = blockIdx.x, j = blockIdx.y, r = blockIdx.z;
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
+  constexpr int DC = DH / 32;            // d chunks of the score MFMA
+  constexpr int DT = DH / 16;            // d tiles of the P.V MFMA
+  constexpr int KST = DH + 8;            // padded K row in LDS (bf16)
+  constexpr int VST = kAttnBlock + 4;    // padded V^T row in LDS (bf16)
+  constexpr int QPW = 2;                 // q tiles per wave (8 waves x 2 x 16 = 256 q-rows)
+  constexpr int SEGS = DH / 8;           // 16-byte segments per K or V row
+  constexpr int LOADS = (2 * kAttnBlock * SEGS) / 512;
+  __shared__ __align__(16) uint16_t Ks[kAttnBlock * KST];
+  __shared__ __align__(16) uint16_t Vt[DH * VST];
+
+  const int split = blockIdx.x, h = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = lane & 15, g = lane >> 4;
   const int kv_len = a.params[0];
-  const int ctx = kv_len + r + 1;
-  const int t0 = split * kAttnSplit;
-  if (t0 >= ctx) return;
-  const int t1 = min(ctx, t0 + kAttnSplit);
-  const int h = j / (a.nq / a.nkv);
-  for (int d = lane; d < DH; d += 64) qs[d] = a.q[((size_t)r * a.nq + j) * DH + d];
-  __syncthreads();
+  const int G = a.nq / a.nkv;
+  const int n_qr = a.M * G;
+  const int n_qt = (n_qr + 15) >> 4;
+  const int ctx_max = kv_len + a.M;
 
+  // union of the rows' ranges for this split (rows with fewer splits sit out)
+  int u_lo = 0x7fffffff, u_hi = 0;
+  for (int r = 0; r < a.M; ++r) {
+    const int ctx = kv_len + r + 1;
+    if (split >= attn_ns(ctx)) continue;
+    const int bps = attn_bps(ctx);
+    u_lo = min(u_lo, split * bps * kAttnBlock);
+    u_hi = max(u_hi, min((split + 1) * bps * kAttnBlock, ctx));
+  }
+  if (u_lo >= u_hi) return;
   const size_t layer_base = (size_t)a.layer * a.n_pages;
-  auto kv_row = [&](int pos, int kv) -> const uint16_t* {
-    const int page = a.page_table[pos / kPage];
-    const size_t off = (((layer_base + page) * 2 + kv) * a.nkv + h) * kPage + (pos % kPage);
-    return a.kv_pool + off * DH;
+
+  uint4 qop[QPW][DC];
+  f32x4 o[QPW][DT];
+  float m[QPW], l[QPW];
+  int lo_q[QPW], hi_q[QPW];
+#pragma unroll
+  for (int u = 0; u < QPW; ++u) {
+    const int qr = (wave + 8 * u) * 16 + j;
+    const bool have = qr < n_qr;
+    const int r = have ? qr / G : 0;
+    const int head = h * G + (have ? qr % G : 0);
+    const int ctx = kv_len + r + 1;
+    lo_q[u] = 0;
+    hi_q[u] = 0;
+    if (have && split < attn_ns(ctx)) {
+      const int bps = attn_bps(ctx);
+      lo_q[u] = split * bps * kAttnBlock;
+      hi_q[u] = min((split + 1) * bps * kAttnBlock, ctx);
+    }
+#pragma unroll
+    for (int c = 0; c < DC; ++c)
+      qop[u][c] = have ? *reinterpret_cast<const uint4*>(a.q + ((size_t)r * a.nq + head) * DH + c * 32 + g * 8)
+                       : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[u] = -INFINITY;
+    l[u] = 0.f;
+  }
+
+  // global -> register fetch of one block (K and V), zero past ctx_max
+  uint4 pre[LOADS];
+  auto fetch = [&](int blk) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int idx = threadIdx.x + i * 512;
+      const int kv = idx / (kAttnBlock * SEGS);
+      const int rem = idx % (kAttnBlock * SEGS);
+      const int t = rem / SEGS, seg = rem % SEGS;
+      const int pos = blk + t;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (pos < ctx_max) {
+        const int page = a.page_table[pos / kPage];
+        const size_t off = (((layer_base + page) * 2 + kv) * a.nkv + h) * kPage + (pos % kPage);
+        v = *reinterpret_cast<const uint4*>(a.kv_pool + off * DH + seg * 8);
+      }
+      pre[i] = v;
+    }
   };
-
-  float m = -INFINITY, l = 0.f;
-  float o[PER];
+  fetch(u_lo);
+  for (int blk = u_lo; blk < u_hi; blk += kAttnBlock) {
+    __syncthreads();
 #pragma unroll
-  for (int e = 0; e < PER; ++e) o[e] = 0.f;
-
-  for (int b = t0; b < t1; b += 64) {
-    const int t = b + lane;
-    const bool valid = t < t1;
-    float s = -INFINITY;
-    if (valid) {
-      const uint4* kp = reinterpret_cast<const uint4*>(kv_row(t, 0));
-      float dot = 0.f;
-#pragma unroll 4
-      for (int d8 = 0; d8 < DH / 8; ++d8) {
-        const uint4 kk = kp[d8];
-        const uint32_t w[4] = {kk.x, kk.y, kk.z, kk.w};
+    for (int i = 0; i < LOADS; ++i) {
+      const int idx = threadIdx.x + i * 512;
+      const int kv = idx / (kAttnBlock * SEGS);
+      const int rem = idx % (kAttnBlock * SEGS);
+      const int t = rem / SEGS, seg = rem % SEGS;
+      if (kv == 0) {
+        *reinterpret_cast<uint4*>(&Ks[t * KST + seg * 8]) = pre[i];
+      } else {
+        const uint32_t w[4] = {pre[i].x, pre[i].y, pre[i].z, pre[i].w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float kf = bf2f((uint16_t)((w[e >> 1] >> ((e & 1) * 16)) & 0xffffu));
-          dot = fmaf(qs[d8 * 8 + e], kf, dot);
+        for (int e = 0; e < 8; ++e)
+          Vt[(seg * 8 + e) * VST + t] = (uint16_t)((w[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+      }
+    }
+    __syncthreads();
+    if (blk + kAttnBlock < u_hi) fetch(blk + kAttnBlock);
+
+#pragma unroll
+    for (int u = 0; u < QPW; ++u) {
+      if (wave + 8 * u >= n_qt) continue;   // wave-uniform
+      f32x4 sc[4];
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          const uint4 kA = *reinterpret_cast<const uint4*>(&Ks[(pt * 16 + j) * KST + c * 32 + g * 8]);
+          acc = mfma16x16x32(kA, qop[u][c], acc);
+        }
+        sc[pt] = acc;
+      }
+      // lane (g, j) holds scores of q-row j at positions blk + pt*16 + 4g + v
+      float s[16];
+      float bmax = -INFINITY;
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int tpos = blk + pt * 16 + 4 * g + v;
+          const float sv = sc[pt][v] * a.scale_log2;
+          s[pt * 4 + v] = (tpos >= lo_q[u] && tpos < hi_q[u]) ? sv : -INFINITY;
+          bmax = fmaxf(bmax, s[pt * 4 + v]);
+        }
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+      const float mn = fmaxf(m[u], bmax);
+      const float alpha = (mn == -INFINITY) ? 1.0f : exp2f(m[u] - mn);
+      uint16_t pb[16];
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pv = (s[e] == -INFINITY) ? 0.f : exp2f(s[e] - mn);
+        pb[e] = f2bf(pv);
+        psum = psum + bf2f(pb[e]);
+      }
+      psum = psum + __shfl_xor(psum, 16);
+      psum = psum + __shfl_xor(psum, 32);
+      l[u] = l[u] * alpha + psum;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        o[u][dt].x = o[u][dt].x * alpha; o[u][dt].y = o[u][dt].y * alpha;
+        o[u][dt].z = o[u][dt].z * alpha; o[u][dt].w = o[u][dt].w * alpha;
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int pa = 2 * ks, pbt = 2 * ks + 1;
+        const uint4 Bp = make_uint4(pack2(pb[pa * 4 + 0], pb[pa * 4 + 1]), pack2(pb[pa * 4 + 2], pb[pa * 4 + 3]),
+                                    pack2(pb[pbt * 4 + 0], pb[pbt * 4 + 1]), pack2(pb[pbt * 4 + 2], pb[pbt * 4 + 3]));
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const uint16_t* vr = &Vt[(dt * 16 + j) * VST];
+          const uint2 vlo = *reinterpret_cast<const uint2*>(vr + pa * 16 + 4 * g);
+          const uint2 vhi = *reinterpret_cast<const uint2*>(vr + pbt * 16 + 4 * g);
+          o[u][dt] = mfma16x16x32(make_uint4(vlo.x, vlo.y, vhi.x, vhi.y), Bp, o[u][dt]);
         }
       }
-      s = dot * a.scale_log2;
+      m[u] = mn;
     }
-    const float mn = fmaxf(m, wave_max(s));
-    const float alpha = exp2f(m - mn);
-    const float p = valid ? exp2f(s - mn) : 0.f;
-    l = l * alpha + wave_sum(p);
-    const int nt = min(64, t1 - b);
-    float accv[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) accv[e] = 0.f;
-    for (int tt = 0; tt < nt; ++tt) {
-      const float pt = __shfl(p, tt);
-      const uint16_t* vp = kv_row(b + tt, 1) + lane * PER;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) accv[e] = fmaf(pt, bf2f(vp[e]), accv[e]);
-    }
-#pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] = o[e] * alpha + accv[e];
-    m = mn;
   }
-  float* part = a.part + (((size_t)r * a.nq + j) * a.n_split + split) * (DH + 2);
-  if (lane == 0) { part[0] = m; part[1] = l; }
+  // lane (g, j) holds o of q-row j for d = dt*16 + 4g + v
 #pragma unroll
-  for (int e = 0; e < PER; ++e) part[2 + lane * PER + e] = o[e];
+  for (int u = 0; u < QPW; ++u) {
+    const int qr = (wave + 8 * u) * 16 + j;
+    if (wave + 8 * u >= n_qt || qr >= n_qr || hi_q[u] <= lo_q[u]) continue;
+    const int r = qr / G, head = h * G + qr % G;
+    float* part = a.part + (((size_t)r * a.nq + head) * kAttnMaxSplits + split) * (DH + 4);
+    if (g == 0) { part[0] = m[u]; part[1] = l[u]; }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(part + 4 + dt * 16 + 4 * g) = make_float4(o[u][dt].x, o[u][dt].y, o[u][dt].z, o[u][dt].w);
+  }
 }
 
 // Combine the row's splits in split order: o = sum_i w_i o_i / sum_i w_i l_i
-// with w_i = 2^(m_i - max m).
+// with w_i = 2^(m_i - max m).  Partial record: [m, l, -, -, o[dh]].
 template <int DH>
 __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
   constexpr int PER = DH / 64;
   const int j = blockIdx.x, r = blockIdx.y, lane = threadIdx.x;
   const int ctx = a.params[0] + r + 1;
-  const int ns = (ctx + kAttnSplit - 1) / kAttnSplit;
-  const float* base = a.part + ((size_t)r * a.nq + j) * a.n_split * (DH + 2);
+  const int ns = attn_ns(ctx);
+  const float* base = a.part + ((size_t)r * a.nq + j) * kAttnMaxSplits * (DH + 4);
   float mx = base[0];
-  for (int i = 1; i < ns; ++i) mx = fmaxf(mx, base[(size_t)i * (DH + 2)]);
+  for (int i = 1; i < ns; ++i) mx = fmaxf(mx, base[(size_t)i * (DH + 4)]);
   float L = 0.f, O[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) O[e] = 0.f;
   for (int i = 0; i < ns; ++i) {
-    const float* p = base + (size_t)i * (DH + 2);
+    const float* p = base + (size_t)i * (DH + 4);
     const float w = exp2f(p[0] - mx);
     L = L + p[1] * w;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) O[e] = O[e] + p[2 + lane * PER + e] * w;
+    for (int e = 0; e < PER; ++e) O[e] = O[e] + p[4 + lane * PER + e] * w;
   }
 #pragma unroll
   for (int e = 0; e < PER; ++e)
@@ -547,11 +678,12 @@ __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
+  if (a.M * (a.nq / a.nkv) > kAttnQRows || a.n_split < 1 || a.n_split > kAttnMaxSplits) return hipErrorInvalidValue;
   if (a.dh == 128) {
-    hipLaunchKernelGGL(k_attn_split<128>, dim3(a.n_split, a.nq, a.M), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(k_attn_mfma<128>, dim3(a.n_split, a.nkv), dim3(512), 0, st, a);
     hipLaunchKernelGGL(k_attn_combine<128>, dim3(a.nq, a.M), dim3(64), 0, st, a);
   } else if (a.dh == 64) {
-    hipLaunchKernelGGL(k_attn_split<64>, dim3(a.n_split, a.nq, a.M), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(k_attn_mfma<64>, dim3(a.n_split, a.nkv), dim3(512), 0, st, a);
     hipLaunchKernelGGL(k_attn_combine<64>, dim3(a.nq, a.M), dim3(64), 0, st, a);
   } else {
     return hipErrorInvalidValue;
@@ -560,47 +692,54 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
 }
 
 // ------------------------------------------------------------ embedding gather
-// x[r] = E[id_r] widened to fp32, plus the per-256-column sums of squares the
-// first RMSNorm reads (same slicing and order as the residual epilogue).
-__global__ __launch_bounds__(256) void k_embed(const int* params, const uint16_t* E, int d, float* x, float* ss) {
-  __shared__ float red4[4];
-  const int r = blockIdx.x, t = threadIdx.x;
+// x[r] = E[id_r] widened to fp32, plus the per-16-column sums of squares the
+// first RMSNorm reads (16-lane butterfly, like the residual epilogue).
+__global__ __launch_bounds__(256) void k_embed(const int* params, const uint16_t* E, int vocab, int d, float* x,
+                                               float* ss) {
+  const int r = blockIdx.x;
   const int id = params[2 + r];
-  const int KC = d >> 5;
-  for (int c = 0; c < (d >> 8); ++c) {
-    const int k = c * 256 + t;
-    const size_t off = ((size_t)(id >> 4) * KC + (k >> 5)) * 512 + (size_t)(((k & 31) >> 3) * 16 + (id & 15)) * 8 + (k & 7);
+  (void)vocab;
+  for (int k = threadIdx.x; k < d; k += 256) {
+    const size_t off = ((size_t)(id >> 4) * (d >> 5) + (k >> 5)) * 512 + (size_t)(((k & 31) >> 3) * 16 + (id & 15)) * 8 + (k & 7);
     const float v = bf2f(E[off]);
     x[(size_t)r * d + k] = v;
-    const float sq = block_sum256(v * v, red4);
-    if (t == 0) ss[(size_t)r * (d >> 8) + c] = sq;
+    float sq = v * v;
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) sq += __shfl_xor(sq, o);
+    if ((k & 15) == 0) ss[(size_t)r * (d >> 4) + (k >> 4)] = sq;
   }
 }
 
 hipError_t launch_embed(const int* params, int M, const void* embed, int vocab, int d, float* x, float* ss,
                         hipStream_t st) {
-  (void)vocab;
-  hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, params, (const uint16_t*)embed, d, x, ss);
+  hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, params, (const uint16_t*)embed, vocab, d, x, ss);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------ argmax + acceptance
-// Row argmax over the LM head's per-64-column bests (max of packed keys,
+// Row argmax over the LM head's per-16-column bests (max of packed keys,
 // order-free), then the greedy acceptance: n = number of leading drafts equal
 // to the argmax of the row before them; next = argmax of row n.
 // result: [0] n, [1] next, [2 + r] argmax of row r.
 __global__ __launch_bounds__(1024) void k_accept(const int* params, int M, int verify, const uint64_t* best,
                                                  int n_groups, int* result) {
   __shared__ int am[kMaxRows];
+  __shared__ uint64_t wbest[16];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int r = wave; r < M; r += 16) {
+  for (int r = 0; r < M; ++r) {
     uint64_t b = 0;
-    for (int i = lane; i < n_groups; i += 64) b = umax64(b, best[(size_t)r * n_groups + i]);
+    for (int i = threadIdx.x; i < n_groups; i += 1024) b = umax64(b, best[(size_t)r * n_groups + i]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) b = umax64(b, __shfl_xor(b, o));
-    if (lane == 0) am[r] = (int)(0xffffffffu - (uint32_t)(b & 0xffffffffu));
+    if (lane == 0) wbest[wave] = b;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint64_t bb = wbest[0];
+      for (int w = 1; w < 16; ++w) bb = umax64(bb, wbest[w]);
+      am[r] = (int)(0xffffffffu - (uint32_t)(bb & 0xffffffffu));
+    }
+    __syncthreads();
   }
-  __syncthreads();
   if (wave == 0) {
     const int a_r = lane < M ? am[lane] : 0;
     if (lane < M) result[2 + lane] = a_r;
@@ -625,44 +764,59 @@ hipError_t launch_accept(const int* params, int M, int verify, const uint64_t* b
 }
 
 // ------------------------------------------------------------ weight packing
-// Pure permutation into the tile layouts above.  Output tile T takes source
-// tile T (no interleave) or, when src1 is given, tile T/2 of src0 (T even)
-// or src1 (T odd): gate and up outputs of the same 16 features share a
-// 32-output pair of tiles.
-__global__ void k_pack_bf16(const uint16_t* s0, const uint16_t* s1, int n, int k, uint4* dst) {
+// Pure permutation into the tile layouts above.  Row i (0..15) of output
+// tile T comes from:
+//   layout 0: src0 row 16T + i
+//   layout 1 (gate/up): i < 8: src0 (gate) row 8T + i; else src1 (up) row 8T + i - 8
+//   layout 2 (QKV, per head of head_dim rows, gph = head_dim/16 tiles per
+//            head): tile (head h, s) holds dims 8s + i (i < 8) and their
+//            RoPE partners dh/2 + 8s + (i - 8)
+__device__ __forceinline__ int pack_src_row(int layout, int T, int i, int dh, int& which) {
+  which = 0;
+  if (layout == 1) {
+    which = i >= 8;
+    return 8 * T + (i & 7);
+  }
+  if (layout == 2) {
+    const int half = dh >> 1, gph = half >> 3;
+    const int hh = T / gph, sb = T % gph;
+    return hh * dh + (i < 8 ? 0 : half) + 8 * sb + (i & 7);
+  }
+  return T * 16 + i;
+}
+
+// bf16 tiles are stored tile-major: chunk kc of tile T is KiB (T * KC + kc),
+// so one workgroup streams one contiguous run per item.
+__global__ void k_pack_bf16(int layout, const uint16_t* s0, const uint16_t* s1, int n_out, int k, int dh, uint4* dst) {
   const int KC = k >> 5;
-  const int n_tiles_out = (s1 ? 2 * n : n) >> 4;
-  const size_t total = (size_t)n_tiles_out * KC * 64;
+  const int n_tiles = n_out >> 4;
+  const size_t total = (size_t)n_tiles * KC * 64;
   for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += (size_t)gridDim.x * blockDim.x) {
     const int lane = (int)(idx & 63);
     const size_t tk = idx >> 6;
     const int kc = (int)(tk % KC);
     const int T = (int)(tk / KC);
-    const uint16_t* src = s0;
-    int st = T;
-    if (s1) { src = (T & 1) ? s1 : s0; st = T >> 1; }
-    const int row = st * 16 + (lane & 15);
+    int which;
+    const int row = pack_src_row(layout, T, lane & 15, dh, which);
+    const uint16_t* src = which ? s1 : s0;
     const int col = kc * 32 + (lane >> 4) * 8;
     dst[idx] = *reinterpret_cast<const uint4*>(src + (size_t)row * k + col);
   }
 }
 
-__global__ void k_pack_int4(const int8_t* s0, const uint16_t* s0s, const int8_t* s1, const uint16_t* s1s, int n,
-                            int k, uint4* dst, uint16_t* dst_s) {
+__global__ void k_pack_int4(int layout, const int8_t* s0, const uint16_t* s0s, const int8_t* s1, const uint16_t* s1s,
+                            int n_out, int k, int dh, uint4* dst, uint16_t* dst_s) {
   const int KT = k >> 7;
-  const int n_tiles_out = (s1 ? 2 * n : n) >> 4;
-  const size_t total = (size_t)n_tiles_out * KT * 64;
+  const size_t total = (size_t)(n_out >> 4) * KT * 64;
   for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += (size_t)gridDim.x * blockDim.x) {
     const int lane = (int)(idx & 63);
     const size_t tk = idx >> 6;
     const int kt = (int)(tk % KT);
     const int T = (int)(tk / KT);
-    const int8_t* src = s0;
-    const uint16_t* srcs = s0s;
-    int st = T;
-    if (s1) { src = (T & 1) ? s1 : s0; srcs = (T & 1) ? s1s : s0s; st = T >> 1; }
+    int which;
     const int i = lane & 15, g = lane >> 4;
-    const int row = st * 16 + i;
+    const int row = pack_src_row(layout, T, i, dh, which);
+    const int8_t* src = which ? s1 : s0;
     uint32_t w[4] = {0u, 0u, 0u, 0u};
     for (int c = 0; c < 32; ++c) {
       const int col = kt * 128 + (c >> 4) * 64 + ((c & 15) >> 3) * 32 + g * 8 + (c & 7);
@@ -673,20 +827,24 @@ __global__ void k_pack_int4(const int8_t* s0, const uint16_t* s0s, const int8_t*
     // scales: tile (T, kt) holds [group 0..1][16 outputs]; lanes 0..31 write one each
     if (lane < 32) {
       const int gq = lane >> 4, ii = lane & 15;
-      dst_s[tk * 32 + lane] = srcs[(size_t)(st * 16 + ii) * (k >> 6) + kt * 2 + gq];
+      int w2;
+      const int srow = pack_src_row(layout, T, ii, dh, w2);
+      dst_s[tk * 32 + lane] = (w2 ? s1s : s0s)[(size_t)srow * (k >> 6) + kt * 2 + gq];
     }
   }
 }
 
-hipError_t launch_pack(int fmt, const void* src0, const void* src0_scales, const void* src1, const void* src1_scales,
-                       int n, int k, void* dst, void* dst_scales, hipStream_t st) {
+hipError_t launch_pack(int fmt, int layout, const void* src0, const void* src0_scales, const void* src1,
+                       const void* src1_scales, int n, int k, int dh, void* dst, void* dst_scales, hipStream_t st) {
   const int blocks = 2048;
+  const int n_out = layout == 1 ? 2 * n : n;
   if (fmt == 0) {
-    hipLaunchKernelGGL(k_pack_bf16, dim3(blocks), dim3(256), 0, st, (const uint16_t*)src0, (const uint16_t*)src1, n, k,
-                       (uint4*)dst);
+    hipLaunchKernelGGL(k_pack_bf16, dim3(blocks), dim3(256), 0, st, layout, (const uint16_t*)src0,
+                       (const uint16_t*)src1, n_out, k, dh, (uint4*)dst);
   } else {
-    hipLaunchKernelGGL(k_pack_int4, dim3(blocks), dim3(256), 0, st, (const int8_t*)src0, (const uint16_t*)src0_scales,
-                       (const int8_t*)src1, (const uint16_t*)src1_scales, n, k, (uint4*)dst, (uint16_t*)dst_scales);
+    hipLaunchKernelGGL(k_pack_int4, dim3(blocks), dim3(256), 0, st, layout, (const int8_t*)src0,
+                       (const uint16_t*)src0_scales, (const int8_t*)src1, (const uint16_t*)src1_scales, n_out, k, dh,
+                       (uint4*)dst, (uint16_t*)dst_scales);
   }
   return hipGetLastError();
 }

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
+#include <cstdlib>
+#include <map>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -17,30 +20,26 @@ using namespace sv;
 namespace {
 
 struct GemmPlan {
-  int N = 0, K = 0, S = 1, fmt = 0;
+  int N = 0, K = 0, S = 1, fmt = 0;   // S: waves splitting K in one workgroup
+  int grid = 1;                       // persistent workgroups (each loops over 16-output items)
 };
 
 struct Layout {
-  size_t params = 0, x = 0, ss = 0, q = 0, attn_part = 0, attn_out = 0, act = 0, partial = 0, best = 0,
-         result = 0, logits = 0, rope = 0, total = 0;
+  size_t params = 0, x = 0, ss = 0, q = 0, attn_part = 0, attn_out = 0, act = 0, best = 0, result = 0,
+         logits = 0, rope = 0, total = 0;
   int max_split = 1;
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Split-K count of one weight matrix.  It depends only on the matrix shape,
-// never on the number of rows, so every row count shares one summation order.
-int choose_split(int N, int K, int unit) {
-  const int groups = N / kColGroup;
-  const int kc = K / unit;
-  int best = 1;
-  for (int s = 1; s * 4 <= kc; ++s) {
-    if (kc % (s * 4) != 0) continue;
-    if (kc / (s * 4) < 2 && s > 1) break;
-    best = s;
-    if (groups * s >= 768) break;
-  }
-  return best;
+// Waves that split K inside one GEMM workgroup.  It depends only on the
+// matrix shape, never on the number of rows, so every row count shares one
+// summation order.
+int choose_waves(int K, int unit, int max_chunks_per_wave) {
+  const int chunks = K / unit;
+  for (int w : {16, 12, 8, 6, 4, 3, 2, 1})
+    if (chunks % w == 0 && chunks / w <= max_chunks_per_wave) return w;
+  return 0;
 }
 
 bool valid_config(const sv_config& c) {
@@ -55,6 +54,7 @@ bool valid_config(const sv_config& c) {
   if (c.weight_fmt == 1 && (c.d_model % 512 || (c.n_q_heads * c.head_dim) % 512 || c.d_ff % 512)) return false;
   if (c.page_size != kPage || c.max_ctx < kPage || c.max_ctx % kPage) return false;
   if (c.max_k < 0 || c.max_k > kMaxRows - 1) return false;
+  if (c.max_k + 1 > std::min(kMaxRows, kAttnQRows / (c.n_q_heads / c.n_kv_heads))) return false;
   if (!(c.rms_eps > 0.f) || !(c.rope_theta > 1.f)) return false;
   return true;
 }
@@ -63,23 +63,38 @@ struct Plans {
   GemmPlan qkv, o, gu, d, lm;
 };
 
-Plans make_plans(const sv_config& c) {
+// Workgroups per GEMM: enough to cover two per compute unit, never more
+// than there are 16-output items.  Any grid gives the same bits.
+int grid_for(int N, int n_cu) { return std::max(1, std::min(N / 16, 2 * n_cu)); }
+
+Plans make_plans(const sv_config& c, int n_cu) {
   const int qd = c.n_q_heads * c.head_dim, kd = c.n_kv_heads * c.head_dim;
-  const int unit = c.weight_fmt == 1 ? 128 : 32;
+  const bool i4 = c.weight_fmt == 1;
+  const int unit = i4 ? 128 : 32;
+  // bf16 GEMMs that normalise their input keep each wave's activations in
+  // registers: at most 8 chunks of 32 inputs per wave.
+  const int norm_cap = i4 ? 1 << 20 : 8;
   Plans p;
-  p.qkv = {qd + 2 * kd, c.d_model, choose_split(qd + 2 * kd, c.d_model, unit), c.weight_fmt};
-  p.o = {c.d_model, qd, choose_split(c.d_model, qd, unit), c.weight_fmt};
-  p.gu = {2 * c.d_ff, c.d_model, choose_split(2 * c.d_ff, c.d_model, unit), c.weight_fmt};
-  p.d = {c.d_model, c.d_ff, choose_split(c.d_model, c.d_ff, unit), c.weight_fmt};
-  p.lm = {c.vocab, c.d_model, 1, 0};
+  p.qkv = {qd + 2 * kd, c.d_model, choose_waves(c.d_model, unit, norm_cap), c.weight_fmt};
+  p.o = {c.d_model, qd, choose_waves(qd, unit, 1 << 20), c.weight_fmt};
+  p.gu = {2 * c.d_ff, c.d_model, choose_waves(c.d_model, unit, norm_cap), c.weight_fmt};
+  p.d = {c.d_model, c.d_ff, choose_waves(c.d_ff, unit, 1 << 20), c.weight_fmt};
+  p.lm = {c.vocab, c.d_model, choose_waves(c.d_model, 32, 8), 0};
+  for (GemmPlan* g : {&p.qkv, &p.o, &p.gu, &p.d, &p.lm}) g->grid = grid_for(g->N, n_cu);
   return p;
+}
+
+bool plans_ok(const Plans& p) {
+  for (const GemmPlan* g : {&p.qkv, &p.o, &p.gu, &p.d, &p.lm})
+    if (g->S < 1) return false;
+  return true;
 }
 
 Layout make_layout(const sv_config& c, const Plans& p) {
   Layout L;
   const size_t R = kMaxRows;
   const int qd = c.n_q_heads * c.head_dim;
-  L.max_split = (c.max_ctx + kAttnSplit - 1) / kAttnSplit;
+  L.max_split = kAttnMaxSplits;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -88,20 +103,23 @@ Layout make_layout(const sv_config& c, const Plans& p) {
   };
   L.params = take(sizeof(int) * kParamInts);
   L.x = take(R * c.d_model * 4);
-  L.ss = take(R * (c.d_model / 256) * 4);
-  L.q = take(R * qd * 4);
-  L.attn_part = take(R * c.n_q_heads * (size_t)L.max_split * (c.head_dim + 2) * 4);
+  L.ss = take(R * (c.d_model / 16) * 4);
+  L.q = take(R * qd * 2);
+  L.attn_part = take(R * c.n_q_heads * (size_t)L.max_split * (c.head_dim + 4) * 4);
   L.attn_out = take(R * qd * 2);
   L.act = take(R * c.d_ff * 2);
-  size_t part = 0;
-  for (const GemmPlan* g : {&p.qkv, &p.o, &p.gu, &p.d}) part = std::max(part, (size_t)g->S * g->N);
-  L.partial = take(part * R * 4);
-  L.best = take(R * (c.vocab / kColGroup) * 8);
+  L.best = take(R * (c.vocab / 16) * 8);
   L.result = take(sizeof(int) * (2 + kMaxRows));
   L.logits = take(R * (size_t)c.vocab * 4);
   L.rope = take((size_t)c.max_ctx * (c.head_dim / 2) * 8);
   L.total = off;
   return L;
+}
+
+// Rows one forward may carry: at most 64, and the attention workgroup holds
+// at most kAttnQRows (row, q head) pairs of one KV head.
+int max_rows(const sv_config& c) {
+  return std::min(kMaxRows, kAttnQRows / (c.n_q_heads / c.n_kv_heads));
 }
 
 size_t kv_pool_bytes_for(const sv_config& c, int n_pages) {
@@ -137,6 +155,11 @@ struct sv_ctx {
   double prof_ms[kRoles] = {};
   int64_t prof_n[kRoles] = {};
 
+  // HIP graphs of whole forwards, keyed by (rows, attention splits, mode, logits)
+  hipStream_t cap_stream = nullptr;
+  bool use_graphs = true;
+  std::map<std::array<int, 4>, hipGraphExec_t> graphs;
+
   template <class T>
   T* at(size_t off) { return reinterpret_cast<T*>(ws + off); }
 };
@@ -168,99 +191,116 @@ void prof_collect(sv_ctx* c) {
   c->ev_next = 0;
 }
 
-hipError_t gemm_timed(sv_ctx* c, const GemmArgs& g, int role) {
+hipError_t gemm_timed(sv_ctx* c, const GemmArgs& g, int role, int grid, hipStream_t st) {
   hipError_t e = prof_mark(c, role, true);
-  if (e == hipSuccess) e = launch_gemm(g, role, c->stream);
+  if (e == hipSuccess) e = launch_gemm(g, role, grid, st);
   if (e == hipSuccess) e = prof_mark(c, role, false);
   return e;
 }
 
-sv_status forward(sv_ctx* c, int M, const int* ids, int verify) {
+// Queue one whole forward of M rows (kernels only) on `st`.
+hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, hipStream_t st) {
   const sv_config& cfg = c->cfg;
+  const int* d_params = c->at<int>(c->lay.params);
+  float* x = c->at<float>(c->lay.x);
+  float* ss = c->at<float>(c->lay.ss);
+  uint16_t* q = c->at<uint16_t>(c->lay.q);
+  uint16_t* attn_out = c->at<uint16_t>(c->lay.attn_out);
+  uint16_t* act = c->at<uint16_t>(c->lay.act);
+  uint16_t* kv = static_cast<uint16_t*>(c->buf.kv_pool);
+
+  hipError_t e = launch_embed(d_params, M, c->w.embed, cfg.vocab, cfg.d_model, x, ss, st);
+  if (e != hipSuccess) return e;
+
+  GemmArgs g{};
+  g.M = M;
+  g.eps = cfg.rms_eps;
+  g.params = d_params;
+  g.x = x;
+  g.ss_out = ss;
+  g.act_out = act;
+  g.act = cfg.act;
+  g.q_out = q;
+  g.kv_pool = kv;
+  g.page_table = c->buf.page_table;
+  g.n_pages = c->buf.n_pages;
+  g.nq = cfg.n_q_heads;
+  g.nkv = cfg.n_kv_heads;
+  g.dh = cfg.head_dim;
+  g.rope = c->at<const float2>(c->lay.rope);
+  auto plan = [&](const GemmPlan& p, const void* W, const void* Ws) {
+    g.W = W; g.Wscale = Ws; g.N = p.N; g.K = p.K; g.S = p.S; g.fmt = p.fmt;
+  };
+
+  for (int l = 0; l < cfg.n_layers; ++l) {
+    const sv_layer_weights& L = c->layers[l];
+    g.layer = l;
+    // attention block: norm + QKV + RoPE + KV append, attention, O + residual
+    plan(c->plans.qkv, L.wqkv, L.wqkv_scales);
+    g.xf = x; g.ss = ss; g.gain = static_cast<const uint16_t*>(L.g_attn);
+    if ((e = gemm_timed(c, g, kRoleQkv, c->plans.qkv.grid, st)) != hipSuccess) return e;
+    AttnArgs at{};
+    at.params = d_params; at.q = q; at.kv_pool = kv; at.page_table = c->buf.page_table; at.n_pages = c->buf.n_pages;
+    at.layer = l; at.nq = cfg.n_q_heads; at.nkv = cfg.n_kv_heads; at.dh = cfg.head_dim; at.M = M;
+    at.n_split = n_split; at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cfg.head_dim));
+    at.part = c->at<float>(c->lay.attn_part); at.out = attn_out;
+    if ((e = prof_mark(c, kRoleAttn, true)) != hipSuccess) return e;
+    if ((e = launch_attention(at, st)) != hipSuccess) return e;
+    if ((e = prof_mark(c, kRoleAttn, false)) != hipSuccess) return e;
+    plan(c->plans.o, L.wo, L.wo_scales);
+    g.xb = attn_out;
+    if ((e = gemm_timed(c, g, kRoleO, c->plans.o.grid, st)) != hipSuccess) return e;
+    // MLP block: norm + gate/up + activation, down + residual
+    plan(c->plans.gu, L.wgu, L.wgu_scales);
+    g.xf = x; g.ss = ss; g.gain = static_cast<const uint16_t*>(L.g_mlp);
+    if ((e = gemm_timed(c, g, kRoleGateUp, c->plans.gu.grid, st)) != hipSuccess) return e;
+    plan(c->plans.d, L.wd, L.wd_scales);
+    g.xb = act;
+    if ((e = gemm_timed(c, g, kRoleDown, c->plans.d.grid, st)) != hipSuccess) return e;
+  }
+
+  // final norm + LM head + per-64-column argmax, then acceptance
+  plan(c->plans.lm, c->w.lm_head, nullptr);
+  g.xf = x; g.ss = ss; g.gain = static_cast<const uint16_t*>(c->w.g_final);
+  g.best = c->at<uint64_t>(c->lay.best);
+  g.logits = c->store_logits ? c->at<float>(c->lay.logits) : nullptr;
+  if ((e = gemm_timed(c, g, kRoleLmHead, c->plans.lm.grid, st)) != hipSuccess) return e;
+  return launch_accept(d_params, M, verify, g.best, cfg.vocab / 16, c->at<int>(c->lay.result), st);
+}
+
+sv_status forward(sv_ctx* c, int M, const int* ids, int verify) {
   hipStream_t st = c->stream;
-  const int qd = cfg.n_q_heads * cfg.head_dim;
   int* d_params = c->at<int>(c->lay.params);
   c->h_params[0] = c->kv_len;
   c->h_params[1] = M;
   std::memcpy(c->h_params + 2, ids, sizeof(int) * M);
   if (hipMemcpyAsync(d_params, c->h_params, sizeof(int) * (2 + M), hipMemcpyHostToDevice, st) != hipSuccess)
     return SV_EDEVICE;
+  const int n_split = attn_splits(c->kv_len + M);
 
-  float* x = c->at<float>(c->lay.x);
-  float* ss = c->at<float>(c->lay.ss);
-  float* q = c->at<float>(c->lay.q);
-  float* partial = c->at<float>(c->lay.partial);
-  uint16_t* attn_out = c->at<uint16_t>(c->lay.attn_out);
-  uint16_t* act = c->at<uint16_t>(c->lay.act);
-  const float2* rope = c->at<const float2>(c->lay.rope);
-  uint16_t* kv = static_cast<uint16_t*>(c->buf.kv_pool);
-
-  hipError_t e = launch_embed(d_params, M, c->w.embed, cfg.vocab, cfg.d_model, x, ss, st);
-  if (e != hipSuccess) return SV_EDEVICE;
-
-  const int n_split = (c->kv_len + M + kAttnSplit - 1) / kAttnSplit;
-  for (int l = 0; l < cfg.n_layers && e == hipSuccess; ++l) {
-    const sv_layer_weights& L = c->layers[l];
-    GemmArgs g{};
-    g.M = M;
-    g.eps = cfg.rms_eps;
-    g.partial = partial;
-
-    // attention block
-    g.W = L.wqkv; g.Wscale = L.wqkv_scales; g.N = c->plans.qkv.N; g.K = c->plans.qkv.K; g.S = c->plans.qkv.S;
-    g.fmt = c->plans.qkv.fmt;
-    g.xf = x; g.ss = ss; g.gain = static_cast<const uint16_t*>(L.g_attn);
-    if ((e = gemm_timed(c, g, kRoleQkv)) != hipSuccess) break;
-    EpiArgs ep{};
-    ep.partial = partial; ep.S = g.S; ep.M = M; ep.N = g.N; ep.kind = kEpiQkv; ep.params = d_params;
-    ep.q_out = q; ep.kv_pool = kv; ep.page_table = c->buf.page_table; ep.n_pages = c->buf.n_pages; ep.layer = l;
-    ep.nq = cfg.n_q_heads; ep.nkv = cfg.n_kv_heads; ep.dh = cfg.head_dim; ep.rope = rope;
-    if ((e = launch_epilogue(ep, st)) != hipSuccess) break;
-    AttnArgs at{};
-    at.params = d_params; at.q = q; at.kv_pool = kv; at.page_table = c->buf.page_table; at.n_pages = c->buf.n_pages;
-    at.layer = l; at.nq = cfg.n_q_heads; at.nkv = cfg.n_kv_heads; at.dh = cfg.head_dim; at.M = M;
-    at.n_split = n_split; at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cfg.head_dim));
-    at.part = c->at<float>(c->lay.attn_part); at.out = attn_out;
-    if ((e = prof_mark(c, kRoleAttn, true)) != hipSuccess) break;
-    if ((e = launch_attention(at, st)) != hipSuccess) break;
-    if ((e = prof_mark(c, kRoleAttn, false)) != hipSuccess) break;
-    g.W = L.wo; g.Wscale = L.wo_scales; g.N = c->plans.o.N; g.K = c->plans.o.K; g.S = c->plans.o.S;
-    g.xb = attn_out;
-    if ((e = gemm_timed(c, g, kRoleO)) != hipSuccess) break;
-    ep = EpiArgs{};
-    ep.partial = partial; ep.S = g.S; ep.M = M; ep.N = g.N; ep.kind = kEpiResid; ep.params = d_params;
-    ep.x = x; ep.ss = ss;
-    if ((e = launch_epilogue(ep, st)) != hipSuccess) break;
-
-    // MLP block
-    g.W = L.wgu; g.Wscale = L.wgu_scales; g.N = c->plans.gu.N; g.K = c->plans.gu.K; g.S = c->plans.gu.S;
-    g.xf = x; g.ss = ss; g.gain = static_cast<const uint16_t*>(L.g_mlp);
-    if ((e = gemm_timed(c, g, kRoleGateUp)) != hipSuccess) break;
-    ep = EpiArgs{};
-    ep.partial = partial; ep.S = g.S; ep.M = M; ep.N = g.N; ep.kind = kEpiGlu; ep.params = d_params;
-    ep.act_out = act; ep.act = cfg.act;
-    if ((e = launch_epilogue(ep, st)) != hipSuccess) break;
-    g.W = L.wd; g.Wscale = L.wd_scales; g.N = c->plans.d.N; g.K = c->plans.d.K; g.S = c->plans.d.S;
-    g.xb = act;
-    if ((e = gemm_timed(c, g, kRoleDown)) != hipSuccess) break;
-    ep = EpiArgs{};
-    ep.partial = partial; ep.S = g.S; ep.M = M; ep.N = g.N; ep.kind = kEpiResid; ep.params = d_params;
-    ep.x = x; ep.ss = ss;
-    if ((e = launch_epilogue(ep, st)) != hipSuccess) break;
+  if (c->use_graphs && c->prof_mask == 0) {
+    const std::array<int, 4> key = {M, n_split, verify, c->store_logits};
+    auto it = c->graphs.find(key);
+    if (it == c->graphs.end()) {
+      hipGraph_t graph = nullptr;
+      hipGraphExec_t exec = nullptr;
+      if (hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal) != hipSuccess) return SV_EDEVICE;
+      const hipError_t e = enqueue_forward(c, M, verify, n_split, c->cap_stream);
+      const hipError_t e2 = hipStreamEndCapture(c->cap_stream, &graph);
+      if (e != hipSuccess || e2 != hipSuccess || graph == nullptr) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return SV_EDEVICE;
+      }
+      const hipError_t e3 = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+      (void)hipGraphDestroy(graph);
+      if (e3 != hipSuccess) return SV_EDEVICE;
+      it = c->graphs.emplace(key, exec).first;
+    }
+    if (hipGraphLaunch(it->second, st) != hipSuccess) return SV_EDEVICE;
+  } else {
+    if (enqueue_forward(c, M, verify, n_split, st) != hipSuccess) return SV_EDEVICE;
   }
-  if (e != hipSuccess) return SV_EDEVICE;
-
-  // final norm + LM head + per-64-column argmax, then acceptance
-  GemmArgs g{};
-  g.M = M; g.eps = cfg.rms_eps; g.fmt = 0;
-  g.W = c->w.lm_head; g.N = c->plans.lm.N; g.K = c->plans.lm.K; g.S = 1;
-  g.xf = x; g.ss = ss; g.gain = static_cast<const uint16_t*>(c->w.g_final);
-  g.best = c->at<uint64_t>(c->lay.best);
-  g.logits = c->store_logits ? c->at<float>(c->lay.logits) : nullptr;
-  if (gemm_timed(c, g, kRoleLmHead) != hipSuccess) return SV_EDEVICE;
   int* d_result = c->at<int>(c->lay.result);
-  if (launch_accept(d_params, M, verify, g.best, cfg.vocab / kColGroup, d_result, st) != hipSuccess)
-    return SV_EDEVICE;
   if (hipMemcpyAsync(c->h_result, d_result, sizeof(int) * (2 + M), hipMemcpyDeviceToHost, st) != hipSuccess)
     return SV_EDEVICE;
   if (hipStreamSynchronize(st) != hipSuccess) return SV_EDEVICE;
@@ -295,7 +335,8 @@ const char* sv_status_str(sv_status s) {
 
 sv_status sv_query_sizes(const sv_config* cfg, int64_t* kv_pool_bytes, int64_t* workspace_bytes) {
   if (!cfg || !valid_config(*cfg)) return SV_EINVAL;
-  const Plans p = make_plans(*cfg);
+  const Plans p = make_plans(*cfg, 256);
+  if (!plans_ok(p)) return SV_EUNSUPPORTED;
   const Layout L = make_layout(*cfg, p);
   if (kv_pool_bytes) *kv_pool_bytes = (int64_t)kv_pool_bytes_for(*cfg, cfg->max_ctx / kPage);
   if (workspace_bytes) *workspace_bytes = (int64_t)L.total;
@@ -319,13 +360,17 @@ sv_status sv_packed_linear_bytes(int32_t fmt, int32_t n, int32_t k, int64_t* byt
   return SV_EINVAL;
 }
 
-sv_status sv_pack_linear(int32_t fmt, const void* src0, const void* src0_scales, const void* src1,
-                         const void* src1_scales, int32_t n, int32_t k, void* dst, void* dst_scales, void* stream) {
+sv_status sv_pack_linear(int32_t fmt, int32_t layout, const void* src0, const void* src0_scales, const void* src1,
+                         const void* src1_scales, int32_t n, int32_t k, int32_t head_dim, void* dst, void* dst_scales,
+                         void* stream) {
   if (!src0 || !dst) return SV_EINVAL;
   if (sv_packed_linear_bytes(fmt, n, k, nullptr, nullptr) != SV_OK) return SV_EINVAL;
   if (fmt == 1 && (!src0_scales || !dst_scales || (src1 && !src1_scales))) return SV_EINVAL;
-  if (launch_pack(fmt, src0, src0_scales, src1, src1_scales, n, k, dst, dst_scales, (hipStream_t)stream) !=
-      hipSuccess)
+  if (layout < 0 || layout > 2) return SV_EINVAL;
+  if ((layout == 1) != (src1 != nullptr)) return SV_EINVAL;
+  if (layout == 2 && ((head_dim != 64 && head_dim != 128) || n % head_dim)) return SV_EINVAL;
+  if (launch_pack(fmt, layout, src0, src0_scales, src1, src1_scales, n, k, head_dim, dst, dst_scales,
+                  (hipStream_t)stream) != hipSuccess)
     return SV_EDEVICE;
   return SV_OK;
 }
@@ -340,7 +385,12 @@ sv_status sv_create(const sv_config* cfg, const sv_weights* w, const sv_buffers*
     if (!L.wqkv || !L.wo || !L.wgu || !L.wd || !L.g_attn || !L.g_mlp) return SV_EINVAL;
     if (cfg->weight_fmt == 1 && (!L.wqkv_scales || !L.wo_scales || !L.wgu_scales || !L.wd_scales)) return SV_EINVAL;
   }
-  const Plans p = make_plans(*cfg);
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+    return SV_EDEVICE;
+  const Plans p = make_plans(*cfg, n_cu);
+  if (!plans_ok(p)) return SV_EUNSUPPORTED;
   const Layout lay = make_layout(*cfg, p);
   if (!buf->kv_pool || !buf->page_table || !buf->workspace) return SV_EINVAL;
   if (buf->n_pages < 1 || buf->kv_pool_bytes < (int64_t)kv_pool_bytes_for(*cfg, buf->n_pages)) return SV_EINVAL;
@@ -380,6 +430,13 @@ sv_status sv_create(const sv_config* cfg, const sv_weights* w, const sv_buffers*
       tab[((size_t)pos * half + i) * 2 + 0] = (float)std::cos(ang);
       tab[((size_t)pos * half + i) * 2 + 1] = (float)std::sin(ang);
     }
+  const char* ng = std::getenv("SV_NO_GRAPH");
+  c->use_graphs = !(ng && ng[0] == '1');
+  if (hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking) != hipSuccess) {
+    c->cap_stream = nullptr;
+    sv_destroy(c);
+    return SV_EDEVICE;
+  }
   if (hipMemcpyAsync(c->ws + lay.rope, tab.data(), tab.size() * 4, hipMemcpyHostToDevice, c->stream) != hipSuccess ||
       hipStreamSynchronize(c->stream) != hipSuccess) {
     sv_destroy(c);
@@ -392,6 +449,8 @@ sv_status sv_create(const sv_config* cfg, const sv_weights* w, const sv_buffers*
 void sv_destroy(sv_ctx* c) {
   if (!c) return;
   for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
+  for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);
+  if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
   if (c->h_params) (void)hipHostFree(c->h_params);
   if (c->h_result) (void)hipHostFree(c->h_result);
   delete c;
@@ -404,8 +463,9 @@ sv_status sv_prefill(sv_ctx* c, const int32_t* ids, int32_t n, int32_t* next_id)
   if (!c || !ids || n < 1) return SV_EINVAL;
   if (!ids_ok(c, ids, n)) return SV_EINVAL;
   if ((int64_t)c->kv_len + n > c->cfg.max_ctx) return SV_ENOSPACE;
-  for (int off = 0; off < n; off += kMaxRows) {
-    const int m = std::min(kMaxRows, n - off);
+  const int chunk = max_rows(c->cfg);
+  for (int off = 0; off < n; off += chunk) {
+    const int m = std::min(chunk, n - off);
     const sv_status s = forward(c, m, ids + off, 0);
     if (s != SV_OK) return s;
     for (int r = 0; r < m; ++r) c->hist[c->kv_len + r] = c->h_result[2 + r];

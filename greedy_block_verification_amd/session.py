@@ -38,16 +38,16 @@ class DeviceModel:
         cfg = self.cfg
         fmt = 0 if cfg.weight_fmt == "bf16" else 1
         self.fmt = fmt
-        self.embed = self._pack(0, weights.embed, None)[0]
+        self.embed = self._pack(0, 0, weights.embed, None)[0]
         self.g_final = self._keep(_dev(weights.g_final, self.device))
         self.layer_structs = (B.sv_layer_weights * cfg.n_layers)()
         for l, L in enumerate(weights.layers):
             qkv = np.concatenate([L["wq"], L["wk"], L["wv"]], axis=0)
             qkv_s = np.concatenate([L["wq_s"], L["wk_s"], L["wv_s"]], axis=0) if fmt else None
-            wqkv, wqkv_s = self._pack(fmt, qkv, qkv_s)
-            wo, wo_s = self._pack(fmt, L["wo"], L.get("wo_s"))
-            wgu, wgu_s = self._pack(fmt, L["wg"], L.get("wg_s"), L["wu"], L.get("wu_s"))
-            wd, wd_s = self._pack(fmt, L["wd"], L.get("wd_s"))
+            wqkv, wqkv_s = self._pack(fmt, 2, qkv, qkv_s)
+            wo, wo_s = self._pack(fmt, 0, L["wo"], L.get("wo_s"))
+            wgu, wgu_s = self._pack(fmt, 1, L["wg"], L.get("wg_s"), L["wu"], L.get("wu_s"))
+            wd, wd_s = self._pack(fmt, 0, L["wd"], L.get("wd_s"))
             ga = self._keep(_dev(L["g_attn"], self.device))
             gm = self._keep(_dev(L["g_mlp"], self.device))
             s = self.layer_structs[l]
@@ -62,7 +62,7 @@ class DeviceModel:
         self.keep.append(t)
         return t.data_ptr()
 
-    def _pack(self, fmt, w0, s0, w1=None, s1=None):
+    def _pack(self, fmt, layout, w0, s0, w1=None, s1=None):
         n, k = w0.shape
         nb, sb = B.sv_packed_linear_bytes(fmt, n * (2 if w1 is not None else 1), k)
         dst = torch.empty(nb, dtype=torch.uint8, device=self.device)
@@ -71,9 +71,9 @@ class DeviceModel:
         t1 = _dev(w1, self.device) if w1 is not None else None
         ts0 = _dev(s0, self.device) if fmt else None
         ts1 = _dev(s1, self.device) if (fmt and w1 is not None) else None
-        B.sv_pack_linear(fmt, t0.data_ptr(), ts0.data_ptr() if ts0 is not None else None,
+        B.sv_pack_linear(fmt, layout, t0.data_ptr(), ts0.data_ptr() if ts0 is not None else None,
                          t1.data_ptr() if t1 is not None else None, ts1.data_ptr() if ts1 is not None else None,
-                         n, k, dst.data_ptr(), dst_s.data_ptr() if dst_s is not None else None,
+                         n, k, self.cfg.head_dim, dst.data_ptr(), dst_s.data_ptr() if dst_s is not None else None,
                          self.stream.cuda_stream)
         torch.cuda.synchronize(self.device)
         del t0, t1, ts0, ts1

@@ -55,9 +55,9 @@ typedef struct {
 
 /* One layer's weights, all device pointers in the packed layouts that
  * sv_pack_linear produces:
- *   wqkv  [q | k | v] rows (n_q*dh + 2*n_kv*dh outputs) x d_model inputs
+ *   wqkv  [q | k | v] rows (n_q*dh + 2*n_kv*dh outputs) x d_model inputs, layout 2
  *   wo    d_model outputs x n_q*dh inputs
- *   wgu   gate and up, interleaved by sv_pack_linear(src1 != NULL), 2*d_ff outputs x d_model
+ *   wgu   gate and up, interleaved by sv_pack_linear layout 1, 2*d_ff outputs x d_model
  *   wd    d_model outputs x d_ff inputs
  *   *_scales: packed bf16 group scales (int4 only, else NULL)
  *   g_attn, g_mlp: bf16 RMSNorm gains [d_model] (plain, unpacked). */
@@ -101,13 +101,18 @@ sv_status sv_packed_linear_bytes(int32_t fmt, int32_t n, int32_t k, int64_t *byt
 /* Repack a row-major linear into the tiled layout the kernels stream
  * (a pure permutation, bit-exact).  src0: device [n x k] (bf16, or int8 codes
  * in [-8, 7] for fmt 1) with src0_scales device bf16 [n x k/64] (fmt 1).
- * If src1 != NULL (gate/up), src1 is a second [n x k] matrix and the packed
- * output holds 2n outputs, interleaving 16-output blocks of src0 and src1.
+ * layout 0: plain (O, down, embedding / LM head).
+ * layout 1: gate/up; src1 is the up matrix [n x k] (+ scales), and the packed
+ *           output holds 2n outputs, 16-output blocks of src0 and src1
+ *           interleaved.
+ * layout 2: fused QKV ([q heads | k heads | v heads] x head_dim rows); rows
+ *           are reordered inside each head so every 64-output group holds
+ *           RoPE pairs (i, i + head_dim/2).  head_dim is 64 or 128.
  * dst / dst_scales: device, sizes from sv_packed_linear_bytes (for 2n outputs
- * when interleaving).  Runs on `stream` (hipStream_t, NULL = default). */
-sv_status sv_pack_linear(int32_t fmt, const void *src0, const void *src0_scales,
+ * with layout 1).  Runs on `stream` (hipStream_t, NULL = default). */
+sv_status sv_pack_linear(int32_t fmt, int32_t layout, const void *src0, const void *src0_scales,
                          const void *src1, const void *src1_scales, int32_t n, int32_t k,
-                         void *dst, void *dst_scales, void *stream);
+                         int32_t head_dim, void *dst, void *dst_scales, void *stream);
 
 /* Create a context at kv_len = 0.  Validates cfg and buffer sizes, uploads the
  * RoPE table (angle pos * theta^(-2i/head_dim), cos/sin evaluated in double and
