@@ -67,6 +67,8 @@ SIGNATURES = {
     "sv_set_debug": (C.c_int, [C.c_void_p, C.c_int32]),
     "sv_get_logits": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32]),
     "sv_last_argmax": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
+    "sv_history": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32]),
+    "sv_restore": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_int32)]),
     "sv_set_profile": (C.c_int, [C.c_void_p, C.c_int32]),
     "sv_profile_read": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
     "sv_profile_reset": (C.c_int, [C.c_void_p]),
@@ -198,3 +200,13 @@ def sv_profile_read(ctx, role: int):
 
 def sv_profile_reset(ctx):
     _check(lib().sv_profile_reset(ctx), "sv_profile_reset")
+
+
+def sv_history(ctx, n: int):
+    buf = (C.c_int32 * max(1, n))()
+    _check(lib().sv_history(ctx, buf, int(n)), "sv_history")
+    return list(buf[:n])
+
+
+def sv_restore(ctx, kv_len: int, greedy_hist):
+    _check(lib().sv_restore(ctx, int(kv_len), _i32_array(greedy_hist)), "sv_restore")

@@ -20,6 +20,7 @@
 namespace sv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 
@@ -41,6 +42,15 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 }
 
 __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
+
+// fp32 -> IEEE binary16 bits, round to nearest even (hardware conversion).
+__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+__device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                0);
+}
 
 __device__ __forceinline__ f32x4 mfma16x16x32(uint4 a, uint4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
@@ -101,37 +111,78 @@ __device__ __forceinline__ float block_sum256(float v, float* lds4) {
 // output tile (16 outputs) over the whole K.  A workgroup of NW waves takes
 // items blockIdx.x, blockIdx.x + gridDim.x, ...; its waves split K into NW
 // contiguous slices (fixed per matrix).  Each wave runs its chunks in
-// ascending order through one MFMA accumulator chain per row tile; the NW
-// wave partials are added in wave order through LDS.  The row count only
-// sets how many row tiles are computed, and no value crosses workgroups, so a
-// row's result never depends on M.  Weights are requested before anything
-// else, the normalised activations of a wave's K slice are built once per
-// workgroup (kept in registers), and the next item's weights are in flight
-// while the current item is reduced and finished.  Epilogue per role:
-//   QKV      tile = 8 dims + their RoPE partners (+ dh/2): RoPE, K/V into the
-//            paged cache (bf16), q (bf16) to the workspace
-//   O, down  residual add, per-16-column sum of squares for RMSNorm
-//   gate/up  tile = 8 gate + 8 up outputs of the same features: act(g) * u
-//   LM head  per-16-column (max logit, lowest id), optional fp32 logits
+// ascending order through one MFMA accumulator chain per row tile, the hi
+// plane of a chunk before its lo plane; the NW wave partials are added in
+// wave order through LDS.  The row count only sets how many row tiles are
+// computed, and no value crosses workgroups, so a row's result never depends
+// on M.  Weights are requested before anything else and the next item's
+// weights are in flight while the current item is reduced and finished.
+//
+// RMSNorm commutes with the product: W (x * g / rms) = (W (x * g)) / rms, so
+// producers hand over planes of x * g and the consumer scales its outputs by
+// 1 / rms in the epilogue.  Epilogue per role:
+//   QKV      tile = 8 dims + their RoPE partners (+ dh/2): 1/rms, RoPE, K/V
+//            into the paged cache (fp16), q (fp32) to the workspace
+//   O, down  residual add, per-16-column sum of squares, planes of x * g_next
+//   gate/up  tile = 8 gate + 8 up outputs of the same features: 1/rms,
+//            act(g) * u as planes
+//   LM head  1/rms, per-16-column (max logit, lowest id), optional fp32 logits
 
-template <int BM>
-__device__ __forceinline__ uint4 load_b(const GemmArgs& a, int r, int k0, float inv) {
-  if (BM == kBBf16) {
-    return *reinterpret_cast<const uint4*>(a.xb + (size_t)r * a.K + k0);
-  } else {
-    const float4* xp = reinterpret_cast<const float4*>(a.xf + (size_t)r * a.K + k0);
-    const float4 x0 = xp[0], x1 = xp[1];
-    const uint4 gb = *reinterpret_cast<const uint4*>(a.gain + k0);
-    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    const uint32_t gw[4] = {gb.x, gb.y, gb.z, gb.w};
-    uint16_t h[8];
+// An fp32 vector as the MFMA operand pair hi = bf16(h), lo = bf16(h - hi)
+// (the difference is exact in fp32): two MFMAs against the exact bf16
+// weights give the products of h to about 16 significant bits.
+struct BPair {
+  uint4 hi, lo;
+};
+
+__device__ __forceinline__ BPair split8(const float (&h)[8]) {
+  uint16_t hb[8], lb[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float g = bf2f((uint16_t)((gw[e >> 1] >> ((e & 1) * 16)) & 0xffffu));
-      h[e] = f2bf((xs[e] * inv) * g);
-    }
-    return make_uint4(pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7]));
+  for (int e = 0; e < 8; ++e) {
+    hb[e] = f2bf(h[e]);
+    lb[e] = f2bf(h[e] - bf2f(hb[e]));
   }
+  BPair b;
+  b.hi = make_uint4(pack2(hb[0], hb[1]), pack2(hb[2], hb[3]), pack2(hb[4], hb[5]), pack2(hb[6], hb[7]));
+  b.lo = make_uint4(pack2(lb[0], lb[1]), pack2(lb[2], lb[3]), pack2(lb[4], lb[5]), pack2(lb[6], lb[7]));
+  return b;
+}
+
+__device__ __forceinline__ void split1(float h, uint16_t& hi, uint16_t& lo) {
+  hi = f2bf(h);
+  lo = f2bf(h - bf2f(hi));
+}
+
+__device__ __forceinline__ BPair bzero() { return BPair{make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)}; }
+
+__device__ __forceinline__ BPair load_planes(const GemmArgs& a, int r, int k0) {
+  const size_t off = (size_t)r * a.K + k0;
+  return BPair{*reinterpret_cast<const uint4*>(a.bhi + off), *reinterpret_cast<const uint4*>(a.blo + off)};
+}
+
+__device__ __forceinline__ f32x4 mfma_pair(uint4 a, const BPair& b, f32x4 c) {
+  c = mfma16x16x32(a, b.hi, c);
+  return mfma16x16x32(a, b.lo, c);
+}
+
+// The same compensated pair in fp16 (hi = fp16(h), lo = fp16(h - hi)), for
+// products against the fp16 KV cache.
+__device__ __forceinline__ BPair split8_f16(const float (&h)[8]) {
+  uint16_t hb[8], lb[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    hb[e] = f2h(h[e]);
+    lb[e] = f2h(h[e] - h2f(hb[e]));
+  }
+  BPair b;
+  b.hi = make_uint4(pack2(hb[0], hb[1]), pack2(hb[2], hb[3]), pack2(hb[4], hb[5]), pack2(hb[6], hb[7]));
+  b.lo = make_uint4(pack2(lb[0], lb[1]), pack2(lb[2], lb[3]), pack2(lb[4], lb[5]), pack2(lb[6], lb[7]));
+  return b;
+}
+
+__device__ __forceinline__ f32x4 mfma_pair_f16(uint4 a, const BPair& b, f32x4 c) {
+  c = mfma16x16x32_f16(a, b.hi, c);
+  return mfma16x16x32_f16(a, b.lo, c);
 }
 
 // int4 nibble -> bf16 bits of the integer code (exact).
@@ -155,20 +206,21 @@ __device__ __forceinline__ float act_fn(float x, int act) {
 }
 
 constexpr int kMaxWaves = 16;
-constexpr int kBatch = 8;       // chunks (1 KiB of weights each) one wave keeps in flight
-constexpr int kCacheB = 8;      // most chunks per wave whose activations stay in registers
+constexpr int kStageBytes = kGemmStageBytes;   // LDS for staged activation planes (hi + lo)
 
 struct GemmShared {
   f32x4 red[kMaxWaves][64];   // wave partials of one row tile
   float y[kMaxRows][16];      // finished outputs of the item
-  float inv[kMaxRows];        // 1 / rms of each row (kBNorm)
+  float inv[kMaxRows];        // 1 / rms of each row (RMSNorm consumers)
 };
+
+__device__ __forceinline__ constexpr bool norm_role(int role) {
+  return role == kRoleQkv || role == kRoleGateUp || role == kRoleLmHead;
+}
 
 // 1 / sqrt(mean(x^2) + eps) per row from the per-16-column sums of squares:
 // one wave per row, each lane adds its slices in order, then a butterfly.
-template <int BM>
 __device__ __forceinline__ void rows_inv_rms(const GemmArgs& a, GemmShared& sh, int wave, int lane, int nw) {
-  if (BM != kBNorm) return;
   const int nsl = a.K >> 4;
   for (int r = wave; r < a.M; r += nw) {
     const float* p = a.ss + (size_t)r * nsl;
@@ -177,7 +229,6 @@ __device__ __forceinline__ void rows_inv_rms(const GemmArgs& a, GemmShared& sh, 
     v = wave_sum(v);
     if (lane == 0) sh.inv[r] = 1.0f / sqrtf(v / (float)a.K + a.eps);
   }
-  __syncthreads();
 }
 
 // Epilogue on the finished 16 columns of item (tile) T.
@@ -185,7 +236,8 @@ template <int ROLE>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, GemmShared& sh, int T) {
   for (int idx = threadIdx.x; idx < a.M * 16; idx += blockDim.x) {
     const int r = idx >> 4, c = idx & 15;
-    const float y = sh.y[r][c];
+    float y = sh.y[r][c];
+    if (norm_role(ROLE)) y = y * sh.inv[r];
     if (ROLE == kRoleO || ROLE == kRoleDown) {
       const int n = T * 16 + c;
       const size_t xi = (size_t)r * a.N + n;
@@ -195,8 +247,13 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, GemmShared& sh,
 #pragma unroll
       for (int o = 8; o >= 1; o >>= 1) sq += __shfl_xor(sq, o);
       if (c == 0) a.ss_out[(size_t)r * (a.N >> 4) + T] = sq;
+      split1(xn * bf2f(a.gnext[n]), a.uhi[xi], a.ulo[xi]);
     } else if (ROLE == kRoleGateUp) {               // [gate 8 | up 8] of features 8T..8T+7
-      if (c < 8) a.act_out[(size_t)r * (a.N >> 1) + T * 8 + c] = f2bf(act_fn(y, a.act) * sh.y[r][c + 8]);
+      const float up = sh.y[r][(c & 7) + 8] * sh.inv[r];
+      if (c < 8) {
+        const size_t ai = (size_t)r * (a.N >> 1) + T * 8 + c;
+        split1(act_fn(y, a.act) * up, a.ahi[ai], a.alo[ai]);
+      }
     } else if (ROLE == kRoleQkv) {                  // [dims 8s+i | half + 8s + i], i < 8
       const int half = a.dh >> 1;
       const int gph = half >> 3;
@@ -208,17 +265,17 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, GemmShared& sh,
       float out = y;
       if (hh < a.nq + a.nkv) {
         const float2 cs = a.rope[(size_t)pos * half + i];
-        const float partner = sh.y[r][c ^ 8];
+        const float partner = sh.y[r][c ^ 8] * sh.inv[r];
         out = lo ? (y * cs.x - partner * cs.y) : (y * cs.x + partner * cs.y);
       }
       if (hh < a.nq) {
-        a.q_out[((size_t)r * a.nq + hh) * a.dh + d] = f2bf(out);
+        a.q_out[((size_t)r * a.nq + hh) * a.dh + d] = out;
       } else {
         const int kv = hh < a.nq + a.nkv ? 0 : 1;
         const int head = hh - a.nq - kv * a.nkv;
         const int page = a.page_table[pos / kPage];
         const size_t off = ((((size_t)a.layer * a.n_pages + page) * 2 + kv) * a.nkv + head) * kPage + (pos % kPage);
-        a.kv_pool[off * a.dh + d] = f2bf(out);
+        a.kv_pool[off * a.dh + d] = f2h(out);
       }
     } else {                                        // kRoleLmHead
       const int n = T * 16 + c;
@@ -257,103 +314,144 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& a, GemmShared& sh, f
   __syncthreads();
 }
 
-template <int TM, int BM, int ROLE>
+// Activation planes of chunk range [c_lo, c_lo + n_chunks) of every row,
+// staged in LDS as [row][k] with a 16-byte pad per row (bank spread).
+// `unit` = inputs per chunk (32 for bf16, 128 for int4).
+struct Stage {
+  uint16_t* hi;
+  uint16_t* lo;
+  int stride;   // bf16 elements per LDS row
+};
+
+__device__ __forceinline__ void stage_planes(const GemmArgs& a, const Stage& st, int c_lo, int n_chunks, int unit) {
+  const int width = n_chunks * unit;            // inputs per row in the stage
+  const int vec_per_row = width >> 3;           // 16-byte vectors per row and plane
+  const int total = a.M * vec_per_row;
+  const size_t k0 = (size_t)c_lo * unit;
+  for (int i = threadIdx.x; i < total; i += blockDim.x) {
+    const int r = i / vec_per_row, v = i % vec_per_row;
+    const size_t src = (size_t)r * a.K + k0 + (size_t)v * 8;
+    *reinterpret_cast<uint4*>(st.hi + r * st.stride + v * 8) = *reinterpret_cast<const uint4*>(a.bhi + src);
+    *reinterpret_cast<uint4*>(st.lo + r * st.stride + v * 8) = *reinterpret_cast<const uint4*>(a.blo + src);
+  }
+}
+
+// MFMA column (row slot) r of a row tile reads row min(r, M - 1).  An MFMA
+// output column depends only on its own B column, so the duplicated columns
+// past M change no kept result; they are dropped at the end.  Clamping keeps
+// every MFMA out of divergent control flow: an MFMA in a branch that only
+// some lanes take has been seen to overwrite registers that the lanes on the
+// other side of the branch still hold live.
+__device__ __forceinline__ int row_of(int r, int M) { return r < M ? r : M - 1; }
+
+__device__ __forceinline__ BPair lds_pair(const Stage& st, int r, int k) {
+  return BPair{*reinterpret_cast<const uint4*>(st.hi + r * st.stride + k),
+               *reinterpret_cast<const uint4*>(st.lo + r * st.stride + k)};
+}
+
+// Chunks per LDS stage: the largest multiple of nw dividing the chunk count
+// whose activation planes for M rows fit the stage budget.  It only decides
+// when activations are staged, never the order of any sum.
+__host__ __device__ __forceinline__ int stage_chunks(int n_chunks, int nw, int M, int unit) {
+  int best = nw;
+  for (int cs = nw; cs <= n_chunks; cs += nw) {
+    if (n_chunks % cs) continue;
+    if ((size_t)M * (cs * unit + 8) * 4 <= (size_t)kStageBytes) best = cs;
+  }
+  return best;
+}
+
+// Wave w accumulates chunks w, w + NW, w + 2 NW, ... in that order.
+template <int TM, int ROLE>
 __global__ __launch_bounds__(1024) void k_gemm_bf16(GemmArgs a) {
   __shared__ GemmShared sh;
+  __shared__ __align__(16) uint16_t stage_mem[kStageBytes / 2];
   const int nw = blockDim.x >> 6;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int KC = a.K >> 5;
-  const int cpw = KC / nw;
-  const int kc0 = wave * cpw;
+  const int cs = stage_chunks(KC, nw, a.M, 32);
+  const int n_stages = KC / cs;
+  const int cpws = cs / nw;                     // chunks per wave per stage
+  Stage st;
+  st.stride = cs * 32 + 8;
+  st.hi = stage_mem;
+  st.lo = stage_mem + (size_t)a.M * st.stride;
   const int n_items = a.N >> 4;
   int T = blockIdx.x;
   const uint4* W4 = reinterpret_cast<const uint4*>(a.W) + lane;
   // packed weights are tile-major: chunk kc of tile T is the KiB at (T * KC + kc)
   auto wptr = [&](int t, int kc) { return W4 + ((size_t)t * KC + kc) * 64; };
+  constexpr int NB = 8;                         // weight chunks in flight per wave
 
-  // weights of the first batch of the first item: requested before anything else
-  uint4 A[kBatch];
+  uint4 A[NB];
+  auto load_a = [&](int t, int s, int b0) {
 #pragma unroll
-  for (int u = 0; u < kBatch; ++u)
-    if (u < cpw) A[u] = ld_stream(wptr(T, kc0 + u));
-
-  // normalised activations of this wave's K slice, built once
-  rows_inv_rms<BM>(a, sh, wave, lane, nw);
-  constexpr bool CACHE = (BM == kBNorm);
-  uint4 Bc[CACHE ? kCacheB : 1][TM];
-  if (CACHE) {
-#pragma unroll
-    for (int rt = 0; rt < TM; ++rt) {
-      const int r = rt * 16 + j;
-      const float inv = r < a.M ? sh.inv[r] : 0.f;
-#pragma unroll
-      for (int u = 0; u < kCacheB; ++u) {
-        Bc[CACHE ? u : 0][rt] = make_uint4(0u, 0u, 0u, 0u);
-        if (u < cpw && r < a.M) Bc[CACHE ? u : 0][rt] = load_b<BM>(a, r, (kc0 + u) * 32 + g * 8, inv);
-      }
-    }
+    for (int u = 0; u < NB; ++u)
+      if (b0 + u < cpws) A[u] = ld_stream(wptr(t, s * cs + wave + nw * (b0 + u)));
+  };
+  load_a(T, 0, 0);                              // requested before anything else
+  if (norm_role(ROLE)) rows_inv_rms(a, sh, wave, lane, nw);   // read only by the epilogue
+  if (n_stages == 1) {
+    stage_planes(a, st, 0, cs, 32);
+    __syncthreads();
   }
 
   for (;;) {
     f32x4 acc[TM];
 #pragma unroll
     for (int rt = 0; rt < TM; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int b0 = 0; b0 < cpw; b0 += kBatch) {
-      if (b0 > 0) {
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u)
-          if (b0 + u < cpw) A[u] = ld_stream(wptr(T, kc0 + b0 + u));
+    for (int s = 0; s < n_stages; ++s) {
+      if (n_stages > 1) {
+        __syncthreads();
+        stage_planes(a, st, s * cs, cs, 32);
+        __syncthreads();
       }
+      for (int b0 = 0; b0 < cpws; b0 += NB) {
+        if (s > 0 || b0 > 0) load_a(T, s, b0);
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (b0 + u < cpw) {
+        for (int u = 0; u < NB; ++u) {
+          if (b0 + u < cpws) {
+            const int kl = (wave + nw * (b0 + u)) * 32 + g * 8;   // input index inside the stage
 #pragma unroll
-          for (int rt = 0; rt < TM; ++rt) {
-            uint4 B;
-            if (CACHE) {
-              B = Bc[CACHE ? u : 0][rt];
-            } else {
-              const int r = rt * 16 + j;
-              B = make_uint4(0u, 0u, 0u, 0u);
-              if (r < a.M) B = load_b<BM>(a, r, (kc0 + b0 + u) * 32 + g * 8, 0.f);
-            }
-            acc[rt] = mfma16x16x32(A[u], B, acc[rt]);
+            for (int rt = 0; rt < TM; ++rt)
+              acc[rt] = mfma_pair(A[u], lds_pair(st, row_of(rt * 16 + j, a.M), kl), acc[rt]);
           }
         }
       }
     }
     const int Tn = T + gridDim.x;
-    if (Tn < n_items) {
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-        if (u < cpw) A[u] = ld_stream(wptr(Tn, kc0 + u));
-    }
+    if (Tn < n_items) load_a(Tn, 0, 0);
     gemm_finish<TM, ROLE>(a, sh, acc, T, wave, lane, nw);
     if (Tn >= n_items) break;
     T = Tn;
   }
 }
 
-// int4 weights: per row tile and per scale group, two MFMAs over the group's
-// 64 inputs start from zero; the group sum is then scaled by the fp32 group
-// scale and added to the running fp32 sum in group order.
-template <int TM, int BM, int ROLE>
+// int4 weights: wave w takes 128-input tiles w, w + NW, ...; per row tile and
+// per scale group, the MFMAs over the group's 64 inputs (hi and lo planes of
+// each 32-input chunk) start from zero; the group sum is then scaled by the
+// fp32 group scale and added to the running fp32 sum in group order.
+template <int TM, int ROLE>
 __global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
   __shared__ GemmShared sh;
+  __shared__ __align__(16) uint16_t stage_mem[kStageBytes / 2];
   const int nw = blockDim.x >> 6;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int KT = a.K >> 7;                 // 128-input tiles
-  const int tpw = KT / nw;
-  const int kt0 = wave * tpw;
+  const int cs = stage_chunks(KT, nw, a.M, 128);
+  const int n_stages = KT / cs;
+  const int cpws = cs / nw;
+  Stage st;
+  st.stride = cs * 128 + 8;
+  st.hi = stage_mem;
+  st.lo = stage_mem + (size_t)a.M * st.stride;
   const int n_items = a.N >> 4;
-  rows_inv_rms<BM>(a, sh, wave, lane, nw);
-  float inv[TM];
-#pragma unroll
-  for (int rt = 0; rt < TM; ++rt) {
-    const int r = rt * 16 + j;
-    inv[rt] = (BM == kBNorm && r < a.M) ? sh.inv[r] : 0.f;
+  if (norm_role(ROLE)) rows_inv_rms(a, sh, wave, lane, nw);
+  if (n_stages == 1) {
+    stage_planes(a, st, 0, cs, 128);
+    __syncthreads();
   }
   for (int T = blockIdx.x; T < n_items; T += gridDim.x) {
     f32x4 acc[TM];
@@ -361,31 +459,34 @@ __global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
     for (int rt = 0; rt < TM; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint4* Wt = reinterpret_cast<const uint4*>(a.W) + (size_t)T * KT * 64 + lane;
     const uint2* St = reinterpret_cast<const uint2*>(a.Wscale) + (size_t)T * KT * 8 + g;
-    for (int c = 0; c < tpw; ++c) {
-      const int kt = kt0 + c;
-      const uint4 Q = ld_stream(Wt + (size_t)kt * 64);
-      const uint2 SC0 = St[(size_t)kt * 8], SC1 = St[(size_t)kt * 8 + 4];
+    for (int s = 0; s < n_stages; ++s) {
+      if (n_stages > 1) {
+        __syncthreads();
+        stage_planes(a, st, s * cs, cs, 128);
+        __syncthreads();
+      }
+      for (int c = 0; c < cpws; ++c) {
+        const int kt = s * cs + wave + nw * c;
+        const int kl = (wave + nw * c) * 128;      // input index inside the stage
+        const uint4 Q = ld_stream(Wt + (size_t)kt * 64);
+        const uint2 SC0 = St[(size_t)kt * 8], SC1 = St[(size_t)kt * 8 + 4];
 #pragma unroll
-      for (int gq = 0; gq < 2; ++gq) {
-        const uint2 SC = gq == 0 ? SC0 : SC1;
-        const uint4 A0 = codes8(gq == 0 ? Q.x : Q.z), A1 = codes8(gq == 0 ? Q.y : Q.w);
-        const float s0 = bf2f((uint16_t)(SC.x & 0xffffu)), s1 = bf2f((uint16_t)(SC.x >> 16));
-        const float s2 = bf2f((uint16_t)(SC.y & 0xffffu)), s3 = bf2f((uint16_t)(SC.y >> 16));
+        for (int gq = 0; gq < 2; ++gq) {
+          const uint2 SC = gq == 0 ? SC0 : SC1;
+          const uint4 A0 = codes8(gq == 0 ? Q.x : Q.z), A1 = codes8(gq == 0 ? Q.y : Q.w);
+          const float s0 = bf2f((uint16_t)(SC.x & 0xffffu)), s1 = bf2f((uint16_t)(SC.x >> 16));
+          const float s2 = bf2f((uint16_t)(SC.y & 0xffffu)), s3 = bf2f((uint16_t)(SC.y >> 16));
 #pragma unroll
-        for (int rt = 0; rt < TM; ++rt) {
-          const int r = rt * 16 + j;
-          uint4 B0 = make_uint4(0u, 0u, 0u, 0u), B1 = B0;
-          if (r < a.M) {
-            B0 = load_b<BM>(a, r, kt * 128 + gq * 64 + g * 8, inv[rt]);
-            B1 = load_b<BM>(a, r, kt * 128 + gq * 64 + 32 + g * 8, inv[rt]);
+          for (int rt = 0; rt < TM; ++rt) {
+            const int r = row_of(rt * 16 + j, a.M);
+            f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
+            p = mfma_pair(A0, lds_pair(st, r, kl + gq * 64 + g * 8), p);
+            p = mfma_pair(A1, lds_pair(st, r, kl + gq * 64 + 32 + g * 8), p);
+            acc[rt].x = fmaf(s0, p.x, acc[rt].x);
+            acc[rt].y = fmaf(s1, p.y, acc[rt].y);
+            acc[rt].z = fmaf(s2, p.z, acc[rt].z);
+            acc[rt].w = fmaf(s3, p.w, acc[rt].w);
           }
-          f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
-          p = mfma16x16x32(A0, B0, p);
-          p = mfma16x16x32(A1, B1, p);
-          acc[rt].x = fmaf(s0, p.x, acc[rt].x);
-          acc[rt].y = fmaf(s1, p.y, acc[rt].y);
-          acc[rt].z = fmaf(s2, p.z, acc[rt].z);
-          acc[rt].w = fmaf(s3, p.w, acc[rt].w);
         }
       }
     }
@@ -393,24 +494,24 @@ __global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
   }
 }
 
-template <int BM, int ROLE, bool INT4>
+template <int ROLE, bool INT4>
 static hipError_t gemm_dispatch(const GemmArgs& a, int grid, hipStream_t st) {
   const dim3 block(64 * a.S);
   const int tm = (a.M + 15) / 16;
   if constexpr (INT4) {
     switch (tm) {
-      case 1: hipLaunchKernelGGL((k_gemm_int4<1, BM, ROLE>), dim3(grid), block, 0, st, a); break;
-      case 2: hipLaunchKernelGGL((k_gemm_int4<2, BM, ROLE>), dim3(grid), block, 0, st, a); break;
-      case 3: hipLaunchKernelGGL((k_gemm_int4<3, BM, ROLE>), dim3(grid), block, 0, st, a); break;
-      case 4: hipLaunchKernelGGL((k_gemm_int4<4, BM, ROLE>), dim3(grid), block, 0, st, a); break;
+      case 1: hipLaunchKernelGGL((k_gemm_int4<1, ROLE>), dim3(grid), block, 0, st, a); break;
+      case 2: hipLaunchKernelGGL((k_gemm_int4<2, ROLE>), dim3(grid), block, 0, st, a); break;
+      case 3: hipLaunchKernelGGL((k_gemm_int4<3, ROLE>), dim3(grid), block, 0, st, a); break;
+      case 4: hipLaunchKernelGGL((k_gemm_int4<4, ROLE>), dim3(grid), block, 0, st, a); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (tm) {
-      case 1: hipLaunchKernelGGL((k_gemm_bf16<1, BM, ROLE>), dim3(grid), block, 0, st, a); break;
-      case 2: hipLaunchKernelGGL((k_gemm_bf16<2, BM, ROLE>), dim3(grid), block, 0, st, a); break;
-      case 3: hipLaunchKernelGGL((k_gemm_bf16<3, BM, ROLE>), dim3(grid), block, 0, st, a); break;
-      case 4: hipLaunchKernelGGL((k_gemm_bf16<4, BM, ROLE>), dim3(grid), block, 0, st, a); break;
+      case 1: hipLaunchKernelGGL((k_gemm_bf16<1, ROLE>), dim3(grid), block, 0, st, a); break;
+      case 2: hipLaunchKernelGGL((k_gemm_bf16<2, ROLE>), dim3(grid), block, 0, st, a); break;
+      case 3: hipLaunchKernelGGL((k_gemm_bf16<3, ROLE>), dim3(grid), block, 0, st, a); break;
+      case 4: hipLaunchKernelGGL((k_gemm_bf16<4, ROLE>), dim3(grid), block, 0, st, a); break;
       default: return hipErrorInvalidValue;
     }
   }
@@ -422,20 +523,19 @@ static hipError_t gemm_dispatch(const GemmArgs& a, int grid, hipStream_t st) {
 hipError_t launch_gemm(const GemmArgs& a, int role, int grid, hipStream_t st) {
   if (a.M < 1 || a.M > kMaxRows || a.S < 1 || a.S > kMaxWaves || a.N % 16 || grid < 1) return hipErrorInvalidValue;
   if (a.fmt == 1 ? (a.K % (128 * a.S)) : (a.K % (32 * a.S))) return hipErrorInvalidValue;
-  if (a.fmt == 0 && (role == kRoleQkv || role == kRoleGateUp || role == kRoleLmHead) && a.K / 32 / a.S > kCacheB)
-    return hipErrorInvalidValue;
+  // the smallest activation stage (one chunk per wave) must fit the LDS budget
+  if (a.M > gemm_max_rows(a.fmt == 1 ? 128 : 32, a.S)) return hipErrorInvalidValue;
   grid = grid > (a.N >> 4) ? (a.N >> 4) : grid;
   const bool i4 = a.fmt == 1;
   switch (role) {
-    case kRoleQkv: return i4 ? gemm_dispatch<kBNorm, kRoleQkv, true>(a, grid, st) : gemm_dispatch<kBNorm, kRoleQkv, false>(a, grid, st);
-    case kRoleO: return i4 ? gemm_dispatch<kBBf16, kRoleO, true>(a, grid, st) : gemm_dispatch<kBBf16, kRoleO, false>(a, grid, st);
+    case kRoleQkv: return i4 ? gemm_dispatch<kRoleQkv, true>(a, grid, st) : gemm_dispatch<kRoleQkv, false>(a, grid, st);
+    case kRoleO: return i4 ? gemm_dispatch<kRoleO, true>(a, grid, st) : gemm_dispatch<kRoleO, false>(a, grid, st);
     case kRoleGateUp:
-      return i4 ? gemm_dispatch<kBNorm, kRoleGateUp, true>(a, grid, st) : gemm_dispatch<kBNorm, kRoleGateUp, false>(a, grid, st);
-    case kRoleDown:
-      return i4 ? gemm_dispatch<kBBf16, kRoleDown, true>(a, grid, st) : gemm_dispatch<kBBf16, kRoleDown, false>(a, grid, st);
+      return i4 ? gemm_dispatch<kRoleGateUp, true>(a, grid, st) : gemm_dispatch<kRoleGateUp, false>(a, grid, st);
+    case kRoleDown: return i4 ? gemm_dispatch<kRoleDown, true>(a, grid, st) : gemm_dispatch<kRoleDown, false>(a, grid, st);
     case kRoleLmHead:
       if (i4) return hipErrorInvalidValue;
-      return gemm_dispatch<kBNorm, kRoleLmHead, false>(a, grid, st);
+      return gemm_dispatch<kRoleLmHead, false>(a, grid, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -465,8 +565,10 @@ int attn_splits(int ctx) { return attn_ns(ctx); }
 // Per block and q-row:
 //   s_t = (K_t . q) * log2(e)/sqrt(dh)        one MFMA chain over d
 //   positions outside the row's range -> -inf by select; block max;
-//   p_t = bf16(2^(s_t - m_new)) (0 when masked), l = l * 2^(m - m_new) + sum p,
+//   p_t = 2^(s_t - m_new) (0 when masked),      l = l * 2^(m - m_new) + sum p,
 //   o   = o * 2^(m - m_new) + V^T p             one MFMA chain over t.
+// The KV cache holds fp16; q and p enter the f16 MFMAs as compensated fp16
+// pairs (hi + lo).
 // A block with no valid position leaves (m, l, o) exactly as they were (the
 // rescale factor is 1 while the running max is still -inf).  Every reduction
 // runs in the same order for every q-row slot, so a row's result does not
@@ -487,7 +589,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   __shared__ __align__(16) uint16_t Vt[DH * VST];
 
   const int split = blockIdx.x, h = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int kv_len = a.params[0];
   const int G = a.nq / a.nkv;
@@ -507,7 +609,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   if (u_lo >= u_hi) return;
   const size_t layer_base = (size_t)a.layer * a.n_pages;
 
-  uint4 qop[QPW][DC];
+  BPair qop[QPW][DC];
   f32x4 o[QPW][DT];
   float m[QPW], l[QPW];
   int lo_q[QPW], hi_q[QPW];
@@ -526,9 +628,15 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       hi_q[u] = min((split + 1) * bps * kAttnBlock, ctx);
     }
 #pragma unroll
-    for (int c = 0; c < DC; ++c)
-      qop[u][c] = have ? *reinterpret_cast<const uint4*>(a.q + ((size_t)r * a.nq + head) * DH + c * 32 + g * 8)
-                       : make_uint4(0u, 0u, 0u, 0u);
+    for (int c = 0; c < DC; ++c) {
+      qop[u][c] = bzero();
+      if (have) {
+        const float4* qp = reinterpret_cast<const float4*>(a.q + ((size_t)r * a.nq + head) * DH + c * 32 + g * 8);
+        const float4 q0 = qp[0], q1 = qp[1];
+        const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        qop[u][c] = split8_f16(qv);
+      }
+    }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     m[u] = -INFINITY;
@@ -585,7 +693,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
           const uint4 kA = *reinterpret_cast<const uint4*>(&Ks[(pt * 16 + j) * KST + c * 32 + g * 8]);
-          acc = mfma16x16x32(kA, qop[u][c], acc);
+          acc = mfma_pair_f16(kA, qop[u][c], acc);
         }
         sc[pt] = acc;
       }
@@ -605,13 +713,14 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
       const float mn = fmaxf(m[u], bmax);
       const float alpha = (mn == -INFINITY) ? 1.0f : exp2f(m[u] - mn);
-      uint16_t pb[16];
+      uint16_t pb[16], pl[16];
       float psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float pv = (s[e] == -INFINITY) ? 0.f : exp2f(s[e] - mn);
-        pb[e] = f2bf(pv);
-        psum = psum + bf2f(pb[e]);
+        pb[e] = f2h(pv);
+        pl[e] = f2h(pv - h2f(pb[e]));
+        psum = psum + pv;
       }
       psum = psum + __shfl_xor(psum, 16);
       psum = psum + __shfl_xor(psum, 32);
@@ -624,14 +733,17 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int pa = 2 * ks, pbt = 2 * ks + 1;
-        const uint4 Bp = make_uint4(pack2(pb[pa * 4 + 0], pb[pa * 4 + 1]), pack2(pb[pa * 4 + 2], pb[pa * 4 + 3]),
-                                    pack2(pb[pbt * 4 + 0], pb[pbt * 4 + 1]), pack2(pb[pbt * 4 + 2], pb[pbt * 4 + 3]));
+        BPair Bp;
+        Bp.hi = make_uint4(pack2(pb[pa * 4 + 0], pb[pa * 4 + 1]), pack2(pb[pa * 4 + 2], pb[pa * 4 + 3]),
+                           pack2(pb[pbt * 4 + 0], pb[pbt * 4 + 1]), pack2(pb[pbt * 4 + 2], pb[pbt * 4 + 3]));
+        Bp.lo = make_uint4(pack2(pl[pa * 4 + 0], pl[pa * 4 + 1]), pack2(pl[pa * 4 + 2], pl[pa * 4 + 3]),
+                           pack2(pl[pbt * 4 + 0], pl[pbt * 4 + 1]), pack2(pl[pbt * 4 + 2], pl[pbt * 4 + 3]));
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const uint16_t* vr = &Vt[(dt * 16 + j) * VST];
           const uint2 vlo = *reinterpret_cast<const uint2*>(vr + pa * 16 + 4 * g);
           const uint2 vhi = *reinterpret_cast<const uint2*>(vr + pbt * 16 + 4 * g);
-          o[u][dt] = mfma16x16x32(make_uint4(vlo.x, vlo.y, vhi.x, vhi.y), Bp, o[u][dt]);
+          o[u][dt] = mfma_pair_f16(make_uint4(vlo.x, vlo.y, vhi.x, vhi.y), Bp, o[u][dt]);
         }
       }
       m[u] = mn;
@@ -673,8 +785,10 @@ __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
     for (int e = 0; e < PER; ++e) O[e] = O[e] + p[4 + lane * PER + e] * w;
   }
 #pragma unroll
-  for (int e = 0; e < PER; ++e)
-    a.out[(size_t)r * a.nq * DH + (size_t)j * DH + lane * PER + e] = f2bf(O[e] / L);
+  for (int e = 0; e < PER; ++e) {
+    const size_t oi = (size_t)r * a.nq * DH + (size_t)j * DH + lane * PER + e;
+    split1(O[e] / L, a.ohi[oi], a.olo[oi]);
+  }
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
@@ -692,10 +806,11 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
 }
 
 // ------------------------------------------------------------ embedding gather
-// x[r] = E[id_r] widened to fp32, plus the per-16-column sums of squares the
-// first RMSNorm reads (16-lane butterfly, like the residual epilogue).
+// x[r] = E[id_r] widened to fp32, the per-16-column sums of squares the
+// first RMSNorm reads (16-lane butterfly, like the residual epilogue), and
+// the planes of x * g_attn of layer 0.
 __global__ __launch_bounds__(256) void k_embed(const int* params, const uint16_t* E, int vocab, int d, float* x,
-                                               float* ss) {
+                                               float* ss, const uint16_t* g0, uint16_t* uhi, uint16_t* ulo) {
   const int r = blockIdx.x;
   const int id = params[2 + r];
   (void)vocab;
@@ -707,12 +822,13 @@ __global__ __launch_bounds__(256) void k_embed(const int* params, const uint16_t
 #pragma unroll
     for (int o = 8; o >= 1; o >>= 1) sq += __shfl_xor(sq, o);
     if ((k & 15) == 0) ss[(size_t)r * (d >> 4) + (k >> 4)] = sq;
+    split1(v * bf2f(g0[k]), uhi[(size_t)r * d + k], ulo[(size_t)r * d + k]);
   }
 }
 
 hipError_t launch_embed(const int* params, int M, const void* embed, int vocab, int d, float* x, float* ss,
-                        hipStream_t st) {
-  hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, params, (const uint16_t*)embed, vocab, d, x, ss);
+                        const uint16_t* g0, uint16_t* uhi, uint16_t* ulo, hipStream_t st) {
+  hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, params, (const uint16_t*)embed, vocab, d, x, ss, g0, uhi, ulo);
   return hipGetLastError();
 }
 
@@ -725,7 +841,7 @@ __global__ __launch_bounds__(1024) void k_accept(const int* params, int M, int v
                                                  int n_groups, int* result) {
   __shared__ int am[kMaxRows];
   __shared__ uint64_t wbest[16];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   for (int r = 0; r < M; ++r) {
     uint64_t b = 0;
     for (int i = threadIdx.x; i < n_groups; i += 1024) b = umax64(b, best[(size_t)r * n_groups + i]);

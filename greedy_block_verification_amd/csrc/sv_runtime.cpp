@@ -25,8 +25,8 @@ struct GemmPlan {
 };
 
 struct Layout {
-  size_t params = 0, x = 0, ss = 0, q = 0, attn_part = 0, attn_out = 0, act = 0, best = 0, result = 0,
-         logits = 0, rope = 0, total = 0;
+  size_t params = 0, x = 0, ss = 0, q = 0, attn_part = 0, uplanes = 0, oplanes = 0, aplanes = 0, best = 0,
+         result = 0, logits = 0, rope = 0, total = 0;
   int max_split = 1;
 };
 
@@ -35,10 +35,10 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Waves that split K inside one GEMM workgroup.  It depends only on the
 // matrix shape, never on the number of rows, so every row count shares one
 // summation order.
-int choose_waves(int K, int unit, int max_chunks_per_wave) {
+int choose_waves(int K, int unit, int max_waves) {
   const int chunks = K / unit;
   for (int w : {16, 12, 8, 6, 4, 3, 2, 1})
-    if (chunks % w == 0 && chunks / w <= max_chunks_per_wave) return w;
+    if (w <= max_waves && chunks % w == 0) return w;
   return 0;
 }
 
@@ -54,7 +54,6 @@ bool valid_config(const sv_config& c) {
   if (c.weight_fmt == 1 && (c.d_model % 512 || (c.n_q_heads * c.head_dim) % 512 || c.d_ff % 512)) return false;
   if (c.page_size != kPage || c.max_ctx < kPage || c.max_ctx % kPage) return false;
   if (c.max_k < 0 || c.max_k > kMaxRows - 1) return false;
-  if (c.max_k + 1 > std::min(kMaxRows, kAttnQRows / (c.n_q_heads / c.n_kv_heads))) return false;
   if (!(c.rms_eps > 0.f) || !(c.rope_theta > 1.f)) return false;
   return true;
 }
@@ -71,23 +70,33 @@ Plans make_plans(const sv_config& c, int n_cu) {
   const int qd = c.n_q_heads * c.head_dim, kd = c.n_kv_heads * c.head_dim;
   const bool i4 = c.weight_fmt == 1;
   const int unit = i4 ? 128 : 32;
-  // bf16 GEMMs that normalise their input keep each wave's activations in
-  // registers: at most 8 chunks of 32 inputs per wave.
-  const int norm_cap = i4 ? 1 << 20 : 8;
+  // int4 chunks are 128 inputs wide: at most 12 waves keeps a one-chunk-per-wave
+  // activation stage small enough for 22 rows
+  const int maxw = i4 ? 12 : 16;
   Plans p;
-  p.qkv = {qd + 2 * kd, c.d_model, choose_waves(c.d_model, unit, norm_cap), c.weight_fmt};
-  p.o = {c.d_model, qd, choose_waves(qd, unit, 1 << 20), c.weight_fmt};
-  p.gu = {2 * c.d_ff, c.d_model, choose_waves(c.d_model, unit, norm_cap), c.weight_fmt};
-  p.d = {c.d_model, c.d_ff, choose_waves(c.d_ff, unit, 1 << 20), c.weight_fmt};
-  p.lm = {c.vocab, c.d_model, choose_waves(c.d_model, 32, 8), 0};
+  p.qkv = {qd + 2 * kd, c.d_model, choose_waves(c.d_model, unit, maxw), c.weight_fmt};
+  p.o = {c.d_model, qd, choose_waves(qd, unit, maxw), c.weight_fmt};
+  p.gu = {2 * c.d_ff, c.d_model, choose_waves(c.d_model, unit, maxw), c.weight_fmt};
+  p.d = {c.d_model, c.d_ff, choose_waves(c.d_ff, unit, maxw), c.weight_fmt};
+  p.lm = {c.vocab, c.d_model, choose_waves(c.d_model, 32, 16), 0};
   for (GemmPlan* g : {&p.qkv, &p.o, &p.gu, &p.d, &p.lm}) g->grid = grid_for(g->N, n_cu);
   return p;
 }
 
-bool plans_ok(const Plans& p) {
+// Rows one forward may carry: at most 64, at most kAttnQRows (row, q head)
+// pairs of one KV head in the attention workgroup, and no more than every
+// GEMM can stage in LDS.
+int max_rows(const sv_config& c, const Plans& p) {
+  int m = std::min(kMaxRows, kAttnQRows / (c.n_q_heads / c.n_kv_heads));
+  for (const GemmPlan* g : {&p.qkv, &p.o, &p.gu, &p.d, &p.lm})
+    if (g->S > 0) m = std::min(m, gemm_max_rows(g->fmt == 1 ? 128 : 32, g->S));
+  return m;
+}
+
+bool plans_ok(const sv_config& c, const Plans& p) {
   for (const GemmPlan* g : {&p.qkv, &p.o, &p.gu, &p.d, &p.lm})
     if (g->S < 1) return false;
-  return true;
+  return c.max_k + 1 <= max_rows(c, p);
 }
 
 Layout make_layout(const sv_config& c, const Plans& p) {
@@ -104,22 +113,17 @@ Layout make_layout(const sv_config& c, const Plans& p) {
   L.params = take(sizeof(int) * kParamInts);
   L.x = take(R * c.d_model * 4);
   L.ss = take(R * (c.d_model / 16) * 4);
-  L.q = take(R * qd * 2);
+  L.q = take(R * qd * 4);
   L.attn_part = take(R * c.n_q_heads * (size_t)L.max_split * (c.head_dim + 4) * 4);
-  L.attn_out = take(R * qd * 2);
-  L.act = take(R * c.d_ff * 2);
+  L.uplanes = take(2 * R * c.d_model * 2);   // hi, lo planes of x * g (RMSNorm consumers' input)
+  L.oplanes = take(2 * R * qd * 2);          // attention output
+  L.aplanes = take(2 * R * c.d_ff * 2);      // act(gate) * up
   L.best = take(R * (c.vocab / 16) * 8);
   L.result = take(sizeof(int) * (2 + kMaxRows));
   L.logits = take(R * (size_t)c.vocab * 4);
   L.rope = take((size_t)c.max_ctx * (c.head_dim / 2) * 8);
   L.total = off;
   return L;
-}
-
-// Rows one forward may carry: at most 64, and the attention workgroup holds
-// at most kAttnQRows (row, q head) pairs of one KV head.
-int max_rows(const sv_config& c) {
-  return std::min(kMaxRows, kAttnQRows / (c.n_q_heads / c.n_kv_heads));
 }
 
 size_t kv_pool_bytes_for(const sv_config& c, int n_pages) {
@@ -201,24 +205,36 @@ hipError_t gemm_timed(sv_ctx* c, const GemmArgs& g, int role, int grid, hipStrea
 // Queue one whole forward of M rows (kernels only) on `st`.
 hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, hipStream_t st) {
   const sv_config& cfg = c->cfg;
+  const int R = kMaxRows;
+  const int qd = cfg.n_q_heads * cfg.head_dim;
   const int* d_params = c->at<int>(c->lay.params);
   float* x = c->at<float>(c->lay.x);
   float* ss = c->at<float>(c->lay.ss);
-  uint16_t* q = c->at<uint16_t>(c->lay.q);
-  uint16_t* attn_out = c->at<uint16_t>(c->lay.attn_out);
-  uint16_t* act = c->at<uint16_t>(c->lay.act);
+  float* q = c->at<float>(c->lay.q);
+  uint16_t* uhi = c->at<uint16_t>(c->lay.uplanes);
+  uint16_t* ulo = uhi + (size_t)R * cfg.d_model;
+  uint16_t* ohi = c->at<uint16_t>(c->lay.oplanes);
+  uint16_t* olo = ohi + (size_t)R * qd;
+  uint16_t* ahi = c->at<uint16_t>(c->lay.aplanes);
+  uint16_t* alo = ahi + (size_t)R * cfg.d_ff;
   uint16_t* kv = static_cast<uint16_t*>(c->buf.kv_pool);
+  auto gain = [](const void* p) { return static_cast<const uint16_t*>(p); };
 
-  hipError_t e = launch_embed(d_params, M, c->w.embed, cfg.vocab, cfg.d_model, x, ss, st);
+  hipError_t e = launch_embed(d_params, M, c->w.embed, cfg.vocab, cfg.d_model, x, ss, gain(c->layers[0].g_attn), uhi,
+                              ulo, st);
   if (e != hipSuccess) return e;
 
   GemmArgs g{};
   g.M = M;
   g.eps = cfg.rms_eps;
   g.params = d_params;
+  g.ss = ss;
   g.x = x;
   g.ss_out = ss;
-  g.act_out = act;
+  g.uhi = uhi;
+  g.ulo = ulo;
+  g.ahi = ahi;
+  g.alo = alo;
   g.act = cfg.act;
   g.q_out = q;
   g.kv_pool = kv;
@@ -228,40 +244,37 @@ hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, hipStream_
   g.nkv = cfg.n_kv_heads;
   g.dh = cfg.head_dim;
   g.rope = c->at<const float2>(c->lay.rope);
-  auto plan = [&](const GemmPlan& p, const void* W, const void* Ws) {
-    g.W = W; g.Wscale = Ws; g.N = p.N; g.K = p.K; g.S = p.S; g.fmt = p.fmt;
+  auto plan = [&](const GemmPlan& p, const void* W, const void* Ws, const uint16_t* bhi, const uint16_t* blo) {
+    g.W = W; g.Wscale = Ws; g.N = p.N; g.K = p.K; g.S = p.S; g.fmt = p.fmt; g.bhi = bhi; g.blo = blo;
   };
 
   for (int l = 0; l < cfg.n_layers; ++l) {
     const sv_layer_weights& L = c->layers[l];
     g.layer = l;
-    // attention block: norm + QKV + RoPE + KV append, attention, O + residual
-    plan(c->plans.qkv, L.wqkv, L.wqkv_scales);
-    g.xf = x; g.ss = ss; g.gain = static_cast<const uint16_t*>(L.g_attn);
+    // attention block: (norm) QKV + RoPE + KV append, attention, O + residual
+    plan(c->plans.qkv, L.wqkv, L.wqkv_scales, uhi, ulo);
     if ((e = gemm_timed(c, g, kRoleQkv, c->plans.qkv.grid, st)) != hipSuccess) return e;
     AttnArgs at{};
     at.params = d_params; at.q = q; at.kv_pool = kv; at.page_table = c->buf.page_table; at.n_pages = c->buf.n_pages;
     at.layer = l; at.nq = cfg.n_q_heads; at.nkv = cfg.n_kv_heads; at.dh = cfg.head_dim; at.M = M;
     at.n_split = n_split; at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cfg.head_dim));
-    at.part = c->at<float>(c->lay.attn_part); at.out = attn_out;
+    at.part = c->at<float>(c->lay.attn_part); at.ohi = ohi; at.olo = olo;
     if ((e = prof_mark(c, kRoleAttn, true)) != hipSuccess) return e;
     if ((e = launch_attention(at, st)) != hipSuccess) return e;
     if ((e = prof_mark(c, kRoleAttn, false)) != hipSuccess) return e;
-    plan(c->plans.o, L.wo, L.wo_scales);
-    g.xb = attn_out;
+    plan(c->plans.o, L.wo, L.wo_scales, ohi, olo);
+    g.gnext = gain(L.g_mlp);
     if ((e = gemm_timed(c, g, kRoleO, c->plans.o.grid, st)) != hipSuccess) return e;
-    // MLP block: norm + gate/up + activation, down + residual
-    plan(c->plans.gu, L.wgu, L.wgu_scales);
-    g.xf = x; g.ss = ss; g.gain = static_cast<const uint16_t*>(L.g_mlp);
+    // MLP block: (norm) gate/up + activation, down + residual
+    plan(c->plans.gu, L.wgu, L.wgu_scales, uhi, ulo);
     if ((e = gemm_timed(c, g, kRoleGateUp, c->plans.gu.grid, st)) != hipSuccess) return e;
-    plan(c->plans.d, L.wd, L.wd_scales);
-    g.xb = act;
+    plan(c->plans.d, L.wd, L.wd_scales, ahi, alo);
+    g.gnext = l + 1 < cfg.n_layers ? gain(c->layers[l + 1].g_attn) : gain(c->w.g_final);
     if ((e = gemm_timed(c, g, kRoleDown, c->plans.d.grid, st)) != hipSuccess) return e;
   }
 
-  // final norm + LM head + per-64-column argmax, then acceptance
-  plan(c->plans.lm, c->w.lm_head, nullptr);
-  g.xf = x; g.ss = ss; g.gain = static_cast<const uint16_t*>(c->w.g_final);
+  // (final norm) LM head + per-16-column argmax, then acceptance
+  plan(c->plans.lm, c->w.lm_head, nullptr, uhi, ulo);
   g.best = c->at<uint64_t>(c->lay.best);
   g.logits = c->store_logits ? c->at<float>(c->lay.logits) : nullptr;
   if ((e = gemm_timed(c, g, kRoleLmHead, c->plans.lm.grid, st)) != hipSuccess) return e;
@@ -336,7 +349,7 @@ const char* sv_status_str(sv_status s) {
 sv_status sv_query_sizes(const sv_config* cfg, int64_t* kv_pool_bytes, int64_t* workspace_bytes) {
   if (!cfg || !valid_config(*cfg)) return SV_EINVAL;
   const Plans p = make_plans(*cfg, 256);
-  if (!plans_ok(p)) return SV_EUNSUPPORTED;
+  if (!plans_ok(*cfg, p)) return SV_EUNSUPPORTED;
   const Layout L = make_layout(*cfg, p);
   if (kv_pool_bytes) *kv_pool_bytes = (int64_t)kv_pool_bytes_for(*cfg, cfg->max_ctx / kPage);
   if (workspace_bytes) *workspace_bytes = (int64_t)L.total;
@@ -390,7 +403,7 @@ sv_status sv_create(const sv_config* cfg, const sv_weights* w, const sv_buffers*
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
     return SV_EDEVICE;
   const Plans p = make_plans(*cfg, n_cu);
-  if (!plans_ok(p)) return SV_EUNSUPPORTED;
+  if (!plans_ok(*cfg, p)) return SV_EUNSUPPORTED;
   const Layout lay = make_layout(*cfg, p);
   if (!buf->kv_pool || !buf->page_table || !buf->workspace) return SV_EINVAL;
   if (buf->n_pages < 1 || buf->kv_pool_bytes < (int64_t)kv_pool_bytes_for(*cfg, buf->n_pages)) return SV_EINVAL;
@@ -463,7 +476,7 @@ sv_status sv_prefill(sv_ctx* c, const int32_t* ids, int32_t n, int32_t* next_id)
   if (!c || !ids || n < 1) return SV_EINVAL;
   if (!ids_ok(c, ids, n)) return SV_EINVAL;
   if ((int64_t)c->kv_len + n > c->cfg.max_ctx) return SV_ENOSPACE;
-  const int chunk = max_rows(c->cfg);
+  const int chunk = max_rows(c->cfg, c->plans);
   for (int off = 0; off < n; off += chunk) {
     const int m = std::min(chunk, n - off);
     const sv_status s = forward(c, m, ids + off, 0);
@@ -515,6 +528,21 @@ sv_status sv_kv_truncate(sv_ctx* c, int32_t new_len) {
   if (new_len < 1 || new_len > c->kv_len) return SV_EINVAL;
   c->kv_len = new_len;
   c->next_id = c->hist[new_len - 1];
+  return SV_OK;
+}
+
+sv_status sv_history(const sv_ctx* c, int32_t* host_dst, int32_t n) {
+  if (!c || !host_dst || n < 0 || n > c->kv_len) return SV_EINVAL;
+  for (int i = 0; i < n; ++i) host_dst[i] = c->hist[i];
+  return SV_OK;
+}
+
+sv_status sv_restore(sv_ctx* c, int32_t kv_len, const int32_t* greedy_hist) {
+  if (!c || !greedy_hist || kv_len < 1 || kv_len > c->cfg.max_ctx) return SV_EINVAL;
+  if (!ids_ok(c, greedy_hist, kv_len)) return SV_EINVAL;
+  for (int i = 0; i < kv_len; ++i) c->hist[i] = greedy_hist[i];
+  c->kv_len = kv_len;
+  c->next_id = greedy_hist[kv_len - 1];
   return SV_OK;
 }
 

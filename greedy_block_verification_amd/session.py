@@ -26,7 +26,7 @@ def _dev(arr: np.ndarray, device) -> torch.Tensor:
 class DeviceModel:
     """Packed device weights of one model (shared by any number of sessions)."""
 
-    def __init__(self, weights, device="cuda:0"):
+    def __init__(self, weights, device="cuda:0", share_layers_with=None):
         import torch.cuda
         if not torch.cuda.is_available():
             raise RuntimeError("DeviceModel needs a ROCm GPU")
@@ -41,7 +41,12 @@ class DeviceModel:
         self.embed = self._pack(0, 0, weights.embed, None)[0]
         self.g_final = self._keep(_dev(weights.g_final, self.device))
         self.layer_structs = (B.sv_layer_weights * cfg.n_layers)()
-        for l, L in enumerate(weights.layers):
+        if share_layers_with is not None:
+            # same layer weights (device memory shared), own embedding / LM head
+            self.keep.append(share_layers_with)
+            for l in range(cfg.n_layers):
+                self.layer_structs[l] = share_layers_with.layer_structs[l]
+        for l, L in enumerate(weights.layers if share_layers_with is None else []):
             qkv = np.concatenate([L["wq"], L["wk"], L["wv"]], axis=0)
             qkv_s = np.concatenate([L["wq_s"], L["wk_s"], L["wv_s"]], axis=0) if fmt else None
             wqkv, wqkv_s = self._pack(fmt, 2, qkv, qkv_s)
@@ -89,15 +94,18 @@ class Session:
     the committed length would reach the logits.
     """
 
-    def __init__(self, model: DeviceModel, page_perm=None, poison: bool = False):
+    def __init__(self, model: DeviceModel, page_perm=None, poison: bool = False, cfg=None):
         self.m = model
-        cfg = model.cfg
-        kv_bytes, ws_bytes = B.sv_query_sizes(model.config)
+        cfg = cfg or model.cfg
+        self.cfg = cfg
+        config = B.make_config(cfg)
+        self.config = config
+        kv_bytes, ws_bytes = B.sv_query_sizes(config)
         n_pages = cfg.max_ctx // cfg.page_size
         dev = model.device
         self.kv = torch.empty(kv_bytes // 2, dtype=torch.int16, device=dev)
         if poison:
-            self.kv.fill_(0x7FC1)            # bf16 quiet-NaN pattern
+            self.kv.fill_(0x7FC1)            # fp16 NaN pattern
         else:
             self.kv.zero_()
         perm = np.arange(n_pages, dtype=np.int32) if page_perm is None else np.asarray(page_perm, dtype=np.int32)
@@ -106,7 +114,7 @@ class Session:
         torch.cuda.synchronize(dev)
         self.buffers = B.sv_buffers(self.kv.data_ptr(), kv_bytes, self.page_table.data_ptr(), n_pages,
                                     self.ws.data_ptr(), ws_bytes)
-        self.ctx = B.sv_create(model.config, model.weights, self.buffers, model.stream.cuda_stream)
+        self.ctx = B.sv_create(config, model.weights, self.buffers, model.stream.cuda_stream)
 
     def close(self):
         if self.ctx:
@@ -144,18 +152,33 @@ class Session:
         B.sv_set_debug(self.ctx, 1 if on else 0)
 
     def logits(self, row: int) -> np.ndarray:
-        return B.sv_get_logits(self.ctx, row, self.m.cfg.vocab)
+        return B.sv_get_logits(self.ctx, row, self.cfg.vocab)
 
     def last_argmax(self):
         return B.sv_last_argmax(self.ctx)
 
-    def kv_positions(self, n_positions: int) -> np.ndarray:
-        """Host copy of the K/V bits of positions [0, n): int16 [n, L, 2, n_kv, dh]."""
-        cfg = self.m.cfg
+    def history(self, n=None):
+        return B.sv_history(self.ctx, self.kv_len if n is None else n)
+
+    def snapshot(self):
+        """(KV pool copy, greedy history): everything a restore needs."""
+        torch.cuda.synchronize(self.kv.device)
+        return self.kv.clone(), self.history()
+
+    def restore(self, snap):
+        kv, hist = snap
+        self.kv.copy_(kv)
+        torch.cuda.synchronize(self.kv.device)
+        B.sv_restore(self.ctx, len(hist), hist)
+
+    def kv_positions(self, n_positions: int, start: int = 0) -> np.ndarray:
+        """Host copy of the K/V bits of positions [start, n): int16 [n - start, L, 2, n_kv, dh]."""
+        cfg = self.cfg
         n_pages = cfg.max_ctx // cfg.page_size
         pool = self.kv.view(cfg.n_layers, n_pages, 2, cfg.n_kv_heads, cfg.page_size, cfg.head_dim)
         pt = self.page_table.cpu().numpy()
-        pos = np.arange(n_positions)
+        pos = np.arange(start, n_positions)
         pages = pt[pos // cfg.page_size].astype(np.int64)
-        sub = pool[:, torch.from_numpy(pages).to(self.kv.device)].cpu().numpy()   # [L, n, 2, nkv, 16, dh]
-        return sub[:, pos, :, :, pos % cfg.page_size, :]                          # [n, L, 2, nkv, dh]
+        upages, inv = np.unique(pages, return_inverse=True)
+        sub = pool[:, torch.from_numpy(upages).to(self.kv.device)].cpu().numpy()   # [L, u, 2, nkv, 16, dh]
+        return sub[:, inv, :, :, pos % cfg.page_size, :]                          # [n, L, 2, nkv, dh]

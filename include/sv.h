@@ -75,7 +75,7 @@ typedef struct {
 } sv_weights;
 
 /* Caller-owned device buffers.
- *   kv_pool: bf16, n_pages pages; page p, layer l, kv (0 = K, 1 = V), head h,
+ *   kv_pool: IEEE fp16, n_pages pages; page p, layer l, kv (0 = K, 1 = V), head h,
  *            slot s, element e lives at
  *            ((((l*n_pages + p)*2 + kv)*n_kv + h)*16 + s)*head_dim + e.
  *   page_table: int32 [max_ctx/16], logical page -> physical page in
@@ -156,6 +156,18 @@ sv_status sv_verify(sv_ctx *ctx, int32_t prefix_len, const int32_t *draft_ids, i
  * next_id = the greedy id recorded after position new_len - 1.  KV past
  * new_len is left in place and never read again.  1 <= new_len <= kv_len. */
 sv_status sv_kv_truncate(sv_ctx *ctx, int32_t new_len);
+
+/* Checkpoint / resume of a sequence.  sv_history copies the greedy id
+ * recorded after each of the first n committed positions (n <= kv_len) to
+ * host_dst.  sv_restore declares that positions [0, kv_len) of this
+ * context's KV pool (through its page table) hold a committed prefix -- for
+ * instance a copy of another context's pool -- with greedy history
+ * greedy_hist (host int32 [kv_len], ids in [0, vocab)); afterwards kv_len is
+ * that value and next_id = greedy_hist[kv_len - 1].  The library does not
+ * read the pool here: the caller vouches for its contents.  Errors:
+ * SV_EINVAL (kv_len outside [1, max_ctx], bad id, null pointer). */
+sv_status sv_history(const sv_ctx *ctx, int32_t *host_dst, int32_t n);
+sv_status sv_restore(sv_ctx *ctx, int32_t kv_len, const int32_t *greedy_hist);
 
 int32_t sv_kv_len(const sv_ctx *ctx);
 int32_t sv_next_id(const sv_ctx *ctx);
