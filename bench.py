@@ -43,11 +43,13 @@ def algorithmic_step_bytes(cfg, m, kv_len):
 
 
 def gate_up_bytes(cfg, m):
-    """Algorithmic bytes of one gate/up GEMM launch: packed weights, the fp32
-    residual rows and gains it normalises, and the m x 2F fp32 outputs."""
+    """Algorithmic bytes of one gate/up GEMM launch: the packed weights once,
+    the m rows of normalised input as bf16 hi/lo planes (4 B per element),
+    their per-16-column sums of squares, and the m x F activation output as
+    hi/lo planes."""
     n, k = 2 * cfg.d_ff, cfg.d_model
     w = n * k * 2 if cfg.weight_fmt == "bf16" else n * k // 2 + n * (k // 64) * 2
-    return w + m * k * 4 + k * 2 + m * n * 4
+    return w + m * k * 4 + m * (k // 16) * 4 + m * cfg.d_ff * 4
 
 
 def load_traffic(kernel_src_sha):
@@ -143,6 +145,9 @@ def main():
     ap.add_argument("--p-correct", type=float, default=0.66)
     ap.add_argument("--cpu-tokens", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device-to-device copy of this many MiB first (the reference "
+                         "dispatch that scales HBM counter readings)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -187,6 +192,16 @@ def main():
     decode_tpot_ms = 1000.0 * t_decode / (P * G)
     log(f"[bench] {P} prompts prefetched; baseline decode {decode_tpot_ms:.3f} ms/token")
 
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {n} bytes read, {n} bytes written")
+        del src, dst
+
     srcs = [DraftSource(cfg.seed, p, cfg.vocab, p_correct=args.p_correct) for p in range(P)]
     run_spec(sessions[:1], truth[:1], L, G, args.k, [DraftSource(cfg.seed, 10_000, cfg.vocab, p_correct=args.p_correct)],
              args.warmup)
@@ -206,7 +221,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": load_traffic(hashlib.sha256(ksrc).hexdigest()),
-                "kernel": "k_gemm_bf16<1,kBNorm,kOutPartial,kRoleGateUp> (gate/up GEMM, 8B shape)",
+                "kernel": "sv::k_gemm_bf16<1, 2> (gate/up GEMM with SwiGLU epilogue, 8B shape, M <= 16)",
                 "launches": gu_n, "mean_launch_us": round(1000.0 * gu_ms / max(1, gu_n), 2),
                 "bytes_per_launch": int(gu_bytes / max(1, gu_n))}
     step_bytes = sum(algorithmic_step_bytes(cfg, k_eff + 1, kv) for k_eff, _, kv in st["steps"])

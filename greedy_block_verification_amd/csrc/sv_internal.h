@@ -56,6 +56,7 @@ struct GemmArgs {
   // LM head
   uint64_t* best;        // [M][N/16] packed (orderable logit, ~id)
   float* logits;         // optional [M][N] fp32
+  unsigned long long* prof;   // optional [2]: (min start, max end) device wall clock
 };
 
 struct AttnArgs {
@@ -68,6 +69,7 @@ struct AttnArgs {
   float* part;           // [M][nq][kAttnMaxSplits][dh + 4]  (m, l, -, -, o[dh])
   uint16_t* ohi;         // output planes [M][nq*dh]
   uint16_t* olo;
+  unsigned long long* prof;   // optional [2]: start stamped by the split kernel, end by the combine
 };
 
 hipError_t launch_gemm(const GemmArgs& a, int role, int grid, hipStream_t st);
@@ -83,6 +85,8 @@ hipError_t launch_embed(const int* params, int M, const void* embed, int vocab, 
                         const uint16_t* g0, uint16_t* uhi, uint16_t* ulo, hipStream_t st);
 hipError_t launch_accept(const int* params, int M, int verify, const uint64_t* best, int n_groups,
                          int* result, hipStream_t st);
+// Profiling slots: (start, end) pairs set to (max, 0) before a forward.
+hipError_t launch_prof_reset(unsigned long long* slots, int n_pairs, hipStream_t st);
 hipError_t launch_pack(int fmt, int layout, const void* src0, const void* src0_scales, const void* src1,
                        const void* src1_scales, int n, int k, int dh, void* dst, void* dst_scales,
                        hipStream_t st);

@@ -205,6 +205,20 @@ __device__ __forceinline__ float act_fn(float x, int act) {
   return 0.5f * x * (1.0f + tanhf(c * (x + 0.044715f * (x * x * x))));
 }
 
+// Kernel span measurement: every workgroup stamps the device's constant-rate
+// wall clock when it starts and when it ends; the slot keeps the earliest
+// start and the latest end (global atomics, read by the host after the
+// stream has synchronised).
+__device__ __forceinline__ void prof_start(unsigned long long* prof) {
+  if (prof != nullptr && threadIdx.x == 0) atomicMin(prof, (unsigned long long)wall_clock64());
+}
+__device__ __forceinline__ void prof_end(unsigned long long* prof) {
+  if (prof != nullptr) {
+    __syncthreads();
+    if (threadIdx.x == 0) atomicMax(prof + 1, (unsigned long long)wall_clock64());
+  }
+}
+
 constexpr int kMaxWaves = 16;
 constexpr int kStageBytes = kGemmStageBytes;   // LDS for staged activation planes (hi + lo)
 
@@ -366,6 +380,7 @@ template <int TM, int ROLE>
 __global__ __launch_bounds__(1024) void k_gemm_bf16(GemmArgs a) {
   __shared__ GemmShared sh;
   __shared__ __align__(16) uint16_t stage_mem[kStageBytes / 2];
+  prof_start(a.prof);
   const int nw = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
@@ -426,6 +441,7 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16(GemmArgs a) {
     if (Tn >= n_items) break;
     T = Tn;
   }
+  prof_end(a.prof);
 }
 
 // int4 weights: wave w takes 128-input tiles w, w + NW, ...; per row tile and
@@ -436,6 +452,7 @@ template <int TM, int ROLE>
 __global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
   __shared__ GemmShared sh;
   __shared__ __align__(16) uint16_t stage_mem[kStageBytes / 2];
+  prof_start(a.prof);
   const int nw = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
@@ -492,6 +509,7 @@ __global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
     }
     gemm_finish<TM, ROLE>(a, sh, acc, T, wave, lane, nw);
   }
+  prof_end(a.prof);
 }
 
 template <int ROLE, bool INT4>
@@ -588,6 +606,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   __shared__ __align__(16) uint16_t Ks[kAttnBlock * KST];
   __shared__ __align__(16) uint16_t Vt[DH * VST];
 
+  prof_start(a.prof);
   const int split = blockIdx.x, h = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
@@ -789,6 +808,7 @@ __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
     const size_t oi = (size_t)r * a.nq * DH + (size_t)j * DH + lane * PER + e;
     split1(O[e] / L, a.ohi[oi], a.olo[oi]);
   }
+  prof_end(a.prof);
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
@@ -948,6 +968,18 @@ __global__ void k_pack_int4(int layout, const int8_t* s0, const uint16_t* s0s, c
       dst_s[tk * 32 + lane] = (w2 ? s1s : s0s)[(size_t)srow * (k >> 6) + kt * 2 + gq];
     }
   }
+}
+
+__global__ void k_prof_reset(unsigned long long* slots, int n_pairs) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_pairs; i += gridDim.x * blockDim.x) {
+    slots[2 * i] = ~0ull;
+    slots[2 * i + 1] = 0ull;
+  }
+}
+
+hipError_t launch_prof_reset(unsigned long long* slots, int n_pairs, hipStream_t st) {
+  hipLaunchKernelGGL(k_prof_reset, dim3(1), dim3(256), 0, st, slots, n_pairs);
+  return hipGetLastError();
 }
 
 hipError_t launch_pack(int fmt, int layout, const void* src0, const void* src0_scales, const void* src1,

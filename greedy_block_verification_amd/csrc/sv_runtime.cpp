@@ -26,7 +26,7 @@ struct GemmPlan {
 
 struct Layout {
   size_t params = 0, x = 0, ss = 0, q = 0, attn_part = 0, uplanes = 0, oplanes = 0, aplanes = 0, best = 0,
-         result = 0, logits = 0, rope = 0, total = 0;
+         result = 0, logits = 0, rope = 0, prof = 0, total = 0;
   int max_split = 1;
 };
 
@@ -99,6 +99,13 @@ bool plans_ok(const sv_config& c, const Plans& p) {
   return c.max_k + 1 <= max_rows(c, p);
 }
 
+// Kernel roles the profiler can time (sv_set_profile).
+constexpr int kProfRoles = 6;
+constexpr int kRoleAttn = 5;
+// One (start, end) slot per profiled launch of a forward: role r of layer l
+// (the LM head uses layer 0).
+int prof_pairs(const sv_config& c) { return kProfRoles * c.n_layers; }
+
 Layout make_layout(const sv_config& c, const Plans& p) {
   Layout L;
   const size_t R = kMaxRows;
@@ -122,6 +129,7 @@ Layout make_layout(const sv_config& c, const Plans& p) {
   L.result = take(sizeof(int) * (2 + kMaxRows));
   L.logits = take(R * (size_t)c.vocab * 4);
   L.rope = take((size_t)c.max_ctx * (c.head_dim / 2) * 8);
+  L.prof = take(prof_pairs(c) * 16);
   L.total = off;
   return L;
 }
@@ -143,6 +151,7 @@ struct sv_ctx {
   char* ws = nullptr;
   int* h_params = nullptr;   // pinned
   int* h_result = nullptr;   // pinned
+  unsigned long long* h_prof = nullptr;   // pinned copy of the profiling slots
   int kv_len = 0;
   int next_id = -1;
   std::vector<int> hist;     // hist[p] = greedy id after positions 0..p
@@ -150,19 +159,17 @@ struct sv_ctx {
   int last_rows = 0;
   int last_stored_logits = 0;
   int last_argmax[kMaxRows] = {};
-  // profiling: events around enabled kernel roles
-  static constexpr int kRoles = 6;
+  // profiling: wall-clock spans of the enabled kernel roles
   int prof_mask = 0;
-  std::vector<hipEvent_t> ev;          // pool, reused every forward
-  std::vector<std::pair<int, int>> ev_used;   // (role, index of start event)
-  size_t ev_next = 0;
-  double prof_ms[kRoles] = {};
-  int64_t prof_n[kRoles] = {};
+  double wall_khz = 0.0;               // device wall-clock rate
+  double prof_ms[kProfRoles] = {};
+  int64_t prof_n[kProfRoles] = {};
 
-  // HIP graphs of whole forwards, keyed by (rows, attention splits, mode, logits)
+  // HIP graphs of whole forwards, keyed by (rows, attention splits, mode,
+  // logits, profile mask)
   hipStream_t cap_stream = nullptr;
   bool use_graphs = true;
-  std::map<std::array<int, 4>, hipGraphExec_t> graphs;
+  std::map<std::array<int, 5>, hipGraphExec_t> graphs;
 
   template <class T>
   T* at(size_t off) { return reinterpret_cast<T*>(ws + off); }
@@ -170,35 +177,30 @@ struct sv_ctx {
 
 namespace {
 
-constexpr int kRoleAttn = 5;
-
-hipError_t prof_mark(sv_ctx* c, int role, bool start) {
-  if (!(c->prof_mask & (1 << role))) return hipSuccess;
-  if (c->ev_next >= c->ev.size()) {
-    hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return hipErrorOutOfMemory;
-    c->ev.push_back(e);
-  }
-  if (start) c->ev_used.push_back({role, (int)c->ev_next});
-  return hipEventRecord(c->ev[c->ev_next++], c->stream);
+// Profiling slot of (role, layer) when that role is enabled, else null.
+unsigned long long* prof_slot(sv_ctx* c, int role, int layer) {
+  if (!(c->prof_mask & (1 << role))) return nullptr;
+  return c->at<unsigned long long>(c->lay.prof) + 2 * ((size_t)role * c->cfg.n_layers + layer);
 }
 
-void prof_collect(sv_ctx* c) {
-  for (const auto& u : c->ev_used) {
-    float ms = 0.f;
-    if (hipEventElapsedTime(&ms, c->ev[u.second], c->ev[u.second + 1]) == hipSuccess) {
-      c->prof_ms[u.first] += ms;
-      c->prof_n[u.first] += 1;
+// Add the spans of the last forward's timed launches (slots copied to host).
+void prof_accumulate(sv_ctx* c) {
+  const int L = c->cfg.n_layers;
+  for (int role = 0; role < kProfRoles; ++role) {
+    if (!(c->prof_mask & (1 << role))) continue;
+    for (int l = 0; l < L; ++l) {
+      const unsigned long long s = c->h_prof[2 * (role * L + l)], e = c->h_prof[2 * (role * L + l) + 1];
+      if (e == 0 || e < s) continue;   // launch not in this forward
+      c->prof_ms[role] += (double)(e - s) / c->wall_khz;
+      c->prof_n[role] += 1;
     }
   }
-  c->ev_used.clear();
-  c->ev_next = 0;
 }
 
-hipError_t gemm_timed(sv_ctx* c, const GemmArgs& g, int role, int grid, hipStream_t st) {
-  hipError_t e = prof_mark(c, role, true);
-  if (e == hipSuccess) e = launch_gemm(g, role, grid, st);
-  if (e == hipSuccess) e = prof_mark(c, role, false);
+hipError_t gemm_timed(sv_ctx* c, GemmArgs& g, int role, int grid, hipStream_t st) {
+  g.prof = prof_slot(c, role, g.layer);
+  const hipError_t e = launch_gemm(g, role, grid, st);
+  g.prof = nullptr;
   return e;
 }
 
@@ -220,7 +222,11 @@ hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, hipStream_
   uint16_t* kv = static_cast<uint16_t*>(c->buf.kv_pool);
   auto gain = [](const void* p) { return static_cast<const uint16_t*>(p); };
 
-  hipError_t e = launch_embed(d_params, M, c->w.embed, cfg.vocab, cfg.d_model, x, ss, gain(c->layers[0].g_attn), uhi,
+  hipError_t e = hipSuccess;
+  if (c->prof_mask != 0 && (e = launch_prof_reset(c->at<unsigned long long>(c->lay.prof), prof_pairs(cfg), st)) !=
+                               hipSuccess)
+    return e;
+  e = launch_embed(d_params, M, c->w.embed, cfg.vocab, cfg.d_model, x, ss, gain(c->layers[0].g_attn), uhi,
                               ulo, st);
   if (e != hipSuccess) return e;
 
@@ -259,9 +265,8 @@ hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, hipStream_
     at.layer = l; at.nq = cfg.n_q_heads; at.nkv = cfg.n_kv_heads; at.dh = cfg.head_dim; at.M = M;
     at.n_split = n_split; at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cfg.head_dim));
     at.part = c->at<float>(c->lay.attn_part); at.ohi = ohi; at.olo = olo;
-    if ((e = prof_mark(c, kRoleAttn, true)) != hipSuccess) return e;
+    at.prof = prof_slot(c, kRoleAttn, l);
     if ((e = launch_attention(at, st)) != hipSuccess) return e;
-    if ((e = prof_mark(c, kRoleAttn, false)) != hipSuccess) return e;
     plan(c->plans.o, L.wo, L.wo_scales, ohi, olo);
     g.gnext = gain(L.g_mlp);
     if ((e = gemm_timed(c, g, kRoleO, c->plans.o.grid, st)) != hipSuccess) return e;
@@ -275,6 +280,7 @@ hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, hipStream_
 
   // (final norm) LM head + per-16-column argmax, then acceptance
   plan(c->plans.lm, c->w.lm_head, nullptr, uhi, ulo);
+  g.layer = 0;
   g.best = c->at<uint64_t>(c->lay.best);
   g.logits = c->store_logits ? c->at<float>(c->lay.logits) : nullptr;
   if ((e = gemm_timed(c, g, kRoleLmHead, c->plans.lm.grid, st)) != hipSuccess) return e;
@@ -291,8 +297,8 @@ sv_status forward(sv_ctx* c, int M, const int* ids, int verify) {
     return SV_EDEVICE;
   const int n_split = attn_splits(c->kv_len + M);
 
-  if (c->use_graphs && c->prof_mask == 0) {
-    const std::array<int, 4> key = {M, n_split, verify, c->store_logits};
+  if (c->use_graphs) {
+    const std::array<int, 5> key = {M, n_split, verify, c->store_logits, c->prof_mask};
     auto it = c->graphs.find(key);
     if (it == c->graphs.end()) {
       hipGraph_t graph = nullptr;
@@ -300,12 +306,9 @@ sv_status forward(sv_ctx* c, int M, const int* ids, int verify) {
       if (hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal) != hipSuccess) return SV_EDEVICE;
       const hipError_t e = enqueue_forward(c, M, verify, n_split, c->cap_stream);
       const hipError_t e2 = hipStreamEndCapture(c->cap_stream, &graph);
-      if (e != hipSuccess || e2 != hipSuccess || graph == nullptr) {
-        if (graph) (void)hipGraphDestroy(graph);
-        return SV_EDEVICE;
-      }
-      const hipError_t e3 = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-      (void)hipGraphDestroy(graph);
+      hipError_t e3 = hipErrorUnknown;
+      if (e == hipSuccess && e2 == hipSuccess && graph != nullptr) e3 = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+      if (graph) (void)hipGraphDestroy(graph);
       if (e3 != hipSuccess) return SV_EDEVICE;
       it = c->graphs.emplace(key, exec).first;
     }
@@ -316,8 +319,11 @@ sv_status forward(sv_ctx* c, int M, const int* ids, int verify) {
   int* d_result = c->at<int>(c->lay.result);
   if (hipMemcpyAsync(c->h_result, d_result, sizeof(int) * (2 + M), hipMemcpyDeviceToHost, st) != hipSuccess)
     return SV_EDEVICE;
+  if (c->prof_mask != 0 && hipMemcpyAsync(c->h_prof, c->at<unsigned long long>(c->lay.prof),
+                                          16 * (size_t)prof_pairs(c->cfg), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return SV_EDEVICE;
   if (hipStreamSynchronize(st) != hipSuccess) return SV_EDEVICE;
-  if (!c->ev_used.empty()) prof_collect(c);
+  if (c->prof_mask != 0) prof_accumulate(c);
   c->last_rows = M;
   c->last_stored_logits = c->store_logits;
   for (int r = 0; r < M; ++r) c->last_argmax[r] = c->h_result[2 + r];
@@ -398,9 +404,10 @@ sv_status sv_create(const sv_config* cfg, const sv_weights* w, const sv_buffers*
     if (!L.wqkv || !L.wo || !L.wgu || !L.wd || !L.g_attn || !L.g_mlp) return SV_EINVAL;
     if (cfg->weight_fmt == 1 && (!L.wqkv_scales || !L.wo_scales || !L.wgu_scales || !L.wd_scales)) return SV_EINVAL;
   }
-  int dev = 0, n_cu = 0;
+  int dev = 0, n_cu = 0, wall_khz = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1 ||
+      hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || wall_khz < 1)
     return SV_EDEVICE;
   const Plans p = make_plans(*cfg, n_cu);
   if (!plans_ok(*cfg, p)) return SV_EUNSUPPORTED;
@@ -427,10 +434,12 @@ sv_status sv_create(const sv_config* cfg, const sv_weights* w, const sv_buffers*
   c->stream = (hipStream_t)stream;
   c->plans = p;
   c->lay = lay;
+  c->wall_khz = wall_khz;
   c->ws = static_cast<char*>(buf->workspace);
   c->hist.assign(cfg->max_ctx, -1);
   if (hipHostMalloc((void**)&c->h_params, sizeof(int) * kParamInts, hipHostMallocDefault) != hipSuccess ||
-      hipHostMalloc((void**)&c->h_result, sizeof(int) * (2 + kMaxRows), hipHostMallocDefault) != hipSuccess) {
+      hipHostMalloc((void**)&c->h_result, sizeof(int) * (2 + kMaxRows), hipHostMallocDefault) != hipSuccess ||
+      hipHostMalloc((void**)&c->h_prof, 16 * (size_t)prof_pairs(*cfg), hipHostMallocDefault) != hipSuccess) {
     sv_destroy(c);
     return SV_EDEVICE;
   }
@@ -461,11 +470,11 @@ sv_status sv_create(const sv_config* cfg, const sv_weights* w, const sv_buffers*
 
 void sv_destroy(sv_ctx* c) {
   if (!c) return;
-  for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
   for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);
   if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
   if (c->h_params) (void)hipHostFree(c->h_params);
   if (c->h_result) (void)hipHostFree(c->h_result);
+  if (c->h_prof) (void)hipHostFree(c->h_prof);
   delete c;
 }
 
@@ -564,13 +573,13 @@ sv_status sv_get_logits(sv_ctx* c, int32_t row, float* host_dst, int32_t vocab) 
 }
 
 sv_status sv_set_profile(sv_ctx* c, int32_t mask) {
-  if (!c || mask < 0 || mask >= (1 << sv_ctx::kRoles)) return SV_EINVAL;
+  if (!c || mask < 0 || mask >= (1 << kProfRoles)) return SV_EINVAL;
   c->prof_mask = mask;
   return SV_OK;
 }
 
 sv_status sv_profile_read(const sv_ctx* c, int32_t role, double* total_ms, int64_t* launches) {
-  if (!c || role < 0 || role >= sv_ctx::kRoles) return SV_EINVAL;
+  if (!c || role < 0 || role >= kProfRoles) return SV_EINVAL;
   if (total_ms) *total_ms = c->prof_ms[role];
   if (launches) *launches = c->prof_n[role];
   return SV_OK;
@@ -578,7 +587,7 @@ sv_status sv_profile_read(const sv_ctx* c, int32_t role, double* total_ms, int64
 
 sv_status sv_profile_reset(sv_ctx* c) {
   if (!c) return SV_EINVAL;
-  for (int r = 0; r < sv_ctx::kRoles; ++r) { c->prof_ms[r] = 0.0; c->prof_n[r] = 0; }
+  for (int r = 0; r < kProfRoles; ++r) { c->prof_ms[r] = 0.0; c->prof_n[r] = 0; }
   return SV_OK;
 }
 

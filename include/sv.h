@@ -187,9 +187,13 @@ sv_status sv_get_logits(sv_ctx *ctx, int32_t row, float *host_dst, int32_t vocab
  * *m receives M.  dst may hold up to 64 entries. */
 sv_status sv_last_argmax(const sv_ctx *ctx, int32_t *dst, int32_t *m);
 
-/* Measurement (the per-kernel timing a roofline figure needs): HIP events
- * recorded on the context's stream around every launch of the enabled kernel
- * roles; elapsed times are summed after each forward's synchronisation.
+/* Measurement (the per-kernel timing a roofline figure needs): every launch
+ * of an enabled kernel role stamps the device's constant-rate wall clock
+ * (hipDeviceAttributeWallClockRate) when its first workgroup starts and when
+ * its last one ends; the spans are summed on the host after each forward's
+ * synchronisation.  A profiled forward runs the same kernels (in the same
+ * HIP graph) as an unprofiled one, plus one small kernel that clears the
+ * stamp slots and a copy of the slots to host.
  * Roles: 0 QKV GEMM, 1 O-projection GEMM, 2 gate/up GEMM, 3 down GEMM,
  * 4 LM-head GEMM, 5 attention (split + combine).  Bit r of `mask` enables
  * role r; mask 0 stops recording and keeps the totals. */
