@@ -54,7 +54,7 @@ struct GemmArgs {
   int n_pages, layer, nq, nkv, dh;
   const float2* rope;    // [max_ctx][dh/2] (cos, sin)
   // LM head
-  uint64_t* best;        // [M][N/16] packed (orderable logit, ~id)
+  unsigned long long* best;   // [M] row argmax keys (orderable logit, ~id), zeroed by the embed kernel
   float* logits;         // optional [M][N] fp32
   unsigned long long* prof;   // optional [2]: (min start, max end) device wall clock
 };
@@ -81,10 +81,15 @@ inline int gemm_max_rows(int unit, int waves) {
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
 // Number of KV splits of a row attending to ctx positions.
 int attn_splits(int ctx);
+// Whether any of rows kv_len + 1 .. kv_len + M spans more than one split (the
+// combine pass is needed only then).
+bool attn_needs_combine(int kv_len, int M);
+// Embedding rows of the forward's ids; also clears the M row-argmax keys.
 hipError_t launch_embed(const int* params, int M, const void* embed, int vocab, int d, float* x, float* ss,
-                        const uint16_t* g0, uint16_t* uhi, uint16_t* ulo, hipStream_t st);
-hipError_t launch_accept(const int* params, int M, int verify, const uint64_t* best, int n_groups,
-                         int* result, hipStream_t st);
+                        const uint16_t* g0, uint16_t* uhi, uint16_t* ulo, unsigned long long* best,
+                        hipStream_t st);
+hipError_t launch_accept(const int* params, int M, int verify, const unsigned long long* best, int* result,
+                         hipStream_t st);
 // Profiling slots: (start, end) pairs set to (max, 0) before a forward.
 hipError_t launch_prof_reset(unsigned long long* slots, int n_pairs, hipStream_t st);
 hipError_t launch_pack(int fmt, int layout, const void* src0, const void* src0_scales, const void* src1,

@@ -226,6 +226,7 @@ struct GemmShared {
   f32x4 red[kMaxWaves][64];   // wave partials of one row tile
   float y[kMaxRows][16];      // finished outputs of the item
   float inv[kMaxRows];        // 1 / rms of each row (RMSNorm consumers)
+  unsigned long long best[kMaxRows];   // LM head: this workgroup's row argmax keys
 };
 
 __device__ __forceinline__ constexpr bool norm_role(int role) {
@@ -297,7 +298,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, GemmShared& sh,
       uint64_t b = argmax_key(y, (uint32_t)n);
 #pragma unroll
       for (int o = 8; o >= 1; o >>= 1) b = umax64(b, __shfl_xor(b, o));
-      if (c == 0) a.best[(size_t)r * (a.N >> 4) + T] = b;
+      if (c == 0) atomicMax(&sh.best[r], (unsigned long long)b);
     }
   }
 }
@@ -326,6 +327,23 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& a, GemmShared& sh, f
   }
   gemm_epilogue<ROLE>(a, sh, T);
   __syncthreads();
+}
+
+// LM head: the workgroup's row maxima start at 0 (below every key) and go to
+// the global row keys with one atomic max per row at the end.  The key orders
+// by logit and then by lowest id, so the maximum does not depend on which
+// workgroup or item contributed first.
+template <int ROLE>
+__device__ __forceinline__ void row_best_init(const GemmArgs& a, GemmShared& sh) {
+  if (ROLE == kRoleLmHead)
+    for (int r = threadIdx.x; r < a.M; r += blockDim.x) sh.best[r] = 0ull;
+}
+template <int ROLE>
+__device__ __forceinline__ void row_best_publish(const GemmArgs& a, GemmShared& sh) {
+  if (ROLE == kRoleLmHead) {
+    __syncthreads();
+    for (int r = threadIdx.x; r < a.M; r += blockDim.x) atomicMax(a.best + r, sh.best[r]);
+  }
 }
 
 // Activation planes of chunk range [c_lo, c_lo + n_chunks) of every row,
@@ -363,20 +381,33 @@ __device__ __forceinline__ BPair lds_pair(const Stage& st, int r, int k) {
                *reinterpret_cast<const uint4*>(st.lo + r * st.stride + k)};
 }
 
-// Chunks per LDS stage: the largest multiple of nw dividing the chunk count
-// whose activation planes for M rows fit the stage budget.  It only decides
-// when activations are staged, never the order of any sum.
-__host__ __device__ __forceinline__ int stage_chunks(int n_chunks, int nw, int M, int unit) {
-  int best = nw;
-  for (int cs = nw; cs <= n_chunks; cs += nw) {
+// Chunks per LDS stage: the largest multiple of nw * nb dividing the chunk
+// count whose activation planes for M rows fit the stage budget (0 if even
+// nw * nb chunks do not fit).  It only decides when activations are staged,
+// never the order of any sum.
+__host__ __device__ __forceinline__ int stage_chunks(int n_chunks, int nw, int M, int unit, int nb) {
+  int best = 0;
+  const int step = nw * nb;
+  for (int cs = step; cs <= n_chunks; cs += step) {
     if (n_chunks % cs) continue;
     if ((size_t)M * (cs * unit + 8) * 4 <= (size_t)kStageBytes) best = cs;
   }
   return best;
 }
 
-// Wave w accumulates chunks w, w + NW, w + 2 NW, ... in that order.
-template <int TM, int ROLE>
+// Weight loads of one wave run as a ring of NB slots: a slot is refilled with
+// the chunk NB positions ahead as soon as its MFMAs are issued, across item
+// boundaries, so NB loads stay in flight through the cross-wave reduction of
+// each item.  Position (item T, c) of wave w is chunk kc = w + nw * c of T;
+// the ring changes only when chunks arrive, never the order of any sum.
+struct LoadCursor {
+  int T, c;
+  size_t off;   // uint4 offset of chunk (T, c) for lane 0 of this wave
+};
+
+// bf16: wave w accumulates chunks w, w + NW, w + 2 NW, ... of each item in
+// that order.
+template <int TM, int ROLE, int NB>
 __global__ __launch_bounds__(1024) void k_gemm_bf16(GemmArgs a) {
   __shared__ GemmShared sh;
   __shared__ __align__(16) uint16_t stage_mem[kStageBytes / 2];
@@ -385,70 +416,81 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int KC = a.K >> 5;
-  const int cs = stage_chunks(KC, nw, a.M, 32);
+  const int cs = stage_chunks(KC, nw, a.M, 32, NB);
   const int n_stages = KC / cs;
-  const int cpws = cs / nw;                     // chunks per wave per stage
+  const int cpws = cs / nw;                     // chunks per wave per stage (multiple of NB)
+  const int cpi = KC / nw;                      // chunks per wave per item (multiple of NB)
   Stage st;
   st.stride = cs * 32 + 8;
   st.hi = stage_mem;
   st.lo = stage_mem + (size_t)a.M * st.stride;
   const int n_items = a.N >> 4;
-  int T = blockIdx.x;
-  const uint4* W4 = reinterpret_cast<const uint4*>(a.W) + lane;
   // packed weights are tile-major: chunk kc of tile T is the KiB at (T * KC + kc)
-  auto wptr = [&](int t, int kc) { return W4 + ((size_t)t * KC + kc) * 64; };
-  constexpr int NB = 8;                         // weight chunks in flight per wave
-
-  uint4 A[NB];
-  auto load_a = [&](int t, int s, int b0) {
-#pragma unroll
-    for (int u = 0; u < NB; ++u)
-      if (b0 + u < cpws) A[u] = ld_stream(wptr(t, s * cs + wave + nw * (b0 + u)));
+  const uint4* W4 = reinterpret_cast<const uint4*>(a.W) + lane;
+  LoadCursor cur{(int)blockIdx.x, 0, ((size_t)blockIdx.x * KC + wave) * 64};
+  // Unconditional: the caller never refills past this workgroup's last item
+  // (loads that may or may not be issued would leave the compiler unable to
+  // count outstanding loads, and every wait would drain them all).
+  auto refill = [&](uint4& slot) {
+    slot = ld_stream(W4 + cur.off);
+    cur.off += (size_t)nw * 64;
+    if (++cur.c == cpi) {
+      cur.c = 0;
+      cur.T += gridDim.x;
+      cur.off = ((size_t)cur.T * KC + wave) * 64;
+    }
   };
-  load_a(T, 0, 0);                              // requested before anything else
+  uint4 A[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) refill(A[u]);     // requested before anything else (NB <= cpi)
+  row_best_init<ROLE>(a, sh);
   if (norm_role(ROLE)) rows_inv_rms(a, sh, wave, lane, nw);   // read only by the epilogue
   if (n_stages == 1) {
     stage_planes(a, st, 0, cs, 32);
     __syncthreads();
   }
 
-  for (;;) {
+  for (int T = blockIdx.x; T < n_items; T += gridDim.x) {
     f32x4 acc[TM];
 #pragma unroll
     for (int rt = 0; rt < TM; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < n_stages; ++s) {
-      if (n_stages > 1) {
+    for (int c0 = 0; c0 < cpi; c0 += NB) {
+      const int cl0 = c0 % cpws;                // position inside the current stage
+      if (n_stages > 1 && cl0 == 0) {
         __syncthreads();
-        stage_planes(a, st, s * cs, cs, 32);
+        stage_planes(a, st, (c0 / cpws) * cs, cs, 32);
         __syncthreads();
       }
-      for (int b0 = 0; b0 < cpws; b0 += NB) {
-        if (s > 0 || b0 > 0) load_a(T, s, b0);
+      auto group = [&](bool refills) {
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
-          if (b0 + u < cpws) {
-            const int kl = (wave + nw * (b0 + u)) * 32 + g * 8;   // input index inside the stage
+          const int kl = (wave + nw * (cl0 + u)) * 32 + g * 8;   // input index inside the stage
 #pragma unroll
-            for (int rt = 0; rt < TM; ++rt)
-              acc[rt] = mfma_pair(A[u], lds_pair(st, row_of(rt * 16 + j, a.M), kl), acc[rt]);
-          }
+          for (int rt = 0; rt < TM; ++rt)
+            acc[rt] = mfma_pair(A[u], lds_pair(st, row_of(rt * 16 + j, a.M), kl), acc[rt]);
+          if (refills) refill(A[u]);
         }
-      }
+      };
+      if (T + (int)gridDim.x < n_items || c0 + NB < cpi) group(true);
+      else group(false);                        // the last NB chunks of this workgroup
     }
-    const int Tn = T + gridDim.x;
-    if (Tn < n_items) load_a(Tn, 0, 0);
     gemm_finish<TM, ROLE>(a, sh, acc, T, wave, lane, nw);
-    if (Tn >= n_items) break;
-    T = Tn;
   }
+  row_best_publish<ROLE>(a, sh);
   prof_end(a.prof);
 }
 
 // int4 weights: wave w takes 128-input tiles w, w + NW, ...; per row tile and
 // per scale group, the MFMAs over the group's 64 inputs (hi and lo planes of
 // each 32-input chunk) start from zero; the group sum is then scaled by the
-// fp32 group scale and added to the running fp32 sum in group order.
-template <int TM, int ROLE>
+// fp32 group scale and added to the running fp32 sum in group order.  The
+// weight ring holds each tile's codes and its two groups' scales.
+struct Int4Slot {
+  uint4 q;
+  uint2 s0, s1;
+};
+
+template <int TM, int ROLE, int NB>
 __global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
   __shared__ GemmShared sh;
   __shared__ __align__(16) uint16_t stage_mem[kStageBytes / 2];
@@ -457,14 +499,33 @@ __global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int KT = a.K >> 7;                 // 128-input tiles
-  const int cs = stage_chunks(KT, nw, a.M, 128);
+  const int cs = stage_chunks(KT, nw, a.M, 128, NB);
   const int n_stages = KT / cs;
   const int cpws = cs / nw;
+  const int cpi = KT / nw;
   Stage st;
   st.stride = cs * 128 + 8;
   st.hi = stage_mem;
   st.lo = stage_mem + (size_t)a.M * st.stride;
   const int n_items = a.N >> 4;
+  const uint4* Wq = reinterpret_cast<const uint4*>(a.W) + lane;
+  const uint2* Ws = reinterpret_cast<const uint2*>(a.Wscale) + g;
+  // tile (T, kt): codes at uint4 (T * KT + kt) * 64, scales at uint2 (T * KT + kt) * 8
+  LoadCursor cur{(int)blockIdx.x, 0, (size_t)blockIdx.x * KT + wave};
+  auto refill = [&](Int4Slot& slot) {   // unconditional, as in the bf16 kernel
+    slot.q = ld_stream(Wq + cur.off * 64);
+    slot.s0 = Ws[cur.off * 8];
+    slot.s1 = Ws[cur.off * 8 + 4];
+    cur.off += nw;
+    if (++cur.c == cpi) {
+      cur.c = 0;
+      cur.T += gridDim.x;
+      cur.off = (size_t)cur.T * KT + wave;
+    }
+  };
+  Int4Slot Q[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) refill(Q[u]);
   if (norm_role(ROLE)) rows_inv_rms(a, sh, wave, lane, nw);
   if (n_stages == 1) {
     stage_planes(a, st, 0, cs, 128);
@@ -474,23 +535,21 @@ __global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
     f32x4 acc[TM];
 #pragma unroll
     for (int rt = 0; rt < TM; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint4* Wt = reinterpret_cast<const uint4*>(a.W) + (size_t)T * KT * 64 + lane;
-    const uint2* St = reinterpret_cast<const uint2*>(a.Wscale) + (size_t)T * KT * 8 + g;
-    for (int s = 0; s < n_stages; ++s) {
-      if (n_stages > 1) {
+    for (int c0 = 0; c0 < cpi; c0 += NB) {
+      const int cl0 = c0 % cpws;
+      if (n_stages > 1 && cl0 == 0) {
         __syncthreads();
-        stage_planes(a, st, s * cs, cs, 128);
+        stage_planes(a, st, (c0 / cpws) * cs, cs, 128);
         __syncthreads();
       }
-      for (int c = 0; c < cpws; ++c) {
-        const int kt = s * cs + wave + nw * c;
-        const int kl = (wave + nw * c) * 128;      // input index inside the stage
-        const uint4 Q = ld_stream(Wt + (size_t)kt * 64);
-        const uint2 SC0 = St[(size_t)kt * 8], SC1 = St[(size_t)kt * 8 + 4];
+      auto group = [&](bool refills) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int kl = (wave + nw * (cl0 + u)) * 128;      // input index inside the stage
 #pragma unroll
         for (int gq = 0; gq < 2; ++gq) {
-          const uint2 SC = gq == 0 ? SC0 : SC1;
-          const uint4 A0 = codes8(gq == 0 ? Q.x : Q.z), A1 = codes8(gq == 0 ? Q.y : Q.w);
+          const uint2 SC = gq == 0 ? Q[u].s0 : Q[u].s1;
+          const uint4 A0 = codes8(gq == 0 ? Q[u].q.x : Q[u].q.z), A1 = codes8(gq == 0 ? Q[u].q.y : Q[u].q.w);
           const float s0 = bf2f((uint16_t)(SC.x & 0xffffu)), s1 = bf2f((uint16_t)(SC.x >> 16));
           const float s2 = bf2f((uint16_t)(SC.y & 0xffffu)), s3 = bf2f((uint16_t)(SC.y >> 16));
 #pragma unroll
@@ -505,35 +564,61 @@ __global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
             acc[rt].w = fmaf(s3, p.w, acc[rt].w);
           }
         }
+        if (refills) refill(Q[u]);
       }
+      };
+      if (T + (int)gridDim.x < n_items || c0 + NB < cpi) group(true);
+      else group(false);
     }
     gemm_finish<TM, ROLE>(a, sh, acc, T, wave, lane, nw);
   }
   prof_end(a.prof);
 }
 
-template <int ROLE, bool INT4>
-static hipError_t gemm_dispatch(const GemmArgs& a, int grid, hipStream_t st) {
+template <int ROLE, bool INT4, int NB>
+static hipError_t gemm_dispatch_nb(const GemmArgs& a, int grid, hipStream_t st) {
   const dim3 block(64 * a.S);
   const int tm = (a.M + 15) / 16;
   if constexpr (INT4) {
     switch (tm) {
-      case 1: hipLaunchKernelGGL((k_gemm_int4<1, ROLE>), dim3(grid), block, 0, st, a); break;
-      case 2: hipLaunchKernelGGL((k_gemm_int4<2, ROLE>), dim3(grid), block, 0, st, a); break;
-      case 3: hipLaunchKernelGGL((k_gemm_int4<3, ROLE>), dim3(grid), block, 0, st, a); break;
-      case 4: hipLaunchKernelGGL((k_gemm_int4<4, ROLE>), dim3(grid), block, 0, st, a); break;
+      case 1: hipLaunchKernelGGL((k_gemm_int4<1, ROLE, NB>), dim3(grid), block, 0, st, a); break;
+      case 2: hipLaunchKernelGGL((k_gemm_int4<2, ROLE, NB>), dim3(grid), block, 0, st, a); break;
+      case 3: hipLaunchKernelGGL((k_gemm_int4<3, ROLE, NB>), dim3(grid), block, 0, st, a); break;
+      case 4: hipLaunchKernelGGL((k_gemm_int4<4, ROLE, NB>), dim3(grid), block, 0, st, a); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (tm) {
-      case 1: hipLaunchKernelGGL((k_gemm_bf16<1, ROLE>), dim3(grid), block, 0, st, a); break;
-      case 2: hipLaunchKernelGGL((k_gemm_bf16<2, ROLE>), dim3(grid), block, 0, st, a); break;
-      case 3: hipLaunchKernelGGL((k_gemm_bf16<3, ROLE>), dim3(grid), block, 0, st, a); break;
-      case 4: hipLaunchKernelGGL((k_gemm_bf16<4, ROLE>), dim3(grid), block, 0, st, a); break;
+      case 1: hipLaunchKernelGGL((k_gemm_bf16<1, ROLE, NB>), dim3(grid), block, 0, st, a); break;
+      case 2: hipLaunchKernelGGL((k_gemm_bf16<2, ROLE, NB>), dim3(grid), block, 0, st, a); break;
+      case 3: hipLaunchKernelGGL((k_gemm_bf16<3, ROLE, NB>), dim3(grid), block, 0, st, a); break;
+      case 4: hipLaunchKernelGGL((k_gemm_bf16<4, ROLE, NB>), dim3(grid), block, 0, st, a); break;
       default: return hipErrorInvalidValue;
     }
   }
   return hipGetLastError();
+}
+
+// Ring depth: the deepest of 8 / 4 / 2 / 1 that divides the chunks each wave
+// takes per item and per LDS stage.
+int gemm_ring_depth(int n_chunks, int waves, int M, int unit) {
+  for (int nb : {8, 4, 2, 1}) {
+    if ((n_chunks / waves) % nb) continue;
+    const int cs = stage_chunks(n_chunks, waves, M, unit, nb);
+    if (cs > 0) return nb;
+  }
+  return 0;
+}
+
+template <int ROLE, bool INT4>
+static hipError_t gemm_dispatch(const GemmArgs& a, int grid, hipStream_t st) {
+  switch (gemm_ring_depth(a.K / (INT4 ? 128 : 32), a.S, a.M, INT4 ? 128 : 32)) {
+    case 8: return gemm_dispatch_nb<ROLE, INT4, 8>(a, grid, st);
+    case 4: return gemm_dispatch_nb<ROLE, INT4, 4>(a, grid, st);
+    case 2: return gemm_dispatch_nb<ROLE, INT4, 2>(a, grid, st);
+    case 1: return gemm_dispatch_nb<ROLE, INT4, 1>(a, grid, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // a.S: waves splitting K inside one workgroup (fixed per matrix, 1..16);
@@ -560,20 +645,25 @@ hipError_t launch_gemm(const GemmArgs& a, int role, int grid, hipStream_t st) {
 
 // ------------------------------------------------------------ attention
 // Split plan of one row, a function of its own ctx only: nb = ceil(ctx/64)
-// blocks of 64 absolute positions, bps = ceil(nb / 32) blocks per split,
-// ns = ceil(nb / bps) splits; split i covers positions
-// [64 i bps, min(64 (i+1) bps, ctx)).  Short contexts get one block per
-// split (many workgroups), long ones at most 32 splits (little partial data).
+// blocks of 64 absolute positions, bps = max(ceil(nb / 32), min(nb, 8))
+// blocks per split, ns = ceil(nb / bps) splits; split i covers positions
+// [64 i bps, min(64 (i+1) bps, ctx)).  Up to 512 positions take one split
+// (one workgroup per KV head walks them; no combine pass), longer contexts
+// spread over up to 32 splits.
+constexpr int kAttnMinBlocks = 8;
 __host__ __device__ __forceinline__ int attn_bps(int ctx) {
   const int nb = (ctx + kAttnBlock - 1) / kAttnBlock;
-  return (nb + kAttnMaxSplits - 1) / kAttnMaxSplits;
+  const int spread = (nb + kAttnMaxSplits - 1) / kAttnMaxSplits;
+  const int floor_blocks = nb < kAttnMinBlocks ? nb : kAttnMinBlocks;
+  return spread > floor_blocks ? spread : floor_blocks;
 }
 __host__ __device__ __forceinline__ int attn_ns(int ctx) {
   const int nb = (ctx + kAttnBlock - 1) / kAttnBlock;
-  const int bps = (nb + kAttnMaxSplits - 1) / kAttnMaxSplits;
+  const int bps = attn_bps(ctx);
   return (nb + bps - 1) / bps;
 }
 int attn_splits(int ctx) { return attn_ns(ctx); }
+bool attn_needs_combine(int kv_len, int M) { return attn_ns(kv_len + M) > 1; }
 
 // One workgroup (8 waves) per (split index, KV head) holds every (row, q
 // head) pair of that KV head as MFMA columns: q-row qr = r*G + jj for query
@@ -625,7 +715,10 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     u_lo = min(u_lo, split * bps * kAttnBlock);
     u_hi = max(u_hi, min((split + 1) * bps * kAttnBlock, ctx));
   }
-  if (u_lo >= u_hi) return;
+  if (u_lo >= u_hi) {
+    if (a.n_split == 1) prof_end(a.prof);
+    return;
+  }
   const size_t layer_base = (size_t)a.layer * a.n_pages;
 
   BPair qop[QPW][DC];
@@ -768,18 +861,34 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       m[u] = mn;
     }
   }
-  // lane (g, j) holds o of q-row j for d = dt*16 + 4g + v
+  // lane (g, j) holds o of q-row j for d = dt*16 + 4g + v.  A row whose
+  // context is a single split is final here: o / l as output planes, the
+  // same arithmetic the combine performs for one split (weight 2^0 = 1).
 #pragma unroll
   for (int u = 0; u < QPW; ++u) {
     const int qr = (wave + 8 * u) * 16 + j;
     if (wave + 8 * u >= n_qt || qr >= n_qr || hi_q[u] <= lo_q[u]) continue;
     const int r = qr / G, head = h * G + qr % G;
+    if (attn_ns(kv_len + r + 1) == 1) {
+      const size_t ob = ((size_t)r * a.nq + head) * DH;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const float ov[4] = {o[u][dt].x, o[u][dt].y, o[u][dt].z, o[u][dt].w};
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const size_t oi = ob + dt * 16 + 4 * g + v;
+          split1(ov[v] / l[u], a.ohi[oi], a.olo[oi]);
+        }
+      }
+      continue;
+    }
     float* part = a.part + (((size_t)r * a.nq + head) * kAttnMaxSplits + split) * (DH + 4);
     if (g == 0) { part[0] = m[u]; part[1] = l[u]; }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
       *reinterpret_cast<float4*>(part + 4 + dt * 16 + 4 * g) = make_float4(o[u][dt].x, o[u][dt].y, o[u][dt].z, o[u][dt].w);
   }
+  if (a.n_split == 1) prof_end(a.prof);   // no combine pass follows
 }
 
 // Combine the row's splits in split order: o = sum_i w_i o_i / sum_i w_i l_i
@@ -790,6 +899,10 @@ __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
   const int j = blockIdx.x, r = blockIdx.y, lane = threadIdx.x;
   const int ctx = a.params[0] + r + 1;
   const int ns = attn_ns(ctx);
+  if (ns == 1) {   // written by the split kernel
+    prof_end(a.prof);
+    return;
+  }
   const float* base = a.part + ((size_t)r * a.nq + j) * kAttnMaxSplits * (DH + 4);
   float mx = base[0];
   for (int i = 1; i < ns; ++i) mx = fmaxf(mx, base[(size_t)i * (DH + 4)]);
@@ -815,10 +928,10 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   if (a.M * (a.nq / a.nkv) > kAttnQRows || a.n_split < 1 || a.n_split > kAttnMaxSplits) return hipErrorInvalidValue;
   if (a.dh == 128) {
     hipLaunchKernelGGL(k_attn_mfma<128>, dim3(a.n_split, a.nkv), dim3(512), 0, st, a);
-    hipLaunchKernelGGL(k_attn_combine<128>, dim3(a.nq, a.M), dim3(64), 0, st, a);
+    if (a.n_split > 1) hipLaunchKernelGGL(k_attn_combine<128>, dim3(a.nq, a.M), dim3(64), 0, st, a);
   } else if (a.dh == 64) {
     hipLaunchKernelGGL(k_attn_mfma<64>, dim3(a.n_split, a.nkv), dim3(512), 0, st, a);
-    hipLaunchKernelGGL(k_attn_combine<64>, dim3(a.nq, a.M), dim3(64), 0, st, a);
+    if (a.n_split > 1) hipLaunchKernelGGL(k_attn_combine<64>, dim3(a.nq, a.M), dim3(64), 0, st, a);
   } else {
     return hipErrorInvalidValue;
   }
@@ -829,26 +942,34 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
 // x[r] = E[id_r] widened to fp32, the per-16-column sums of squares the
 // first RMSNorm reads (16-lane butterfly, like the residual epilogue), and
 // the planes of x * g_attn of layer 0.
-__global__ __launch_bounds__(256) void k_embed(const int* params, const uint16_t* E, int vocab, int d, float* x,
-                                               float* ss, const uint16_t* g0, uint16_t* uhi, uint16_t* ulo) {
-  const int r = blockIdx.x;
+// One thread per (row, feature): x = E[id] (exact bf16 -> fp32), the row's
+// per-16-column sums of squares (16 consecutive lanes), planes of x * g0.
+// Block (r, 0) also clears row r's argmax key for the LM head.
+__global__ __launch_bounds__(256) void k_embed(const int* __restrict__ params, const uint16_t* __restrict__ E, int d,
+                                               float* __restrict__ x, float* __restrict__ ss,
+                                               const uint16_t* __restrict__ g0, uint16_t* __restrict__ uhi,
+                                               uint16_t* __restrict__ ulo, unsigned long long* __restrict__ best) {
+  const int r = blockIdx.y;
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (blockIdx.x == 0 && threadIdx.x == 0) best[r] = 0ull;
+  if (k >= d) return;   // d is a multiple of 16, so whole 16-lane groups exit together
   const int id = params[2 + r];
-  (void)vocab;
-  for (int k = threadIdx.x; k < d; k += 256) {
-    const size_t off = ((size_t)(id >> 4) * (d >> 5) + (k >> 5)) * 512 + (size_t)(((k & 31) >> 3) * 16 + (id & 15)) * 8 + (k & 7);
-    const float v = bf2f(E[off]);
-    x[(size_t)r * d + k] = v;
-    float sq = v * v;
+  // the embedding is packed like a bf16 weight matrix: 16-row tiles of 32-input chunks
+  const size_t off = ((size_t)(id >> 4) * (d >> 5) + (k >> 5)) * 512 + (size_t)(((k & 31) >> 3) * 16 + (id & 15)) * 8 + (k & 7);
+  const float v = bf2f(E[off]);
+  x[(size_t)r * d + k] = v;
+  float sq = v * v;
 #pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) sq += __shfl_xor(sq, o);
-    if ((k & 15) == 0) ss[(size_t)r * (d >> 4) + (k >> 4)] = sq;
-    split1(v * bf2f(g0[k]), uhi[(size_t)r * d + k], ulo[(size_t)r * d + k]);
-  }
+  for (int o = 8; o >= 1; o >>= 1) sq += __shfl_xor(sq, o);
+  if ((k & 15) == 0) ss[(size_t)r * (d >> 4) + (k >> 4)] = sq;
+  split1(v * bf2f(g0[k]), uhi[(size_t)r * d + k], ulo[(size_t)r * d + k]);
 }
 
 hipError_t launch_embed(const int* params, int M, const void* embed, int vocab, int d, float* x, float* ss,
-                        const uint16_t* g0, uint16_t* uhi, uint16_t* ulo, hipStream_t st) {
-  hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, params, (const uint16_t*)embed, vocab, d, x, ss, g0, uhi, ulo);
+                        const uint16_t* g0, uint16_t* uhi, uint16_t* ulo, unsigned long long* best, hipStream_t st) {
+  (void)vocab;
+  hipLaunchKernelGGL(k_embed, dim3((d + 255) / 256, M), dim3(256), 0, st, params, (const uint16_t*)embed, d, x, ss, g0,
+                     uhi, ulo, best);
   return hipGetLastError();
 }
 
@@ -857,45 +978,30 @@ hipError_t launch_embed(const int* params, int M, const void* embed, int vocab, 
 // order-free), then the greedy acceptance: n = number of leading drafts equal
 // to the argmax of the row before them; next = argmax of row n.
 // result: [0] n, [1] next, [2 + r] argmax of row r.
-__global__ __launch_bounds__(1024) void k_accept(const int* params, int M, int verify, const uint64_t* best,
-                                                 int n_groups, int* result) {
-  __shared__ int am[kMaxRows];
-  __shared__ uint64_t wbest[16];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  for (int r = 0; r < M; ++r) {
-    uint64_t b = 0;
-    for (int i = threadIdx.x; i < n_groups; i += 1024) b = umax64(b, best[(size_t)r * n_groups + i]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) b = umax64(b, __shfl_xor(b, o));
-    if (lane == 0) wbest[wave] = b;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      uint64_t bb = wbest[0];
-      for (int w = 1; w < 16; ++w) bb = umax64(bb, wbest[w]);
-      am[r] = (int)(0xffffffffu - (uint32_t)(bb & 0xffffffffu));
-    }
-    __syncthreads();
+// Row argmax a_r from the LM head's row keys; verify rows accept the longest
+// prefix of drafts d_i = a_i (row i+1 holds d_i); result = [n, next, a_0..].
+__global__ __launch_bounds__(64) void k_accept(const int* params, int M, int verify, const unsigned long long* best,
+                                               int* result) {
+  const int lane = threadIdx.x;
+  const int a_r = lane < M ? (int)(0xffffffffu - (uint32_t)(best[lane] & 0xffffffffu)) : 0;
+  if (lane < M) result[2 + lane] = a_r;
+  int n;
+  if (verify) {
+    const int k = M - 1;
+    const bool miss = lane < k && params[2 + lane + 1] != a_r;
+    const unsigned long long mask = __ballot(miss);
+    n = mask ? (__ffsll((long long)mask) - 1) : k;
+  } else {
+    n = M - 1;
   }
-  if (wave == 0) {
-    const int a_r = lane < M ? am[lane] : 0;
-    if (lane < M) result[2 + lane] = a_r;
-    int n;
-    if (verify) {
-      const int k = M - 1;
-      const bool miss = lane < k && params[2 + lane + 1] != a_r;
-      const unsigned long long mask = __ballot(miss);
-      n = mask ? (__ffsll((long long)mask) - 1) : k;
-    } else {
-      n = M - 1;
-    }
-    const int next = __shfl(a_r, n);
-    if (lane == 0) { result[0] = n; result[1] = next; }
-  }
+  const int next = __shfl(a_r, n);
+  if (lane == 0) { result[0] = n; result[1] = next; }
 }
 
-hipError_t launch_accept(const int* params, int M, int verify, const uint64_t* best, int n_groups, int* result,
+hipError_t launch_accept(const int* params, int M, int verify, const unsigned long long* best, int* result,
                          hipStream_t st) {
-  hipLaunchKernelGGL(k_accept, dim3(1), dim3(1024), 0, st, params, M, verify, best, n_groups, result);
+  if (M < 1 || M > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_accept, dim3(1), dim3(64), 0, st, params, M, verify, best, result);
   return hipGetLastError();
 }
 

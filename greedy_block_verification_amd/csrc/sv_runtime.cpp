@@ -64,7 +64,9 @@ struct Plans {
 
 // Workgroups per GEMM: enough to cover two per compute unit, never more
 // than there are 16-output items.  Any grid gives the same bits.
-int grid_for(int N, int n_cu) { return std::max(1, std::min(N / 16, 2 * n_cu)); }
+// One persistent workgroup per CU (a GEMM workgroup holds a whole CU's
+// worth of waves and LDS); the LM head's many items take two per CU.
+int grid_for(int N, int per_cu, int n_cu) { return std::max(1, std::min(N / 16, per_cu * n_cu)); }
 
 Plans make_plans(const sv_config& c, int n_cu) {
   const int qd = c.n_q_heads * c.head_dim, kd = c.n_kv_heads * c.head_dim;
@@ -79,7 +81,8 @@ Plans make_plans(const sv_config& c, int n_cu) {
   p.gu = {2 * c.d_ff, c.d_model, choose_waves(c.d_model, unit, maxw), c.weight_fmt};
   p.d = {c.d_model, c.d_ff, choose_waves(c.d_ff, unit, maxw), c.weight_fmt};
   p.lm = {c.vocab, c.d_model, choose_waves(c.d_model, 32, 16), 0};
-  for (GemmPlan* g : {&p.qkv, &p.o, &p.gu, &p.d, &p.lm}) g->grid = grid_for(g->N, n_cu);
+  for (GemmPlan* g : {&p.qkv, &p.o, &p.gu, &p.d}) g->grid = grid_for(g->N, 1, n_cu);
+  p.lm.grid = grid_for(p.lm.N, 2, n_cu);
   return p;
 }
 
@@ -125,7 +128,7 @@ Layout make_layout(const sv_config& c, const Plans& p) {
   L.uplanes = take(2 * R * c.d_model * 2);   // hi, lo planes of x * g (RMSNorm consumers' input)
   L.oplanes = take(2 * R * qd * 2);          // attention output
   L.aplanes = take(2 * R * c.d_ff * 2);      // act(gate) * up
-  L.best = take(R * (c.vocab / 16) * 8);
+  L.best = take(R * 8);
   L.result = take(sizeof(int) * (2 + kMaxRows));
   L.logits = take(R * (size_t)c.vocab * 4);
   L.rope = take((size_t)c.max_ctx * (c.head_dim / 2) * 8);
@@ -226,8 +229,9 @@ hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, hipStream_
   if (c->prof_mask != 0 && (e = launch_prof_reset(c->at<unsigned long long>(c->lay.prof), prof_pairs(cfg), st)) !=
                                hipSuccess)
     return e;
-  e = launch_embed(d_params, M, c->w.embed, cfg.vocab, cfg.d_model, x, ss, gain(c->layers[0].g_attn), uhi,
-                              ulo, st);
+  unsigned long long* best = c->at<unsigned long long>(c->lay.best);
+  e = launch_embed(d_params, M, c->w.embed, cfg.vocab, cfg.d_model, x, ss, gain(c->layers[0].g_attn), uhi, ulo, best,
+                   st);
   if (e != hipSuccess) return e;
 
   GemmArgs g{};
@@ -281,10 +285,10 @@ hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, hipStream_
   // (final norm) LM head + per-16-column argmax, then acceptance
   plan(c->plans.lm, c->w.lm_head, nullptr, uhi, ulo);
   g.layer = 0;
-  g.best = c->at<uint64_t>(c->lay.best);
+  g.best = best;
   g.logits = c->store_logits ? c->at<float>(c->lay.logits) : nullptr;
   if ((e = gemm_timed(c, g, kRoleLmHead, c->plans.lm.grid, st)) != hipSuccess) return e;
-  return launch_accept(d_params, M, verify, g.best, cfg.vocab / 16, c->at<int>(c->lay.result), st);
+  return launch_accept(d_params, M, verify, best, c->at<int>(c->lay.result), st);
 }
 
 sv_status forward(sv_ctx* c, int M, const int* ids, int verify) {
