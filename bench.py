@@ -143,7 +143,7 @@ def main():
     ap.add_argument("--prompt-len", type=int, default=128)
     ap.add_argument("--gen-tokens", type=int, default=64)
     ap.add_argument("--p-correct", type=float, default=0.66)
-    ap.add_argument("--cpu-tokens", type=int, default=1)
+    ap.add_argument("--cpu-tokens", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB first (the reference "
