@@ -9,7 +9,7 @@ namespace sv {
 constexpr int kMaxRows = 64;        // rows of one forward (verify: k+1; prefill chunk)
 constexpr int kPage = 16;           // positions per KV page
 constexpr int kGemmStageBytes = 136 * 1024;   // LDS a GEMM workgroup stages activation planes in
-constexpr int kAttnBlock = 64;      // positions per online-softmax block
+constexpr int kAttnBlock = 64;      // positions per online-softmax block (4 pages)
 constexpr int kAttnMaxSplits = 32;  // most KV splits of one row (the split plan depends only on its ctx)
 constexpr int kAttnQRows = 256;     // most (row, q head) pairs one attention workgroup holds (16 MFMA tiles)
 constexpr int kColGroup = 64;       // LM-head columns per argmax record (4 MFMA tiles of 16)
@@ -64,12 +64,16 @@ struct AttnArgs {
   const float* q;        // [M][nq][dh] fp32, after RoPE
   const uint16_t* kv_pool;
   const int* page_table;
-  int n_pages, layer, nq, nkv, dh, M, n_split;   // n_split: splits of the longest row (grid x)
+  int n_pages, layer, nq, nkv, dh, M, n_split;   // n_split: splits of the longest row
+  int n_lpages;          // logical pages (page_table entries) = max_ctx / 16
   float scale_log2;      // log2(e) / sqrt(dh)
   float* part;           // [M][nq][kAttnMaxSplits][dh + 4]  (m, l, -, -, o[dh])
   uint16_t* ohi;         // output planes [M][nq*dh]
   uint16_t* olo;
-  unsigned long long* prof;   // optional [2]: start stamped by the split kernel, end by the combine
+  unsigned long long* prof;   // optional [2]: start stamped by the split kernel, end by the last kernel
+  // set by launch_attention
+  int spw;               // splits per workgroup
+  int final_fold;        // 1: one workgroup per KV head folds its splits in LDS and writes the output
 };
 
 hipError_t launch_gemm(const GemmArgs& a, int role, int grid, hipStream_t st);

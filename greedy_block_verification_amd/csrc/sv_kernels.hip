@@ -289,8 +289,10 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, GemmShared& sh,
         const int kv = hh < a.nq + a.nkv ? 0 : 1;
         const int head = hh - a.nq - kv * a.nkv;
         const int page = a.page_table[pos / kPage];
-        const size_t off = ((((size_t)a.layer * a.n_pages + page) * 2 + kv) * a.nkv + head) * kPage + (pos % kPage);
-        a.kv_pool[off * a.dh + d] = f2h(out);
+        const size_t base = ((((size_t)a.layer * a.n_pages + page) * 2 + kv) * a.nkv + head) * kPage * a.dh;
+        // K rows are [slot][dh]; V is stored transposed inside the page, [dh][slot]
+        const size_t e = kv == 0 ? (size_t)(pos % kPage) * a.dh + d : (size_t)d * kPage + (pos % kPage);
+        a.kv_pool[base + e] = f2h(out);
       }
     } else {                                        // kRoleLmHead
       const int n = T * 16 + c;
@@ -645,17 +647,13 @@ hipError_t launch_gemm(const GemmArgs& a, int role, int grid, hipStream_t st) {
 
 // ------------------------------------------------------------ attention
 // Split plan of one row, a function of its own ctx only: nb = ceil(ctx/64)
-// blocks of 64 absolute positions, bps = max(ceil(nb / 32), min(nb, 8))
-// blocks per split, ns = ceil(nb / bps) splits; split i covers positions
-// [64 i bps, min(64 (i+1) bps, ctx)).  Up to 512 positions take one split
-// (one workgroup per KV head walks them; no combine pass), longer contexts
-// spread over up to 32 splits.
-constexpr int kAttnMinBlocks = 8;
+// blocks of 64 absolute positions, bps = ceil(nb / 32) blocks per split,
+// ns = ceil(nb / bps) splits; split i covers positions
+// [64 i bps, min(64 (i+1) bps, ctx)).  Short contexts get one block per
+// split, long ones at most 32 splits.
 __host__ __device__ __forceinline__ int attn_bps(int ctx) {
   const int nb = (ctx + kAttnBlock - 1) / kAttnBlock;
-  const int spread = (nb + kAttnMaxSplits - 1) / kAttnMaxSplits;
-  const int floor_blocks = nb < kAttnMinBlocks ? nb : kAttnMinBlocks;
-  return spread > floor_blocks ? spread : floor_blocks;
+  return (nb + kAttnMaxSplits - 1) / kAttnMaxSplits;
 }
 __host__ __device__ __forceinline__ int attn_ns(int ctx) {
   const int nb = (ctx + kAttnBlock - 1) / kAttnBlock;
@@ -665,166 +663,185 @@ __host__ __device__ __forceinline__ int attn_ns(int ctx) {
 int attn_splits(int ctx) { return attn_ns(ctx); }
 bool attn_needs_combine(int kv_len, int M) { return attn_ns(kv_len + M) > 1; }
 
-// One workgroup (8 waves) per (split index, KV head) holds every (row, q
-// head) pair of that KV head as MFMA columns: q-row qr = r*G + jj for query
-// head h*G + jj.  Row r works on its own split range of its ctx_r = kv_len +
-// r + 1 positions; the workgroup walks the union of the rows' ranges in
-// blocks of 64 absolute positions staged in LDS (K row-major, V transposed).
-// Per block and q-row:
-//   s_t = (K_t . q) * log2(e)/sqrt(dh)        one MFMA chain over d
+// Fold of a row's split partials (m_i, l_i, o_i), in split order:
+//   (M, L, O) = (m_0, l_0, o_0);  for i >= 1: M' = max(M, m_i),
+//   a = 2^(M - M'), b = 2^(m_i - M'), L = L a + l_i b, O = O a + o_i b;
+//   output = O / L.
+// The same sequence of operations runs in the in-workgroup fold and in the
+// combine kernel, so a row's bits do not depend on which one ran.
+struct Fold {
+  float m, l, o;
+  __device__ __forceinline__ void first(float mi, float li, float oi) { m = mi; l = li; o = oi; }
+  __device__ __forceinline__ void add(float mi, float li, float oi) {
+    const float mn = fmaxf(m, mi);
+    const float wa = exp2f(m - mn), wb = exp2f(mi - mn);
+    l = l * wa + li * wb;
+    o = o * wa + oi * wb;
+    m = mn;
+  }
+};
+
+// A unit of attention work is (KV head h, q tile qt, split sp): 16 q-rows
+// (q-row qr = r*G + jj is row r with query head h*G + jj) against the split
+// sp of each row's own context ctx_r = kv_len + r + 1.  One wave computes a
+// unit, walking the union of its rows' ranges in blocks of 64 absolute
+// positions, in increasing order:
+//   s_t = (K_t . q) * log2(e)/sqrt(dh)      MFMA chains over d (K rows of
+//                                           the paged cache as the A operand)
 //   positions outside the row's range -> -inf by select; block max;
-//   p_t = 2^(s_t - m_new) (0 when masked),      l = l * 2^(m - m_new) + sum p,
-//   o   = o * 2^(m - m_new) + V^T p             one MFMA chain over t.
+//   p_t = 2^(s_t - m_new) (0 when masked);  l = l * 2^(m - m_new) + sum p;
+//   o   = o * 2^(m - m_new) + V^T p         MFMA chains over t (V^T rows of
+//                                           the page-transposed V cache)
 // The KV cache holds fp16; q and p enter the f16 MFMAs as compensated fp16
-// pairs (hi + lo).
-// A block with no valid position leaves (m, l, o) exactly as they were (the
-// rescale factor is 1 while the running max is still -inf).  Every reduction
-// runs in the same order for every q-row slot, so a row's result does not
-// depend on which other rows share the launch.  Positions at or past
-// kv_len + M are zero-filled in LDS, so stale or poisoned KV never enters the
-// arithmetic; positions between a row's own ctx and kv_len + M hold this
-// launch's finite K/V and meet p = 0 exactly.
+// pairs (hi + lo).  A block with no valid position for a row leaves its
+// (m, l, o) exactly as they were (the rescale factor is 1, p = 0), so extra
+// blocks of the union change nothing; every MFMA column is one q-row, so a
+// row's result does not depend on the rows beside it.  V elements at
+// positions >= kv_len + M (never written) are zeroed before use, so stale or
+// poisoned cache never meets p = 0 as 0 * NaN.
+//
+// Workgroup (x, h): q tile qt = x % n_qt and splits [s_lo, s_lo + spw) with
+// s_lo = (x / n_qt) * spw; unit u = split s_lo + u on wave u % 8.  With
+// final_fold (spw covers every split) the partials go to LDS and the
+// workgroup folds each row's splits and writes its output planes; otherwise
+// they go to the global partial buffer for the combine kernel.
+constexpr int kAttnLdsUnits = 16;
+
+template <int DH>
+struct AttnUnitLds {
+  float m[16], l[16];
+  float o[16][DH + 4];   // padded rows: the 16 lanes of a wave's stores hit different banks
+};
+
 template <int DH>
 __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   constexpr int DC = DH / 32;            // d chunks of the score MFMA
   constexpr int DT = DH / 16;            // d tiles of the P.V MFMA
-  constexpr int KST = DH + 8;            // padded K row in LDS (bf16)
-  constexpr int VST = kAttnBlock + 4;    // padded V^T row in LDS (bf16)
-  constexpr int QPW = 2;                 // q tiles per wave (8 waves x 2 x 16 = 256 q-rows)
-  constexpr int SEGS = DH / 8;           // 16-byte segments per K or V row
-  constexpr int LOADS = (2 * kAttnBlock * SEGS) / 512;
-  __shared__ __align__(16) uint16_t Ks[kAttnBlock * KST];
-  __shared__ __align__(16) uint16_t Vt[DH * VST];
+  __shared__ AttnUnitLds<DH> ul[kAttnLdsUnits];
 
   prof_start(a.prof);
-  const int split = blockIdx.x, h = blockIdx.y;
+  const int h = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
-  const int kv_len = a.params[0];
   const int G = a.nq / a.nkv;
   const int n_qr = a.M * G;
   const int n_qt = (n_qr + 15) >> 4;
+  const int qt = blockIdx.x % n_qt;
+  const int s_lo = (blockIdx.x / n_qt) * a.spw;
+  const int s_hi = min(s_lo + a.spw, a.n_split);
+  // this lane's q-row (independent of kv_len: its q loads go out first)
+  const int qr = qt * 16 + j;
+  const bool have = qr < n_qr;
+  const int r = have ? qr / G : 0;
+  const int head = h * G + (have ? qr % G : 0);
+  float4 qraw[DC][2];
+  {
+    const float4* qp = reinterpret_cast<const float4*>(a.q + ((size_t)r * a.nq + head) * DH + g * 8);
+#pragma unroll
+    for (int c = 0; c < DC; ++c) { qraw[c][0] = qp[c * 8]; qraw[c][1] = qp[c * 8 + 1]; }
+  }
+  const int kv_len = a.params[0];
   const int ctx_max = kv_len + a.M;
-
-  // union of the rows' ranges for this split (rows with fewer splits sit out)
-  int u_lo = 0x7fffffff, u_hi = 0;
-  for (int r = 0; r < a.M; ++r) {
-    const int ctx = kv_len + r + 1;
-    if (split >= attn_ns(ctx)) continue;
-    const int bps = attn_bps(ctx);
-    u_lo = min(u_lo, split * bps * kAttnBlock);
-    u_hi = max(u_hi, min((split + 1) * bps * kAttnBlock, ctx));
-  }
-  if (u_lo >= u_hi) {
-    if (a.n_split == 1) prof_end(a.prof);
-    return;
-  }
+  const int ctx = kv_len + r + 1;
   const size_t layer_base = (size_t)a.layer * a.n_pages;
-
-  BPair qop[QPW][DC];
-  f32x4 o[QPW][DT];
-  float m[QPW], l[QPW];
-  int lo_q[QPW], hi_q[QPW];
-#pragma unroll
-  for (int u = 0; u < QPW; ++u) {
-    const int qr = (wave + 8 * u) * 16 + j;
-    const bool have = qr < n_qr;
-    const int r = have ? qr / G : 0;
-    const int head = h * G + (have ? qr % G : 0);
-    const int ctx = kv_len + r + 1;
-    lo_q[u] = 0;
-    hi_q[u] = 0;
-    if (have && split < attn_ns(ctx)) {
-      const int bps = attn_bps(ctx);
-      lo_q[u] = split * bps * kAttnBlock;
-      hi_q[u] = min((split + 1) * bps * kAttnBlock, ctx);
+  const size_t page_elems = (size_t)kPage * DH;
+  // physical pages of the 4 logical pages of block b: one 16-byte load of
+  // consecutive page-table entries (the table is 16-byte aligned); a block
+  // overhanging max_ctx (its positions are masked) reads clamped entries
+  auto block_pages = [&](int b) {
+    int4 q;
+    if (4 * b + 4 <= a.n_lpages) {
+      q = *reinterpret_cast<const int4*>(a.page_table + 4 * b);
+    } else {
+      const int last = a.n_lpages - 1;
+      q = make_int4(a.page_table[min(4 * b, last)], a.page_table[min(4 * b + 1, last)],
+                    a.page_table[min(4 * b + 2, last)], a.page_table[min(4 * b + 3, last)]);
     }
+    return q;
+  };
+  // element offset of (page, kv) for this KV head
+  auto page_base = [&](int page, int kv) { return (((layer_base + page) * 2 + kv) * a.nkv + h) * page_elems; };
+  BPair qop[DC];
 #pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      qop[u][c] = bzero();
-      if (have) {
-        const float4* qp = reinterpret_cast<const float4*>(a.q + ((size_t)r * a.nq + head) * DH + c * 32 + g * 8);
-        const float4 q0 = qp[0], q1 = qp[1];
-        const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-        qop[u][c] = split8_f16(qv);
-      }
-    }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m[u] = -INFINITY;
-    l[u] = 0.f;
+  for (int c = 0; c < DC; ++c) {
+    const float4 q0 = qraw[c][0], q1 = qraw[c][1];
+    const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    qop[c] = have ? split8_f16(qv) : bzero();
   }
 
-  // global -> register fetch of one block (K and V), zero past ctx_max
-  uint4 pre[LOADS];
-  auto fetch = [&](int blk) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int idx = threadIdx.x + i * 512;
-      const int kv = idx / (kAttnBlock * SEGS);
-      const int rem = idx % (kAttnBlock * SEGS);
-      const int t = rem / SEGS, seg = rem % SEGS;
-      const int pos = blk + t;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (pos < ctx_max) {
-        const int page = a.page_table[pos / kPage];
-        const size_t off = (((layer_base + page) * 2 + kv) * a.nkv + h) * kPage + (pos % kPage);
-        v = *reinterpret_cast<const uint4*>(a.kv_pool + off * DH + seg * 8);
-      }
-      pre[i] = v;
+  for (int sp = s_lo + wave; sp < s_hi; sp += 8) {     // wave-uniform
+    int lo = 0, hi = 0;
+    if (have && sp < attn_ns(ctx)) {
+      const int bps = attn_bps(ctx);
+      lo = sp * bps * kAttnBlock;
+      hi = min((sp + 1) * bps * kAttnBlock, ctx);
     }
-  };
-  fetch(u_lo);
-  for (int blk = u_lo; blk < u_hi; blk += kAttnBlock) {
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int idx = threadIdx.x + i * 512;
-      const int kv = idx / (kAttnBlock * SEGS);
-      const int rem = idx % (kAttnBlock * SEGS);
-      const int t = rem / SEGS, seg = rem % SEGS;
-      if (kv == 0) {
-        *reinterpret_cast<uint4*>(&Ks[t * KST + seg * 8]) = pre[i];
-      } else {
-        const uint32_t w[4] = {pre[i].x, pre[i].y, pre[i].z, pre[i].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          Vt[(seg * 8 + e) * VST + t] = (uint16_t)((w[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+    // union of the tile's rows' ranges (wave-uniform), in whole blocks
+    int b_lo = 0x7fffffff, b_hi = 0;
+    {
+      const int r0 = (qt * 16) / G, r1 = min((qt * 16 + 15) / G, a.M - 1);
+      for (int rr = r0; rr <= r1; ++rr) {
+        const int c = kv_len + rr + 1;
+        if (sp >= attn_ns(c)) continue;
+        const int bps = attn_bps(c);
+        b_lo = min(b_lo, sp * bps);
+        b_hi = max(b_hi, (min((sp + 1) * bps * kAttnBlock, c) + kAttnBlock - 1) / kAttnBlock);
       }
     }
-    __syncthreads();
-    if (blk + kAttnBlock < u_hi) fetch(blk + kAttnBlock);
+    f32x4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.f;
 
+    int4 pq = block_pages(b_lo < b_hi ? b_lo : 0);
+    for (int b = b_lo; b < b_hi; ++b) {
+      // K operand: lane (g, j) holds K[pos = 64b + 16pt + j][32c + 8g .. +7]; one page per pt
+      uint4 kop[4][DC];
+      // V^T operand of chunk ks: positions {32ks + 4g .. +3} and {32ks + 16 + 4g .. +3} of d = 16dt + j
+      uint2 vlo[DT][2], vhi[DT][2];
+      const int pg[4] = {__builtin_amdgcn_readfirstlane(pq.x), __builtin_amdgcn_readfirstlane(pq.y),
+                         __builtin_amdgcn_readfirstlane(pq.z), __builtin_amdgcn_readfirstlane(pq.w)};
 #pragma unroll
-    for (int u = 0; u < QPW; ++u) {
-      if (wave + 8 * u >= n_qt) continue;   // wave-uniform
+      for (int pt = 0; pt < 4; ++pt) {
+        const uint16_t* kb = a.kv_pool + page_base(pg[pt], 0) + (size_t)j * DH + g * 8;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) kop[pt][c] = *reinterpret_cast<const uint4*>(kb + c * 32);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint16_t* va = a.kv_pool + page_base(pg[2 * ks], 1) + g * 4;
+        const uint16_t* vb = a.kv_pool + page_base(pg[2 * ks + 1], 1) + g * 4;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          vlo[dt][ks] = *reinterpret_cast<const uint2*>(va + (size_t)(dt * 16 + j) * kPage);
+          vhi[dt][ks] = *reinterpret_cast<const uint2*>(vb + (size_t)(dt * 16 + j) * kPage);
+        }
+      }
+      pq = block_pages(b + 1 < b_hi ? b + 1 : b);   // next block's pages, in flight during this block
       f32x4 sc[4];
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < DC; ++c) {
-          const uint4 kA = *reinterpret_cast<const uint4*>(&Ks[(pt * 16 + j) * KST + c * 32 + g * 8]);
-          acc = mfma_pair_f16(kA, qop[u][c], acc);
-        }
+        for (int c = 0; c < DC; ++c) acc = mfma_pair_f16(kop[pt][c], qop[c], acc);
         sc[pt] = acc;
       }
-      // lane (g, j) holds scores of q-row j at positions blk + pt*16 + 4g + v
+      // lane (g, j) holds scores of q-row j at positions 64b + 16pt + 4g + v
       float s[16];
       float bmax = -INFINITY;
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int tpos = blk + pt * 16 + 4 * g + v;
+          const int tpos = b * kAttnBlock + pt * 16 + 4 * g + v;
           const float sv = sc[pt][v] * a.scale_log2;
-          s[pt * 4 + v] = (tpos >= lo_q[u] && tpos < hi_q[u]) ? sv : -INFINITY;
+          s[pt * 4 + v] = (tpos >= lo && tpos < hi) ? sv : -INFINITY;
           bmax = fmaxf(bmax, s[pt * 4 + v]);
         }
       bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
       bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-      const float mn = fmaxf(m[u], bmax);
-      const float alpha = (mn == -INFINITY) ? 1.0f : exp2f(m[u] - mn);
+      const float mn = fmaxf(m, bmax);
+      const float alpha = (mn == -INFINITY) ? 1.0f : exp2f(m - mn);
       uint16_t pb[16], pl[16];
       float psum = 0.f;
 #pragma unroll
@@ -836,12 +853,21 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       }
       psum = psum + __shfl_xor(psum, 16);
       psum = psum + __shfl_xor(psum, 32);
-      l[u] = l[u] * alpha + psum;
+      l = l * alpha + psum;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        o[u][dt].x = o[u][dt].x * alpha; o[u][dt].y = o[u][dt].y * alpha;
-        o[u][dt].z = o[u][dt].z * alpha; o[u][dt].w = o[u][dt].w * alpha;
+        o[dt].x = o[dt].x * alpha; o[dt].y = o[dt].y * alpha;
+        o[dt].z = o[dt].z * alpha; o[dt].w = o[dt].w * alpha;
       }
+      // zero V elements at positions >= kv_len + M (never written in this cache)
+      auto vmask = [&](uint2 v, int pos0) {
+        const int n_ok = ctx_max - pos0;               // valid elements among pos0 .. pos0 + 3
+        if (n_ok >= 4) return v;
+        if (n_ok <= 0) return make_uint2(0u, 0u);
+        const uint32_t m0 = n_ok >= 2 ? 0xffffffffu : 0x0000ffffu;
+        const uint32_t m1 = n_ok >= 4 ? 0xffffffffu : (n_ok == 3 ? 0x0000ffffu : 0u);
+        return make_uint2(v.x & m0, v.y & m1);
+      };
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int pa = 2 * ks, pbt = 2 * ks + 1;
@@ -850,88 +876,105 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
                            pack2(pb[pbt * 4 + 0], pb[pbt * 4 + 1]), pack2(pb[pbt * 4 + 2], pb[pbt * 4 + 3]));
         Bp.lo = make_uint4(pack2(pl[pa * 4 + 0], pl[pa * 4 + 1]), pack2(pl[pa * 4 + 2], pl[pa * 4 + 3]),
                            pack2(pl[pbt * 4 + 0], pl[pbt * 4 + 1]), pack2(pl[pbt * 4 + 2], pl[pbt * 4 + 3]));
+        const int p0 = b * kAttnBlock + pa * 16 + 4 * g, p1 = b * kAttnBlock + pbt * 16 + 4 * g;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const uint16_t* vr = &Vt[(dt * 16 + j) * VST];
-          const uint2 vlo = *reinterpret_cast<const uint2*>(vr + pa * 16 + 4 * g);
-          const uint2 vhi = *reinterpret_cast<const uint2*>(vr + pbt * 16 + 4 * g);
-          o[u][dt] = mfma_pair_f16(make_uint4(vlo.x, vlo.y, vhi.x, vhi.y), Bp, o[u][dt]);
+          const uint2 v0 = vmask(vlo[dt][ks], p0), v1 = vmask(vhi[dt][ks], p1);
+          o[dt] = mfma_pair_f16(make_uint4(v0.x, v0.y, v1.x, v1.y), Bp, o[dt]);
         }
       }
-      m[u] = mn;
+      m = mn;
+    }
+
+    // lane (g, j) holds o of q-row j for d = 16dt + 4g + v
+    if (a.final_fold) {
+      AttnUnitLds<DH>& U = ul[sp];
+      if (g == 0) { U.m[j] = m; U.l[j] = l; }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<float4*>(&U.o[j][dt * 16 + 4 * g]) = make_float4(o[dt].x, o[dt].y, o[dt].z, o[dt].w);
+    } else if (have && hi > lo) {
+      float* part = a.part + (((size_t)r * a.nq + head) * kAttnMaxSplits + sp) * (DH + 4);
+      if (g == 0) { part[0] = m; part[1] = l; }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<float4*>(part + 4 + dt * 16 + 4 * g) = make_float4(o[dt].x, o[dt].y, o[dt].z, o[dt].w);
     }
   }
-  // lane (g, j) holds o of q-row j for d = dt*16 + 4g + v.  A row whose
-  // context is a single split is final here: o / l as output planes, the
-  // same arithmetic the combine performs for one split (weight 2^0 = 1).
-#pragma unroll
-  for (int u = 0; u < QPW; ++u) {
-    const int qr = (wave + 8 * u) * 16 + j;
-    if (wave + 8 * u >= n_qt || qr >= n_qr || hi_q[u] <= lo_q[u]) continue;
-    const int r = qr / G, head = h * G + qr % G;
-    if (attn_ns(kv_len + r + 1) == 1) {
-      const size_t ob = ((size_t)r * a.nq + head) * DH;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const float ov[4] = {o[u][dt].x, o[u][dt].y, o[u][dt].z, o[u][dt].w};
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const size_t oi = ob + dt * 16 + 4 * g + v;
-          split1(ov[v] / l[u], a.ohi[oi], a.olo[oi]);
-        }
+
+  if (a.final_fold) {
+    __syncthreads();
+    // every split of this tile is here: thread (jj, d0) folds 4 outputs of q-row jj in split order
+    constexpr int TPR = DH / 4;              // threads per q-row
+    for (int t = threadIdx.x; t < 16 * TPR; t += blockDim.x) {
+      const int jj = t / TPR, d0 = (t % TPR) * 4;
+      const int q2 = qt * 16 + jj;
+      if (q2 >= n_qr) continue;
+      const int r2 = q2 / G, head2 = h * G + q2 % G;
+      const int ns = attn_ns(kv_len + r2 + 1);
+      const float4 o0 = *reinterpret_cast<const float4*>(&ul[0].o[jj][d0]);
+      Fold f[4];
+      f[0].first(ul[0].m[jj], ul[0].l[jj], o0.x);
+      f[1].first(ul[0].m[jj], ul[0].l[jj], o0.y);
+      f[2].first(ul[0].m[jj], ul[0].l[jj], o0.z);
+      f[3].first(ul[0].m[jj], ul[0].l[jj], o0.w);
+      for (int sp = 1; sp < ns; ++sp) {
+        const float mi = ul[sp].m[jj], li = ul[sp].l[jj];
+        const float4 oi = *reinterpret_cast<const float4*>(&ul[sp].o[jj][d0]);
+        f[0].add(mi, li, oi.x);
+        f[1].add(mi, li, oi.y);
+        f[2].add(mi, li, oi.z);
+        f[3].add(mi, li, oi.w);
       }
-      continue;
-    }
-    float* part = a.part + (((size_t)r * a.nq + head) * kAttnMaxSplits + split) * (DH + 4);
-    if (g == 0) { part[0] = m[u]; part[1] = l[u]; }
+      uint16_t hb[4], lb[4];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<float4*>(part + 4 + dt * 16 + 4 * g) = make_float4(o[u][dt].x, o[u][dt].y, o[u][dt].z, o[u][dt].w);
+      for (int e = 0; e < 4; ++e) split1(f[e].o / f[e].l, hb[e], lb[e]);
+      const size_t oi = ((size_t)r2 * a.nq + head2) * DH + d0;
+      *reinterpret_cast<uint2*>(a.ohi + oi) = make_uint2(pack2(hb[0], hb[1]), pack2(hb[2], hb[3]));
+      *reinterpret_cast<uint2*>(a.olo + oi) = make_uint2(pack2(lb[0], lb[1]), pack2(lb[2], lb[3]));
+    }
+    prof_end(a.prof);
   }
-  if (a.n_split == 1) prof_end(a.prof);   // no combine pass follows
 }
 
-// Combine the row's splits in split order: o = sum_i w_i o_i / sum_i w_i l_i
-// with w_i = 2^(m_i - max m).  Partial record: [m, l, -, -, o[dh]].
+// Fold of the global partials of row r, query head j (record [m, l, -, -, o[dh]]).
 template <int DH>
 __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
   constexpr int PER = DH / 64;
   const int j = blockIdx.x, r = blockIdx.y, lane = threadIdx.x;
-  const int ctx = a.params[0] + r + 1;
-  const int ns = attn_ns(ctx);
-  if (ns == 1) {   // written by the split kernel
-    prof_end(a.prof);
-    return;
-  }
+  const int ns = attn_ns(a.params[0] + r + 1);
   const float* base = a.part + ((size_t)r * a.nq + j) * kAttnMaxSplits * (DH + 4);
-  float mx = base[0];
-  for (int i = 1; i < ns; ++i) mx = fmaxf(mx, base[(size_t)i * (DH + 4)]);
-  float L = 0.f, O[PER];
+  Fold f[PER];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) O[e] = 0.f;
-  for (int i = 0; i < ns; ++i) {
+  for (int e = 0; e < PER; ++e) f[e].first(base[0], base[1], base[4 + lane * PER + e]);
+  for (int i = 1; i < ns; ++i) {
     const float* p = base + (size_t)i * (DH + 4);
-    const float w = exp2f(p[0] - mx);
-    L = L + p[1] * w;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) O[e] = O[e] + p[4 + lane * PER + e] * w;
+    for (int e = 0; e < PER; ++e) f[e].add(p[0], p[1], p[4 + lane * PER + e]);
   }
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const size_t oi = (size_t)r * a.nq * DH + (size_t)j * DH + lane * PER + e;
-    split1(O[e] / L, a.ohi[oi], a.olo[oi]);
+    split1(f[e].o / f[e].l, a.ohi[oi], a.olo[oi]);
   }
   prof_end(a.prof);
 }
 
-hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
-  if (a.M * (a.nq / a.nkv) > kAttnQRows || a.n_split < 1 || a.n_split > kAttnMaxSplits) return hipErrorInvalidValue;
+hipError_t launch_attention(const AttnArgs& a_in, hipStream_t st) {
+  AttnArgs a = a_in;
+  const int G = a.nq / a.nkv;
+  if (a.M * G > kAttnQRows || a.n_split < 1 || a.n_split > kAttnMaxSplits || a.n_lpages < 1)
+    return hipErrorInvalidValue;
+  const int n_qt = (a.M * G + 15) / 16;
+  a.final_fold = a.n_split <= kAttnLdsUnits ? 1 : 0;
+  a.spw = a.final_fold ? a.n_split : 8;
+  const int n_wg = n_qt * ((a.n_split + a.spw - 1) / a.spw);
   if (a.dh == 128) {
-    hipLaunchKernelGGL(k_attn_mfma<128>, dim3(a.n_split, a.nkv), dim3(512), 0, st, a);
-    if (a.n_split > 1) hipLaunchKernelGGL(k_attn_combine<128>, dim3(a.nq, a.M), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(k_attn_mfma<128>, dim3(n_wg, a.nkv), dim3(512), 0, st, a);
+    if (!a.final_fold) hipLaunchKernelGGL(k_attn_combine<128>, dim3(a.nq, a.M), dim3(64), 0, st, a);
   } else if (a.dh == 64) {
-    hipLaunchKernelGGL(k_attn_mfma<64>, dim3(a.n_split, a.nkv), dim3(512), 0, st, a);
-    if (a.n_split > 1) hipLaunchKernelGGL(k_attn_combine<64>, dim3(a.nq, a.M), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(k_attn_mfma<64>, dim3(n_wg, a.nkv), dim3(512), 0, st, a);
+    if (!a.final_fold) hipLaunchKernelGGL(k_attn_combine<64>, dim3(a.nq, a.M), dim3(64), 0, st, a);
   } else {
     return hipErrorInvalidValue;
   }

@@ -267,7 +267,7 @@ hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, hipStream_
     AttnArgs at{};
     at.params = d_params; at.q = q; at.kv_pool = kv; at.page_table = c->buf.page_table; at.n_pages = c->buf.n_pages;
     at.layer = l; at.nq = cfg.n_q_heads; at.nkv = cfg.n_kv_heads; at.dh = cfg.head_dim; at.M = M;
-    at.n_split = n_split; at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cfg.head_dim));
+    at.n_split = n_split; at.n_lpages = cfg.max_ctx / kPage; at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cfg.head_dim));
     at.part = c->at<float>(c->lay.attn_part); at.ohi = ohi; at.olo = olo;
     at.prof = prof_slot(c, kRoleAttn, l);
     if ((e = launch_attention(at, st)) != hipSuccess) return e;
@@ -417,6 +417,7 @@ sv_status sv_create(const sv_config* cfg, const sv_weights* w, const sv_buffers*
   if (!plans_ok(*cfg, p)) return SV_EUNSUPPORTED;
   const Layout lay = make_layout(*cfg, p);
   if (!buf->kv_pool || !buf->page_table || !buf->workspace) return SV_EINVAL;
+  if (reinterpret_cast<uintptr_t>(buf->page_table) % 16 != 0) return SV_EINVAL;   // read 4 entries at a time
   if (buf->n_pages < 1 || buf->kv_pool_bytes < (int64_t)kv_pool_bytes_for(*cfg, buf->n_pages)) return SV_EINVAL;
   if (buf->workspace_bytes < (int64_t)lay.total) return SV_EINVAL;
   // Every logical page must map into the pool: a bad entry would address

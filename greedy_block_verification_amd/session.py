@@ -175,10 +175,15 @@ class Session:
         """Host copy of the K/V bits of positions [start, n): int16 [n - start, L, 2, n_kv, dh]."""
         cfg = self.cfg
         n_pages = cfg.max_ctx // cfg.page_size
-        pool = self.kv.view(cfg.n_layers, n_pages, 2, cfg.n_kv_heads, cfg.page_size, cfg.head_dim)
+        ps, dh = cfg.page_size, cfg.head_dim
+        pool = self.kv.view(cfg.n_layers, n_pages, 2, cfg.n_kv_heads, ps * dh)
         pt = self.page_table.cpu().numpy()
         pos = np.arange(start, n_positions)
-        pages = pt[pos // cfg.page_size].astype(np.int64)
+        pages = pt[pos // ps].astype(np.int64)
         upages, inv = np.unique(pages, return_inverse=True)
-        sub = pool[:, torch.from_numpy(upages).to(self.kv.device)].cpu().numpy()   # [L, u, 2, nkv, 16, dh]
-        return sub[:, inv, :, :, pos % cfg.page_size, :]                          # [n, L, 2, nkv, dh]
+        sub = pool[:, torch.from_numpy(upages).to(self.kv.device)].cpu().numpy()   # [L, u, 2, nkv, 16*dh]
+        L, u = sub.shape[0], sub.shape[1]
+        k = sub[:, :, 0].reshape(L, u, cfg.n_kv_heads, ps, dh)
+        v = sub[:, :, 1].reshape(L, u, cfg.n_kv_heads, dh, ps).transpose(0, 1, 2, 4, 3)   # V is [dh][slot] in a page
+        kv = np.stack([k, v], axis=2)                                              # [L, u, 2, nkv, 16, dh]
+        return kv[:, inv, :, :, pos % ps, :]                                       # [n, L, 2, nkv, dh]

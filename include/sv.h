@@ -75,11 +75,14 @@ typedef struct {
 } sv_weights;
 
 /* Caller-owned device buffers.
- *   kv_pool: IEEE fp16, n_pages pages; page p, layer l, kv (0 = K, 1 = V), head h,
- *            slot s, element e lives at
- *            ((((l*n_pages + p)*2 + kv)*n_kv + h)*16 + s)*head_dim + e.
- *   page_table: int32 [max_ctx/16], logical page -> physical page in
- *            [0, n_pages); read by the kernels, never written.
+ *   kv_pool: IEEE fp16, n_pages pages.  The block of page p, layer l, kv
+ *            (0 = K, 1 = V), head h starts at element
+ *            B = (((l*n_pages + p)*2 + kv)*n_kv + h)*16*head_dim; inside it,
+ *            K of slot s, element e is at B + s*head_dim + e, and V is stored
+ *            transposed, element e of slot s at B + e*16 + s.
+ *   page_table: int32 [max_ctx/16], 16-byte aligned (SV_EINVAL otherwise),
+ *            logical page -> physical page in [0, n_pages); read by the
+ *            kernels, never written.
  *   workspace: at least the size sv_query_sizes reports; its contents are
  *            the library's between calls. */
 typedef struct {
