@@ -246,23 +246,54 @@ __device__ __forceinline__ void rows_inv_rms(const GemmArgs& a, GemmShared& sh, 
   }
 }
 
+// Global operands of the epilogue element (r, c) = (idx / 16, idx % 16) of
+// item T, loaded when the item starts so the epilogue does not wait on them:
+// O / down read the residual and the next gain, QKV the RoPE pair and the
+// physical page of its row.  Only the element idx = threadIdx.x is
+// prefetched (blockDim >= 16 M); any other element loads in the epilogue.
+struct EpiPre {
+  float x, gain;
+  float2 cs;
+  int page;
+};
+
+template <int ROLE>
+__device__ __forceinline__ EpiPre epi_load(const GemmArgs& a, int T, int idx) {
+  EpiPre e{0.f, 0.f, make_float2(0.f, 0.f), 0};
+  if (idx >= a.M * 16) return e;
+  const int r = idx >> 4, c = idx & 15;
+  if (ROLE == kRoleO || ROLE == kRoleDown) {
+    const int n = T * 16 + c;
+    e.x = a.x[(size_t)r * a.N + n];
+    e.gain = bf2f(a.gnext[n]);
+  } else if (ROLE == kRoleQkv) {
+    const int half = a.dh >> 1, gph = half >> 3;
+    const int hh = T / gph, sb = T % gph;
+    const int pos = a.params[0] + r;
+    if (hh < a.nq + a.nkv) e.cs = a.rope[(size_t)pos * half + 8 * sb + (c & 7)];
+    if (hh >= a.nq) e.page = a.page_table[pos / kPage];
+  }
+  return e;
+}
+
 // Epilogue on the finished 16 columns of item (tile) T.
 template <int ROLE>
-__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, GemmShared& sh, int T) {
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, GemmShared& sh, int T, const EpiPre& pre) {
   for (int idx = threadIdx.x; idx < a.M * 16; idx += blockDim.x) {
     const int r = idx >> 4, c = idx & 15;
+    const EpiPre e = idx == (int)threadIdx.x ? pre : epi_load<ROLE>(a, T, idx);
     float y = sh.y[r][c];
     if (norm_role(ROLE)) y = y * sh.inv[r];
     if (ROLE == kRoleO || ROLE == kRoleDown) {
       const int n = T * 16 + c;
       const size_t xi = (size_t)r * a.N + n;
-      const float xn = a.x[xi] + y;
+      const float xn = e.x + y;
       a.x[xi] = xn;
       float sq = xn * xn;
 #pragma unroll
       for (int o = 8; o >= 1; o >>= 1) sq += __shfl_xor(sq, o);
       if (c == 0) a.ss_out[(size_t)r * (a.N >> 4) + T] = sq;
-      split1(xn * bf2f(a.gnext[n]), a.uhi[xi], a.ulo[xi]);
+      split1(xn * e.gain, a.uhi[xi], a.ulo[xi]);
     } else if (ROLE == kRoleGateUp) {               // [gate 8 | up 8] of features 8T..8T+7
       const float up = sh.y[r][(c & 7) + 8] * sh.inv[r];
       if (c < 8) {
@@ -279,7 +310,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, GemmShared& sh,
       const int pos = a.params[0] + r;
       float out = y;
       if (hh < a.nq + a.nkv) {
-        const float2 cs = a.rope[(size_t)pos * half + i];
+        const float2 cs = e.cs;
         const float partner = sh.y[r][c ^ 8] * sh.inv[r];
         out = lo ? (y * cs.x - partner * cs.y) : (y * cs.x + partner * cs.y);
       }
@@ -288,7 +319,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, GemmShared& sh,
       } else {
         const int kv = hh < a.nq + a.nkv ? 0 : 1;
         const int head = hh - a.nq - kv * a.nkv;
-        const int page = a.page_table[pos / kPage];
+        const int page = e.page;
         const size_t base = ((((size_t)a.layer * a.n_pages + page) * 2 + kv) * a.nkv + head) * kPage * a.dh;
         // K rows are [slot][dh]; V is stored transposed inside the page, [dh][slot]
         const size_t e = kv == 0 ? (size_t)(pos % kPage) * a.dh + d : (size_t)d * kPage + (pos % kPage);
@@ -308,26 +339,33 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, GemmShared& sh,
 // Wave partials of one item -> LDS -> summed in wave order -> sh.y -> epilogue.
 template <int TM, int ROLE>
 __device__ __forceinline__ void gemm_finish(const GemmArgs& a, GemmShared& sh, f32x4 (&acc)[TM], int T, int wave,
-                                            int lane, int nw) {
+                                            int lane, int nw, const EpiPre& pre) {
 #pragma unroll
   for (int rt = 0; rt < TM; ++rt) {
     sh.red[wave][lane] = acc[rt];
     __syncthreads();
-    if (threadIdx.x < 64) {
-      const int l = threadIdx.x;
-      f32x4 v = sh.red[0][l];
-      for (int w = 1; w < nw; ++w) {
-        const f32x4 u = sh.red[w][l];
-        v.x = v.x + u.x; v.y = v.y + u.y; v.z = v.z + u.z; v.w = v.w + u.w;
+    // 256 threads: thread t sums component t % 4 of lane t / 4 over the
+    // waves, all partials loaded first, added in wave order
+    const float* red = reinterpret_cast<const float*>(sh.red);
+    for (int t = threadIdx.x; t < 256; t += blockDim.x) {
+      float v = 0.f;
+#pragma unroll
+      for (int w0 = 0; w0 < kMaxWaves; w0 += 8) {   // two batches of 8 loads
+        float part[8];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) part[w] = red[(w0 + w) * 256 + t];
+#pragma unroll
+        for (int w = 0; w < 8; ++w)
+          if (w0 + w < nw) v = (w0 + w == 0) ? part[w] : v + part[w];
       }
-      // v[i] = Y[r = rt*16 + (l & 15)][column 4 (l >> 4) + i]
+      // lane l holds Y[r = rt*16 + (l & 15)][column 4 (l >> 4) + component]
+      const int l = t >> 2;
       const int r = rt * 16 + (l & 15);
-      const int c0 = 4 * (l >> 4);
-      if (r < a.M) { sh.y[r][c0] = v.x; sh.y[r][c0 + 1] = v.y; sh.y[r][c0 + 2] = v.z; sh.y[r][c0 + 3] = v.w; }
+      if (r < a.M) sh.y[r][4 * (l >> 4) + (t & 3)] = v;
     }
     __syncthreads();
   }
-  gemm_epilogue<ROLE>(a, sh, T);
+  gemm_epilogue<ROLE>(a, sh, T, pre);
   __syncthreads();
 }
 
@@ -453,6 +491,7 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16(GemmArgs a) {
   }
 
   for (int T = blockIdx.x; T < n_items; T += gridDim.x) {
+    const EpiPre pre = epi_load<ROLE>(a, T, threadIdx.x);
     f32x4 acc[TM];
 #pragma unroll
     for (int rt = 0; rt < TM; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -476,7 +515,7 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16(GemmArgs a) {
       if (T + (int)gridDim.x < n_items || c0 + NB < cpi) group(true);
       else group(false);                        // the last NB chunks of this workgroup
     }
-    gemm_finish<TM, ROLE>(a, sh, acc, T, wave, lane, nw);
+    gemm_finish<TM, ROLE>(a, sh, acc, T, wave, lane, nw, pre);
   }
   row_best_publish<ROLE>(a, sh);
   prof_end(a.prof);
@@ -534,6 +573,7 @@ __global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
     __syncthreads();
   }
   for (int T = blockIdx.x; T < n_items; T += gridDim.x) {
+    const EpiPre pre = epi_load<ROLE>(a, T, threadIdx.x);
     f32x4 acc[TM];
 #pragma unroll
     for (int rt = 0; rt < TM; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -572,7 +612,7 @@ __global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
       if (T + (int)gridDim.x < n_items || c0 + NB < cpi) group(true);
       else group(false);
     }
-    gemm_finish<TM, ROLE>(a, sh, acc, T, wave, lane, nw);
+    gemm_finish<TM, ROLE>(a, sh, acc, T, wave, lane, nw, pre);
   }
   prof_end(a.prof);
 }
@@ -582,19 +622,35 @@ static hipError_t gemm_dispatch_nb(const GemmArgs& a, int grid, hipStream_t st) 
   const dim3 block(64 * a.S);
   const int tm = (a.M + 15) / 16;
   if constexpr (INT4) {
+    // only the (rows, ring depth) pairs gemm_ring_depth can pick are built
     switch (tm) {
       case 1: hipLaunchKernelGGL((k_gemm_int4<1, ROLE, NB>), dim3(grid), block, 0, st, a); break;
-      case 2: hipLaunchKernelGGL((k_gemm_int4<2, ROLE, NB>), dim3(grid), block, 0, st, a); break;
-      case 3: hipLaunchKernelGGL((k_gemm_int4<3, ROLE, NB>), dim3(grid), block, 0, st, a); break;
-      case 4: hipLaunchKernelGGL((k_gemm_int4<4, ROLE, NB>), dim3(grid), block, 0, st, a); break;
+      case 2:
+        if constexpr (NB <= 2) hipLaunchKernelGGL((k_gemm_int4<2, ROLE, NB>), dim3(grid), block, 0, st, a);
+        else return hipErrorInvalidValue;
+        break;
+      case 3:
+        if constexpr (NB == 1) hipLaunchKernelGGL((k_gemm_int4<3, ROLE, NB>), dim3(grid), block, 0, st, a);
+        else return hipErrorInvalidValue;
+        break;
+      case 4:
+        if constexpr (NB == 1) hipLaunchKernelGGL((k_gemm_int4<4, ROLE, NB>), dim3(grid), block, 0, st, a);
+        else return hipErrorInvalidValue;
+        break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (tm) {
       case 1: hipLaunchKernelGGL((k_gemm_bf16<1, ROLE, NB>), dim3(grid), block, 0, st, a); break;
       case 2: hipLaunchKernelGGL((k_gemm_bf16<2, ROLE, NB>), dim3(grid), block, 0, st, a); break;
-      case 3: hipLaunchKernelGGL((k_gemm_bf16<3, ROLE, NB>), dim3(grid), block, 0, st, a); break;
-      case 4: hipLaunchKernelGGL((k_gemm_bf16<4, ROLE, NB>), dim3(grid), block, 0, st, a); break;
+      case 3:
+        if constexpr (NB <= 4) hipLaunchKernelGGL((k_gemm_bf16<3, ROLE, NB>), dim3(grid), block, 0, st, a);
+        else return hipErrorInvalidValue;
+        break;
+      case 4:
+        if constexpr (NB == 1) hipLaunchKernelGGL((k_gemm_bf16<4, ROLE, NB>), dim3(grid), block, 0, st, a);
+        else return hipErrorInvalidValue;
+        break;
       default: return hipErrorInvalidValue;
     }
   }
@@ -602,9 +658,15 @@ static hipError_t gemm_dispatch_nb(const GemmArgs& a, int grid, hipStream_t st) 
 }
 
 // Ring depth: the deepest of 8 / 4 / 2 / 1 that divides the chunks each wave
-// takes per item and per LDS stage.
+// takes per item and per LDS stage (int4: capped by the row count, so its
+// registers fit).
 int gemm_ring_depth(int n_chunks, int waves, int M, int unit) {
+  // register budget: bf16 rings are 8 deep up to 32 rows, 4 up to 48, then
+  // 1; int4 ring slots also hold scales: 4 deep up to 16 rows, 2 up to 32,
+  // then 1
+  const int cap = unit == 128 ? (M <= 16 ? 4 : (M <= 32 ? 2 : 1)) : (M <= 32 ? 8 : (M <= 48 ? 4 : 1));
   for (int nb : {8, 4, 2, 1}) {
+    if (nb > cap) continue;
     if ((n_chunks / waves) % nb) continue;
     const int cs = stage_chunks(n_chunks, waves, M, unit, nb);
     if (cs > 0) return nb;
@@ -615,7 +677,9 @@ int gemm_ring_depth(int n_chunks, int waves, int M, int unit) {
 template <int ROLE, bool INT4>
 static hipError_t gemm_dispatch(const GemmArgs& a, int grid, hipStream_t st) {
   switch (gemm_ring_depth(a.K / (INT4 ? 128 : 32), a.S, a.M, INT4 ? 128 : 32)) {
-    case 8: return gemm_dispatch_nb<ROLE, INT4, 8>(a, grid, st);
+    case 8:
+      if constexpr (INT4) return hipErrorInvalidValue;
+      else return gemm_dispatch_nb<ROLE, INT4, 8>(a, grid, st);
     case 4: return gemm_dispatch_nb<ROLE, INT4, 4>(a, grid, st);
     case 2: return gemm_dispatch_nb<ROLE, INT4, 2>(a, grid, st);
     case 1: return gemm_dispatch_nb<ROLE, INT4, 1>(a, grid, st);
