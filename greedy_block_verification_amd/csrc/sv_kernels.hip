@@ -223,6 +223,7 @@ constexpr int kMaxWaves = 16;
 constexpr int kStageBytes = kGemmStageBytes;   // LDS for staged activation planes (hi + lo)
 
 struct GemmShared {
+  uint4 dummy;                // target of stage stores that carry no data
   f32x4 red[kMaxWaves][64];   // wave partials of one row tile
   float y[kMaxRows][16];      // finished outputs of the item
   float inv[kMaxRows];        // 1 / rms of each row (RMSNorm consumers)
@@ -435,6 +436,70 @@ __host__ __device__ __forceinline__ int stage_chunks(int n_chunks, int nw, int M
   return best;
 }
 
+// Double-buffered stages (bf16): stage = NB chunks per wave (one ring group),
+// two LDS buffers; the next stage's planes (at most kStageRegs 16-byte
+// vectors per thread) are loaded into registers while the current stage's
+// MFMAs run, then written to the other buffer, with one barrier per stage
+// and no drain of the weight ring.
+constexpr int kStageRegs = 4;
+__host__ __device__ __forceinline__ bool stage_double_ok(int n_chunks, int nw, int M, int unit, int nb,
+                                                         int nthreads) {
+  const int cs = nw * nb;
+  if (n_chunks % cs != 0 || cs == n_chunks) return false;
+  if (2 * (size_t)M * (cs * unit + 8) * 4 > (size_t)kStageBytes) return false;
+  return 2 * M * cs * (unit / 8) <= kStageRegs * nthreads;
+}
+
+// Activation planes of chunks [c_lo, c_lo + n_chunks) of every row into
+// registers (vector i = threadIdx.x + k * blockDim.x of the hi plane, then
+// the lo plane; loads past the end repeat the last vector, so the loads are
+// unconditional) and from registers into a stage buffer.
+struct StageRegs {
+  uint4 v0, v1, v2, v3;   // kStageRegs vectors (plain members: they stay in registers)
+};
+// nthr = threads of the workgroup, passed in: reading blockDim inside the
+// loop is a memory load whose wait would drain the weight ring.
+__device__ __forceinline__ const uint16_t* stage_src(const GemmArgs& a, int c_lo, int n_chunks, int unit, int k,
+                                                     int nthr) {
+  const int vpr = (n_chunks * unit) >> 3;
+  const int per_plane = a.M * vpr;
+  int i = threadIdx.x + k * nthr;
+  i = i < 2 * per_plane ? i : 2 * per_plane - 1;
+  const int pl = i >= per_plane, ii = pl ? i - per_plane : i;
+  const int r = ii / vpr, v = ii % vpr;
+  return (pl ? a.blo : a.bhi) + (size_t)r * a.K + (size_t)c_lo * unit + (size_t)v * 8;
+}
+__device__ __forceinline__ StageRegs stage_fetch(const GemmArgs& a, int c_lo, int n_chunks, int unit, int nthr) {
+  StageRegs s;
+  s.v0 = *reinterpret_cast<const uint4*>(stage_src(a, c_lo, n_chunks, unit, 0, nthr));
+  s.v1 = *reinterpret_cast<const uint4*>(stage_src(a, c_lo, n_chunks, unit, 1, nthr));
+  s.v2 = *reinterpret_cast<const uint4*>(stage_src(a, c_lo, n_chunks, unit, 2, nthr));
+  s.v3 = *reinterpret_cast<const uint4*>(stage_src(a, c_lo, n_chunks, unit, 3, nthr));
+  return s;
+}
+// Unconditional LDS stores (a thread without a vector writes the dummy slot):
+// a store that may or may not run would make the compiler drain every load
+// before reusing its register.
+__device__ __forceinline__ void stage_put(const GemmArgs& a, const Stage& st, int n_chunks, int unit, int k,
+                                          uint4 val, uint4* dummy, int nthr) {
+  const int vpr = (n_chunks * unit) >> 3;
+  const int per_plane = a.M * vpr;
+  const int i = threadIdx.x + k * nthr;
+  const bool ok = i < 2 * per_plane;
+  const int ic = ok ? i : 0;
+  const int pl = ic >= per_plane, ii = pl ? ic - per_plane : ic;
+  const int r = ii / vpr, v = ii % vpr;
+  uint4* dst = reinterpret_cast<uint4*>((pl ? st.lo : st.hi) + r * st.stride + v * 8);
+  *(ok ? dst : dummy) = val;
+}
+__device__ __forceinline__ void stage_store(const GemmArgs& a, const Stage& st, int n_chunks, int unit,
+                                            const StageRegs& s, uint4* dummy, int nthr) {
+  stage_put(a, st, n_chunks, unit, 0, s.v0, dummy, nthr);
+  stage_put(a, st, n_chunks, unit, 1, s.v1, dummy, nthr);
+  stage_put(a, st, n_chunks, unit, 2, s.v2, dummy, nthr);
+  stage_put(a, st, n_chunks, unit, 3, s.v3, dummy, nthr);
+}
+
 // Weight loads of one wave run as a ring of NB slots: a slot is refilled with
 // the chunk NB positions ahead as soon as its MFMAs are issued, across item
 // boundaries, so NB loads stay in flight through the cross-wave reduction of
@@ -446,8 +511,8 @@ struct LoadCursor {
 };
 
 // bf16: wave w accumulates chunks w, w + NW, w + 2 NW, ... of each item in
-// that order.
-template <int TM, int ROLE, int NB>
+// that order (DBL: double-buffered stages of NB chunks per wave).
+template <int TM, int ROLE, int NB, bool DBL>
 __global__ __launch_bounds__(1024) void k_gemm_bf16(GemmArgs a) {
   __shared__ GemmShared sh;
   __shared__ __align__(16) uint16_t stage_mem[kStageBytes / 2];
@@ -456,14 +521,20 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int KC = a.K >> 5;
-  const int cs = stage_chunks(KC, nw, a.M, 32, NB);
+  const int cs = DBL ? nw * NB : stage_chunks(KC, nw, a.M, 32, NB);
   const int n_stages = KC / cs;
-  const int cpws = cs / nw;                     // chunks per wave per stage (multiple of NB)
+  const int cpws = cs / nw;                     // chunks per wave per stage (multiple of NB; DBL: NB)
   const int cpi = KC / nw;                      // chunks per wave per item (multiple of NB)
-  Stage st;
-  st.stride = cs * 32 + 8;
-  st.hi = stage_mem;
-  st.lo = stage_mem + (size_t)a.M * st.stride;
+  const int stride = cs * 32 + 8;
+  const int buf_elems = 2 * a.M * stride;       // one buffer: hi then lo planes
+  // stage buffer b (no array of pointers: a runtime index would put it in scratch)
+  auto stage_buf = [&](int b) {
+    Stage x;
+    x.stride = stride;
+    x.hi = stage_mem + b * buf_elems;
+    x.lo = x.hi + (size_t)a.M * stride;
+    return x;
+  };
   const int n_items = a.N >> 4;
   // packed weights are tile-major: chunk kc of tile T is the KiB at (T * KC + kc)
   const uint4* W4 = reinterpret_cast<const uint4*>(a.W) + lane;
@@ -485,10 +556,11 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16(GemmArgs a) {
   for (int u = 0; u < NB; ++u) refill(A[u]);     // requested before anything else (NB <= cpi)
   row_best_init<ROLE>(a, sh);
   if (norm_role(ROLE)) rows_inv_rms(a, sh, wave, lane, nw);   // read only by the epilogue
-  if (n_stages == 1) {
-    stage_planes(a, st, 0, cs, 32);
+  if (n_stages == 1 || DBL) {
+    stage_planes(a, stage_buf(0), 0, cs, 32);
     __syncthreads();
   }
+  int buf = 0;                                  // DBL: buffer of the current stage
 
   for (int T = blockIdx.x; T < n_items; T += gridDim.x) {
     const EpiPre pre = epi_load<ROLE>(a, T, threadIdx.x);
@@ -497,11 +569,19 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16(GemmArgs a) {
     for (int rt = 0; rt < TM; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int c0 = 0; c0 < cpi; c0 += NB) {
       const int cl0 = c0 % cpws;                // position inside the current stage
-      if (n_stages > 1 && cl0 == 0) {
+      if (!DBL && n_stages > 1 && cl0 == 0) {
         __syncthreads();
-        stage_planes(a, st, (c0 / cpws) * cs, cs, 32);
+        stage_planes(a, stage_buf(0), (c0 / cpws) * cs, cs, 32);
         __syncthreads();
       }
+      StageRegs sreg{};
+      if (DBL) {                                // next stage (cyclically: the next item restarts at 0)
+        const int s_next = c0 / cpws + 1;
+        sreg = stage_fetch(a, s_next < n_stages ? s_next * cs : 0, cs, 32, nw * 64);
+      }
+      const Stage st = stage_buf(DBL ? buf : 0);
+      // (each of the two copies below ends with its own stage store, so the
+      // waits before the store count exactly the loads of that copy)
       auto group = [&](bool refills) {
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
@@ -511,9 +591,16 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16(GemmArgs a) {
             acc[rt] = mfma_pair(A[u], lds_pair(st, row_of(rt * 16 + j, a.M), kl), acc[rt]);
           if (refills) refill(A[u]);
         }
+        if (DBL) {
+          // the other buffer was last read in the previous stage, before the
+          // previous barrier; after this barrier every wave reads the new one
+          stage_store(a, stage_buf(buf ^ 1), cs, 32, sreg, &sh.dummy, nw * 64);
+          __syncthreads();
+        }
       };
       if (T + (int)gridDim.x < n_items || c0 + NB < cpi) group(true);
       else group(false);                        // the last NB chunks of this workgroup
+      if (DBL) buf ^= 1;
     }
     gemm_finish<TM, ROLE>(a, sh, acc, T, wave, lane, nw, pre);
   }
@@ -618,7 +705,7 @@ __global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
 }
 
 template <int ROLE, bool INT4, int NB>
-static hipError_t gemm_dispatch_nb(const GemmArgs& a, int grid, hipStream_t st) {
+static hipError_t gemm_dispatch_nb(const GemmArgs& a, int grid, hipStream_t st, bool dbl) {
   const dim3 block(64 * a.S);
   const int tm = (a.M + 15) / 16;
   if constexpr (INT4) {
@@ -641,15 +728,33 @@ static hipError_t gemm_dispatch_nb(const GemmArgs& a, int grid, hipStream_t st) 
     }
   } else {
     switch (tm) {
-      case 1: hipLaunchKernelGGL((k_gemm_bf16<1, ROLE, NB>), dim3(grid), block, 0, st, a); break;
-      case 2: hipLaunchKernelGGL((k_gemm_bf16<2, ROLE, NB>), dim3(grid), block, 0, st, a); break;
+      case 1:
+        if (dbl) {
+          if constexpr (NB >= 4) hipLaunchKernelGGL((k_gemm_bf16<1, ROLE, NB, true>), dim3(grid), block, 0, st, a);
+          else return hipErrorInvalidValue;
+        } else {
+          hipLaunchKernelGGL((k_gemm_bf16<1, ROLE, NB, false>), dim3(grid), block, 0, st, a);
+        }
+        break;
+      case 2:
+        if (dbl) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((k_gemm_bf16<2, ROLE, NB, false>), dim3(grid), block, 0, st, a);
+        break;
       case 3:
-        if constexpr (NB <= 4) hipLaunchKernelGGL((k_gemm_bf16<3, ROLE, NB>), dim3(grid), block, 0, st, a);
-        else return hipErrorInvalidValue;
+        if constexpr (NB <= 4) {
+          if (dbl) return hipErrorInvalidValue;
+          hipLaunchKernelGGL((k_gemm_bf16<3, ROLE, NB, false>), dim3(grid), block, 0, st, a);
+        } else {
+          return hipErrorInvalidValue;
+        }
         break;
       case 4:
-        if constexpr (NB == 1) hipLaunchKernelGGL((k_gemm_bf16<4, ROLE, NB>), dim3(grid), block, 0, st, a);
-        else return hipErrorInvalidValue;
+        if constexpr (NB == 1) {
+          if (dbl) return hipErrorInvalidValue;
+          hipLaunchKernelGGL((k_gemm_bf16<4, ROLE, NB, false>), dim3(grid), block, 0, st, a);
+        } else {
+          return hipErrorInvalidValue;
+        }
         break;
       default: return hipErrorInvalidValue;
     }
@@ -659,8 +764,20 @@ static hipError_t gemm_dispatch_nb(const GemmArgs& a, int grid, hipStream_t st) 
 
 // Ring depth: the deepest of 8 / 4 / 2 / 1 that divides the chunks each wave
 // takes per item and per LDS stage (int4: capped by the row count, so its
-// registers fit).
-int gemm_ring_depth(int n_chunks, int waves, int M, int unit) {
+// registers fit).  *dbl: double-buffered stages (bf16, one row tile, when K
+// does not fit one stage), preferred over single-buffered restaging.
+int gemm_ring_depth(int n_chunks, int waves, int M, int unit, bool* dbl) {
+  *dbl = false;
+  const int nthreads = 64 * waves;
+  if (unit == 32 && M <= 16 && stage_chunks(n_chunks, waves, M, unit, 1) < n_chunks) {
+    for (int nb : {8, 4}) {
+      if ((n_chunks / waves) % nb) continue;
+      if (stage_double_ok(n_chunks, waves, M, unit, nb, nthreads)) {
+        *dbl = true;
+        return nb;
+      }
+    }
+  }
   // register budget: bf16 rings are 8 deep up to 32 rows, 4 up to 48, then
   // 1; int4 ring slots also hold scales: 4 deep up to 16 rows, 2 up to 32,
   // then 1
@@ -676,13 +793,14 @@ int gemm_ring_depth(int n_chunks, int waves, int M, int unit) {
 
 template <int ROLE, bool INT4>
 static hipError_t gemm_dispatch(const GemmArgs& a, int grid, hipStream_t st) {
-  switch (gemm_ring_depth(a.K / (INT4 ? 128 : 32), a.S, a.M, INT4 ? 128 : 32)) {
+  bool dbl = false;
+  switch (gemm_ring_depth(a.K / (INT4 ? 128 : 32), a.S, a.M, INT4 ? 128 : 32, &dbl)) {
     case 8:
       if constexpr (INT4) return hipErrorInvalidValue;
-      else return gemm_dispatch_nb<ROLE, INT4, 8>(a, grid, st);
-    case 4: return gemm_dispatch_nb<ROLE, INT4, 4>(a, grid, st);
-    case 2: return gemm_dispatch_nb<ROLE, INT4, 2>(a, grid, st);
-    case 1: return gemm_dispatch_nb<ROLE, INT4, 1>(a, grid, st);
+      else return gemm_dispatch_nb<ROLE, INT4, 8>(a, grid, st, dbl);
+    case 4: return gemm_dispatch_nb<ROLE, INT4, 4>(a, grid, st, dbl);
+    case 2: return gemm_dispatch_nb<ROLE, INT4, 2>(a, grid, st, dbl);
+    case 1: return gemm_dispatch_nb<ROLE, INT4, 1>(a, grid, st, dbl);
     default: return hipErrorInvalidValue;
   }
 }
