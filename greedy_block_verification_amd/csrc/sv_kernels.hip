@@ -500,6 +500,77 @@ __device__ __forceinline__ void stage_store(const GemmArgs& a, const Stage& st, 
   stage_put(a, st, n_chunks, unit, 3, s.v3, dummy, nthr);
 }
 
+// Prologue with the loads ordered by need: the first stage's activation
+// planes (up to kProRegs vectors per thread) and the RMSNorm sums (one row
+// per wave, up to kSsRegs slices per lane) are requested before the weight
+// ring, so waiting for them leaves the ring in flight.
+constexpr int kProRegs = 8, kSsRegs = 8;
+struct ProRegs {   // named members, not arrays: they must stay in registers
+  uint4 v0, v1, v2, v3, v4, v5, v6, v7;
+  float s0, s1, s2, s3, s4, s5, s6, s7;
+};
+__device__ __forceinline__ bool prologue_fast(const GemmArgs& a, int cs, int unit, int nw, bool norm) {
+  const int n_vec = 2 * a.M * ((cs * unit) >> 3);
+  if (n_vec > kProRegs * nw * 64) return false;
+  return !norm || (a.M <= nw && (a.K >> 4) <= 64 * kSsRegs);
+}
+// vector k of this thread (index i = threadIdx.x + k * nthr of the hi plane, then the lo plane)
+__device__ __forceinline__ uint4 pro_load(const GemmArgs& a, int vpr, int k, int nthr) {
+  const int per_plane = a.M * vpr;
+  const int i = threadIdx.x + k * nthr;
+  if (i >= 2 * per_plane) return make_uint4(0u, 0u, 0u, 0u);
+  const int pl = i >= per_plane, ii = pl ? i - per_plane : i;
+  const int r = ii / vpr, v = ii % vpr;
+  return *reinterpret_cast<const uint4*>((pl ? a.blo : a.bhi) + (size_t)r * a.K + (size_t)v * 8);
+}
+__device__ __forceinline__ void pro_store(const GemmArgs& a, const Stage& st, int vpr, int k, int nthr, uint4 val) {
+  const int per_plane = a.M * vpr;
+  const int i = threadIdx.x + k * nthr;
+  if (i >= 2 * per_plane) return;
+  const int pl = i >= per_plane, ii = pl ? i - per_plane : i;
+  const int r = ii / vpr, v = ii % vpr;
+  *reinterpret_cast<uint4*>((pl ? st.lo : st.hi) + r * st.stride + v * 8) = val;
+}
+__device__ __forceinline__ float ss_load(const GemmArgs& a, int wave, int lane, int k) {
+  const int nsl = a.K >> 4;
+  const int i = lane + 64 * k;
+  return i < nsl ? a.ss[(size_t)wave * nsl + i] : 0.f;
+}
+__device__ __forceinline__ ProRegs prologue_issue(const GemmArgs& a, int cs, int unit, int nthr, int wave, int lane,
+                                                  bool norm) {
+  const int vpr = (cs * unit) >> 3;
+  ProRegs pr;
+  pr.v0 = pro_load(a, vpr, 0, nthr); pr.v1 = pro_load(a, vpr, 1, nthr);
+  pr.v2 = pro_load(a, vpr, 2, nthr); pr.v3 = pro_load(a, vpr, 3, nthr);
+  pr.v4 = pro_load(a, vpr, 4, nthr); pr.v5 = pro_load(a, vpr, 5, nthr);
+  pr.v6 = pro_load(a, vpr, 6, nthr); pr.v7 = pro_load(a, vpr, 7, nthr);
+  pr.s0 = pr.s1 = pr.s2 = pr.s3 = pr.s4 = pr.s5 = pr.s6 = pr.s7 = 0.f;
+  if (norm && wave < a.M) {
+    pr.s0 = ss_load(a, wave, lane, 0); pr.s1 = ss_load(a, wave, lane, 1);
+    pr.s2 = ss_load(a, wave, lane, 2); pr.s3 = ss_load(a, wave, lane, 3);
+    pr.s4 = ss_load(a, wave, lane, 4); pr.s5 = ss_load(a, wave, lane, 5);
+    pr.s6 = ss_load(a, wave, lane, 6); pr.s7 = ss_load(a, wave, lane, 7);
+  }
+  return pr;
+}
+__device__ __forceinline__ void prologue_finish(const GemmArgs& a, const Stage& st, int cs, int unit, int nthr,
+                                                int wave, int lane, bool norm, const ProRegs& pr, GemmShared& sh) {
+  if (norm && wave < a.M) {
+    // the same order as rows_inv_rms: each lane adds its slices in order (the
+    // zeros past the row's slices add exactly nothing), then the butterfly
+    float v = 0.f;
+    v = v + pr.s0; v = v + pr.s1; v = v + pr.s2; v = v + pr.s3;
+    v = v + pr.s4; v = v + pr.s5; v = v + pr.s6; v = v + pr.s7;
+    v = wave_sum(v);
+    if (lane == 0) sh.inv[wave] = 1.0f / sqrtf(v / (float)a.K + a.eps);
+  }
+  const int vpr = (cs * unit) >> 3;
+  pro_store(a, st, vpr, 0, nthr, pr.v0); pro_store(a, st, vpr, 1, nthr, pr.v1);
+  pro_store(a, st, vpr, 2, nthr, pr.v2); pro_store(a, st, vpr, 3, nthr, pr.v3);
+  pro_store(a, st, vpr, 4, nthr, pr.v4); pro_store(a, st, vpr, 5, nthr, pr.v5);
+  pro_store(a, st, vpr, 6, nthr, pr.v6); pro_store(a, st, vpr, 7, nthr, pr.v7);
+}
+
 // Weight loads of one wave run as a ring of NB slots: a slot is refilled with
 // the chunk NB positions ahead as soon as its MFMAs are issued, across item
 // boundaries, so NB loads stay in flight through the cross-wave reduction of
@@ -551,14 +622,22 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16(GemmArgs a) {
       cur.off = ((size_t)cur.T * KC + wave) * 64;
     }
   };
+  const bool fast = (n_stages == 1 || DBL) && prologue_fast(a, cs, 32, nw, norm_role(ROLE));
+  ProRegs pr{};
+  if (fast) pr = prologue_issue(a, cs, 32, nw * 64, wave, lane, norm_role(ROLE));
   uint4 A[NB];
 #pragma unroll
-  for (int u = 0; u < NB; ++u) refill(A[u]);     // requested before anything else (NB <= cpi)
+  for (int u = 0; u < NB; ++u) refill(A[u]);     // weights stream from here on (NB <= cpi)
   row_best_init<ROLE>(a, sh);
-  if (norm_role(ROLE)) rows_inv_rms(a, sh, wave, lane, nw);   // read only by the epilogue
-  if (n_stages == 1 || DBL) {
-    stage_planes(a, stage_buf(0), 0, cs, 32);
+  if (fast) {
+    prologue_finish(a, stage_buf(0), cs, 32, nw * 64, wave, lane, norm_role(ROLE), pr, sh);
     __syncthreads();
+  } else {
+    if (norm_role(ROLE)) rows_inv_rms(a, sh, wave, lane, nw);   // read only by the epilogue
+    if (n_stages == 1 || DBL) {
+      stage_planes(a, stage_buf(0), 0, cs, 32);
+      __syncthreads();
+    }
   }
   int buf = 0;                                  // DBL: buffer of the current stage
 
@@ -922,11 +1001,6 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
     for (int c = 0; c < DC; ++c) { qraw[c][0] = qp[c * 8]; qraw[c][1] = qp[c * 8 + 1]; }
   }
-  const int kv_len = a.params[0];
-  const int ctx_max = kv_len + a.M;
-  const int ctx = kv_len + r + 1;
-  const size_t layer_base = (size_t)a.layer * a.n_pages;
-  const size_t page_elems = (size_t)kPage * DH;
   // physical pages of the 4 logical pages of block b: one 16-byte load of
   // consecutive page-table entries (the table is 16-byte aligned); a block
   // overhanging max_ctx (its positions are masked) reads clamped entries
@@ -941,6 +1015,15 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     }
     return q;
   };
+  // the first unit's first block is its split index whenever splits are one
+  // block (contexts up to 2048): fetch its pages before the context length is known
+  const int b_guess = s_lo + wave;
+  int4 pq_guess = block_pages(b_guess);
+  const int kv_len = a.params[0];
+  const int ctx_max = kv_len + a.M;
+  const int ctx = kv_len + r + 1;
+  const size_t layer_base = (size_t)a.layer * a.n_pages;
+  const size_t page_elems = (size_t)kPage * DH;
   // element offset of (page, kv) for this KV head
   auto page_base = [&](int page, int kv) { return (((layer_base + page) * 2 + kv) * a.nkv + h) * page_elems; };
   BPair qop[DC];
@@ -975,7 +1058,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, l = 0.f;
 
-    int4 pq = block_pages(b_lo < b_hi ? b_lo : 0);
+    int4 pq = (b_lo == b_guess) ? pq_guess : block_pages(b_lo < b_hi ? b_lo : 0);
     for (int b = b_lo; b < b_hi; ++b) {
       // K operand: lane (g, j) holds K[pos = 64b + 16pt + j][32c + 8g .. +7]; one page per pt
       uint4 kop[4][DC];
@@ -1094,23 +1177,23 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       if (q2 >= n_qr) continue;
       const int r2 = q2 / G, head2 = h * G + q2 % G;
       const int ns = attn_ns(kv_len + r2 + 1);
-      const float4 o0 = *reinterpret_cast<const float4*>(&ul[0].o[jj][d0]);
-      Fold f[4];
-      f[0].first(ul[0].m[jj], ul[0].l[jj], o0.x);
-      f[1].first(ul[0].m[jj], ul[0].l[jj], o0.y);
-      f[2].first(ul[0].m[jj], ul[0].l[jj], o0.z);
-      f[3].first(ul[0].m[jj], ul[0].l[jj], o0.w);
+      // the Fold arithmetic, with the weights of a split shared by the 4 outputs
+      float fm = ul[0].m[jj], fl = ul[0].l[jj];
+      float4 fo = *reinterpret_cast<const float4*>(&ul[0].o[jj][d0]);
       for (int sp = 1; sp < ns; ++sp) {
         const float mi = ul[sp].m[jj], li = ul[sp].l[jj];
         const float4 oi = *reinterpret_cast<const float4*>(&ul[sp].o[jj][d0]);
-        f[0].add(mi, li, oi.x);
-        f[1].add(mi, li, oi.y);
-        f[2].add(mi, li, oi.z);
-        f[3].add(mi, li, oi.w);
+        const float mn = fmaxf(fm, mi);
+        const float wa = exp2f(fm - mn), wb = exp2f(mi - mn);
+        fl = fl * wa + li * wb;
+        fo.x = fo.x * wa + oi.x * wb; fo.y = fo.y * wa + oi.y * wb;
+        fo.z = fo.z * wa + oi.z * wb; fo.w = fo.w * wa + oi.w * wb;
+        fm = mn;
       }
+      const float ov[4] = {fo.x, fo.y, fo.z, fo.w};
       uint16_t hb[4], lb[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) split1(f[e].o / f[e].l, hb[e], lb[e]);
+      for (int e = 0; e < 4; ++e) split1(ov[e] / fl, hb[e], lb[e]);
       const size_t oi = ((size_t)r2 * a.nq + head2) * DH + d0;
       *reinterpret_cast<uint2*>(a.ohi + oi) = make_uint2(pack2(hb[0], hb[1]), pack2(hb[2], hb[3]));
       *reinterpret_cast<uint2*>(a.olo + oi) = make_uint2(pack2(lb[0], lb[1]), pack2(lb[2], lb[3]));
