@@ -1,15 +1,22 @@
 #!/usr/bin/env python3
 """Verified tokens/s of greedy block verification on one MI355X.
 
-Workload (default): the Qwen3-8B-shaped random-init target (36 layers,
-d 4096, 32/8 heads x 128, FFN 12288, vocab 151936, bf16), 50 prompts of 128
-random ids, 64 generated tokens each, K = 4 drafts per verify.  Each draft
-position is the target's true greedy token with probability 0.66, else a
-random wrong id (the first wrong one ends acceptance).  The true continuation
-comes from a plain one-token decode pass run first (also reported as the
-decode baseline).
+Workload (default, ``--config q8b``): the Qwen3-8B-shaped random-init target
+(36 layers, d 4096, 32/8 heads x 128, FFN 12288, vocab 151936, bf16), 50
+prompts of 128 random ids, 64 generated tokens each, K = 4 drafts per verify.
+Each draft position is the target's true greedy token with probability 0.66,
+else a random wrong id (the first wrong one ends acceptance).  The true
+continuation comes from a plain one-token decode pass run first (also
+reported as the decode baseline).
 
-A timed *step* is one ``sv_verify`` call (the whole hot path: embed, 36
+Other workloads (``--config``), each printing its own JSON line:
+``q06b`` (Qwen3-0.6B shape, 8 prompts of 512 ids, 128 generated, K = 4 and
+a sweep over 1, 2, 8, draft accuracy 0.60), ``gemma_int4`` (int4 GeGLU
+target, 87-id prompts, K = 8 and 16), ``q8b_stress`` (the 8B shape over a
+synthetic 32640-position KV cache restored into a 32K context, K = 4 and a
+sweep over 1, 2, 8, 16, 32).
+
+A timed *step* is one ``sv_verify`` call (the whole hot path: embed, all
 layers, LM head + argmax, acceptance, truncate) on one prompt's window; the
 loop walks the prompts' speculative loops in order.  ``value`` = committed
 (verified) tokens / wall seconds of the timed steps.
@@ -52,8 +59,8 @@ def gate_up_bytes(cfg, m):
     return w + m * k * 4 + m * (k // 16) * 4 + m * cfg.d_ff * 4
 
 
-def load_traffic(kernel_src_sha):
-    path = os.path.join(ROOT, "profiles", "gate_up_q8b_traffic.json")
+def load_traffic(config, kernel_src_sha):
+    path = os.path.join(ROOT, "profiles", f"gate_up_{config}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -130,19 +137,59 @@ def cpu_baseline(weights, ids, n_tokens, steps):
             "s_per_decode": s_per_decode, "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
+# Per-workload defaults: the headline is q8b; the others are the remaining
+# synthetic shapes of the study, each printed as its own JSON line.
+WORKLOADS = {
+    "q8b": dict(k=4, k_sweep="8,16", prompts=50, prompt_len=128, gen_tokens=64, p_correct=0.66,
+                steps=300, sweep_steps=150, restore=False, roofline_kernel="sv::k_gemm_bf16<1, 2>",
+                what="Qwen3-8B-shaped target"),
+    "q06b": dict(k=4, k_sweep="1,2,8", prompts=8, prompt_len=512, gen_tokens=128, p_correct=0.60,
+                 steps=400, sweep_steps=300, restore=False, roofline_kernel="sv::k_gemm_bf16<1, 2>",
+                 what="Qwen3-0.6B-shaped target"),
+    "gemma_int4": dict(k=8, k_sweep="16", prompts=16, prompt_len=87, gen_tokens=64, p_correct=0.66,
+                       steps=300, sweep_steps=200, restore=False, roofline_kernel="sv::k_gemm_int4<1, 2>",
+                       what="Gemma-style int4 (group 64, bf16 scales) GeGLU target"),
+    "q8b_stress": dict(k=4, k_sweep="1,2,8,16,32", prompts=1, prompt_len=32640, gen_tokens=64, p_correct=0.66,
+                       steps=150, sweep_steps=60, restore=True, roofline_kernel="sv::k_gemm_bf16<1, 2>",
+                       what="Qwen3-8B-shaped target over a synthetic 32K-position KV cache"),
+}
+ROLE_NAMES = ["qkv", "o_proj", "gate_up", "down", "lm_head", "attention"]
+
+
+def restore_synthetic_prefix(session, cfg, prefix_len, seed):
+    """Fill the first prefix_len positions of every layer's KV pages with
+    seeded random fp16 values and declare them committed with a random greedy
+    history (a long context the bench cannot prefill in its time budget)."""
+    import numpy as np
+    import torch
+    from greedy_block_verification_amd import binding as B
+    n_pages = cfg.max_ctx // cfg.page_size
+    pool = session.kv.view(cfg.n_layers, n_pages, -1)
+    g = torch.Generator(device=session.kv.device)
+    g.manual_seed(seed)
+    used = (prefix_len + cfg.page_size - 1) // cfg.page_size
+    for layer in range(cfg.n_layers):
+        vals = torch.randn((used, pool.shape[2]), generator=g, device=session.kv.device, dtype=torch.float32)
+        pool[layer, :used] = vals.to(torch.float16).view(torch.int16)
+    torch.cuda.synchronize()
+    hist = np.random.default_rng(seed + 1).integers(0, cfg.vocab, prefix_len).tolist()
+    B.sv_restore(session.ctx, prefix_len, hist)
+    return hist
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=300, help="timed verify steps at the headline K")
+    ap.add_argument("--config", default="q8b", choices=sorted(WORKLOADS))
+    ap.add_argument("--steps", type=int, default=None, help="timed verify steps at the headline K")
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="q8b")
-    ap.add_argument("--k", type=int, default=4)
-    ap.add_argument("--k-sweep", default="8,16", help="extra K values timed after the headline (empty: none)")
-    ap.add_argument("--sweep-steps", type=int, default=150)
-    ap.add_argument("--prompts", type=int, default=50)
-    ap.add_argument("--prompt-len", type=int, default=128)
-    ap.add_argument("--gen-tokens", type=int, default=64)
-    ap.add_argument("--p-correct", type=float, default=0.66)
+    ap.add_argument("--k", type=int, default=None)
+    ap.add_argument("--k-sweep", default=None, help="extra K values timed after the headline (empty: none)")
+    ap.add_argument("--sweep-steps", type=int, default=None)
+    ap.add_argument("--prompts", type=int, default=None)
+    ap.add_argument("--prompt-len", type=int, default=None)
+    ap.add_argument("--gen-tokens", type=int, default=None)
+    ap.add_argument("--p-correct", type=float, default=None)
     ap.add_argument("--cpu-tokens", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -153,6 +200,10 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU sharding)", file=sys.stderr)
         sys.exit(2)
+    wl = WORKLOADS[args.config]
+    for key in ("k", "k_sweep", "prompts", "prompt_len", "gen_tokens", "p_correct", "steps", "sweep_steps"):
+        if getattr(args, key) is None:
+            setattr(args, key, wl[key])
 
     import numpy as np
     import torch
@@ -162,6 +213,11 @@ def main():
     from seeded_inputs import DraftSource, generate_weights, get_config, prompt_ids
 
     cfg = get_config(args.config)
+    P, L, G = args.prompts, args.prompt_len, args.gen_tokens
+    if L + G + cfg.max_k + 1 > cfg.max_ctx or args.k > cfg.max_k:
+        print(f"prompt {L} + {G} generated + K exceeds the {cfg.name} context {cfg.max_ctx} "
+              f"(or K > {cfg.max_k})", file=sys.stderr)
+        sys.exit(2)
     t = time.perf_counter()
     weights = generate_weights(cfg, threads=min(16, len(os.sched_getaffinity(0))))
     log(f"[bench] weights generated in {time.perf_counter() - t:.1f} s")
@@ -169,15 +225,18 @@ def main():
     dm = DeviceModel(weights)
     log(f"[bench] weights uploaded and packed in {time.perf_counter() - t:.1f} s")
 
-    P, L, G = args.prompts, args.prompt_len, args.gen_tokens
     sessions, truth, prompts = [], [], []
     t_prefill = t_decode = 0.0
     for p in range(P):
         s = Session(dm)
-        ids = prompt_ids(cfg.seed, p, L, cfg.vocab).tolist()
         torch.cuda.synchronize()
         t = time.perf_counter()
-        nx = s.prefill(ids)
+        if wl["restore"]:
+            ids = restore_synthetic_prefix(s, cfg, L, cfg.seed + 300 + 2 * p)
+            nx = s.next_id
+        else:
+            ids = prompt_ids(cfg.seed, p, L, cfg.vocab).tolist()
+            nx = s.prefill(ids)
         t_prefill += time.perf_counter() - t
         seq = [nx]
         t = time.perf_counter()
@@ -190,7 +249,7 @@ def main():
         truth.append(seq)
         prompts.append(ids)
     decode_tpot_ms = 1000.0 * t_decode / (P * G)
-    log(f"[bench] {P} prompts prefetched; baseline decode {decode_tpot_ms:.3f} ms/token")
+    log(f"[bench] {P} prompts ready; baseline decode {decode_tpot_ms:.3f} ms/token")
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 20
@@ -205,23 +264,30 @@ def main():
     srcs = [DraftSource(cfg.seed, p, cfg.vocab, p_correct=args.p_correct) for p in range(P)]
     run_spec(sessions[:1], truth[:1], L, G, args.k, [DraftSource(cfg.seed, 10_000, cfg.vocab, p_correct=args.p_correct)],
              args.warmup)
-    st = run_spec(sessions, truth, L, G, args.k, srcs, args.steps, profile_mask=1 << ROLE_GATE_UP)
-    gu_ms = sum(B.sv_profile_read(s.ctx, ROLE_GATE_UP)[0] for s in sessions)
-    gu_n = sum(B.sv_profile_read(s.ctx, ROLE_GATE_UP)[1] for s in sessions)
+    for s in sessions:
+        B.sv_profile_reset(s.ctx)
+    st = run_spec(sessions, truth, L, G, args.k, srcs, args.steps, profile_mask=(1 << len(ROLE_NAMES)) - 1)
+    prof = {}
+    for r, name in enumerate(ROLE_NAMES):
+        ms = sum(B.sv_profile_read(s.ctx, r)[0] for s in sessions)
+        n = sum(B.sv_profile_read(s.ctx, r)[1] for s in sessions)
+        prof[name] = (ms, n)
+    gu_ms, gu_n = prof["gate_up"]
     value = metrics.verified_tok_s(st["tokens"], st["seconds"])
     ms_step = 1000.0 * st["seconds"] / args.steps
     log(f"[bench] K={args.k}: {value:.1f} verified tok/s, {ms_step:.3f} ms/step, "
         f"acceptance {metrics.acceptance_rate(st['accepted'], st['proposed']):.4f}")
 
     # roofline of the dominant kernel (gate/up GEMM): algorithmic bytes per
-    # launch over its mean event-timed duration in the timed region
+    # launch over its mean device-timed duration in the timed region
     gu_bytes = sum(gate_up_bytes(cfg, k_eff + 1) for k_eff, _, _ in st["steps"]) * cfg.n_layers
     achieved = gu_bytes / (gu_ms / 1000.0) / 1e9 if gu_ms > 0 else 0.0
     ksrc = open(os.path.join(ROOT, "greedy_block_verification_amd", "csrc", "sv_kernels.hip"), "rb").read()
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": load_traffic(hashlib.sha256(ksrc).hexdigest()),
-                "kernel": "sv::k_gemm_bf16<1, 2> (gate/up GEMM with SwiGLU epilogue, 8B shape, M <= 16)",
+                "traffic": load_traffic(args.config, hashlib.sha256(ksrc).hexdigest()),
+                "kernel": f"{wl['roofline_kernel']} (gate/up GEMM with its gated-activation epilogue, "
+                          f"{cfg.name} shape, M <= 16)",
                 "launches": gu_n, "mean_launch_us": round(1000.0 * gu_ms / max(1, gu_n), 2),
                 "bytes_per_launch": int(gu_bytes / max(1, gu_n))}
     step_bytes = sum(algorithmic_step_bytes(cfg, k_eff + 1, kv) for k_eff, _, kv in st["steps"])
@@ -236,7 +302,9 @@ def main():
         "baseline_decode_tpot_ms": round(decode_tpot_ms, 4),
         "baseline_decode_tok_s": round(1000.0 / decode_tpot_ms, 2),
         "speedup_vs_decode": round(value / (1000.0 / decode_tpot_ms), 4),
-        "prefill_ms_per_prompt": round(1000.0 * t_prefill / P, 3),
+        ("restore_ms_per_prompt" if wl["restore"] else "prefill_ms_per_prompt"): round(1000.0 * t_prefill / P, 3),
+        "kernel_us_per_step": {name: round(1000.0 * ms / args.steps, 1) for name, (ms, n) in prof.items()},
+        "kernel_launches_per_step": {name: round(n / args.steps, 2) for name, (ms, n) in prof.items()},
     }
     sweep = {}
     for k in [int(x) for x in args.k_sweep.split(",") if x.strip()]:
@@ -254,19 +322,25 @@ def main():
     extra["k_sweep"] = sweep
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if wl["restore"]:
+        extra["cpu_baseline_note"] = ("not run: the oracle would have to rebuild the synthetic "
+                                      f"{L}-position cache in fp64 before its first decode")
+    elif not args.no_cpu_baseline:
         t = time.perf_counter()
         cpu = cpu_baseline(weights, prompts[0], args.cpu_tokens, st["steps"])
         log(f"[bench] cpu baseline {cpu['value']:.4f} tok/s in {time.perf_counter() - t:.1f} s")
 
+    prompt_desc = (f"{P} synthetic {L}-position prefix(es) (seeded random fp16 K/V, restored)" if wl["restore"]
+                   else f"{P} prompts x {L} ids")
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "verified tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int4 weights, bf16 MFMA" if cfg.weight_fmt == "int4" else "bf16",
         "data": "synthetic (seeded random-init weights and random-id prompts)",
-        "config": {"workload": f"{cfg.name}: Qwen3-8B-shaped target, {cfg.n_layers} layers, d {cfg.d_model}, "
+        "config": {"workload": f"{cfg.name}: {wl['what']}, {cfg.n_layers} layers, d {cfg.d_model}, "
                                f"{cfg.n_q_heads}/{cfg.n_kv_heads} heads x {cfg.head_dim}, FFN {cfg.d_ff}, "
-                               f"vocab {cfg.vocab}; {P} prompts x {L} ids, {G} generated, K={args.k}, "
+                               f"vocab {cfg.vocab}; {prompt_desc}, {G} generated, K={args.k}, "
                                f"per-position draft accuracy {args.p_correct}",
                    "k": args.k, "prompts": P, "prompt_len": L, "gen_tokens": G, "p_correct": args.p_correct,
                    "kv_capacity": cfg.max_ctx},
