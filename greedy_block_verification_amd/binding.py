@@ -27,7 +27,7 @@ class sv_config(C.Structure):
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("d_ff", C.c_int32),
                 ("vocab", C.c_int32), ("act", C.c_int32), ("weight_fmt", C.c_int32), ("tied", C.c_int32),
                 ("rms_eps", C.c_float), ("rope_theta", C.c_float), ("page_size", C.c_int32),
-                ("max_ctx", C.c_int32), ("max_k", C.c_int32)]
+                ("max_ctx", C.c_int32), ("max_k", C.c_int32), ("max_prefill_rows", C.c_int32)]
 
 
 class sv_layer_weights(C.Structure):
@@ -105,11 +105,13 @@ def _i32_array(vals):
     return (C.c_int32 * max(1, len(vals)))(*vals)
 
 
-def make_config(cfg) -> sv_config:
-    """sv_config from a ``seeded_inputs.ModelConfig``."""
+def make_config(cfg, max_prefill_rows: int = 0) -> sv_config:
+    """sv_config from a ``seeded_inputs.ModelConfig`` (max_prefill_rows: rows of
+    one row-tiled prefill forward, 0 for 64-row forwards only)."""
     return sv_config(cfg.n_layers, cfg.d_model, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.d_ff,
                      cfg.vocab, 0 if cfg.act == "swiglu" else 1, 0 if cfg.weight_fmt == "bf16" else 1,
-                     1 if cfg.tied else 0, cfg.rms_eps, cfg.rope_theta, cfg.page_size, cfg.max_ctx, cfg.max_k)
+                     1 if cfg.tied else 0, cfg.rms_eps, cfg.rope_theta, cfg.page_size, cfg.max_ctx, cfg.max_k,
+                     int(max_prefill_rows))
 
 
 def sv_query_sizes(cfg: sv_config):
@@ -181,8 +183,8 @@ def sv_get_logits(ctx, row: int, vocab: int):
     return out
 
 
-def sv_last_argmax(ctx):
-    buf = (C.c_int32 * 64)()
+def sv_last_argmax(ctx, max_rows: int = 64):
+    buf = (C.c_int32 * max(64, int(max_rows)))()
     m = C.c_int32()
     _check(lib().sv_last_argmax(ctx, buf, C.byref(m)), "sv_last_argmax")
     return list(buf[:m.value])

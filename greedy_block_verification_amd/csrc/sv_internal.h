@@ -6,18 +6,18 @@
 
 namespace sv {
 
-constexpr int kMaxRows = 64;        // rows of one forward (verify: k+1; prefill chunk)
+constexpr int kMaxRows = 64;        // rows of a weight-streaming forward (verify: k+1; short prefill chunks)
+constexpr int kMaxPrefillRows = 16384;   // most rows of one row-tiled (prefill) forward
 constexpr int kPage = 16;           // positions per KV page
 constexpr int kGemmStageBytes = 136 * 1024;   // LDS a GEMM workgroup stages activation planes in
 constexpr int kAttnBlock = 64;      // positions per online-softmax block (4 pages)
-constexpr int kAttnMaxSplits = 32;  // most KV splits of one row (the split plan depends only on its ctx)
+constexpr int kAttnMaxSplits = 128; // most KV splits of one row (the split plan depends only on its ctx)
 constexpr int kAttnQRows = 256;     // most (row, q head) pairs one attention workgroup holds (16 MFMA tiles)
 constexpr int kColGroup = 64;       // LM-head columns per argmax record (4 MFMA tiles of 16)
 constexpr int kEpiCols = 256;       // columns one epilogue workgroup owns (whole heads, 8 gate/up tiles)
 
 // Parameters of one forward, staged host -> device before the launches.
-// Layout in device memory: int32 [0] kv_len, [1] rows, [2..2+64) row ids.
-constexpr int kParamInts = 2 + kMaxRows;
+// Layout in device memory: int32 [0] kv_len, [1] rows, [2..2+rows) row ids.
 
 // Weight-matrix roles of the skinny GEMM (each has its own epilogue).
 enum GemmRole { kRoleQkv = 0, kRoleO = 1, kRoleGateUp = 2, kRoleDown = 3, kRoleLmHead = 4 };
@@ -67,7 +67,8 @@ struct AttnArgs {
   int n_pages, layer, nq, nkv, dh, M, n_split;   // n_split: splits of the longest row
   int n_lpages;          // logical pages (page_table entries) = max_ctx / 16
   float scale_log2;      // log2(e) / sqrt(dh)
-  float* part;           // [M][nq][kAttnMaxSplits][dh + 4]  (m, l, -, -, o[dh])
+  float* part;           // [M][nq][part_splits][dh + 4]  (m, l, -, -, o[dh])
+  int part_splits;       // split slots per (row, q head) in `part` (most splits any row of this context can have)
   uint16_t* ohi;         // output planes [M][nq*dh]
   uint16_t* olo;
   unsigned long long* prof;   // optional [2]: start stamped by the split kernel, end by the last kernel
@@ -83,11 +84,16 @@ inline int gemm_max_rows(int unit, int waves) {
   return kGemmStageBytes / ((waves * unit + 8) * 4);
 }
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+// Forwards of many rows (prefill chunks): the same per-row arithmetic as
+// launch_gemm / launch_attention, tiled for rows instead of streamed for
+// weights.  M is any row count; bf16 weights only.
+hipError_t launch_gemm_tiled(const GemmArgs& a, int role, hipStream_t st);
+hipError_t launch_attention_rows(const AttnArgs& a, hipStream_t st);
 // Number of KV splits of a row attending to ctx positions.
 int attn_splits(int ctx);
-// Whether any of rows kv_len + 1 .. kv_len + M spans more than one split (the
-// combine pass is needed only then).
-bool attn_needs_combine(int kv_len, int M);
+// Most splits of any row of a forward of M rows after kv_len positions (the
+// rows attend to kv_len + 1 .. kv_len + M positions).
+int attn_splits_max(int kv_len, int M);
 // Embedding rows of the forward's ids; also clears the M row-argmax keys.
 hipError_t launch_embed(const int* params, int M, const void* embed, int vocab, int d, float* x, float* ss,
                         const uint16_t* g0, uint16_t* uhi, uint16_t* ulo, unsigned long long* best,

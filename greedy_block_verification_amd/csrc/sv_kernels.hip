@@ -17,6 +17,13 @@
 
 #include "sv_internal.h"
 
+// No implicit fused multiply-adds: every expression rounds exactly as
+// written, so an operation written once and used by two kernels (the GEMM
+// epilogues, the attention block step, the split fold) gives the same bits
+// in both, whatever code surrounds it.  Fused operations are written out
+// (fmaf) where they are meant.
+#pragma clang fp contract(off)
+
 namespace sv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -234,16 +241,21 @@ __device__ __forceinline__ constexpr bool norm_role(int role) {
   return role == kRoleQkv || role == kRoleGateUp || role == kRoleLmHead;
 }
 
-// 1 / sqrt(mean(x^2) + eps) per row from the per-16-column sums of squares:
-// one wave per row, each lane adds its slices in order, then a butterfly.
-__device__ __forceinline__ void rows_inv_rms(const GemmArgs& a, GemmShared& sh, int wave, int lane, int nw) {
+// 1 / sqrt(mean(x^2) + eps) of row r from its per-16-column sums of
+// squares: each lane adds its slices lane, lane + 64, ... in order, then a
+// butterfly over the wave (one wave per row).
+__device__ __forceinline__ float row_inv_rms(const GemmArgs& a, int r, int lane) {
   const int nsl = a.K >> 4;
+  const float* p = a.ss + (size_t)r * nsl;
+  float v = 0.f;
+  for (int i = lane; i < nsl; i += 64) v = v + p[i];
+  v = wave_sum(v);
+  return 1.0f / sqrtf(v / (float)a.K + a.eps);
+}
+__device__ __forceinline__ void rows_inv_rms(const GemmArgs& a, GemmShared& sh, int wave, int lane, int nw) {
   for (int r = wave; r < a.M; r += nw) {
-    const float* p = a.ss + (size_t)r * nsl;
-    float v = 0.f;
-    for (int i = lane; i < nsl; i += 64) v = v + p[i];
-    v = wave_sum(v);
-    if (lane == 0) sh.inv[r] = 1.0f / sqrtf(v / (float)a.K + a.eps);
+    const float v = row_inv_rms(a, r, lane);
+    if (lane == 0) sh.inv[r] = v;
   }
 }
 
@@ -277,63 +289,74 @@ __device__ __forceinline__ EpiPre epi_load(const GemmArgs& a, int T, int idx) {
   return e;
 }
 
+// Epilogue of element (r, c) of item (tile) T: yv(cc) is the finished sum of
+// column cc of row r, invr the row's 1 / rms (RMSNorm consumers), best_r the
+// workgroup's argmax key slot of the row (LM head, in LDS).  Both GEMM
+// kernels call this, so an output does not depend on which one produced it.
+// The caller runs whole 16-lane groups (the 16 columns of one row) together.
+template <int ROLE, class YV>
+__device__ __forceinline__ void epi_element(const GemmArgs& a, int T, int r, int c, const EpiPre& e, float invr,
+                                            YV yv, unsigned long long* best_r) {
+  float y = yv(c);
+  if (norm_role(ROLE)) y = y * invr;
+  if (ROLE == kRoleO || ROLE == kRoleDown) {
+    const int n = T * 16 + c;
+    const size_t xi = (size_t)r * a.N + n;
+    const float xn = e.x + y;
+    a.x[xi] = xn;
+    float sq = xn * xn;
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) sq += __shfl_xor(sq, o);
+    if (c == 0) a.ss_out[(size_t)r * (a.N >> 4) + T] = sq;
+    split1(xn * e.gain, a.uhi[xi], a.ulo[xi]);
+  } else if (ROLE == kRoleGateUp) {               // [gate 8 | up 8] of features 8T..8T+7
+    const float up = yv((c & 7) + 8) * invr;
+    if (c < 8) {
+      const size_t ai = (size_t)r * (a.N >> 1) + T * 8 + c;
+      split1(act_fn(y, a.act) * up, a.ahi[ai], a.alo[ai]);
+    }
+  } else if (ROLE == kRoleQkv) {                  // [dims 8s+i | half + 8s + i], i < 8
+    const int half = a.dh >> 1;
+    const int gph = half >> 3;
+    const int hh = T / gph, sb = T % gph;
+    const bool lo = c < 8;
+    const int i = 8 * sb + (c & 7);
+    const int d = lo ? i : half + i;
+    const int pos = a.params[0] + r;
+    float out = y;
+    if (hh < a.nq + a.nkv) {
+      const float2 cs = e.cs;
+      const float partner = yv(c ^ 8) * invr;
+      out = lo ? (y * cs.x - partner * cs.y) : (y * cs.x + partner * cs.y);
+    }
+    if (hh < a.nq) {
+      a.q_out[((size_t)r * a.nq + hh) * a.dh + d] = out;
+    } else {
+      const int kv = hh < a.nq + a.nkv ? 0 : 1;
+      const int head = hh - a.nq - kv * a.nkv;
+      const int page = e.page;
+      const size_t base = ((((size_t)a.layer * a.n_pages + page) * 2 + kv) * a.nkv + head) * kPage * a.dh;
+      // K rows are [slot][dh]; V is stored transposed inside the page, [dh][slot]
+      const size_t el = kv == 0 ? (size_t)(pos % kPage) * a.dh + d : (size_t)d * kPage + (pos % kPage);
+      a.kv_pool[base + el] = f2h(out);
+    }
+  } else {                                        // kRoleLmHead
+    const int n = T * 16 + c;
+    if (a.logits != nullptr) a.logits[(size_t)r * a.N + n] = y;
+    uint64_t b = argmax_key(y, (uint32_t)n);
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) b = umax64(b, __shfl_xor(b, o));
+    if (c == 0) atomicMax(best_r, (unsigned long long)b);
+  }
+}
+
 // Epilogue on the finished 16 columns of item (tile) T.
 template <int ROLE>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, GemmShared& sh, int T, const EpiPre& pre) {
   for (int idx = threadIdx.x; idx < a.M * 16; idx += blockDim.x) {
     const int r = idx >> 4, c = idx & 15;
     const EpiPre e = idx == (int)threadIdx.x ? pre : epi_load<ROLE>(a, T, idx);
-    float y = sh.y[r][c];
-    if (norm_role(ROLE)) y = y * sh.inv[r];
-    if (ROLE == kRoleO || ROLE == kRoleDown) {
-      const int n = T * 16 + c;
-      const size_t xi = (size_t)r * a.N + n;
-      const float xn = e.x + y;
-      a.x[xi] = xn;
-      float sq = xn * xn;
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) sq += __shfl_xor(sq, o);
-      if (c == 0) a.ss_out[(size_t)r * (a.N >> 4) + T] = sq;
-      split1(xn * e.gain, a.uhi[xi], a.ulo[xi]);
-    } else if (ROLE == kRoleGateUp) {               // [gate 8 | up 8] of features 8T..8T+7
-      const float up = sh.y[r][(c & 7) + 8] * sh.inv[r];
-      if (c < 8) {
-        const size_t ai = (size_t)r * (a.N >> 1) + T * 8 + c;
-        split1(act_fn(y, a.act) * up, a.ahi[ai], a.alo[ai]);
-      }
-    } else if (ROLE == kRoleQkv) {                  // [dims 8s+i | half + 8s + i], i < 8
-      const int half = a.dh >> 1;
-      const int gph = half >> 3;
-      const int hh = T / gph, sb = T % gph;
-      const bool lo = c < 8;
-      const int i = 8 * sb + (c & 7);
-      const int d = lo ? i : half + i;
-      const int pos = a.params[0] + r;
-      float out = y;
-      if (hh < a.nq + a.nkv) {
-        const float2 cs = e.cs;
-        const float partner = sh.y[r][c ^ 8] * sh.inv[r];
-        out = lo ? (y * cs.x - partner * cs.y) : (y * cs.x + partner * cs.y);
-      }
-      if (hh < a.nq) {
-        a.q_out[((size_t)r * a.nq + hh) * a.dh + d] = out;
-      } else {
-        const int kv = hh < a.nq + a.nkv ? 0 : 1;
-        const int head = hh - a.nq - kv * a.nkv;
-        const int page = e.page;
-        const size_t base = ((((size_t)a.layer * a.n_pages + page) * 2 + kv) * a.nkv + head) * kPage * a.dh;
-        // K rows are [slot][dh]; V is stored transposed inside the page, [dh][slot]
-        const size_t e = kv == 0 ? (size_t)(pos % kPage) * a.dh + d : (size_t)d * kPage + (pos % kPage);
-        a.kv_pool[base + e] = f2h(out);
-      }
-    } else {                                        // kRoleLmHead
-      const int n = T * 16 + c;
-      if (a.logits != nullptr) a.logits[(size_t)r * a.N + n] = y;
-      uint64_t b = argmax_key(y, (uint32_t)n);
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) b = umax64(b, __shfl_xor(b, o));
-      if (c == 0) atomicMax(&sh.best[r], (unsigned long long)b);
-    }
+    epi_element<ROLE>(a, T, r, c, e, sh.inv[r], [&](int cc) { return sh.y[r][cc]; }, &sh.best[r]);
   }
 }
 
@@ -906,12 +929,200 @@ hipError_t launch_gemm(const GemmArgs& a, int role, int grid, hipStream_t st) {
   }
 }
 
+// ------------------------------------------------------------ tiled GEMM (many rows)
+// The same sums as the weight-streaming kernels, for forwards of many rows
+// (prefill chunks).  Per output, chain w (w < S) adds chunks w, w + S,
+// w + 2S, ... in that order through one MFMA accumulator (hi plane before lo
+// plane), and the S chain sums are added in chain order: in the
+// weight-streaming kernel chain w is wave w and the chains meet in LDS; here
+// every wave runs all S chains in turn for its own output tile, keeping the
+// running chain sum in registers.  So all waves of a workgroup walk one
+// chunk sequence (chain 0's chunks, then chain 1's, ...) and share each
+// chunk's weights and activations through LDS, and each weight tile is read
+// from HBM once per row block instead of once per 64 rows.
+//
+// Workgroup: 4 waves and a tile of 128 rows x 8 items (128 outputs); wave
+// (wr, wc) owns rows 64 wr .. +63 and items 4 wc .. +3 (4 x 4 MFMA tiles).
+// One chunk per pipeline step: its activation planes (128 rows x 32 inputs,
+// stored in MFMA operand order) and its 8 weight tiles (1 KiB each, already
+// in operand order) are fetched to registers one step ahead and written to
+// the other of two LDS buffers; one barrier per step.  Rows past M read row
+// M - 1 (their MFMA columns are dropped) and items past N read the last item
+// (their outputs are not stored).
+constexpr int kTileRows = 128, kTileItems = 8;
+constexpr int kTileActVecs = kTileRows * 4;                       // 16-byte vectors of one plane of one step
+constexpr int kTileStepVecs = 2 * kTileActVecs + kTileItems * 64;  // hi, lo, weights: 1536 (24 KiB)
+
+struct TileShared {
+  float inv[kTileRows];
+  unsigned long long best[kTileRows];
+};
+
+struct TileRegs {   // one step of this thread's loads (plain members: they stay in registers)
+  uint4 h0, h1, l0, l1, w0, w1;
+};
+
+template <int ROLE>
+__global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a) {
+  __shared__ TileShared sh;
+  __shared__ uint4 lds[2 * kTileStepVecs];
+  prof_start(a.prof);
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int n_items = a.N >> 4;
+  const int n_rb = (a.M + kTileRows - 1) / kTileRows;
+  const int n_cb = (n_items + kTileItems - 1) / kTileItems;
+  // Workgroup -> (row block, column block).  Workgroups are dealt to the 8
+  // XCDs round-robin; each XCD gets a contiguous range of the column-major
+  // (column block, row block) order, so the row blocks of one column block
+  // run side by side on one XCD and read its weight tiles through one L2.
+  const int nblk = n_rb * n_cb;
+  const int q8 = nblk >> 3, rem = nblk & 7, xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+  const int lin = (xcd < rem ? xcd * (q8 + 1) : rem * (q8 + 1) + (xcd - rem) * q8) + loc;
+  const int cb = lin / n_rb, rb = lin % n_rb;
+  const int r0 = rb * kTileRows, T0 = cb * kTileItems;
+  const int KC = a.K >> 5, S = a.S, cpi = KC / S;
+
+  // this thread's vectors of a step: activation vector v = t + 256 i (row
+  // v / 4, inputs 8 (v % 4) ..) of each plane, weight vector t + 256 i
+  size_t asrc0, asrc1;
+  int adst0, adst1;
+  {
+    const int v0 = t, v1 = t + 256;
+    const int rr0 = v0 >> 2, rr1 = v1 >> 2;
+    asrc0 = (size_t)min(r0 + rr0, a.M - 1) * a.K + (v0 & 3) * 8;
+    asrc1 = (size_t)min(r0 + rr1, a.M - 1) * a.K + (v1 & 3) * 8;
+    adst0 = (rr0 >> 4) * 64 + (v0 & 3) * 16 + (rr0 & 15);
+    adst1 = (rr1 >> 4) * 64 + (v1 & 3) * 16 + (rr1 & 15);
+  }
+  const uint4* W4 = reinterpret_cast<const uint4*>(a.W);
+  const size_t wsrc0 = (size_t)min(T0 + (t >> 6), n_items - 1) * KC * 64 + (t & 63);
+  const size_t wsrc1 = (size_t)min(T0 + ((t + 256) >> 6), n_items - 1) * KC * 64 + (t & 63);
+  auto fetch = [&](int kc) {
+    TileRegs g;
+    const size_t ko = (size_t)kc * 32;
+    g.h0 = *reinterpret_cast<const uint4*>(a.bhi + asrc0 + ko);
+    g.h1 = *reinterpret_cast<const uint4*>(a.bhi + asrc1 + ko);
+    g.l0 = *reinterpret_cast<const uint4*>(a.blo + asrc0 + ko);
+    g.l1 = *reinterpret_cast<const uint4*>(a.blo + asrc1 + ko);
+    g.w0 = W4[wsrc0 + (size_t)kc * 64];
+    g.w1 = W4[wsrc1 + (size_t)kc * 64];
+    return g;
+  };
+  auto put = [&](int b, const TileRegs& g) {
+    uint4* B = lds + b * kTileStepVecs;
+    B[adst0] = g.h0;
+    B[adst1] = g.h1;
+    B[kTileActVecs + adst0] = g.l0;
+    B[kTileActVecs + adst1] = g.l1;
+    B[2 * kTileActVecs + t] = g.w0;
+    B[2 * kTileActVecs + 256 + t] = g.w1;
+  };
+
+  put(0, fetch(0));
+  if (norm_role(ROLE))
+    for (int rl = wave; rl < kTileRows; rl += 4) {
+      const float v = r0 + rl < a.M ? row_inv_rms(a, r0 + rl, lane) : 0.f;
+      if (lane == 0) sh.inv[rl] = v;
+    }
+  if (ROLE == kRoleLmHead && t < kTileRows) sh.best[t] = 0ull;
+  __syncthreads();
+
+  f32x4 acc[4][4], y[4][4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      y[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  int w = 0, c = 0;   // chain and position of the current step
+  for (int s = 0; s < KC; ++s) {
+    // next step's chunk (the last step fetches its own again: the loads stay unconditional)
+    const int wn = c + 1 == cpi ? w + 1 : w, cn = c + 1 == cpi ? 0 : c + 1;
+    const TileRegs g = fetch(s + 1 < KC ? wn + S * cn : w + S * c);
+    const uint4* B = lds + (s & 1) * kTileStepVecs;
+    uint4 A[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) A[ct] = B[2 * kTileActVecs + (wc * 4 + ct) * 64 + lane];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const BPair bp{B[(wr * 4 + rt) * 64 + lane], B[kTileActVecs + (wr * 4 + rt) * 64 + lane]};
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = mfma_pair(A[ct], bp, acc[rt][ct]);
+    }
+    if (c + 1 == cpi) {   // chain w complete: add it to the running sum in chain order
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          y[rt][ct] = w == 0 ? acc[rt][ct] : y[rt][ct] + acc[rt][ct];
+          acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    put((s + 1) & 1, g);
+    __syncthreads();
+    w = wn;
+    c = cn;
+  }
+
+  // Epilogue, two items per wave at a time: the wave's finished sums go to
+  // its own LDS slice [64 rows][2 items][16] (the stage buffers are free
+  // after the last barrier), then 16-lane groups run the shared element
+  // epilogue row by row.
+  float* ys = reinterpret_cast<float*>(lds) + wave * 2048;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const f32x4 v = y[rt][2 * p + c2];
+        *reinterpret_cast<float4*>(ys + ((rt * 16 + (lane & 15)) * 2 + c2) * 16 + 4 * (lane >> 4)) =
+            make_float4(v.x, v.y, v.z, v.w);
+      }
+    __syncthreads();
+    for (int it = 0; it < 32; ++it) {
+      const int idx = it * 64 + lane;
+      const int c2 = idx >> 10, rl = (idx >> 4) & 63, cc = idx & 15;
+      const int r = r0 + wr * 64 + rl, T = T0 + wc * 4 + 2 * p + c2;
+      if (r < a.M && T < n_items) {
+        const float* yr = ys + (rl * 2 + c2) * 16;
+        const int rs = wr * 64 + rl;
+        epi_element<ROLE>(a, T, r, cc, epi_load<ROLE>(a, T, r * 16 + cc), sh.inv[rs],
+                          [&](int k) { return yr[k]; }, &sh.best[rs]);
+      }
+    }
+    __syncthreads();
+  }
+  if (ROLE == kRoleLmHead && t < kTileRows && r0 + t < a.M) atomicMax(a.best + r0 + t, sh.best[t]);
+  prof_end(a.prof);
+}
+
+hipError_t launch_gemm_tiled(const GemmArgs& a, int role, hipStream_t st) {
+  if (a.M < 1 || a.S < 1 || a.N % 16 || a.fmt != 0 || a.K % (32 * a.S)) return hipErrorInvalidValue;
+  const int n_items = a.N >> 4;
+  const int nblk = ((a.M + kTileRows - 1) / kTileRows) * ((n_items + kTileItems - 1) / kTileItems);
+  const dim3 grid(nblk), block(256);
+  switch (role) {
+    case kRoleQkv: hipLaunchKernelGGL(k_gemm_tiled<kRoleQkv>, grid, block, 0, st, a); break;
+    case kRoleO: hipLaunchKernelGGL(k_gemm_tiled<kRoleO>, grid, block, 0, st, a); break;
+    case kRoleGateUp: hipLaunchKernelGGL(k_gemm_tiled<kRoleGateUp>, grid, block, 0, st, a); break;
+    case kRoleDown: hipLaunchKernelGGL(k_gemm_tiled<kRoleDown>, grid, block, 0, st, a); break;
+    case kRoleLmHead: hipLaunchKernelGGL(k_gemm_tiled<kRoleLmHead>, grid, block, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------ attention
 // Split plan of one row, a function of its own ctx only: nb = ceil(ctx/64)
-// blocks of 64 absolute positions, bps = ceil(nb / 32) blocks per split,
+// blocks of 64 absolute positions, bps = ceil(nb / 128) blocks per split,
 // ns = ceil(nb / bps) splits; split i covers positions
-// [64 i bps, min(64 (i+1) bps, ctx)).  Short contexts get one block per
-// split, long ones at most 32 splits.
+// [64 i bps, min(64 (i+1) bps, ctx)).  Contexts up to 8192 get one block per
+// split, longer ones at most 128 splits (a 32K context: 128 splits of 4
+// blocks), so a long row still spreads over many waves.
 __host__ __device__ __forceinline__ int attn_bps(int ctx) {
   const int nb = (ctx + kAttnBlock - 1) / kAttnBlock;
   return (nb + kAttnMaxSplits - 1) / kAttnMaxSplits;
@@ -922,7 +1133,14 @@ __host__ __device__ __forceinline__ int attn_ns(int ctx) {
   return (nb + bps - 1) / bps;
 }
 int attn_splits(int ctx) { return attn_ns(ctx); }
-bool attn_needs_combine(int kv_len, int M) { return attn_ns(kv_len + M) > 1; }
+// The split count is not monotone in ctx (ctx 8192: 128 one-block splits;
+// ctx 8193: 65 two-block splits), so a launch covers the most splits of any
+// of its rows, not those of its longest row.
+int attn_splits_max(int kv_len, int M) {
+  int n = 1;
+  for (int r = 0; r < M; ++r) n = max(n, attn_ns(kv_len + r + 1));
+  return n;
+}
 
 // Fold of a row's split partials (m_i, l_i, o_i), in split order:
 //   (M, L, O) = (m_0, l_0, o_0);  for i >= 1: M' = max(M, m_i),
@@ -974,6 +1192,152 @@ struct AttnUnitLds {
   float o[16][DH + 4];   // padded rows: the 16 lanes of a wave's stores hit different banks
 };
 
+// Physical pages of the 4 logical pages of block b: one 16-byte load of
+// consecutive page-table entries (the table is 16-byte aligned); a block
+// overhanging max_ctx (its positions are masked) reads clamped entries.
+__device__ __forceinline__ int4 attn_block_pages(const AttnArgs& a, int b) {
+  int4 q;
+  if (4 * b + 4 <= a.n_lpages) {
+    q = *reinterpret_cast<const int4*>(a.page_table + 4 * b);
+  } else {
+    const int last = a.n_lpages - 1;
+    q = make_int4(a.page_table[min(4 * b, last)], a.page_table[min(4 * b + 1, last)],
+                  a.page_table[min(4 * b + 2, last)], a.page_table[min(4 * b + 3, last)]);
+  }
+  return q;
+}
+
+// MFMA operands of one block of 64 positions for KV head h.
+template <int DH>
+struct AttnKV {
+  uint4 k[4][DH / 32];          // lane (g, j): K[pos = 64b + 16pt + j][32c + 8g .. +7], one page per pt
+  uint2 vlo[DH / 16][2];        // V^T of chunk ks: positions {32ks + 4g .. +3} of d = 16dt + j
+  uint2 vhi[DH / 16][2];        //                  positions {32ks + 16 + 4g .. +3}
+};
+
+template <int DH>
+__device__ __forceinline__ void attn_load_kv(const AttnArgs& a, int h, int j, int g, int4 pq, AttnKV<DH>& kv) {
+  constexpr int DC = DH / 32, DT = DH / 16;
+  const size_t layer_base = (size_t)a.layer * a.n_pages;
+  const size_t page_elems = (size_t)kPage * DH;
+  // element offset of (page, kv) for this KV head
+  auto page_base = [&](int page, int w) { return (((layer_base + page) * 2 + w) * a.nkv + h) * page_elems; };
+  const int pg[4] = {__builtin_amdgcn_readfirstlane(pq.x), __builtin_amdgcn_readfirstlane(pq.y),
+                     __builtin_amdgcn_readfirstlane(pq.z), __builtin_amdgcn_readfirstlane(pq.w)};
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt) {
+    const uint16_t* kb = a.kv_pool + page_base(pg[pt], 0) + (size_t)j * DH + g * 8;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) kv.k[pt][c] = *reinterpret_cast<const uint4*>(kb + c * 32);
+  }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const uint16_t* va = a.kv_pool + page_base(pg[2 * ks], 1) + g * 4;
+    const uint16_t* vb = a.kv_pool + page_base(pg[2 * ks + 1], 1) + g * 4;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      kv.vlo[dt][ks] = *reinterpret_cast<const uint2*>(va + (size_t)(dt * 16 + j) * kPage);
+      kv.vhi[dt][ks] = *reinterpret_cast<const uint2*>(vb + (size_t)(dt * 16 + j) * kPage);
+    }
+  }
+}
+
+// One block b of a unit: scores, mask to the lane's row range [lo, hi),
+// online-softmax update of (m, l, o).  Both attention kernels run exactly
+// this sequence of operations.
+template <int DH>
+__device__ __forceinline__ void attn_block_step(const AttnArgs& a, const AttnKV<DH>& kv, const BPair (&qop)[DH / 32],
+                                                int b, int g, int lo, int hi, int ctx_max, float& m, float& l,
+                                                f32x4 (&o)[DH / 16]) {
+  constexpr int DC = DH / 32, DT = DH / 16;
+  f32x4 sc[4];
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < DC; ++c) acc = mfma_pair_f16(kv.k[pt][c], qop[c], acc);
+    sc[pt] = acc;
+  }
+  // lane (g, j) holds scores of q-row j at positions 64b + 16pt + 4g + v
+  float s[16];
+  float bmax = -INFINITY;
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int tpos = b * kAttnBlock + pt * 16 + 4 * g + v;
+      const float sv = sc[pt][v] * a.scale_log2;
+      s[pt * 4 + v] = (tpos >= lo && tpos < hi) ? sv : -INFINITY;
+      bmax = fmaxf(bmax, s[pt * 4 + v]);
+    }
+  bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+  bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+  const float mn = fmaxf(m, bmax);
+  const float alpha = (mn == -INFINITY) ? 1.0f : exp2f(m - mn);
+  uint16_t pb[16], pl[16];
+  float psum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float pv = (s[e] == -INFINITY) ? 0.f : exp2f(s[e] - mn);
+    pb[e] = f2h(pv);
+    pl[e] = f2h(pv - h2f(pb[e]));
+    psum = psum + pv;
+  }
+  psum = psum + __shfl_xor(psum, 16);
+  psum = psum + __shfl_xor(psum, 32);
+  l = l * alpha + psum;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    o[dt].x = o[dt].x * alpha; o[dt].y = o[dt].y * alpha;
+    o[dt].z = o[dt].z * alpha; o[dt].w = o[dt].w * alpha;
+  }
+  // zero V elements at positions >= kv_len + M (never written in this cache)
+  auto vmask = [&](uint2 v, int pos0) {
+    const int n_ok = ctx_max - pos0;               // valid elements among pos0 .. pos0 + 3
+    if (n_ok >= 4) return v;
+    if (n_ok <= 0) return make_uint2(0u, 0u);
+    const uint32_t m0 = n_ok >= 2 ? 0xffffffffu : 0x0000ffffu;
+    const uint32_t m1 = n_ok >= 4 ? 0xffffffffu : (n_ok == 3 ? 0x0000ffffu : 0u);
+    return make_uint2(v.x & m0, v.y & m1);
+  };
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int pa = 2 * ks, pbt = 2 * ks + 1;
+    BPair Bp;
+    Bp.hi = make_uint4(pack2(pb[pa * 4 + 0], pb[pa * 4 + 1]), pack2(pb[pa * 4 + 2], pb[pa * 4 + 3]),
+                       pack2(pb[pbt * 4 + 0], pb[pbt * 4 + 1]), pack2(pb[pbt * 4 + 2], pb[pbt * 4 + 3]));
+    Bp.lo = make_uint4(pack2(pl[pa * 4 + 0], pl[pa * 4 + 1]), pack2(pl[pa * 4 + 2], pl[pa * 4 + 3]),
+                       pack2(pl[pbt * 4 + 0], pl[pbt * 4 + 1]), pack2(pl[pbt * 4 + 2], pl[pbt * 4 + 3]));
+    const int p0 = b * kAttnBlock + pa * 16 + 4 * g, p1 = b * kAttnBlock + pbt * 16 + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint2 v0 = vmask(kv.vlo[dt][ks], p0), v1 = vmask(kv.vhi[dt][ks], p1);
+      o[dt] = mfma_pair_f16(make_uint4(v0.x, v0.y, v1.x, v1.y), Bp, o[dt]);
+    }
+  }
+  m = mn;
+}
+
+// Rows of q tile qt whose ranges make up a unit: r0 .. r1.
+__device__ __forceinline__ void attn_tile_rows(int qt, int G, int M, int& r0, int& r1) {
+  r0 = (qt * 16) / G;
+  r1 = min((qt * 16 + 15) / G, M - 1);
+}
+
+// Union of the tile rows' ranges of split sp, in whole blocks [b_lo, b_hi)
+// (wave-uniform; empty when no row of the tile has that split).
+__device__ __forceinline__ void attn_split_union(int kv_len, int r0, int r1, int sp, int& b_lo, int& b_hi) {
+  b_lo = 0x7fffffff;
+  b_hi = 0;
+  for (int rr = r0; rr <= r1; ++rr) {
+    const int c = kv_len + rr + 1;
+    if (sp >= attn_ns(c)) continue;
+    const int bps = attn_bps(c);
+    b_lo = min(b_lo, sp * bps);
+    b_hi = max(b_hi, (min((sp + 1) * bps * kAttnBlock, c) + kAttnBlock - 1) / kAttnBlock);
+  }
+}
+
 template <int DH>
 __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   constexpr int DC = DH / 32;            // d chunks of the score MFMA
@@ -981,14 +1345,30 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   __shared__ AttnUnitLds<DH> ul[kAttnLdsUnits];
 
   prof_start(a.prof);
-  const int h = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int G = a.nq / a.nkv;
   const int n_qr = a.M * G;
   const int n_qt = (n_qr + 15) >> 4;
-  const int qt = blockIdx.x % n_qt;
-  const int s_lo = (blockIdx.x / n_qt) * a.spw;
+  // Workgroup -> (q tile, split group, KV head).  Workgroups are dealt to the
+  // 8 XCDs round-robin in launch order; when the (split group, head) units
+  // come in multiples of 8, the q tiles of one unit are placed 8 apart so
+  // they run on the same XCD and read the unit's K/V through one L2.
+  const int n_sg = (a.n_split + a.spw - 1) / a.spw;
+  const int n_units = n_sg * a.nkv;
+  const int lid = blockIdx.x + n_qt * n_sg * blockIdx.y;
+  int qt, sg, h;
+  if (n_qt > 1 && (n_units & 7) == 0) {
+    qt = (lid >> 3) % n_qt;
+    const int u = (lid / (8 * n_qt)) * 8 + (lid & 7);
+    sg = u % n_sg;
+    h = u / n_sg;
+  } else {
+    qt = blockIdx.x % n_qt;
+    sg = blockIdx.x / n_qt;
+    h = blockIdx.y;
+  }
+  const int s_lo = sg * a.spw;
   const int s_hi = min(s_lo + a.spw, a.n_split);
   // this lane's q-row (independent of kv_len: its q loads go out first)
   const int qr = qt * 16 + j;
@@ -1001,31 +1381,14 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
     for (int c = 0; c < DC; ++c) { qraw[c][0] = qp[c * 8]; qraw[c][1] = qp[c * 8 + 1]; }
   }
-  // physical pages of the 4 logical pages of block b: one 16-byte load of
-  // consecutive page-table entries (the table is 16-byte aligned); a block
-  // overhanging max_ctx (its positions are masked) reads clamped entries
-  auto block_pages = [&](int b) {
-    int4 q;
-    if (4 * b + 4 <= a.n_lpages) {
-      q = *reinterpret_cast<const int4*>(a.page_table + 4 * b);
-    } else {
-      const int last = a.n_lpages - 1;
-      q = make_int4(a.page_table[min(4 * b, last)], a.page_table[min(4 * b + 1, last)],
-                    a.page_table[min(4 * b + 2, last)], a.page_table[min(4 * b + 3, last)]);
-    }
-    return q;
-  };
+  auto block_pages = [&](int b) { return attn_block_pages(a, b); };
   // the first unit's first block is its split index whenever splits are one
-  // block (contexts up to 2048): fetch its pages before the context length is known
+  // block (contexts up to 8192): fetch its pages before the context length is known
   const int b_guess = s_lo + wave;
   int4 pq_guess = block_pages(b_guess);
   const int kv_len = a.params[0];
   const int ctx_max = kv_len + a.M;
   const int ctx = kv_len + r + 1;
-  const size_t layer_base = (size_t)a.layer * a.n_pages;
-  const size_t page_elems = (size_t)kPage * DH;
-  // element offset of (page, kv) for this KV head
-  auto page_base = [&](int page, int kv) { return (((layer_base + page) * 2 + kv) * a.nkv + h) * page_elems; };
   BPair qop[DC];
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
@@ -1042,16 +1405,11 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       hi = min((sp + 1) * bps * kAttnBlock, ctx);
     }
     // union of the tile's rows' ranges (wave-uniform), in whole blocks
-    int b_lo = 0x7fffffff, b_hi = 0;
+    int b_lo, b_hi;
     {
-      const int r0 = (qt * 16) / G, r1 = min((qt * 16 + 15) / G, a.M - 1);
-      for (int rr = r0; rr <= r1; ++rr) {
-        const int c = kv_len + rr + 1;
-        if (sp >= attn_ns(c)) continue;
-        const int bps = attn_bps(c);
-        b_lo = min(b_lo, sp * bps);
-        b_hi = max(b_hi, (min((sp + 1) * bps * kAttnBlock, c) + kAttnBlock - 1) / kAttnBlock);
-      }
+      int r0, r1;
+      attn_tile_rows(qt, G, a.M, r0, r1);
+      attn_split_union(kv_len, r0, r1, sp, b_lo, b_hi);
     }
     f32x4 o[DT];
 #pragma unroll
@@ -1060,95 +1418,10 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
 
     int4 pq = (b_lo == b_guess) ? pq_guess : block_pages(b_lo < b_hi ? b_lo : 0);
     for (int b = b_lo; b < b_hi; ++b) {
-      // K operand: lane (g, j) holds K[pos = 64b + 16pt + j][32c + 8g .. +7]; one page per pt
-      uint4 kop[4][DC];
-      // V^T operand of chunk ks: positions {32ks + 4g .. +3} and {32ks + 16 + 4g .. +3} of d = 16dt + j
-      uint2 vlo[DT][2], vhi[DT][2];
-      const int pg[4] = {__builtin_amdgcn_readfirstlane(pq.x), __builtin_amdgcn_readfirstlane(pq.y),
-                         __builtin_amdgcn_readfirstlane(pq.z), __builtin_amdgcn_readfirstlane(pq.w)};
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        const uint16_t* kb = a.kv_pool + page_base(pg[pt], 0) + (size_t)j * DH + g * 8;
-#pragma unroll
-        for (int c = 0; c < DC; ++c) kop[pt][c] = *reinterpret_cast<const uint4*>(kb + c * 32);
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const uint16_t* va = a.kv_pool + page_base(pg[2 * ks], 1) + g * 4;
-        const uint16_t* vb = a.kv_pool + page_base(pg[2 * ks + 1], 1) + g * 4;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          vlo[dt][ks] = *reinterpret_cast<const uint2*>(va + (size_t)(dt * 16 + j) * kPage);
-          vhi[dt][ks] = *reinterpret_cast<const uint2*>(vb + (size_t)(dt * 16 + j) * kPage);
-        }
-      }
+      AttnKV<DH> kv;
+      attn_load_kv<DH>(a, h, j, g, pq, kv);
       pq = block_pages(b + 1 < b_hi ? b + 1 : b);   // next block's pages, in flight during this block
-      f32x4 sc[4];
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < DC; ++c) acc = mfma_pair_f16(kop[pt][c], qop[c], acc);
-        sc[pt] = acc;
-      }
-      // lane (g, j) holds scores of q-row j at positions 64b + 16pt + 4g + v
-      float s[16];
-      float bmax = -INFINITY;
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int tpos = b * kAttnBlock + pt * 16 + 4 * g + v;
-          const float sv = sc[pt][v] * a.scale_log2;
-          s[pt * 4 + v] = (tpos >= lo && tpos < hi) ? sv : -INFINITY;
-          bmax = fmaxf(bmax, s[pt * 4 + v]);
-        }
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-      const float mn = fmaxf(m, bmax);
-      const float alpha = (mn == -INFINITY) ? 1.0f : exp2f(m - mn);
-      uint16_t pb[16], pl[16];
-      float psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pv = (s[e] == -INFINITY) ? 0.f : exp2f(s[e] - mn);
-        pb[e] = f2h(pv);
-        pl[e] = f2h(pv - h2f(pb[e]));
-        psum = psum + pv;
-      }
-      psum = psum + __shfl_xor(psum, 16);
-      psum = psum + __shfl_xor(psum, 32);
-      l = l * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        o[dt].x = o[dt].x * alpha; o[dt].y = o[dt].y * alpha;
-        o[dt].z = o[dt].z * alpha; o[dt].w = o[dt].w * alpha;
-      }
-      // zero V elements at positions >= kv_len + M (never written in this cache)
-      auto vmask = [&](uint2 v, int pos0) {
-        const int n_ok = ctx_max - pos0;               // valid elements among pos0 .. pos0 + 3
-        if (n_ok >= 4) return v;
-        if (n_ok <= 0) return make_uint2(0u, 0u);
-        const uint32_t m0 = n_ok >= 2 ? 0xffffffffu : 0x0000ffffu;
-        const uint32_t m1 = n_ok >= 4 ? 0xffffffffu : (n_ok == 3 ? 0x0000ffffu : 0u);
-        return make_uint2(v.x & m0, v.y & m1);
-      };
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int pa = 2 * ks, pbt = 2 * ks + 1;
-        BPair Bp;
-        Bp.hi = make_uint4(pack2(pb[pa * 4 + 0], pb[pa * 4 + 1]), pack2(pb[pa * 4 + 2], pb[pa * 4 + 3]),
-                           pack2(pb[pbt * 4 + 0], pb[pbt * 4 + 1]), pack2(pb[pbt * 4 + 2], pb[pbt * 4 + 3]));
-        Bp.lo = make_uint4(pack2(pl[pa * 4 + 0], pl[pa * 4 + 1]), pack2(pl[pa * 4 + 2], pl[pa * 4 + 3]),
-                           pack2(pl[pbt * 4 + 0], pl[pbt * 4 + 1]), pack2(pl[pbt * 4 + 2], pl[pbt * 4 + 3]));
-        const int p0 = b * kAttnBlock + pa * 16 + 4 * g, p1 = b * kAttnBlock + pbt * 16 + 4 * g;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const uint2 v0 = vmask(vlo[dt][ks], p0), v1 = vmask(vhi[dt][ks], p1);
-          o[dt] = mfma_pair_f16(make_uint4(v0.x, v0.y, v1.x, v1.y), Bp, o[dt]);
-        }
-      }
-      m = mn;
+      attn_block_step<DH>(a, kv, qop, b, g, lo, hi, ctx_max, m, l, o);
     }
 
     // lane (g, j) holds o of q-row j for d = 16dt + 4g + v
@@ -1159,7 +1432,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       for (int dt = 0; dt < DT; ++dt)
         *reinterpret_cast<float4*>(&U.o[j][dt * 16 + 4 * g]) = make_float4(o[dt].x, o[dt].y, o[dt].z, o[dt].w);
     } else if (have && hi > lo) {
-      float* part = a.part + (((size_t)r * a.nq + head) * kAttnMaxSplits + sp) * (DH + 4);
+      float* part = a.part + (((size_t)r * a.nq + head) * a.part_splits + sp) * (DH + 4);
       if (g == 0) { part[0] = m; part[1] = l; }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -1202,25 +1475,126 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   }
 }
 
-// Fold of the global partials of row r, query head j (record [m, l, -, -, o[dh]]).
+// Attention for forwards of many rows (prefill chunks): one wave per
+// (q tile, KV head) runs every split of its rows in split order.  Each
+// split's (m, l, o) comes from the same block steps as in k_attn_mfma and is
+// folded into the row's running result as soon as it is done, with the fold
+// arithmetic of the split kernels (split 0 first; then M' = max(M, m_i),
+// L = L 2^(M - M') + l_i 2^(m_i - M'), O likewise), so a row's bits equal
+// those the split kernels give it, with no partial buffer and no combine
+// pass.  Parallelism comes from the many q tiles instead of the splits.
 template <int DH>
-__global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
-  constexpr int PER = DH / 64;
-  const int j = blockIdx.x, r = blockIdx.y, lane = threadIdx.x;
-  const int ns = attn_ns(a.params[0] + r + 1);
-  const float* base = a.part + ((size_t)r * a.nq + j) * kAttnMaxSplits * (DH + 4);
-  Fold f[PER];
+__global__ __launch_bounds__(256) void k_attn_rows(AttnArgs a) {
+  constexpr int DC = DH / 32, DT = DH / 16;
+  prof_start(a.prof);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int j = lane & 15, g = lane >> 4;
+  const int G = a.nq / a.nkv;
+  const int n_qr = a.M * G;
+  const int n_qt = (n_qr + 15) >> 4;
+  const int h = blockIdx.y;
+  const int qt = blockIdx.x * 4 + wave;
+  if (qt < n_qt) {   // wave-uniform
+    const int qr = qt * 16 + j;
+    const bool have = qr < n_qr;
+    const int r = have ? qr / G : 0;
+    const int head = h * G + (have ? qr % G : 0);
+    BPair qop[DC];
+    {
+      const float4* qp = reinterpret_cast<const float4*>(a.q + ((size_t)r * a.nq + head) * DH + g * 8);
 #pragma unroll
-  for (int e = 0; e < PER; ++e) f[e].first(base[0], base[1], base[4 + lane * PER + e]);
-  for (int i = 1; i < ns; ++i) {
-    const float* p = base + (size_t)i * (DH + 4);
+      for (int c = 0; c < DC; ++c) {
+        const float4 q0 = qp[c * 8], q1 = qp[c * 8 + 1];
+        const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        qop[c] = have ? split8_f16(qv) : bzero();
+      }
+    }
+    const int kv_len = a.params[0];
+    const int ctx_max = kv_len + a.M;
+    const int ctx = kv_len + r + 1;
+    const int ns_row = attn_ns(ctx);
+    int r0, r1;
+    attn_tile_rows(qt, G, a.M, r0, r1);
+    int ns_max = 1;
+    for (int rr = r0; rr <= r1; ++rr) ns_max = max(ns_max, attn_ns(kv_len + rr + 1));
+
+    float fm = 0.f, fl = 0.f;
+    f32x4 fo[DT];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) f[e].add(p[0], p[1], p[4 + lane * PER + e]);
+    for (int dt = 0; dt < DT; ++dt) fo[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < ns_max; ++sp) {
+      int lo = 0, hi = 0;
+      if (have && sp < ns_row) {
+        const int bps = attn_bps(ctx);
+        lo = sp * bps * kAttnBlock;
+        hi = min((sp + 1) * bps * kAttnBlock, ctx);
+      }
+      int b_lo, b_hi;
+      attn_split_union(kv_len, r0, r1, sp, b_lo, b_hi);
+      f32x4 o[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      float m = -INFINITY, l = 0.f;
+      int4 pq = attn_block_pages(a, b_lo < b_hi ? b_lo : 0);
+      for (int b = b_lo; b < b_hi; ++b) {
+        AttnKV<DH> kv;
+        attn_load_kv<DH>(a, h, j, g, pq, kv);
+        pq = attn_block_pages(a, b + 1 < b_hi ? b + 1 : b);
+        attn_block_step<DH>(a, kv, qop, b, g, lo, hi, ctx_max, m, l, o);
+      }
+      if (sp == 0) {
+        fm = m;
+        fl = l;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) fo[dt] = o[dt];
+      } else if (sp < ns_row) {
+        const float mn = fmaxf(fm, m);
+        const float wa = exp2f(fm - mn), wb = exp2f(m - mn);
+        fl = fl * wa + l * wb;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          fo[dt].x = fo[dt].x * wa + o[dt].x * wb; fo[dt].y = fo[dt].y * wa + o[dt].y * wb;
+          fo[dt].z = fo[dt].z * wa + o[dt].z * wb; fo[dt].w = fo[dt].w * wa + o[dt].w * wb;
+        }
+        fm = mn;
+      }
+    }
+    if (have) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const float ov[4] = {fo[dt].x, fo[dt].y, fo[dt].z, fo[dt].w};
+        uint16_t hb[4], lb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split1(ov[e] / fl, hb[e], lb[e]);
+        const size_t oi = ((size_t)r * a.nq + head) * DH + dt * 16 + 4 * g;
+        *reinterpret_cast<uint2*>(a.ohi + oi) = make_uint2(pack2(hb[0], hb[1]), pack2(hb[2], hb[3]));
+        *reinterpret_cast<uint2*>(a.olo + oi) = make_uint2(pack2(lb[0], lb[1]), pack2(lb[2], lb[3]));
+      }
+    }
   }
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const size_t oi = (size_t)r * a.nq * DH + (size_t)j * DH + lane * PER + e;
-    split1(f[e].o / f[e].l, a.ohi[oi], a.olo[oi]);
+  prof_end(a.prof);
+}
+
+// Fold of the global partials of row r, query head j (record [m, l, -, -, o[dh]]):
+// the row's records are staged in LDS with coalesced 16-byte loads (a long
+// context has up to 128 of them), then thread d folds output d in split order.
+template <int DH>
+__global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
+  __shared__ float4 rec[kAttnMaxSplits * (DH + 4) / 4];
+  const int j = blockIdx.x, r = blockIdx.y;
+  const int ns = attn_ns(a.params[0] + r + 1);
+  const float4* base = reinterpret_cast<const float4*>(a.part + ((size_t)r * a.nq + j) * a.part_splits * (DH + 4));
+  const int n4 = ns * ((DH + 4) / 4);
+  for (int i = threadIdx.x; i < n4; i += blockDim.x) rec[i] = base[i];
+  __syncthreads();
+  const float* p = reinterpret_cast<const float*>(rec);
+  const int d = threadIdx.x;
+  if (d < DH) {
+    Fold f;
+    f.first(p[0], p[1], p[4 + d]);
+    for (int i = 1; i < ns; ++i) f.add(p[i * (DH + 4)], p[i * (DH + 4) + 1], p[i * (DH + 4) + 4 + d]);
+    const size_t oi = (size_t)r * a.nq * DH + (size_t)j * DH + d;
+    split1(f.o / f.l, a.ohi[oi], a.olo[oi]);
   }
   prof_end(a.prof);
 }
@@ -1228,7 +1602,8 @@ __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
 hipError_t launch_attention(const AttnArgs& a_in, hipStream_t st) {
   AttnArgs a = a_in;
   const int G = a.nq / a.nkv;
-  if (a.M * G > kAttnQRows || a.n_split < 1 || a.n_split > kAttnMaxSplits || a.n_lpages < 1)
+  if (a.M * G > kAttnQRows || a.n_split < 1 || a.n_split > kAttnMaxSplits || a.n_lpages < 1 ||
+      (a.n_split > kAttnLdsUnits && a.n_split > a.part_splits))
     return hipErrorInvalidValue;
   const int n_qt = (a.M * G + 15) / 16;
   a.final_fold = a.n_split <= kAttnLdsUnits ? 1 : 0;
@@ -1236,13 +1611,23 @@ hipError_t launch_attention(const AttnArgs& a_in, hipStream_t st) {
   const int n_wg = n_qt * ((a.n_split + a.spw - 1) / a.spw);
   if (a.dh == 128) {
     hipLaunchKernelGGL(k_attn_mfma<128>, dim3(n_wg, a.nkv), dim3(512), 0, st, a);
-    if (!a.final_fold) hipLaunchKernelGGL(k_attn_combine<128>, dim3(a.nq, a.M), dim3(64), 0, st, a);
+    if (!a.final_fold) hipLaunchKernelGGL(k_attn_combine<128>, dim3(a.nq, a.M), dim3(256), 0, st, a);
   } else if (a.dh == 64) {
     hipLaunchKernelGGL(k_attn_mfma<64>, dim3(n_wg, a.nkv), dim3(512), 0, st, a);
-    if (!a.final_fold) hipLaunchKernelGGL(k_attn_combine<64>, dim3(a.nq, a.M), dim3(64), 0, st, a);
+    if (!a.final_fold) hipLaunchKernelGGL(k_attn_combine<64>, dim3(a.nq, a.M), dim3(256), 0, st, a);
   } else {
     return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_rows(const AttnArgs& a, hipStream_t st) {
+  if (a.M < 1 || a.n_lpages < 1 || a.nkv < 1 || a.nq % a.nkv) return hipErrorInvalidValue;
+  const int n_qt = (a.M * (a.nq / a.nkv) + 15) / 16;
+  const dim3 grid((n_qt + 3) / 4, a.nkv), block(256);
+  if (a.dh == 128) hipLaunchKernelGGL(k_attn_rows<128>, grid, block, 0, st, a);
+  else if (a.dh == 64) hipLaunchKernelGGL(k_attn_rows<64>, grid, block, 0, st, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -1291,10 +1676,12 @@ hipError_t launch_embed(const int* params, int M, const void* embed, int vocab, 
 __global__ __launch_bounds__(64) void k_accept(const int* params, int M, int verify, const unsigned long long* best,
                                                int* result) {
   const int lane = threadIdx.x;
-  const int a_r = lane < M ? (int)(0xffffffffu - (uint32_t)(best[lane] & 0xffffffffu)) : 0;
+  auto id_of = [&](int r) { return (int)(0xffffffffu - (uint32_t)(best[r] & 0xffffffffu)); };
+  const int a_r = lane < M ? id_of(lane) : 0;
   if (lane < M) result[2 + lane] = a_r;
+  for (int r = 64 + lane; r < M; r += 64) result[2 + r] = id_of(r);   // rows past 64 (prefill forwards)
   int n;
-  if (verify) {
+  if (verify) {   // M <= 64
     const int k = M - 1;
     const bool miss = lane < k && params[2 + lane + 1] != a_r;
     const unsigned long long mask = __ballot(miss);
@@ -1302,13 +1689,13 @@ __global__ __launch_bounds__(64) void k_accept(const int* params, int M, int ver
   } else {
     n = M - 1;
   }
-  const int next = __shfl(a_r, n);
+  const int next = n < 64 ? __shfl(a_r, n) : id_of(n);
   if (lane == 0) { result[0] = n; result[1] = next; }
 }
 
 hipError_t launch_accept(const int* params, int M, int verify, const unsigned long long* best, int* result,
                          hipStream_t st) {
-  if (M < 1 || M > 64) return hipErrorInvalidValue;
+  if (M < 1 || (verify && M > 64)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_accept, dim3(1), dim3(64), 0, st, params, M, verify, best, result);
   return hipGetLastError();
 }

@@ -25,6 +25,7 @@ struct GemmPlan {
 };
 
 struct Layout {
+  int rows = 0;   // most rows of one forward: 64, or max_prefill_rows when larger
   size_t params = 0, x = 0, ss = 0, q = 0, attn_part = 0, uplanes = 0, oplanes = 0, aplanes = 0, best = 0,
          result = 0, logits = 0, rope = 0, prof = 0, total = 0;
   int max_split = 1;
@@ -54,6 +55,7 @@ bool valid_config(const sv_config& c) {
   if (c.weight_fmt == 1 && (c.d_model % 512 || (c.n_q_heads * c.head_dim) % 512 || c.d_ff % 512)) return false;
   if (c.page_size != kPage || c.max_ctx < kPage || c.max_ctx % kPage) return false;
   if (c.max_k < 0 || c.max_k > kMaxRows - 1) return false;
+  if (c.max_prefill_rows != 0 && (c.max_prefill_rows <= kMaxRows || c.max_prefill_rows > kMaxPrefillRows)) return false;
   if (!(c.rms_eps > 0.f) || !(c.rope_theta > 1.f)) return false;
   return true;
 }
@@ -99,6 +101,7 @@ int max_rows(const sv_config& c, const Plans& p) {
 bool plans_ok(const sv_config& c, const Plans& p) {
   for (const GemmPlan* g : {&p.qkv, &p.o, &p.gu, &p.d, &p.lm})
     if (g->S < 1) return false;
+  if (c.max_prefill_rows > 0 && c.weight_fmt != 0) return false;   // tiled kernels: bf16 weights only
   return c.max_k + 1 <= max_rows(c, p);
 }
 
@@ -111,25 +114,29 @@ int prof_pairs(const sv_config& c) { return kProfRoles * c.n_layers; }
 
 Layout make_layout(const sv_config& c, const Plans& p) {
   Layout L;
-  const size_t R = kMaxRows;
+  L.rows = std::max(kMaxRows, (int)c.max_prefill_rows);
+  const size_t R = L.rows;
   const int qd = c.n_q_heads * c.head_dim;
-  L.max_split = kAttnMaxSplits;
+  // most splits any row of this context can have: one block per split up to
+  // kAttnMaxSplits blocks, never more than kAttnMaxSplits
+  L.max_split = std::min((c.max_ctx + kAttnBlock - 1) / kAttnBlock, kAttnMaxSplits);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
     off = align_up(off + bytes, 256);
     return o;
   };
-  L.params = take(sizeof(int) * kParamInts);
+  L.params = take(sizeof(int) * (2 + R));
   L.x = take(R * c.d_model * 4);
   L.ss = take(R * (c.d_model / 16) * 4);
   L.q = take(R * qd * 4);
-  L.attn_part = take(R * c.n_q_heads * (size_t)L.max_split * (c.head_dim + 4) * 4);
+  // split partials: only forwards of at most 64 rows use the split kernels
+  L.attn_part = take((size_t)kMaxRows * c.n_q_heads * (size_t)L.max_split * (c.head_dim + 4) * 4);
   L.uplanes = take(2 * R * c.d_model * 2);   // hi, lo planes of x * g (RMSNorm consumers' input)
   L.oplanes = take(2 * R * qd * 2);          // attention output
   L.aplanes = take(2 * R * c.d_ff * 2);      // act(gate) * up
   L.best = take(R * 8);
-  L.result = take(sizeof(int) * (2 + kMaxRows));
+  L.result = take(sizeof(int) * (2 + R));
   L.logits = take(R * (size_t)c.vocab * 4);
   L.rope = take((size_t)c.max_ctx * (c.head_dim / 2) * 8);
   L.prof = take(prof_pairs(c) * 16);
@@ -161,7 +168,7 @@ struct sv_ctx {
   int store_logits = 0;
   int last_rows = 0;
   int last_stored_logits = 0;
-  int last_argmax[kMaxRows] = {};
+  std::vector<int> last_argmax;   // [lay.rows]
   // profiling: wall-clock spans of the enabled kernel roles
   int prof_mask = 0;
   double wall_khz = 0.0;               // device wall-clock rate
@@ -200,9 +207,11 @@ void prof_accumulate(sv_ctx* c) {
   }
 }
 
-hipError_t gemm_timed(sv_ctx* c, GemmArgs& g, int role, int grid, hipStream_t st) {
+// tiled: forwards of more than 64 rows run the row-tiled kernels (the same
+// per-row arithmetic as the weight-streaming ones).
+hipError_t gemm_timed(sv_ctx* c, GemmArgs& g, int role, int grid, hipStream_t st, bool tiled) {
   g.prof = prof_slot(c, role, g.layer);
-  const hipError_t e = launch_gemm(g, role, grid, st);
+  const hipError_t e = tiled ? launch_gemm_tiled(g, role, st) : launch_gemm(g, role, grid, st);
   g.prof = nullptr;
   return e;
 }
@@ -210,7 +219,8 @@ hipError_t gemm_timed(sv_ctx* c, GemmArgs& g, int role, int grid, hipStream_t st
 // Queue one whole forward of M rows (kernels only) on `st`.
 hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, hipStream_t st) {
   const sv_config& cfg = c->cfg;
-  const int R = kMaxRows;
+  const bool tiled = M > kMaxRows;
+  const int R = c->lay.rows;
   const int qd = cfg.n_q_heads * cfg.head_dim;
   const int* d_params = c->at<int>(c->lay.params);
   float* x = c->at<float>(c->lay.x);
@@ -263,23 +273,23 @@ hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, hipStream_
     g.layer = l;
     // attention block: (norm) QKV + RoPE + KV append, attention, O + residual
     plan(c->plans.qkv, L.wqkv, L.wqkv_scales, uhi, ulo);
-    if ((e = gemm_timed(c, g, kRoleQkv, c->plans.qkv.grid, st)) != hipSuccess) return e;
+    if ((e = gemm_timed(c, g, kRoleQkv, c->plans.qkv.grid, st, tiled)) != hipSuccess) return e;
     AttnArgs at{};
     at.params = d_params; at.q = q; at.kv_pool = kv; at.page_table = c->buf.page_table; at.n_pages = c->buf.n_pages;
     at.layer = l; at.nq = cfg.n_q_heads; at.nkv = cfg.n_kv_heads; at.dh = cfg.head_dim; at.M = M;
     at.n_split = n_split; at.n_lpages = cfg.max_ctx / kPage; at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cfg.head_dim));
-    at.part = c->at<float>(c->lay.attn_part); at.ohi = ohi; at.olo = olo;
+    at.part = c->at<float>(c->lay.attn_part); at.part_splits = c->lay.max_split; at.ohi = ohi; at.olo = olo;
     at.prof = prof_slot(c, kRoleAttn, l);
-    if ((e = launch_attention(at, st)) != hipSuccess) return e;
+    if ((e = tiled ? launch_attention_rows(at, st) : launch_attention(at, st)) != hipSuccess) return e;
     plan(c->plans.o, L.wo, L.wo_scales, ohi, olo);
     g.gnext = gain(L.g_mlp);
-    if ((e = gemm_timed(c, g, kRoleO, c->plans.o.grid, st)) != hipSuccess) return e;
+    if ((e = gemm_timed(c, g, kRoleO, c->plans.o.grid, st, tiled)) != hipSuccess) return e;
     // MLP block: (norm) gate/up + activation, down + residual
     plan(c->plans.gu, L.wgu, L.wgu_scales, uhi, ulo);
-    if ((e = gemm_timed(c, g, kRoleGateUp, c->plans.gu.grid, st)) != hipSuccess) return e;
+    if ((e = gemm_timed(c, g, kRoleGateUp, c->plans.gu.grid, st, tiled)) != hipSuccess) return e;
     plan(c->plans.d, L.wd, L.wd_scales, ahi, alo);
     g.gnext = l + 1 < cfg.n_layers ? gain(c->layers[l + 1].g_attn) : gain(c->w.g_final);
-    if ((e = gemm_timed(c, g, kRoleDown, c->plans.d.grid, st)) != hipSuccess) return e;
+    if ((e = gemm_timed(c, g, kRoleDown, c->plans.d.grid, st, tiled)) != hipSuccess) return e;
   }
 
   // (final norm) LM head + per-16-column argmax, then acceptance
@@ -287,7 +297,7 @@ hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, hipStream_
   g.layer = 0;
   g.best = best;
   g.logits = c->store_logits ? c->at<float>(c->lay.logits) : nullptr;
-  if ((e = gemm_timed(c, g, kRoleLmHead, c->plans.lm.grid, st)) != hipSuccess) return e;
+  if ((e = gemm_timed(c, g, kRoleLmHead, c->plans.lm.grid, st, tiled)) != hipSuccess) return e;
   return launch_accept(d_params, M, verify, best, c->at<int>(c->lay.result), st);
 }
 
@@ -299,9 +309,9 @@ sv_status forward(sv_ctx* c, int M, const int* ids, int verify) {
   std::memcpy(c->h_params + 2, ids, sizeof(int) * M);
   if (hipMemcpyAsync(d_params, c->h_params, sizeof(int) * (2 + M), hipMemcpyHostToDevice, st) != hipSuccess)
     return SV_EDEVICE;
-  const int n_split = attn_splits(c->kv_len + M);
+  const int n_split = attn_splits_max(c->kv_len, M);
 
-  if (c->use_graphs) {
+  if (c->use_graphs && M <= kMaxRows) {   // forwards of many rows take milliseconds: launched directly
     const std::array<int, 5> key = {M, n_split, verify, c->store_logits, c->prof_mask};
     auto it = c->graphs.find(key);
     if (it == c->graphs.end()) {
@@ -442,8 +452,9 @@ sv_status sv_create(const sv_config* cfg, const sv_weights* w, const sv_buffers*
   c->wall_khz = wall_khz;
   c->ws = static_cast<char*>(buf->workspace);
   c->hist.assign(cfg->max_ctx, -1);
-  if (hipHostMalloc((void**)&c->h_params, sizeof(int) * kParamInts, hipHostMallocDefault) != hipSuccess ||
-      hipHostMalloc((void**)&c->h_result, sizeof(int) * (2 + kMaxRows), hipHostMallocDefault) != hipSuccess ||
+  c->last_argmax.assign(lay.rows, 0);
+  if (hipHostMalloc((void**)&c->h_params, sizeof(int) * (2 + lay.rows), hipHostMallocDefault) != hipSuccess ||
+      hipHostMalloc((void**)&c->h_result, sizeof(int) * (2 + lay.rows), hipHostMallocDefault) != hipSuccess ||
       hipHostMalloc((void**)&c->h_prof, 16 * (size_t)prof_pairs(*cfg), hipHostMallocDefault) != hipSuccess) {
     sv_destroy(c);
     return SV_EDEVICE;
@@ -490,14 +501,20 @@ sv_status sv_prefill(sv_ctx* c, const int32_t* ids, int32_t n, int32_t* next_id)
   if (!c || !ids || n < 1) return SV_EINVAL;
   if (!ids_ok(c, ids, n)) return SV_EINVAL;
   if ((int64_t)c->kv_len + n > c->cfg.max_ctx) return SV_ENOSPACE;
-  const int chunk = max_rows(c->cfg, c->plans);
-  for (int off = 0; off < n; off += chunk) {
-    const int m = std::min(chunk, n - off);
+  // forwards of up to max_prefill_rows rows (row-tiled kernels) while more
+  // than 64 ids remain, then of up to 64 (weight-streaming kernels); every
+  // row's bits are the same either way
+  const int small = max_rows(c->cfg, c->plans);
+  for (int off = 0; off < n;) {
+    const int left = n - off;
+    const int m = (c->cfg.max_prefill_rows > 0 && left > small) ? std::min(left, (int)c->cfg.max_prefill_rows)
+                                                                : std::min(left, small);
     const sv_status s = forward(c, m, ids + off, 0);
     if (s != SV_OK) return s;
     for (int r = 0; r < m; ++r) c->hist[c->kv_len + r] = c->h_result[2 + r];
     c->kv_len += m;
     c->next_id = c->h_result[1];
+    off += m;
   }
   if (next_id) *next_id = c->next_id;
   return SV_OK;

@@ -94,11 +94,12 @@ class Session:
     the committed length would reach the logits.
     """
 
-    def __init__(self, model: DeviceModel, page_perm=None, poison: bool = False, cfg=None):
+    def __init__(self, model: DeviceModel, page_perm=None, poison: bool = False, cfg=None, prefill_rows: int = 0):
         self.m = model
         cfg = cfg or model.cfg
         self.cfg = cfg
-        config = B.make_config(cfg)
+        self.prefill_rows = int(prefill_rows)
+        config = B.make_config(cfg, self.prefill_rows)
         self.config = config
         kv_bytes, ws_bytes = B.sv_query_sizes(config)
         n_pages = cfg.max_ctx // cfg.page_size
@@ -155,7 +156,7 @@ class Session:
         return B.sv_get_logits(self.ctx, row, self.cfg.vocab)
 
     def last_argmax(self):
-        return B.sv_last_argmax(self.ctx)
+        return B.sv_last_argmax(self.ctx, self.prefill_rows)
 
     def history(self, n=None):
         return B.sv_history(self.ctx, self.kv_len if n is None else n)

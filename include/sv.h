@@ -51,6 +51,12 @@ typedef struct {
   int32_t page_size;    /* must be 16 */
   int32_t max_ctx;      /* KV capacity in positions, multiple of page_size */
   int32_t max_k;        /* most drafts per verify, 0..63 */
+  int32_t max_prefill_rows; /* 0: sv_prefill runs forwards of at most 64 rows
+                               (the weight-streaming kernels of decode and verify);
+                               65..16384 (bf16 weights only, else SV_EUNSUPPORTED):
+                               while more than 64 ids remain, forwards of up to this
+                               many rows through row-tiled kernels with the same
+                               per-row arithmetic.  The workspace grows with it. */
 } sv_config;
 
 /* One layer's weights, all device pointers in the packed layouts that
@@ -127,8 +133,12 @@ void sv_destroy(sv_ctx *ctx);
 /* Commit n ids at positions kv_len..kv_len+n-1 (a fresh prefill when kv_len
  * is 0, a block commit otherwise; the whole committed prefix of the cache
  * histories compared in "Shape and cache history in Gemma block
- * verification", section "Same-prefix controls").  Runs in chunks of at most
- * 64 rows with the same per-row kernels as decode and verify.  On return
+ * verification", section "Same-prefix controls").  Runs in forwards of at
+ * most 64 rows with the kernels of decode and verify, or, with
+ * max_prefill_rows set, of up to that many rows with row-tiled kernels (the
+ * compute-bound prefill: each weight tile is read once per 128 rows); each
+ * row's logits, argmax and KV bits are those a one-token decode gives it
+ * either way.  On return
  * kv_len += n and *next_id (host) is the greedy id after the last row.
  * ids: host int32 [n], each in [0, vocab).  Errors: SV_EINVAL (n < 1, bad id),
  * SV_ENOSPACE (kv_len + n > max_ctx). */
@@ -187,7 +197,7 @@ sv_status sv_set_debug(sv_ctx *ctx, int32_t store_logits);
 sv_status sv_get_logits(sv_ctx *ctx, int32_t row, float *host_dst, int32_t vocab);
 
 /* Argmax a_0..a_{M-1} of every row of the last forward (host int32 [M]);
- * *m receives M.  dst may hold up to 64 entries. */
+ * *m receives M.  dst must hold max(64, max_prefill_rows) entries. */
 sv_status sv_last_argmax(const sv_ctx *ctx, int32_t *dst, int32_t *m);
 
 /* Measurement (the per-kernel timing a roofline figure needs): every launch

@@ -57,3 +57,20 @@ def test_no_oracle_import_in_product_code():
             if f.endswith((".py", ".cpp", ".hip", ".h")):
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in txt and "from oracle" not in txt, f
+
+
+def test_prefill_rows_config_checked_on_host():
+    """max_prefill_rows: 0 or 65..16384, bf16 weights only (host-side checks)."""
+    from greedy_block_verification_amd import binding as B
+    from seeded_inputs import get_config
+    tiny = get_config("tiny")
+    kv0, ws0 = B.sv_query_sizes(B.make_config(tiny))
+    kv1, ws1 = B.sv_query_sizes(B.make_config(tiny, 256))
+    assert kv1 == kv0 and ws1 > ws0
+    for bad in (64, 20000, -1):
+        with pytest.raises(B.SvError) as e:
+            B.sv_query_sizes(B.make_config(tiny, bad))
+        assert e.value.status == -1
+    with pytest.raises(B.SvError) as e:
+        B.sv_query_sizes(B.make_config(get_config("gemma_int4"), 256))
+    assert e.value.status == -5

@@ -76,6 +76,32 @@ def test_stress_verify_equals_decode(stress, k):
     b.close()
 
 
+@pytest.mark.parametrize("kv_len", [1020, 8180])
+def test_stress_verify_equals_decode_across_split_plan_changes(stress, kv_len):
+    """Rows of one verify that straddle a change of the attention split plan:
+    around ctx 1024 (16 splits folded in the workgroup vs 17 folded by the
+    combine pass, chosen by the verify's longest row) and around ctx 8192
+    (one block per split vs two)."""
+    dev, w, cfg, snap = stress
+    k = 16
+    rng = np.random.default_rng(2000 + kv_len)
+    drafts = rng.integers(0, cfg.vocab, k).tolist()
+    a, b = _sess(dev, cfg, snap), _sess(dev, cfg, snap)
+    a.truncate(kv_len)
+    b.truncate(kv_len)
+    rows = [a.next_id] + drafts
+    dec = []
+    for t in rows:
+        a.decode_step(t)
+        dec.append(a.logits(0))
+    b.verify(drafts)
+    for r in range(k + 1):
+        np.testing.assert_array_equal(_bits(b.logits(r)), _bits(dec[r]))
+    np.testing.assert_array_equal(a.kv_positions(kv_len + 1, kv_len - 4), b.kv_positions(kv_len + 1, kv_len - 4))
+    a.close()
+    b.close()
+
+
 def test_stress_rollback_at_every_index(stress):
     dev, w, cfg, snap = stress
     K = 32
