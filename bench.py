@@ -12,9 +12,9 @@ reported as the decode baseline).
 Other workloads (``--config``), each printing its own JSON line:
 ``q06b`` (Qwen3-0.6B shape, 8 prompts of 512 ids, 128 generated, K = 4 and
 a sweep over 1, 2, 8, draft accuracy 0.60), ``gemma_int4`` (int4 GeGLU
-target, 87-id prompts, K = 8 and 16), ``q8b_stress`` (the 8B shape over a
-synthetic 32640-position KV cache restored into a 32K context, K = 4 and a
-sweep over 1, 2, 8, 16, 32).
+target, 87-id prompts, K = 8 and 16), ``q8b_stress`` (the 8B shape with a
+32640-id prompt prefilled into a 32K context through the row-tiled prefill,
+K = 4 and a sweep over 1, 2, 8, 16, 32).
 
 A timed *step* is one ``sv_verify`` call (the whole hot path: embed, all
 layers, LM head + argmax, acceptance, truncate) on one prompt's window; the
@@ -114,6 +114,53 @@ def run_spec(sessions, truth, prompt_len, gen, k, srcs, n_steps, profile_mask=0)
     return st
 
 
+def run_spec_batch(sessions, truth, prompt_len, gen, k, srcs, n_steps):
+    """Batched verify: the B sessions advance together, one sv_verify_batch
+    per step; a session that finishes its continuation restarts at its prompt."""
+    from greedy_block_verification_amd import binding as B
+    import torch
+    st = {"tokens": 0, "accepted": 0, "proposed": 0, "mism": 0, "matched": 0, "finished": 0,
+          "rows": 0, "steps": []}
+    done = [0] * len(sessions)
+    ctxs = [s.ctx for s in sessions]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_steps):
+        drafts, kvs, curs = [], [], []
+        for i, s in enumerate(sessions):
+            c = done[i]
+            k_eff = min(k, gen - c - 1)
+            window = truth[i][c + 1: c + 1 + k_eff]
+            drafts.append(srcs[i].window(window, k_eff) if k_eff > 0 else [])
+            kvs.append(s.kv_len)
+            curs.append(s.next_id)
+        res = B.sv_verify_batch(ctxs, kvs, drafts)
+        row_steps = []
+        for i, s in enumerate(sessions):
+            n, _ = res[i]
+            c = done[i]
+            new = [curs[i]] + drafts[i][:n]
+            st["mism"] += sum(int(a != b) for a, b in zip(new, truth[i][c: c + n + 1]))
+            st["tokens"] += n + 1
+            st["accepted"] += n
+            st["proposed"] += len(drafts[i])
+            st["rows"] += len(drafts[i]) + 1
+            row_steps.append((len(drafts[i]), n, kvs[i]))
+            done[i] = c + n + 1
+            if done[i] >= gen:
+                st["finished"] += 1
+                st["matched"] += int(done[i] == gen)
+                s.truncate(prompt_len)
+                done[i] = 0
+        st["steps"].append(row_steps)
+    torch.cuda.synchronize()
+    st["seconds"] = time.perf_counter() - t0
+    for s in sessions:
+        if s.kv_len != prompt_len:
+            s.truncate(prompt_len)
+    return st
+
+
 def cpu_baseline(weights, ids, n_tokens, steps):
     """The fp64 oracle's per-token decoder on this host (bounded sample)."""
     import numpy as np
@@ -141,40 +188,19 @@ def cpu_baseline(weights, ids, n_tokens, steps):
 # synthetic shapes of the study, each printed as its own JSON line.
 WORKLOADS = {
     "q8b": dict(k=4, k_sweep="8,16", prompts=50, prompt_len=128, gen_tokens=64, p_correct=0.66,
-                steps=300, sweep_steps=150, restore=False, roofline_kernel="sv::k_gemm_bf16<1, 2>",
+                steps=300, sweep_steps=150, prefill_rows=0, roofline_kernel="sv::k_gemm_bf16<1, 2>",
                 what="Qwen3-8B-shaped target"),
     "q06b": dict(k=4, k_sweep="1,2,8", prompts=8, prompt_len=512, gen_tokens=128, p_correct=0.60,
-                 steps=400, sweep_steps=300, restore=False, roofline_kernel="sv::k_gemm_bf16<1, 2>",
+                 steps=400, sweep_steps=300, prefill_rows=512, roofline_kernel="sv::k_gemm_bf16<1, 2>",
                  what="Qwen3-0.6B-shaped target"),
     "gemma_int4": dict(k=8, k_sweep="16", prompts=16, prompt_len=87, gen_tokens=64, p_correct=0.66,
-                       steps=300, sweep_steps=200, restore=False, roofline_kernel="sv::k_gemm_int4<1, 2>",
+                       steps=300, sweep_steps=200, prefill_rows=0, roofline_kernel="sv::k_gemm_int4<1, 2>",
                        what="Gemma-style int4 (group 64, bf16 scales) GeGLU target"),
     "q8b_stress": dict(k=4, k_sweep="1,2,8,16,32", prompts=1, prompt_len=32640, gen_tokens=64, p_correct=0.66,
-                       steps=150, sweep_steps=60, restore=True, roofline_kernel="sv::k_gemm_bf16<1, 2>",
-                       what="Qwen3-8B-shaped target over a synthetic 32K-position KV cache"),
+                       steps=150, sweep_steps=60, prefill_rows=2048, roofline_kernel="sv::k_gemm_bf16<1, 2>",
+                       what="Qwen3-8B-shaped target at a 32K-position context"),
 }
 ROLE_NAMES = ["qkv", "o_proj", "gate_up", "down", "lm_head", "attention"]
-
-
-def restore_synthetic_prefix(session, cfg, prefix_len, seed):
-    """Fill the first prefix_len positions of every layer's KV pages with
-    seeded random fp16 values and declare them committed with a random greedy
-    history (a long context the bench cannot prefill in its time budget)."""
-    import numpy as np
-    import torch
-    from greedy_block_verification_amd import binding as B
-    n_pages = cfg.max_ctx // cfg.page_size
-    pool = session.kv.view(cfg.n_layers, n_pages, -1)
-    g = torch.Generator(device=session.kv.device)
-    g.manual_seed(seed)
-    used = (prefix_len + cfg.page_size - 1) // cfg.page_size
-    for layer in range(cfg.n_layers):
-        vals = torch.randn((used, pool.shape[2]), generator=g, device=session.kv.device, dtype=torch.float32)
-        pool[layer, :used] = vals.to(torch.float16).view(torch.int16)
-    torch.cuda.synchronize()
-    hist = np.random.default_rng(seed + 1).integers(0, cfg.vocab, prefix_len).tolist()
-    B.sv_restore(session.ctx, prefix_len, hist)
-    return hist
 
 
 def main():
@@ -191,6 +217,9 @@ def main():
     ap.add_argument("--gen-tokens", type=int, default=None)
     ap.add_argument("--p-correct", type=float, default=None)
     ap.add_argument("--cpu-tokens", type=int, default=3)
+    ap.add_argument("--batch", default="",
+                    help="also time batched verify (sv_verify_batch) of B sequences per step, "
+                         "for each B in this comma list (needs --prompts >= B)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB first (the reference "
@@ -225,18 +254,19 @@ def main():
     dm = DeviceModel(weights)
     log(f"[bench] weights uploaded and packed in {time.perf_counter() - t:.1f} s")
 
+    batches = [int(x) for x in args.batch.split(",") if x.strip()]
+    # the first session carries batched forwards of more than 64 rows through the row-tiled kernels
+    big = max([b * (args.k + 1) for b in batches] + [0])
     sessions, truth, prompts = [], [], []
     t_prefill = t_decode = 0.0
     for p in range(P):
-        s = Session(dm)
+        rows0 = max(wl["prefill_rows"], 128 * ((big + 127) // 128) if big > 64 else 0) if p == 0 else wl["prefill_rows"]
+        s = Session(dm, prefill_rows=rows0)
+        ids = prompt_ids(cfg.seed, p, L, cfg.vocab).tolist()
         torch.cuda.synchronize()
         t = time.perf_counter()
-        if wl["restore"]:
-            ids = restore_synthetic_prefix(s, cfg, L, cfg.seed + 300 + 2 * p)
-            nx = s.next_id
-        else:
-            ids = prompt_ids(cfg.seed, p, L, cfg.vocab).tolist()
-            nx = s.prefill(ids)
+        nx = s.prefill(ids)
+        torch.cuda.synchronize()
         t_prefill += time.perf_counter() - t
         seq = [nx]
         t = time.perf_counter()
@@ -302,7 +332,9 @@ def main():
         "baseline_decode_tpot_ms": round(decode_tpot_ms, 4),
         "baseline_decode_tok_s": round(1000.0 / decode_tpot_ms, 2),
         "speedup_vs_decode": round(value / (1000.0 / decode_tpot_ms), 4),
-        ("restore_ms_per_prompt" if wl["restore"] else "prefill_ms_per_prompt"): round(1000.0 * t_prefill / P, 3),
+        "prefill_ms_per_prompt": round(1000.0 * t_prefill / P, 3),
+        "prefill_tok_s": round(P * L / t_prefill, 1),
+        "prefill_rows_per_forward": wl["prefill_rows"] or 64,
         "kernel_us_per_step": {name: round(1000.0 * ms / args.steps, 1) for name, (ms, n) in prof.items()},
         "kernel_launches_per_step": {name: round(n / args.steps, 2) for name, (ms, n) in prof.items()},
     }
@@ -320,18 +352,36 @@ def main():
                            "verify_decode_mismatches": sk["mism"]}
         log(f"[bench] K={k}: {sweep[f'K={k}']}")
     extra["k_sweep"] = sweep
+    bsweep = {}
+    for b in batches:
+        if b > P:
+            continue
+        sb_ = run_spec_batch(sessions[:b], truth[:b], L, G, args.k,
+                             [DraftSource(cfg.seed, 30_000 + p, cfg.vocab, p_correct=args.p_correct) for p in range(b)],
+                             args.sweep_steps)
+        # per step: the weights once, each sequence's KV read and written and its embedding rows
+        W = cfg.weight_bytes_per_forward()
+        byts = sum(W + sum(algorithmic_step_bytes(cfg, ke + 1, kv) - W for ke, _, kv in row) for row in sb_["steps"])
+        bsweep[f"B={b}"] = {"verified_tok_s": round(metrics.verified_tok_s(sb_["tokens"], sb_["seconds"]), 1),
+                            "ms_per_step": round(1000.0 * sb_["seconds"] / args.sweep_steps, 4),
+                            "rows_per_step": round(sb_["rows"] / args.sweep_steps, 2),
+                            "acceptance_rate": round(metrics.acceptance_rate(sb_["accepted"], sb_["proposed"]), 4),
+                            "step_hbm_gbs": round(byts / sb_["seconds"] / 1e9, 1),
+                            "verify_decode_mismatches": sb_["mism"]}
+        log(f"[bench] batch B={b} K={args.k}: {bsweep[f'B={b}']}")
+    if bsweep:
+        extra["batch_sweep"] = bsweep
 
     cpu = None
-    if wl["restore"]:
-        extra["cpu_baseline_note"] = ("not run: the oracle would have to rebuild the synthetic "
-                                      f"{L}-position cache in fp64 before its first decode")
+    if L > 4096:
+        extra["cpu_baseline_note"] = (f"not run: the oracle's decoder would first have to decode the {L}-id "
+                                      "prompt one position at a time in fp64")
     elif not args.no_cpu_baseline:
         t = time.perf_counter()
         cpu = cpu_baseline(weights, prompts[0], args.cpu_tokens, st["steps"])
         log(f"[bench] cpu baseline {cpu['value']:.4f} tok/s in {time.perf_counter() - t:.1f} s")
 
-    prompt_desc = (f"{P} synthetic {L}-position prefix(es) (seeded random fp16 K/V, restored)" if wl["restore"]
-                   else f"{P} prompts x {L} ids")
+    prompt_desc = f"{P} prompt(s) x {L} ids"
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "verified tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),

@@ -61,6 +61,8 @@ SIGNATURES = {
     "sv_decode_step": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_int32)]),
     "sv_verify": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_int32), C.c_int32, C.POINTER(C.c_int32),
                             C.POINTER(C.c_int32)]),
+    "sv_verify_batch": (C.c_int, [C.POINTER(C.c_void_p), C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
+                                  C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
     "sv_kv_truncate": (C.c_int, [C.c_void_p, C.c_int32]),
     "sv_kv_len": (C.c_int32, [C.c_void_p]),
     "sv_next_id": (C.c_int32, [C.c_void_p]),
@@ -158,6 +160,17 @@ def sv_verify(ctx, prefix_len: int, draft_ids):
     _check(lib().sv_verify(ctx, int(prefix_len), _i32_array(draft_ids), len(draft_ids), C.byref(n), C.byref(nx)),
            "sv_verify")
     return n.value, nx.value
+
+
+def sv_verify_batch(ctxs, prefix_lens, drafts):
+    """drafts: one list of draft ids per context; returns [(n_accepted, next_id)]."""
+    n = len(ctxs)
+    arr = (C.c_void_p * n)(*ctxs)
+    flat = [int(t) for d in drafts for t in d]
+    na, nx = (C.c_int32 * n)(), (C.c_int32 * n)()
+    _check(lib().sv_verify_batch(arr, n, _i32_array(prefix_lens), _i32_array([len(d) for d in drafts]),
+                                 _i32_array(flat), na, nx), "sv_verify_batch")
+    return [(na[i], nx[i]) for i in range(n)]
 
 
 def sv_kv_truncate(ctx, new_len: int):

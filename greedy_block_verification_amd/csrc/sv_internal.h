@@ -19,6 +19,16 @@ constexpr int kEpiCols = 256;       // columns one epilogue workgroup owns (whol
 // Parameters of one forward, staged host -> device before the launches.
 // Layout in device memory: int32 [0] kv_len, [1] rows, [2..2+rows) row ids.
 
+// One sequence of a batched forward (several contexts' windows in one pass):
+// its KV pool and page table, its committed length and its rows [row0, row0 + m).
+struct SeqDev {
+  uint16_t* kv_pool;
+  const int* page_table;
+  int n_pages, n_lpages;   // physical pages of its pool, logical pages (max_ctx / 16)
+  int kv_len, row0, m, pad;
+};
+constexpr int kMaxBatch = 64;       // most sequences of one batched forward
+
 // Weight-matrix roles of the skinny GEMM (each has its own epilogue).
 enum GemmRole { kRoleQkv = 0, kRoleO = 1, kRoleGateUp = 2, kRoleDown = 3, kRoleLmHead = 4 };
 
@@ -53,6 +63,10 @@ struct GemmArgs {
   const int* page_table;
   int n_pages, layer, nq, nkv, dh;
   const float2* rope;    // [max_ctx][dh/2] (cos, sin)
+  // batched forward (else null): row r belongs to sequence rowseq[r]; its
+  // position, pool and page table come from seqs[] instead of the fields above
+  const SeqDev* seqs;
+  const int* rowseq;
   // LM head
   unsigned long long* best;   // [M] row argmax keys (orderable logit, ~id), zeroed by the embed kernel
   float* logits;         // optional [M][N] fp32
@@ -72,6 +86,12 @@ struct AttnArgs {
   uint16_t* ohi;         // output planes [M][nq*dh]
   uint16_t* olo;
   unsigned long long* prof;   // optional [2]: start stamped by the split kernel, end by the last kernel
+  // batched forward (else null): q tile t covers q-rows tiles[t].y .. +15 of
+  // sequence tiles[t].x (a tile never mixes sequences)
+  const SeqDev* seqs;
+  const int* rowseq;
+  const int2* tiles;
+  int n_tiles;
   // set by launch_attention
   int spw;               // splits per workgroup
   int final_fold;        // 1: one workgroup per KV head folds its splits in LDS and writes the output
@@ -100,6 +120,10 @@ hipError_t launch_embed(const int* params, int M, const void* embed, int vocab, 
                         hipStream_t st);
 hipError_t launch_accept(const int* params, int M, int verify, const unsigned long long* best, int* result,
                          hipStream_t st);
+// Batched verify: per sequence s, n_s leading matches among its rows and
+// next_s = argmax of row row0_s + n_s, at result[2 + M + 2 s], [2 + M + 2 s + 1].
+hipError_t launch_accept_batch(const int* params, int M, const SeqDev* seqs, int n_seq,
+                               const unsigned long long* best, int* result, hipStream_t st);
 // Profiling slots: (start, end) pairs set to (max, 0) before a forward.
 hipError_t launch_prof_reset(unsigned long long* slots, int n_pairs, hipStream_t st);
 hipError_t launch_pack(int fmt, int layout, const void* src0, const void* src0_scales, const void* src1,

@@ -267,12 +267,14 @@ __device__ __forceinline__ void rows_inv_rms(const GemmArgs& a, GemmShared& sh, 
 struct EpiPre {
   float x, gain;
   float2 cs;
-  int page;
+  int page, pos;          // QKV: physical page and position of the row
+  uint16_t* pool;         // QKV: KV pool of the row's sequence
+  int n_pages;
 };
 
 template <int ROLE>
 __device__ __forceinline__ EpiPre epi_load(const GemmArgs& a, int T, int idx) {
-  EpiPre e{0.f, 0.f, make_float2(0.f, 0.f), 0};
+  EpiPre e{0.f, 0.f, make_float2(0.f, 0.f), 0, 0, nullptr, 0};
   if (idx >= a.M * 16) return e;
   const int r = idx >> 4, c = idx & 15;
   if (ROLE == kRoleO || ROLE == kRoleDown) {
@@ -282,9 +284,20 @@ __device__ __forceinline__ EpiPre epi_load(const GemmArgs& a, int T, int idx) {
   } else if (ROLE == kRoleQkv) {
     const int half = a.dh >> 1, gph = half >> 3;
     const int hh = T / gph, sb = T % gph;
-    const int pos = a.params[0] + r;
-    if (hh < a.nq + a.nkv) e.cs = a.rope[(size_t)pos * half + 8 * sb + (c & 7)];
-    if (hh >= a.nq) e.page = a.page_table[pos / kPage];
+    const int* table = a.page_table;
+    e.pool = a.kv_pool;
+    e.n_pages = a.n_pages;
+    if (a.seqs != nullptr) {   // batched: the row's own sequence
+      const SeqDev& sd = a.seqs[a.rowseq[r]];
+      e.pos = sd.kv_len + r - sd.row0;
+      table = sd.page_table;
+      e.pool = sd.kv_pool;
+      e.n_pages = sd.n_pages;
+    } else {
+      e.pos = a.params[0] + r;
+    }
+    if (hh < a.nq + a.nkv) e.cs = a.rope[(size_t)e.pos * half + 8 * sb + (c & 7)];
+    if (hh >= a.nq) e.page = table[e.pos / kPage];
   }
   return e;
 }
@@ -322,7 +335,7 @@ __device__ __forceinline__ void epi_element(const GemmArgs& a, int T, int r, int
     const bool lo = c < 8;
     const int i = 8 * sb + (c & 7);
     const int d = lo ? i : half + i;
-    const int pos = a.params[0] + r;
+    const int pos = e.pos;
     float out = y;
     if (hh < a.nq + a.nkv) {
       const float2 cs = e.cs;
@@ -335,10 +348,10 @@ __device__ __forceinline__ void epi_element(const GemmArgs& a, int T, int r, int
       const int kv = hh < a.nq + a.nkv ? 0 : 1;
       const int head = hh - a.nq - kv * a.nkv;
       const int page = e.page;
-      const size_t base = ((((size_t)a.layer * a.n_pages + page) * 2 + kv) * a.nkv + head) * kPage * a.dh;
+      const size_t base = ((((size_t)a.layer * e.n_pages + page) * 2 + kv) * a.nkv + head) * kPage * a.dh;
       // K rows are [slot][dh]; V is stored transposed inside the page, [dh][slot]
       const size_t el = kv == 0 ? (size_t)(pos % kPage) * a.dh + d : (size_t)d * kPage + (pos % kPage);
-      a.kv_pool[base + el] = f2h(out);
+      e.pool[base + el] = f2h(out);
     }
   } else {                                        // kRoleLmHead
     const int n = T * 16 + c;
@@ -1318,10 +1331,40 @@ __device__ __forceinline__ void attn_block_step(const AttnArgs& a, const AttnKV<
   m = mn;
 }
 
-// Rows of q tile qt whose ranges make up a unit: r0 .. r1.
-__device__ __forceinline__ void attn_tile_rows(int qt, int G, int M, int& r0, int& r1) {
-  r0 = (qt * 16) / G;
-  r1 = min((qt * 16 + 15) / G, M - 1);
+// Rows of the q tile starting at q-row qbase (of a sequence of M rows) whose
+// ranges make up a unit: r0 .. r1.
+__device__ __forceinline__ void attn_tile_rows(int qbase, int G, int M, int& r0, int& r1) {
+  r0 = qbase / G;
+  r1 = min((qbase + 15) / G, M - 1);
+}
+
+// The view of one q tile: its sequence's pool, page table and length, the
+// q-row the tile starts at and the sequence's rows [row0, row0 + m).  A
+// single-sequence forward is one sequence of all M rows.
+struct AttnView {
+  AttnArgs av;   // the arguments with the sequence's pool and page table
+  int qbase, row0, m;
+};
+__device__ __forceinline__ AttnView attn_view(const AttnArgs& a, int qt) {
+  AttnView v{a, qt * 16, 0, a.M};
+  if (a.seqs != nullptr) {
+    const int2 tl = a.tiles[qt];
+    const SeqDev& sd = a.seqs[tl.x];
+    v.av.kv_pool = sd.kv_pool;
+    v.av.page_table = sd.page_table;
+    v.av.n_pages = sd.n_pages;
+    v.av.n_lpages = sd.n_lpages;
+    v.qbase = tl.y;
+    v.row0 = sd.row0;
+    v.m = sd.m;
+  }
+  return v;
+}
+__device__ __forceinline__ int attn_kv_len(const AttnArgs& a, int qt) {
+  return a.seqs != nullptr ? a.seqs[a.tiles[qt].x].kv_len : a.params[0];
+}
+__device__ __forceinline__ int attn_n_tiles(const AttnArgs& a) {
+  return a.seqs != nullptr ? a.n_tiles : (a.M * (a.nq / a.nkv) + 15) >> 4;
 }
 
 // Union of the tile rows' ranges of split sp, in whole blocks [b_lo, b_hi)
@@ -1348,8 +1391,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int G = a.nq / a.nkv;
-  const int n_qr = a.M * G;
-  const int n_qt = (n_qr + 15) >> 4;
+  const int n_qt = attn_n_tiles(a);
   // Workgroup -> (q tile, split group, KV head).  Workgroups are dealt to the
   // 8 XCDs round-robin in launch order; when the (split group, head) units
   // come in multiples of 8, the q tiles of one unit are placed 8 apart so
@@ -1370,24 +1412,28 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   }
   const int s_lo = sg * a.spw;
   const int s_hi = min(s_lo + a.spw, a.n_split);
-  // this lane's q-row (independent of kv_len: its q loads go out first)
-  const int qr = qt * 16 + j;
+  const AttnView V = attn_view(a, qt);
+  const AttnArgs& av = V.av;
+  const int n_qr = V.m * G;
+  // this lane's q-row (independent of kv_len: its q loads go out first);
+  // r is the row inside the tile's sequence
+  const int qr = V.qbase + j;
   const bool have = qr < n_qr;
   const int r = have ? qr / G : 0;
   const int head = h * G + (have ? qr % G : 0);
   float4 qraw[DC][2];
   {
-    const float4* qp = reinterpret_cast<const float4*>(a.q + ((size_t)r * a.nq + head) * DH + g * 8);
+    const float4* qp = reinterpret_cast<const float4*>(a.q + ((size_t)(V.row0 + r) * a.nq + head) * DH + g * 8);
 #pragma unroll
     for (int c = 0; c < DC; ++c) { qraw[c][0] = qp[c * 8]; qraw[c][1] = qp[c * 8 + 1]; }
   }
-  auto block_pages = [&](int b) { return attn_block_pages(a, b); };
+  auto block_pages = [&](int b) { return attn_block_pages(av, b); };
   // the first unit's first block is its split index whenever splits are one
   // block (contexts up to 8192): fetch its pages before the context length is known
   const int b_guess = s_lo + wave;
   int4 pq_guess = block_pages(b_guess);
-  const int kv_len = a.params[0];
-  const int ctx_max = kv_len + a.M;
+  const int kv_len = attn_kv_len(a, qt);
+  const int ctx_max = kv_len + V.m;
   const int ctx = kv_len + r + 1;
   BPair qop[DC];
 #pragma unroll
@@ -1408,7 +1454,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     int b_lo, b_hi;
     {
       int r0, r1;
-      attn_tile_rows(qt, G, a.M, r0, r1);
+      attn_tile_rows(V.qbase, G, V.m, r0, r1);
       attn_split_union(kv_len, r0, r1, sp, b_lo, b_hi);
     }
     f32x4 o[DT];
@@ -1419,9 +1465,9 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     int4 pq = (b_lo == b_guess) ? pq_guess : block_pages(b_lo < b_hi ? b_lo : 0);
     for (int b = b_lo; b < b_hi; ++b) {
       AttnKV<DH> kv;
-      attn_load_kv<DH>(a, h, j, g, pq, kv);
+      attn_load_kv<DH>(av, h, j, g, pq, kv);
       pq = block_pages(b + 1 < b_hi ? b + 1 : b);   // next block's pages, in flight during this block
-      attn_block_step<DH>(a, kv, qop, b, g, lo, hi, ctx_max, m, l, o);
+      attn_block_step<DH>(av, kv, qop, b, g, lo, hi, ctx_max, m, l, o);
     }
 
     // lane (g, j) holds o of q-row j for d = 16dt + 4g + v
@@ -1432,7 +1478,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       for (int dt = 0; dt < DT; ++dt)
         *reinterpret_cast<float4*>(&U.o[j][dt * 16 + 4 * g]) = make_float4(o[dt].x, o[dt].y, o[dt].z, o[dt].w);
     } else if (have && hi > lo) {
-      float* part = a.part + (((size_t)r * a.nq + head) * a.part_splits + sp) * (DH + 4);
+      float* part = a.part + (((size_t)(V.row0 + r) * a.nq + head) * a.part_splits + sp) * (DH + 4);
       if (g == 0) { part[0] = m; part[1] = l; }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -1446,7 +1492,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     constexpr int TPR = DH / 4;              // threads per q-row
     for (int t = threadIdx.x; t < 16 * TPR; t += blockDim.x) {
       const int jj = t / TPR, d0 = (t % TPR) * 4;
-      const int q2 = qt * 16 + jj;
+      const int q2 = V.qbase + jj;
       if (q2 >= n_qr) continue;
       const int r2 = q2 / G, head2 = h * G + q2 % G;
       const int ns = attn_ns(kv_len + r2 + 1);
@@ -1467,7 +1513,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       uint16_t hb[4], lb[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) split1(ov[e] / fl, hb[e], lb[e]);
-      const size_t oi = ((size_t)r2 * a.nq + head2) * DH + d0;
+      const size_t oi = ((size_t)(V.row0 + r2) * a.nq + head2) * DH + d0;
       *reinterpret_cast<uint2*>(a.ohi + oi) = make_uint2(pack2(hb[0], hb[1]), pack2(hb[2], hb[3]));
       *reinterpret_cast<uint2*>(a.olo + oi) = make_uint2(pack2(lb[0], lb[1]), pack2(lb[2], lb[3]));
     }
@@ -1490,18 +1536,20 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int G = a.nq / a.nkv;
-  const int n_qr = a.M * G;
-  const int n_qt = (n_qr + 15) >> 4;
+  const int n_qt = attn_n_tiles(a);
   const int h = blockIdx.y;
   const int qt = blockIdx.x * 4 + wave;
   if (qt < n_qt) {   // wave-uniform
-    const int qr = qt * 16 + j;
+    const AttnView V = attn_view(a, qt);
+    const AttnArgs& av = V.av;
+    const int n_qr = V.m * G;
+    const int qr = V.qbase + j;
     const bool have = qr < n_qr;
     const int r = have ? qr / G : 0;
     const int head = h * G + (have ? qr % G : 0);
     BPair qop[DC];
     {
-      const float4* qp = reinterpret_cast<const float4*>(a.q + ((size_t)r * a.nq + head) * DH + g * 8);
+      const float4* qp = reinterpret_cast<const float4*>(a.q + ((size_t)(V.row0 + r) * a.nq + head) * DH + g * 8);
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
         const float4 q0 = qp[c * 8], q1 = qp[c * 8 + 1];
@@ -1509,12 +1557,12 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnArgs a) {
         qop[c] = have ? split8_f16(qv) : bzero();
       }
     }
-    const int kv_len = a.params[0];
-    const int ctx_max = kv_len + a.M;
+    const int kv_len = attn_kv_len(a, qt);
+    const int ctx_max = kv_len + V.m;
     const int ctx = kv_len + r + 1;
     const int ns_row = attn_ns(ctx);
     int r0, r1;
-    attn_tile_rows(qt, G, a.M, r0, r1);
+    attn_tile_rows(V.qbase, G, V.m, r0, r1);
     int ns_max = 1;
     for (int rr = r0; rr <= r1; ++rr) ns_max = max(ns_max, attn_ns(kv_len + rr + 1));
 
@@ -1535,12 +1583,12 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnArgs a) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
       float m = -INFINITY, l = 0.f;
-      int4 pq = attn_block_pages(a, b_lo < b_hi ? b_lo : 0);
+      int4 pq = attn_block_pages(av, b_lo < b_hi ? b_lo : 0);
       for (int b = b_lo; b < b_hi; ++b) {
         AttnKV<DH> kv;
-        attn_load_kv<DH>(a, h, j, g, pq, kv);
-        pq = attn_block_pages(a, b + 1 < b_hi ? b + 1 : b);
-        attn_block_step<DH>(a, kv, qop, b, g, lo, hi, ctx_max, m, l, o);
+        attn_load_kv<DH>(av, h, j, g, pq, kv);
+        pq = attn_block_pages(av, b + 1 < b_hi ? b + 1 : b);
+        attn_block_step<DH>(av, kv, qop, b, g, lo, hi, ctx_max, m, l, o);
       }
       if (sp == 0) {
         fm = m;
@@ -1566,7 +1614,7 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnArgs a) {
         uint16_t hb[4], lb[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) split1(ov[e] / fl, hb[e], lb[e]);
-        const size_t oi = ((size_t)r * a.nq + head) * DH + dt * 16 + 4 * g;
+        const size_t oi = ((size_t)(V.row0 + r) * a.nq + head) * DH + dt * 16 + 4 * g;
         *reinterpret_cast<uint2*>(a.ohi + oi) = make_uint2(pack2(hb[0], hb[1]), pack2(hb[2], hb[3]));
         *reinterpret_cast<uint2*>(a.olo + oi) = make_uint2(pack2(lb[0], lb[1]), pack2(lb[2], lb[3]));
       }
@@ -1578,14 +1626,33 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnArgs a) {
 // Fold of the global partials of row r, query head j (record [m, l, -, -, o[dh]]):
 // the row's records are staged in LDS with coalesced 16-byte loads (a long
 // context has up to 128 of them), then thread d folds output d in split order.
+// Launched with 256 threads.
 template <int DH>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   __shared__ float4 rec[kAttnMaxSplits * (DH + 4) / 4];
   const int j = blockIdx.x, r = blockIdx.y;
-  const int ns = attn_ns(a.params[0] + r + 1);
+  int ctx = a.params[0] + r + 1;
+  if (a.seqs != nullptr) {
+    const SeqDev& sd = a.seqs[a.rowseq[r]];
+    ctx = sd.kv_len + r - sd.row0 + 1;
+  }
+  const int ns = attn_ns(ctx);
   const float4* base = reinterpret_cast<const float4*>(a.part + ((size_t)r * a.nq + j) * a.part_splits * (DH + 4));
   const int n4 = ns * ((DH + 4) / 4);
-  for (int i = threadIdx.x; i < n4; i += blockDim.x) rec[i] = base[i];
+  constexpr int U = 8;   // 8 loads in flight per thread before their LDS stores
+  for (int i0 = threadIdx.x; i0 < n4; i0 += U * 256) {
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * 256;
+      v[u] = base[i < n4 ? i : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * 256;
+      if (i < n4) rec[i] = v[u];
+    }
+  }
   __syncthreads();
   const float* p = reinterpret_cast<const float*>(rec);
   const int d = threadIdx.x;
@@ -1602,10 +1669,11 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
 hipError_t launch_attention(const AttnArgs& a_in, hipStream_t st) {
   AttnArgs a = a_in;
   const int G = a.nq / a.nkv;
-  if (a.M * G > kAttnQRows || a.n_split < 1 || a.n_split > kAttnMaxSplits || a.n_lpages < 1 ||
+  if ((a.seqs == nullptr && a.M * G > kAttnQRows) || a.n_split < 1 || a.n_split > kAttnMaxSplits || a.n_lpages < 1 ||
+      (a.seqs != nullptr && (a.n_tiles < 1 || a.rowseq == nullptr)) ||
       (a.n_split > kAttnLdsUnits && a.n_split > a.part_splits))
     return hipErrorInvalidValue;
-  const int n_qt = (a.M * G + 15) / 16;
+  const int n_qt = a.seqs != nullptr ? a.n_tiles : (a.M * G + 15) / 16;
   a.final_fold = a.n_split <= kAttnLdsUnits ? 1 : 0;
   a.spw = a.final_fold ? a.n_split : 8;
   const int n_wg = n_qt * ((a.n_split + a.spw - 1) / a.spw);
@@ -1623,7 +1691,7 @@ hipError_t launch_attention(const AttnArgs& a_in, hipStream_t st) {
 
 hipError_t launch_attention_rows(const AttnArgs& a, hipStream_t st) {
   if (a.M < 1 || a.n_lpages < 1 || a.nkv < 1 || a.nq % a.nkv) return hipErrorInvalidValue;
-  const int n_qt = (a.M * (a.nq / a.nkv) + 15) / 16;
+  const int n_qt = a.seqs != nullptr ? a.n_tiles : (a.M * (a.nq / a.nkv) + 15) / 16;
   const dim3 grid((n_qt + 3) / 4, a.nkv), block(256);
   if (a.dh == 128) hipLaunchKernelGGL(k_attn_rows<128>, grid, block, 0, st, a);
   else if (a.dh == 64) hipLaunchKernelGGL(k_attn_rows<64>, grid, block, 0, st, a);
@@ -1697,6 +1765,29 @@ hipError_t launch_accept(const int* params, int M, int verify, const unsigned lo
                          hipStream_t st) {
   if (M < 1 || (verify && M > 64)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_accept, dim3(1), dim3(64), 0, st, params, M, verify, best, result);
+  return hipGetLastError();
+}
+
+// Batched verify: every row's argmax, then per sequence (one lane each) the
+// same acceptance rule over its own rows.
+__global__ __launch_bounds__(64) void k_accept_batch(const int* params, int M, const SeqDev* seqs, int n_seq,
+                                                     const unsigned long long* best, int* result) {
+  const int lane = threadIdx.x;
+  auto id_of = [&](int r) { return (int)(0xffffffffu - (uint32_t)(best[r] & 0xffffffffu)); };
+  for (int r = lane; r < M; r += 64) result[2 + r] = id_of(r);
+  if (lane < n_seq) {
+    const SeqDev& sd = seqs[lane];
+    int n = 0;
+    while (n < sd.m - 1 && params[2 + sd.row0 + n + 1] == id_of(sd.row0 + n)) ++n;
+    result[2 + M + 2 * lane] = n;
+    result[2 + M + 2 * lane + 1] = id_of(sd.row0 + n);
+  }
+}
+
+hipError_t launch_accept_batch(const int* params, int M, const SeqDev* seqs, int n_seq,
+                               const unsigned long long* best, int* result, hipStream_t st) {
+  if (M < 1 || n_seq < 1 || n_seq > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_accept_batch, dim3(1), dim3(64), 0, st, params, M, seqs, n_seq, best, result);
   return hipGetLastError();
 }
 

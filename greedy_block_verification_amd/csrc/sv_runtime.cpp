@@ -26,6 +26,8 @@ struct GemmPlan {
 
 struct Layout {
   int rows = 0;   // most rows of one forward: 64, or max_prefill_rows when larger
+  int max_tiles = 0;   // attention q tiles of a batched forward
+  size_t batch = 0, batch_bytes = 0;   // batched-forward tables: rowseq [rows], seqs [kMaxBatch], tiles
   size_t params = 0, x = 0, ss = 0, q = 0, attn_part = 0, uplanes = 0, oplanes = 0, aplanes = 0, best = 0,
          result = 0, logits = 0, rope = 0, prof = 0, total = 0;
   int max_split = 1;
@@ -127,6 +129,11 @@ Layout make_layout(const sv_config& c, const Plans& p) {
     return o;
   };
   L.params = take(sizeof(int) * (2 + R));
+  // batched forward tables (one host-to-device copy with the params)
+  const int G = c.n_q_heads / c.n_kv_heads;
+  L.max_tiles = (int)((R * G + 15) / 16) + kMaxBatch;
+  L.batch_bytes = R * 4 + kMaxBatch * sizeof(SeqDev) + (size_t)L.max_tiles * 8;
+  L.batch = take(L.batch_bytes);
   L.x = take(R * c.d_model * 4);
   L.ss = take(R * (c.d_model / 16) * 4);
   L.q = take(R * qd * 4);
@@ -136,7 +143,7 @@ Layout make_layout(const sv_config& c, const Plans& p) {
   L.oplanes = take(2 * R * qd * 2);          // attention output
   L.aplanes = take(2 * R * c.d_ff * 2);      // act(gate) * up
   L.best = take(R * 8);
-  L.result = take(sizeof(int) * (2 + R));
+  L.result = take(sizeof(int) * (2 + R + 2 * kMaxBatch));
   L.logits = take(R * (size_t)c.vocab * 4);
   L.rope = take((size_t)c.max_ctx * (c.head_dim / 2) * 8);
   L.prof = take(prof_pairs(c) * 16);
@@ -161,6 +168,7 @@ struct sv_ctx {
   char* ws = nullptr;
   int* h_params = nullptr;   // pinned
   int* h_result = nullptr;   // pinned
+  char* h_batch = nullptr;   // pinned staging of the batched-forward tables
   unsigned long long* h_prof = nullptr;   // pinned copy of the profiling slots
   int kv_len = 0;
   int next_id = -1;
@@ -176,10 +184,10 @@ struct sv_ctx {
   int64_t prof_n[kProfRoles] = {};
 
   // HIP graphs of whole forwards, keyed by (rows, attention splits, mode,
-  // logits, profile mask)
+  // logits, profile mask, batch sequences, batch q tiles)
   hipStream_t cap_stream = nullptr;
   bool use_graphs = true;
-  std::map<std::array<int, 5>, hipGraphExec_t> graphs;
+  std::map<std::array<int, 7>, hipGraphExec_t> graphs;
 
   template <class T>
   T* at(size_t off) { return reinterpret_cast<T*>(ws + off); }
@@ -217,7 +225,27 @@ hipError_t gemm_timed(sv_ctx* c, GemmArgs& g, int role, int grid, hipStream_t st
 }
 
 // Queue one whole forward of M rows (kernels only) on `st`.
-hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, hipStream_t st) {
+// Device tables of a batched forward (all null / 0 for one sequence).
+struct BatchDev {
+  const SeqDev* seqs = nullptr;
+  const int* rowseq = nullptr;
+  const int2* tiles = nullptr;
+  int n_seq = 0, n_tiles = 0;
+};
+
+BatchDev batch_dev(sv_ctx* c, int n_seq, int n_tiles) {
+  BatchDev b;
+  if (n_seq == 0) return b;
+  char* base = c->at<char>(c->lay.batch);
+  b.rowseq = reinterpret_cast<const int*>(base);
+  b.seqs = reinterpret_cast<const SeqDev*>(base + (size_t)c->lay.rows * 4);
+  b.tiles = reinterpret_cast<const int2*>(base + (size_t)c->lay.rows * 4 + kMaxBatch * sizeof(SeqDev));
+  b.n_seq = n_seq;
+  b.n_tiles = n_tiles;
+  return b;
+}
+
+hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, int logits, const BatchDev& bd, hipStream_t st) {
   const sv_config& cfg = c->cfg;
   const bool tiled = M > kMaxRows;
   const int R = c->lay.rows;
@@ -264,6 +292,8 @@ hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, hipStream_
   g.nkv = cfg.n_kv_heads;
   g.dh = cfg.head_dim;
   g.rope = c->at<const float2>(c->lay.rope);
+  g.seqs = bd.seqs;
+  g.rowseq = bd.rowseq;
   auto plan = [&](const GemmPlan& p, const void* W, const void* Ws, const uint16_t* bhi, const uint16_t* blo) {
     g.W = W; g.Wscale = Ws; g.N = p.N; g.K = p.K; g.S = p.S; g.fmt = p.fmt; g.bhi = bhi; g.blo = blo;
   };
@@ -280,6 +310,7 @@ hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, hipStream_
     at.n_split = n_split; at.n_lpages = cfg.max_ctx / kPage; at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cfg.head_dim));
     at.part = c->at<float>(c->lay.attn_part); at.part_splits = c->lay.max_split; at.ohi = ohi; at.olo = olo;
     at.prof = prof_slot(c, kRoleAttn, l);
+    at.seqs = bd.seqs; at.rowseq = bd.rowseq; at.tiles = bd.tiles; at.n_tiles = bd.n_tiles;
     if ((e = tiled ? launch_attention_rows(at, st) : launch_attention(at, st)) != hipSuccess) return e;
     plan(c->plans.o, L.wo, L.wo_scales, ohi, olo);
     g.gnext = gain(L.g_mlp);
@@ -296,12 +327,18 @@ hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, hipStream_
   plan(c->plans.lm, c->w.lm_head, nullptr, uhi, ulo);
   g.layer = 0;
   g.best = best;
-  g.logits = c->store_logits ? c->at<float>(c->lay.logits) : nullptr;
+  g.logits = logits ? c->at<float>(c->lay.logits) : nullptr;
   if ((e = gemm_timed(c, g, kRoleLmHead, c->plans.lm.grid, st, tiled)) != hipSuccess) return e;
+  if (bd.seqs != nullptr) return launch_accept_batch(d_params, M, bd.seqs, bd.n_seq, best, c->at<int>(c->lay.result), st);
   return launch_accept(d_params, M, verify, best, c->at<int>(c->lay.result), st);
 }
 
-sv_status forward(sv_ctx* c, int M, const int* ids, int verify) {
+// One forward of M rows on c's stream: params (and, for a batched forward of
+// n_seq > 0 sequences, the tables the caller staged in h_batch) go up, the
+// kernels run (a cached HIP graph for up to 64 rows), the result
+// [n, next, a_0 .. a_{M-1}, (n_s, next_s) per sequence] and the profiling
+// slots come back.  kv_len: the params' length (one sequence).
+sv_status run_forward(sv_ctx* c, int M, const int* ids, int verify, int n_split, int n_seq, int n_tiles, int logits) {
   hipStream_t st = c->stream;
   int* d_params = c->at<int>(c->lay.params);
   c->h_params[0] = c->kv_len;
@@ -309,16 +346,19 @@ sv_status forward(sv_ctx* c, int M, const int* ids, int verify) {
   std::memcpy(c->h_params + 2, ids, sizeof(int) * M);
   if (hipMemcpyAsync(d_params, c->h_params, sizeof(int) * (2 + M), hipMemcpyHostToDevice, st) != hipSuccess)
     return SV_EDEVICE;
-  const int n_split = attn_splits_max(c->kv_len, M);
+  if (n_seq > 0 && hipMemcpyAsync(c->at<char>(c->lay.batch), c->h_batch, c->lay.batch_bytes, hipMemcpyHostToDevice,
+                                  st) != hipSuccess)
+    return SV_EDEVICE;
+  const BatchDev bd = batch_dev(c, n_seq, n_tiles);
 
   if (c->use_graphs && M <= kMaxRows) {   // forwards of many rows take milliseconds: launched directly
-    const std::array<int, 5> key = {M, n_split, verify, c->store_logits, c->prof_mask};
+    const std::array<int, 7> key = {M, n_split, verify, logits, c->prof_mask, n_seq, n_tiles};
     auto it = c->graphs.find(key);
     if (it == c->graphs.end()) {
       hipGraph_t graph = nullptr;
       hipGraphExec_t exec = nullptr;
       if (hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal) != hipSuccess) return SV_EDEVICE;
-      const hipError_t e = enqueue_forward(c, M, verify, n_split, c->cap_stream);
+      const hipError_t e = enqueue_forward(c, M, verify, n_split, logits, bd, c->cap_stream);
       const hipError_t e2 = hipStreamEndCapture(c->cap_stream, &graph);
       hipError_t e3 = hipErrorUnknown;
       if (e == hipSuccess && e2 == hipSuccess && graph != nullptr) e3 = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
@@ -328,16 +368,23 @@ sv_status forward(sv_ctx* c, int M, const int* ids, int verify) {
     }
     if (hipGraphLaunch(it->second, st) != hipSuccess) return SV_EDEVICE;
   } else {
-    if (enqueue_forward(c, M, verify, n_split, st) != hipSuccess) return SV_EDEVICE;
+    if (enqueue_forward(c, M, verify, n_split, logits, bd, st) != hipSuccess) return SV_EDEVICE;
   }
   int* d_result = c->at<int>(c->lay.result);
-  if (hipMemcpyAsync(c->h_result, d_result, sizeof(int) * (2 + M), hipMemcpyDeviceToHost, st) != hipSuccess)
+  if (hipMemcpyAsync(c->h_result, d_result, sizeof(int) * (2 + M + 2 * n_seq), hipMemcpyDeviceToHost, st) !=
+      hipSuccess)
     return SV_EDEVICE;
   if (c->prof_mask != 0 && hipMemcpyAsync(c->h_prof, c->at<unsigned long long>(c->lay.prof),
                                           16 * (size_t)prof_pairs(c->cfg), hipMemcpyDeviceToHost, st) != hipSuccess)
     return SV_EDEVICE;
   if (hipStreamSynchronize(st) != hipSuccess) return SV_EDEVICE;
   if (c->prof_mask != 0) prof_accumulate(c);
+  return SV_OK;
+}
+
+sv_status forward(sv_ctx* c, int M, const int* ids, int verify) {
+  const sv_status s = run_forward(c, M, ids, verify, attn_splits_max(c->kv_len, M), 0, 0, c->store_logits);
+  if (s != SV_OK) return s;
   c->last_rows = M;
   c->last_stored_logits = c->store_logits;
   for (int r = 0; r < M; ++r) c->last_argmax[r] = c->h_result[2 + r];
@@ -454,7 +501,9 @@ sv_status sv_create(const sv_config* cfg, const sv_weights* w, const sv_buffers*
   c->hist.assign(cfg->max_ctx, -1);
   c->last_argmax.assign(lay.rows, 0);
   if (hipHostMalloc((void**)&c->h_params, sizeof(int) * (2 + lay.rows), hipHostMallocDefault) != hipSuccess ||
-      hipHostMalloc((void**)&c->h_result, sizeof(int) * (2 + lay.rows), hipHostMallocDefault) != hipSuccess ||
+      hipHostMalloc((void**)&c->h_result, sizeof(int) * (2 + lay.rows + 2 * kMaxBatch), hipHostMallocDefault) !=
+          hipSuccess ||
+      hipHostMalloc((void**)&c->h_batch, lay.batch_bytes, hipHostMallocDefault) != hipSuccess ||
       hipHostMalloc((void**)&c->h_prof, 16 * (size_t)prof_pairs(*cfg), hipHostMallocDefault) != hipSuccess) {
     sv_destroy(c);
     return SV_EDEVICE;
@@ -490,6 +539,7 @@ void sv_destroy(sv_ctx* c) {
   if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
   if (c->h_params) (void)hipHostFree(c->h_params);
   if (c->h_result) (void)hipHostFree(c->h_result);
+  if (c->h_batch) (void)hipHostFree(c->h_batch);
   if (c->h_prof) (void)hipHostFree(c->h_prof);
   delete c;
 }
@@ -551,6 +601,86 @@ sv_status sv_verify(sv_ctx* c, int32_t prefix_len, const int32_t* draft_ids, int
   c->next_id = c->h_result[1];
   if (n_accepted) *n_accepted = n;
   if (next_id) *next_id = c->next_id;
+  return SV_OK;
+}
+
+sv_status sv_verify_batch(sv_ctx* const* ctxs, int32_t n, const int32_t* prefix_lens, const int32_t* ks,
+                          const int32_t* draft_ids, int32_t* n_accepted, int32_t* next_ids) {
+  if (!ctxs || n < 1 || n > kMaxBatch || !prefix_lens || !ks) return SV_EINVAL;
+  sv_ctx* c0 = ctxs[0];
+  if (!c0) return SV_EINVAL;
+  // every argument is checked before anything runs
+  int M = 0, n_drafts = 0;
+  for (int i = 0; i < n; ++i) {
+    const sv_ctx* c = ctxs[i];
+    if (!c) return SV_EINVAL;
+    for (int j = 0; j < i; ++j)
+      if (ctxs[j] == c) return SV_EINVAL;
+    sv_config a = c->cfg, b = c0->cfg;
+    a.max_prefill_rows = b.max_prefill_rows = 0;
+    if (std::memcmp(&a, &b, sizeof(sv_config)) != 0) return SV_EINVAL;
+    if (c->w.embed != c0->w.embed || c->w.lm_head != c0->w.lm_head || c->w.g_final != c0->w.g_final ||
+        std::memcmp(c->layers.data(), c0->layers.data(), sizeof(sv_layer_weights) * c0->layers.size()) != 0)
+      return SV_EINVAL;
+    if (ks[i] < 0 || ks[i] > c->cfg.max_k || (ks[i] > 0 && !draft_ids)) return SV_EINVAL;
+    if (ks[i] > 0 && !ids_ok(c, draft_ids + n_drafts, ks[i])) return SV_EINVAL;
+    if (prefix_lens[i] != c->kv_len || c->next_id < 0) return SV_ESTATE;
+    if ((int64_t)c->kv_len + ks[i] + 1 > c->cfg.max_ctx) return SV_ENOSPACE;
+    M += ks[i] + 1;
+    n_drafts += ks[i];
+  }
+  if (M > c0->lay.rows) return SV_EINVAL;
+
+  // rows, their sequences, the sequence table and the attention q tiles
+  std::vector<int> rows(M);
+  int* rowseq = reinterpret_cast<int*>(c0->h_batch);
+  SeqDev* seqs = reinterpret_cast<SeqDev*>(c0->h_batch + (size_t)c0->lay.rows * 4);
+  int2* tiles = reinterpret_cast<int2*>(c0->h_batch + (size_t)c0->lay.rows * 4 + kMaxBatch * sizeof(SeqDev));
+  const int G = c0->cfg.n_q_heads / c0->cfg.n_kv_heads;
+  int row = 0, d = 0, n_tiles = 0, n_split = 1, logits = 0;
+  for (int i = 0; i < n; ++i) {
+    sv_ctx* c = ctxs[i];
+    const int m = ks[i] + 1;
+    SeqDev sd{};
+    sd.kv_pool = static_cast<uint16_t*>(c->buf.kv_pool);
+    sd.page_table = c->buf.page_table;
+    sd.n_pages = c->buf.n_pages;
+    sd.n_lpages = c->cfg.max_ctx / kPage;
+    sd.kv_len = c->kv_len;
+    sd.row0 = row;
+    sd.m = m;
+    seqs[i] = sd;
+    rows[row] = c->next_id;
+    for (int j = 0; j < ks[i]; ++j) rows[row + 1 + j] = draft_ids[d + j];
+    for (int j = 0; j < m; ++j) rowseq[row + j] = i;
+    for (int q = 0; q < m * G; q += 16) tiles[n_tiles++] = make_int2(i, q);
+    n_split = std::max(n_split, attn_splits_max(c->kv_len, m));
+    logits |= c->store_logits;
+    row += m;
+    d += ks[i];
+  }
+  const sv_status s = run_forward(c0, M, rows.data(), 1, n_split, n, n_tiles, logits);
+  if (s != SV_OK) return s;
+  // commit each sequence as its own verify would; observer-mode contexts get
+  // their rows' logits in their own workspace
+  for (int i = 0; i < n; ++i) {
+    sv_ctx* c = ctxs[i];
+    const int r0 = seqs[i].row0, m = seqs[i].m;
+    const int na = c0->h_result[2 + M + 2 * i], nx = c0->h_result[2 + M + 2 * i + 1];
+    if (c->store_logits && c != c0 &&
+        hipMemcpyAsync(c->at<float>(c->lay.logits), c0->at<float>(c0->lay.logits) + (size_t)r0 * c0->cfg.vocab,
+                       sizeof(float) * (size_t)m * c0->cfg.vocab, hipMemcpyDeviceToDevice, c0->stream) != hipSuccess)
+      return SV_EDEVICE;
+    for (int r = 0; r < m; ++r) c->last_argmax[r] = c0->h_result[2 + r0 + r];
+    for (int r = 0; r <= na; ++r) c->hist[c->kv_len + r] = c0->h_result[2 + r0 + r];
+    c->kv_len += na + 1;
+    c->next_id = nx;
+    c->last_rows = m;
+    c->last_stored_logits = c->store_logits;
+    if (n_accepted) n_accepted[i] = na;
+    if (next_ids) next_ids[i] = nx;
+  }
+  if (hipStreamSynchronize(c0->stream) != hipSuccess) return SV_EDEVICE;
   return SV_OK;
 }
 

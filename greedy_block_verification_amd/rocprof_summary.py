@@ -1,7 +1,7 @@
 """Condense rocprofv3 CSV output into the short text summaries kept under
 ``profiles/``.
 
-Two commands:
+Three commands:
 
 * ``stats``: per-kernel duration table from ``*_kernel_trace.csv`` (all
   dispatches, and the last ``--last`` dispatches of ``--kernel``, which are the
@@ -10,6 +10,11 @@ Two commands:
   (``FETCH_SIZE`` and ``WRITE_SIZE``, KiB per dispatch).  Each counter is
   scaled by what it reads for the largest plain device-to-device copy in the
   same run (``bench.py --copy-probe-mib``), whose true size is known.
+* ``mfma``: MFMA rate and busy fraction per kernel from one ``--pmc`` run of
+  ``SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16
+  SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE``: FLOPs = MOPS x 512 over the
+  dispatch's own duration, against the dense bf16 / fp16 peak; busy % =
+  MFMA busy cycles / (GPU active cycles per XCC x SIMDs).
 
 Usage::
 
@@ -131,6 +136,43 @@ def _table(args, scale_f, scale_w):
     open(args.table_out, "w").write("\n".join(lines) + "\n")
 
 
+PEAK_MFMA_16BIT_TFLOPS = 2500.0   # dense bf16 / fp16
+
+
+def mfma(args):
+    per = defaultdict(lambda: defaultdict(dict))
+    for r in csv.DictReader(open(args.counters)):
+        d = per[r["Kernel_Name"]][int(r["Dispatch_Id"])]
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    need = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+    lines = [f"# MFMA rate per kernel: {args.title}", "", "Command:", "", "```", args.command, "```", "",
+             f"FLOPs = (MOPS_BF16 + MOPS_F16) x 512 per dispatch over its duration; peak {PEAK_MFMA_16BIT_TFLOPS:.0f} "
+             f"TFLOP/s dense 16-bit.  Busy % = MFMA busy cycles / (GRBM_GUI_ACTIVE / {args.xcc} XCCs x "
+             f"{args.simds} SIMDs).  Means over the last {args.last} dispatches of each kernel.", "",
+             "| kernel | dispatches | mean us | MFMA GFLOP per dispatch | MFMA TFLOP/s | % of peak | MFMA busy % |",
+             "|---|---|---|---|---|---|---|"]
+    rows = []
+    for k, ds in per.items():
+        ds = [ds[i] for i in sorted(ds)][-args.last:]
+        ds = [d for d in ds if all(n in d for n in need)]
+        if not ds:
+            continue
+        ns = sum(d["ns"] for d in ds) / len(ds)
+        fl = sum((d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] + d["SQ_INSTS_VALU_MFMA_MOPS_F16"]) * 512 for d in ds) / len(ds)
+        if fl <= 0:
+            continue
+        busy = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in ds) / len(ds)
+        gui = sum(d["GRBM_GUI_ACTIVE"] for d in ds) / len(ds)
+        tf = fl / ns / 1e3
+        util = 100.0 * busy / (gui / args.xcc * args.simds) if gui > 0 else 0.0
+        rows.append((tf, f"| `{_short(k)}` | {len(ds)} | {ns / 1000:.2f} | {fl / 1e9:.2f} | {tf:.1f} | "
+                         f"{100 * tf / PEAK_MFMA_16BIT_TFLOPS:.1f} | {util:.1f} |"))
+    lines += [r for _, r in sorted(rows, key=lambda x: -x[0])]
+    open(args.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -154,8 +196,16 @@ def main():
     t.add_argument("--table-out", default="")
     t.add_argument("--table-last", type=int, default=200)
     t.add_argument("--title", default="")
+    m = sub.add_parser("mfma")
+    m.add_argument("--counters", required=True)
+    m.add_argument("--last", type=int, default=1000)
+    m.add_argument("--xcc", type=int, default=8)
+    m.add_argument("--simds", type=int, default=1024)
+    m.add_argument("--title", default="")
+    m.add_argument("--command", required=True)
+    m.add_argument("--out", required=True)
     a = ap.parse_args()
-    stats(a) if a.cmd == "stats" else traffic(a)
+    {"stats": stats, "traffic": traffic, "mfma": mfma}[a.cmd](a)
 
 
 if __name__ == "__main__":

@@ -164,6 +164,26 @@ sv_status sv_decode_step(sv_ctx *ctx, int32_t token, int32_t *next_id);
 sv_status sv_verify(sv_ctx *ctx, int32_t prefix_len, const int32_t *draft_ids, int32_t k,
                     int32_t *n_accepted, int32_t *next_id);
 
+/* Batched greedy block verify: n contexts of one model (identical sv_config
+ * apart from max_prefill_rows, identical weight pointers) each verify their
+ * own window -- rows [next_id_i, draft_ids of i] at positions kv_len_i ..
+ * kv_len_i + k_i -- in ONE forward of M = sum(k_i + 1) rows.  Rows of
+ * different sequences meet only in the weight GEMMs, whose per-row
+ * arithmetic does not depend on the other rows, and attention reads each
+ * row's own sequence's KV pool and page table; so every context ends in
+ * exactly the state (KV bits, history, next_id, observer logits) that
+ * sv_verify on it alone gives, whatever the batch holds or its order.
+ * ks: host int32 [n], 0 <= k_i <= max_k; draft_ids: host int32 [sum k_i],
+ * sequence i's drafts after sequence i-1's; prefix_lens: host int32 [n],
+ * each equal to that context's kv_len (SV_ESTATE otherwise).  n_accepted,
+ * next_ids: host int32 [n] outputs (may be NULL).  1 <= n <= 64; M at most
+ * the rows of ctxs[0] (64, or its max_prefill_rows when larger): the forward
+ * runs in ctxs[0]'s workspace on its stream.  Contexts must be distinct.
+ * Errors: SV_EINVAL (shapes, ids, mismatched contexts, too many rows),
+ * SV_ESTATE, SV_ENOSPACE; all checked before any launch. */
+sv_status sv_verify_batch(sv_ctx *const *ctxs, int32_t n, const int32_t *prefix_lens, const int32_t *ks,
+                          const int32_t *draft_ids, int32_t *n_accepted, int32_t *next_ids);
+
 /* Roll back to the first new_len committed positions in O(1) ("Phase 23:
  * Speculative Verify Parity", section 2, step 5): kv_len = new_len and
  * next_id = the greedy id recorded after position new_len - 1.  KV past

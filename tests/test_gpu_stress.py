@@ -9,7 +9,9 @@ GPU-vs-GPU properties that hold at any size:
   equals the state built by one-token commits (logits and KV bits);
 * planted near-ties in the LM head (a row copied exactly, and a row one
   bf16 ulp away) resolve identically in verify and decode, and an exact tie
-  goes to the lower id.
+  goes to the lower id;
+* rows straddling a change of the attention split plan, and a 32640-id
+  prompt prefilled through the row-tiled kernels, verify == decode bitwise.
 """
 import numpy as np
 import pytest
@@ -100,6 +102,34 @@ def test_stress_verify_equals_decode_across_split_plan_changes(stress, kv_len):
     np.testing.assert_array_equal(a.kv_positions(kv_len + 1, kv_len - 4), b.kv_positions(kv_len + 1, kv_len - 4))
     a.close()
     b.close()
+
+
+def test_stress_prefilled_32k_context_verify_equals_decode(q8b_device):
+    """A 32640-id prompt prefilled through the row-tiled kernels (2048-row
+    forwards), then a K = 8 verify at that context: bit-identical to one-token
+    decodes of the same rows."""
+    from greedy_block_verification_amd.session import Session
+    from seeded_inputs import get_config, prompt_ids
+    dev, w = q8b_device
+    cfg = get_config("q8b_stress")
+    ids = prompt_ids(cfg.seed, 900, 32640, cfg.vocab).tolist()
+    a = Session(dev, cfg=cfg, prefill_rows=2048)
+    nx = a.prefill(ids)
+    assert a.kv_len == 32640 and a.next_id == nx
+    snap = a.snapshot()
+    a.close()
+    drafts = np.random.default_rng(9).integers(0, cfg.vocab, 8).tolist()
+    b, c = _sess(dev, cfg, snap), _sess(dev, cfg, snap)
+    dec = []
+    for t in [b.next_id] + drafts:
+        b.decode_step(t)
+        dec.append((b.last_argmax()[0], b.logits(0)))
+    c.verify(drafts)
+    for r in range(9):
+        assert c.last_argmax()[r] == dec[r][0]
+        np.testing.assert_array_equal(_bits(c.logits(r)), _bits(dec[r][1]))
+    b.close()
+    c.close()
 
 
 def test_stress_rollback_at_every_index(stress):
