@@ -94,6 +94,7 @@ struct AttnArgs {
   int n_tiles;
   // set by launch_attention
   int spw;               // splits per workgroup
+  int wpb;               // waves per workgroup
   int final_fold;        // 1: one workgroup per KV head folds its splits in LDS and writes the output
 };
 

@@ -819,6 +819,153 @@ __global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
   prof_end(a.prof);
 }
 
+// bf16 items in groups, stages outermost (17..33 rows whose activation planes
+// do not fit one LDS stage): a workgroup takes its items IG at a time and,
+// for each stage of one chunk per wave (two LDS buffers; the next stage's
+// planes come to registers while this one computes), runs that stage for all
+// IG items, so the planes are staged once per group instead of once per
+// item, and the weight ring never waits for them.  Wave w still adds chunks
+// w, w + NW, w + 2 NW, ... of each item in that order (one per stage) and an
+// item's wave partials meet in LDS in wave order: the weight-streaming
+// kernel's sums.  Ring slot ig streams item ig of the group; the slots of a
+// partial last group re-read the workgroup's last item, and those items are
+// not finished.
+constexpr int kGrpStageRegs = 5;
+struct GrpStageRegs {   // plain members: they stay in registers
+  uint4 v0, v1, v2, v3, v4;
+};
+__host__ __device__ __forceinline__ bool grp_fits(int M, int waves) {
+  return 2 * (size_t)M * (waves * 32 + 8) * 4 <= (size_t)kStageBytes && 2 * M * 4 <= kGrpStageRegs * 64;
+}
+
+template <int TM, int ROLE, int IG>
+__global__ __launch_bounds__(1024) void k_gemm_grp(GemmArgs a) {
+  __shared__ GemmShared sh;
+  __shared__ __align__(16) uint16_t stage_mem[kStageBytes / 2];
+  prof_start(a.prof);
+  const int nw = a.S, nthr = 64 * a.S;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int j = lane & 15, g = lane >> 4;
+  const int KC = a.K >> 5;
+  const int n_st = KC / nw;                     // stages of one chunk per wave
+  const int stride = nw * 32 + 8;
+  const int buf_elems = 2 * a.M * stride;
+  auto stage_buf = [&](int b) {
+    Stage x;
+    x.stride = stride;
+    x.hi = stage_mem + b * buf_elems;
+    x.lo = x.hi + (size_t)a.M * stride;
+    return x;
+  };
+  auto fetch = [&](int s) {                     // planes of stage s into registers (unconditional loads)
+    GrpStageRegs r;
+    r.v0 = *reinterpret_cast<const uint4*>(stage_src(a, s * nw, nw, 32, 0, nthr));
+    r.v1 = *reinterpret_cast<const uint4*>(stage_src(a, s * nw, nw, 32, 1, nthr));
+    r.v2 = *reinterpret_cast<const uint4*>(stage_src(a, s * nw, nw, 32, 2, nthr));
+    r.v3 = *reinterpret_cast<const uint4*>(stage_src(a, s * nw, nw, 32, 3, nthr));
+    r.v4 = *reinterpret_cast<const uint4*>(stage_src(a, s * nw, nw, 32, 4, nthr));
+    return r;
+  };
+  auto store = [&](const Stage& st, const GrpStageRegs& r) {
+    stage_put(a, st, nw, 32, 0, r.v0, &sh.dummy, nthr);
+    stage_put(a, st, nw, 32, 1, r.v1, &sh.dummy, nthr);
+    stage_put(a, st, nw, 32, 2, r.v2, &sh.dummy, nthr);
+    stage_put(a, st, nw, 32, 3, r.v3, &sh.dummy, nthr);
+    stage_put(a, st, nw, 32, 4, r.v4, &sh.dummy, nthr);
+  };
+  const int n_items = a.N >> 4;
+  const int n_my = (n_items - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;   // items of this workgroup (>= 1)
+  const int n_grp = (n_my + IG - 1) / IG;
+  const uint4* W4 = reinterpret_cast<const uint4*>(a.W) + lane;
+  auto item_of = [&](int grp, int ig) {
+    const int k = grp * IG + ig;
+    return (int)blockIdx.x + (k < n_my ? k : n_my - 1) * (int)gridDim.x;
+  };
+  auto chunk = [&](int grp, int s, int ig) {   // chunk wave + nw s of slot ig's item
+    return ld_stream(W4 + ((size_t)item_of(grp, ig) * KC + wave + (size_t)nw * s) * 64);
+  };
+
+  GrpStageRegs sr = fetch(0);
+  uint4 A[IG];
+#pragma unroll
+  for (int ig = 0; ig < IG; ++ig) A[ig] = chunk(0, 0, ig);
+  row_best_init<ROLE>(a, sh);
+  if (norm_role(ROLE)) rows_inv_rms(a, sh, wave, lane, nw);   // read only by the epilogue
+  store(stage_buf(0), sr);
+  __syncthreads();
+  int buf = 0;
+  for (int grp = 0; grp < n_grp; ++grp) {
+    EpiPre pre[IG];
+#pragma unroll
+    for (int ig = 0; ig < IG; ++ig) pre[ig] = epi_load<ROLE>(a, item_of(grp, ig), threadIdx.x);
+    f32x4 acc[IG][TM];
+#pragma unroll
+    for (int ig = 0; ig < IG; ++ig)
+#pragma unroll
+      for (int rt = 0; rt < TM; ++rt) acc[ig][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < n_st; ++s) {
+      // the ring's next round: the next stage of this group, else stage 0 of
+      // the next group, else (end of the stream) this round again
+      int gn = grp, sn = s + 1;
+      if (sn == n_st) {
+        sn = 0;
+        gn = grp + 1;
+        if (gn == n_grp) {
+          gn = grp;
+          sn = s;
+        }
+      }
+      sr = fetch(s + 1 < n_st ? s + 1 : 0);
+      const Stage st = stage_buf(buf);
+      const int kl = wave * 32 + g * 8;         // this wave's chunk inside the stage
+#pragma unroll
+      for (int ig = 0; ig < IG; ++ig) {
+#pragma unroll
+        for (int rt = 0; rt < TM; ++rt)
+          acc[ig][rt] = mfma_pair(A[ig], lds_pair(st, row_of(rt * 16 + j, a.M), kl), acc[ig][rt]);
+        A[ig] = chunk(gn, sn, ig);
+      }
+      // the other buffer was last read in the previous stage, before the
+      // previous barrier; after this barrier every wave reads the new one
+      store(stage_buf(buf ^ 1), sr);
+      __syncthreads();
+      buf ^= 1;
+    }
+#pragma unroll
+    for (int ig = 0; ig < IG; ++ig)
+      if (grp * IG + ig < n_my) gemm_finish<TM, ROLE>(a, sh, acc[ig], item_of(grp, ig), wave, lane, nw, pre[ig]);
+  }
+  row_best_publish<ROLE>(a, sh);
+  prof_end(a.prof);
+}
+
+// Group size: up to the workgroup's item count, capped where the
+// accumulators, ring slots and epilogue prefetches still fit 128 VGPRs
+// without spilling (4 for one row tile, 2 for two or three; QKV, whose
+// epilogue prefetch is largest, one less step).
+template <int TM, int ROLE>
+constexpr int grp_max_items() {
+  return TM == 1 ? (ROLE == kRoleQkv ? 2 : 4) : (TM == 2 ? 2 : (ROLE == kRoleQkv ? 1 : 2));
+}
+template <int TM, int ROLE>
+static void launch_grp(const GemmArgs& a, int grid, int per, hipStream_t st) {
+  constexpr int IGM = grp_max_items<TM, ROLE>();
+  const dim3 block(64 * a.S), g(grid);
+  if (IGM >= 4 && per >= 4) hipLaunchKernelGGL((k_gemm_grp<TM, ROLE, (IGM >= 4 ? 4 : 1)>), g, block, 0, st, a);
+  else if (IGM >= 2 && per >= 2) hipLaunchKernelGGL((k_gemm_grp<TM, ROLE, (IGM >= 2 ? 2 : 1)>), g, block, 0, st, a);
+  else hipLaunchKernelGGL((k_gemm_grp<TM, ROLE, 1>), g, block, 0, st, a);
+}
+template <int ROLE>
+static hipError_t gemm_dispatch_grp(const GemmArgs& a, int grid, hipStream_t st) {
+  const int tm = (a.M + 15) / 16;
+  const int per = ((a.N >> 4) + grid - 1) / grid;   // most items of one workgroup
+  if (tm == 1) launch_grp<1, ROLE>(a, grid, per, st);
+  else if (tm == 2) launch_grp<2, ROLE>(a, grid, per, st);
+  else if (tm == 3) launch_grp<3, ROLE>(a, grid, per, st);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 template <int ROLE, bool INT4, int NB>
 static hipError_t gemm_dispatch_nb(const GemmArgs& a, int grid, hipStream_t st, bool dbl) {
   const dim3 block(64 * a.S);
@@ -929,6 +1076,18 @@ hipError_t launch_gemm(const GemmArgs& a, int role, int grid, hipStream_t st) {
   if (a.M > gemm_max_rows(a.fmt == 1 ? 128 : 32, a.S)) return hipErrorInvalidValue;
   grid = grid > (a.N >> 4) ? (a.N >> 4) : grid;
   const bool i4 = a.fmt == 1;
+  // 17..33 rows whose bf16 planes do not fit one stage: items in groups,
+  // stages outermost (for 9..16 rows the restaging kernel is faster)
+  if (!i4 && a.M >= 17 && grp_fits(a.M, a.S) && stage_chunks(a.K >> 5, a.S, a.M, 32, 1) < (a.K >> 5)) {
+    switch (role) {
+      case kRoleQkv: return gemm_dispatch_grp<kRoleQkv>(a, grid, st);
+      case kRoleO: return gemm_dispatch_grp<kRoleO>(a, grid, st);
+      case kRoleGateUp: return gemm_dispatch_grp<kRoleGateUp>(a, grid, st);
+      case kRoleDown: return gemm_dispatch_grp<kRoleDown>(a, grid, st);
+      case kRoleLmHead: return gemm_dispatch_grp<kRoleLmHead>(a, grid, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (role) {
     case kRoleQkv: return i4 ? gemm_dispatch<kRoleQkv, true>(a, grid, st) : gemm_dispatch<kRoleQkv, false>(a, grid, st);
     case kRoleO: return i4 ? gemm_dispatch<kRoleO, true>(a, grid, st) : gemm_dispatch<kRoleO, false>(a, grid, st);
@@ -1193,11 +1352,12 @@ struct Fold {
 // poisoned cache never meets p = 0 as 0 * NaN.
 //
 // Workgroup (x, h): q tile qt = x % n_qt and splits [s_lo, s_lo + spw) with
-// s_lo = (x / n_qt) * spw; unit u = split s_lo + u on wave u % 8.  With
+// s_lo = (x / n_qt) * spw; unit u = split s_lo + u on wave u % wpb.  With
 // final_fold (spw covers every split) the partials go to LDS and the
 // workgroup folds each row's splits and writes its output planes; otherwise
 // they go to the global partial buffer for the combine kernel.
 constexpr int kAttnLdsUnits = 16;
+constexpr int kAttnSplitWaves = 4;   // waves (one split each) per workgroup when splits go to the combine pass
 
 template <int DH>
 struct AttnUnitLds {
@@ -1381,11 +1541,11 @@ __device__ __forceinline__ void attn_split_union(int kv_len, int r0, int r1, int
   }
 }
 
-template <int DH>
+template <int DH, bool FOLD>
 __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   constexpr int DC = DH / 32;            // d chunks of the score MFMA
   constexpr int DT = DH / 16;            // d tiles of the P.V MFMA
-  __shared__ AttnUnitLds<DH> ul[kAttnLdsUnits];
+  __shared__ AttnUnitLds<DH> ul[FOLD ? kAttnLdsUnits : 1];
 
   prof_start(a.prof);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -1443,7 +1603,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     qop[c] = have ? split8_f16(qv) : bzero();
   }
 
-  for (int sp = s_lo + wave; sp < s_hi; sp += 8) {     // wave-uniform
+  for (int sp = s_lo + wave; sp < s_hi; sp += a.wpb) {     // wave-uniform
     int lo = 0, hi = 0;
     if (have && sp < attn_ns(ctx)) {
       const int bps = attn_bps(ctx);
@@ -1471,7 +1631,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     }
 
     // lane (g, j) holds o of q-row j for d = 16dt + 4g + v
-    if (a.final_fold) {
+    if constexpr (FOLD) {
       AttnUnitLds<DH>& U = ul[sp];
       if (g == 0) { U.m[j] = m; U.l[j] = l; }
 #pragma unroll
@@ -1486,7 +1646,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     }
   }
 
-  if (a.final_fold) {
+  if constexpr (FOLD) {
     __syncthreads();
     // every split of this tile is here: thread (jj, d0) folds 4 outputs of q-row jj in split order
     constexpr int TPR = DH / 4;              // threads per q-row
@@ -1639,19 +1799,18 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   const int ns = attn_ns(ctx);
   const float4* base = reinterpret_cast<const float4*>(a.part + ((size_t)r * a.nq + j) * a.part_splits * (DH + 4));
   const int n4 = ns * ((DH + 4) / 4);
-  constexpr int U = 8;   // 8 loads in flight per thread before their LDS stores
-  for (int i0 = threadIdx.x; i0 < n4; i0 += U * 256) {
-    float4 v[U];
+  // every record of the row in one round of loads (at most 17 per thread)
+  constexpr int U = (kAttnMaxSplits * (DH + 4) / 4 + 255) / 256;
+  float4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + u * 256;
-      v[u] = base[i < n4 ? i : 0];
-    }
+  for (int u = 0; u < U; ++u) {
+    const int i = threadIdx.x + u * 256;
+    v[u] = base[i < n4 ? i : 0];
+  }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + u * 256;
-      if (i < n4) rec[i] = v[u];
-    }
+  for (int u = 0; u < U; ++u) {
+    const int i = threadIdx.x + u * 256;
+    if (i < n4) rec[i] = v[u];
   }
   __syncthreads();
   const float* p = reinterpret_cast<const float*>(rec);
@@ -1659,6 +1818,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   if (d < DH) {
     Fold f;
     f.first(p[0], p[1], p[4 + d]);
+#pragma unroll 8
     for (int i = 1; i < ns; ++i) f.add(p[i * (DH + 4)], p[i * (DH + 4) + 1], p[i * (DH + 4) + 4 + d]);
     const size_t oi = (size_t)r * a.nq * DH + (size_t)j * DH + d;
     split1(f.o / f.l, a.ohi[oi], a.olo[oi]);
@@ -1674,14 +1834,21 @@ hipError_t launch_attention(const AttnArgs& a_in, hipStream_t st) {
       (a.n_split > kAttnLdsUnits && a.n_split > a.part_splits))
     return hipErrorInvalidValue;
   const int n_qt = a.seqs != nullptr ? a.n_tiles : (a.M * G + 15) / 16;
+  // up to 16 splits: one workgroup of 8 waves per (q tile, KV head) folds
+  // them in LDS; more: workgroups of kAttnSplitWaves waves, one split each,
+  // and the combine pass
   a.final_fold = a.n_split <= kAttnLdsUnits ? 1 : 0;
-  a.spw = a.final_fold ? a.n_split : 8;
+  a.spw = a.final_fold ? a.n_split : kAttnSplitWaves;
+  a.wpb = a.final_fold ? 8 : kAttnSplitWaves;
   const int n_wg = n_qt * ((a.n_split + a.spw - 1) / a.spw);
+  const dim3 grid(n_wg, a.nkv), block(64 * a.wpb);
   if (a.dh == 128) {
-    hipLaunchKernelGGL(k_attn_mfma<128>, dim3(n_wg, a.nkv), dim3(512), 0, st, a);
+    if (a.final_fold) hipLaunchKernelGGL((k_attn_mfma<128, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_attn_mfma<128, false>), grid, block, 0, st, a);
     if (!a.final_fold) hipLaunchKernelGGL(k_attn_combine<128>, dim3(a.nq, a.M), dim3(256), 0, st, a);
   } else if (a.dh == 64) {
-    hipLaunchKernelGGL(k_attn_mfma<64>, dim3(n_wg, a.nkv), dim3(512), 0, st, a);
+    if (a.final_fold) hipLaunchKernelGGL((k_attn_mfma<64, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_attn_mfma<64, false>), grid, block, 0, st, a);
     if (!a.final_fold) hipLaunchKernelGGL(k_attn_combine<64>, dim3(a.nq, a.M), dim3(256), 0, st, a);
   } else {
     return hipErrorInvalidValue;
