@@ -161,6 +161,87 @@ def run_spec_batch(sessions, truth, prompt_len, gen, k, srcs, n_steps):
     return st
 
 
+def run_draft_loop(args, cfg, sessions, truth, prompts, L, G, decode_tpot_ms):
+    """The draft model in the loop (draft_loop.DraftLoop): per round, K draft
+    decodes of the pending token and the proposals, one target verify, the
+    draft's rollback.  Proposals come from the seeded synthetic windows (the
+    random-init draft's own guesses would almost never match), but the draft
+    decodes them, so its cost is the real one.  Reports end-to-end committed
+    tokens/s with the draft and verify time split, against plain decoding."""
+    from greedy_block_verification_amd.draft_loop import DraftLoop
+    from greedy_block_verification_amd.session import DeviceModel, Session
+    from greedy_block_verification_amd import metrics
+    from seeded_inputs import DraftSource, generate_weights, get_config
+    import torch
+    dcfg = get_config(args.draft)
+    if dcfg.vocab != cfg.vocab or dcfg.max_ctx < L + G + dcfg.max_k + 1:
+        raise SystemExit(f"draft {dcfg.name} does not fit this workload (vocabulary or context)")
+    ddm = DeviceModel(generate_weights(dcfg, threads=min(16, len(os.sched_getaffinity(0)))))
+    P = len(sessions)
+    dsess = []
+    for p in range(P):
+        d = Session(ddm)
+        d.prefill(prompts[p])
+        dsess.append(d)
+    out = {"draft": f"{dcfg.name}: {dcfg.n_layers} layers, d {dcfg.d_model}"}
+    # the draft's own one-token decode rate
+    d0 = dsess[0]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    x = d0.next_id
+    for _ in range(32):
+        x = d0.decode_step(x)
+    torch.cuda.synchronize()
+    draft_tpot_ms = 1000.0 * (time.perf_counter() - t0) / 32
+    d0.truncate(L)
+    out["draft_decode_tpot_ms"] = round(draft_tpot_ms, 4)
+    base_tok_s = 1000.0 / decode_tpot_ms
+    for k in [int(v) for v in args.draft_ks.split(",") if v.strip()]:
+        if k > min(cfg.max_k, dcfg.max_k):
+            continue
+        done = [0] * P
+        srcs = [DraftSource(cfg.seed, 40_000 + p, cfg.vocab, p_correct=args.p_correct) for p in range(P)]
+
+        def proposer_for(p):
+            return lambda kk: srcs[p].window(truth[p][done[p] + 1: done[p] + 1 + kk], kk)
+        loops = [DraftLoop(sessions[p], dsess[p], proposer_for(p)) for p in range(P)]
+        tokens = mism = 0
+        p = 0
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.sweep_steps):
+            c = done[p]
+            k_eff = min(k, G - c - 1)
+            got = loops[p].step(k_eff)
+            mism += sum(int(a != b) for a, b in zip(got, truth[p][c: c + len(got)]))
+            tokens += len(got)
+            done[p] = c + len(got)
+            if done[p] >= G:
+                sessions[p].truncate(L)
+                dsess[p].truncate(L)
+                done[p] = 0
+                p = (p + 1) % P
+        torch.cuda.synchronize()
+        sec = time.perf_counter() - t0
+        for q in range(P):
+            if sessions[q].kv_len != L:
+                sessions[q].truncate(L)
+                dsess[q].truncate(L)
+        acc = sum(lp.accepted for lp in loops)
+        prop = sum(lp.proposed for lp in loops)
+        e2e = tokens / sec
+        out[f"K={k}"] = {"e2e_tok_s": round(e2e, 1),
+                         "draft_ms_per_round": round(1000.0 * sum(lp.draft_s for lp in loops) / args.sweep_steps, 4),
+                         "verify_ms_per_round": round(1000.0 * sum(lp.verify_s for lp in loops) / args.sweep_steps, 4),
+                         "acceptance_rate": round(metrics.acceptance_rate(acc, prop), 4),
+                         "speedup_e2e": round(metrics.speedup(e2e, base_tok_s), 4),
+                         "verify_decode_mismatches": mism}
+        log(f"[bench] draft loop K={k}: {out[f'K={k}']}")
+    for d in dsess:
+        d.close()
+    return out
+
+
 def cpu_baseline(weights, ids, n_tokens, steps):
     """The fp64 oracle's per-token decoder on this host (bounded sample)."""
     import numpy as np
@@ -217,6 +298,9 @@ def main():
     ap.add_argument("--gen-tokens", type=int, default=None)
     ap.add_argument("--p-correct", type=float, default=None)
     ap.add_argument("--cpu-tokens", type=int, default=3)
+    ap.add_argument("--draft", default="", help="also run the draft model in the loop: a workload name "
+                    "(e.g. q06b) whose model drafts for this one (same vocabulary)")
+    ap.add_argument("--draft-ks", default="1,2,4,8", help="window sizes of the draft loop")
     ap.add_argument("--batch", default="",
                     help="also time batched verify (sv_verify_batch) of B sequences per step, "
                          "for each B in this comma list (needs --prompts >= B)")
@@ -371,6 +455,8 @@ def main():
         log(f"[bench] batch B={b} K={args.k}: {bsweep[f'B={b}']}")
     if bsweep:
         extra["batch_sweep"] = bsweep
+    if args.draft:
+        extra["draft_loop"] = run_draft_loop(args, cfg, sessions, truth, prompts, L, G, decode_tpot_ms)
 
     cpu = None
     if L > 4096:

@@ -64,6 +64,10 @@ SIGNATURES = {
     "sv_verify_batch": (C.c_int, [C.POINTER(C.c_void_p), C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
                                   C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
     "sv_kv_truncate": (C.c_int, [C.c_void_p, C.c_int32]),
+    "sv_topk": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_float)]),
+    "sv_selected_logits": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_int32), C.c_int32,
+                                     C.POINTER(C.c_float)]),
+    "sv_clone_state": (C.c_int, [C.c_void_p, C.c_void_p]),
     "sv_kv_len": (C.c_int32, [C.c_void_p]),
     "sv_next_id": (C.c_int32, [C.c_void_p]),
     "sv_set_debug": (C.c_int, [C.c_void_p, C.c_int32]),
@@ -171,6 +175,24 @@ def sv_verify_batch(ctxs, prefix_lens, drafts):
     _check(lib().sv_verify_batch(arr, n, _i32_array(prefix_lens), _i32_array([len(d) for d in drafts]),
                                  _i32_array(flat), na, nx), "sv_verify_batch")
     return [(na[i], nx[i]) for i in range(n)]
+
+
+def sv_topk(ctx, row: int, k: int):
+    """[(id, logit)] of the k largest logits of a row of the last forward."""
+    ids, vals = (C.c_int32 * k)(), (C.c_float * k)()
+    _check(lib().sv_topk(ctx, int(row), int(k), ids, vals), "sv_topk")
+    return [(ids[i], vals[i]) for i in range(k)]
+
+
+def sv_selected_logits(ctx, row: int, ids):
+    n = len(ids)
+    vals = (C.c_float * max(1, n))()
+    _check(lib().sv_selected_logits(ctx, int(row), _i32_array(ids), n, vals), "sv_selected_logits")
+    return [vals[i] for i in range(n)]
+
+
+def sv_clone_state(dst, src):
+    _check(lib().sv_clone_state(dst, src), "sv_clone_state")
 
 
 def sv_kv_truncate(ctx, new_len: int):

@@ -125,6 +125,15 @@ hipError_t launch_accept(const int* params, int M, int verify, const unsigned lo
 // next_s = argmax of row row0_s + n_s, at result[2 + M + 2 s], [2 + M + 2 s + 1].
 hipError_t launch_accept_batch(const int* params, int M, const SeqDev* seqs, int n_seq,
                                const unsigned long long* best, int* result, hipStream_t st);
+// Audit mode.  Top-k of an fp32 row in argmax-key order (cand: kTopkBlocks *
+// kTopkMax scratch keys, out: k keys), selected-logit gather, and the copy of
+// one context's committed KV pages into another's pool.
+constexpr int kTopkMax = 64, kTopkSlice = 1024, kTopkBlocks = 1024;
+hipError_t launch_topk(const float* row, int V, int k, unsigned long long* cand, unsigned long long* out,
+                       hipStream_t st);
+hipError_t launch_gather(const float* row, const int* ids, int n, float* out, hipStream_t st);
+hipError_t launch_copy_pages(const void* src, const int* src_pt, int src_pages, void* dst, const int* dst_pt,
+                             int dst_pages, int n_lp, int n_layers, int page_bytes, hipStream_t st);
 // Profiling slots: (start, end) pairs set to (max, 0) before a forward.
 hipError_t launch_prof_reset(unsigned long long* slots, int n_pairs, hipStream_t st);
 hipError_t launch_pack(int fmt, int layout, const void* src0, const void* src0_scales, const void* src1,

@@ -1958,6 +1958,97 @@ hipError_t launch_accept_batch(const int* params, int M, const SeqDev* seqs, int
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------ audit mode
+// Top-k of one fp32 logits row by the argmax key order (larger logit first,
+// the lower id among equal logits): every block takes k rounds of a block
+// max over its slice (the winner is removed each round), then one block
+// does the same over the blocks' candidates.  k <= kTopkMax.
+__device__ __forceinline__ unsigned long long block_max_key(unsigned long long v, unsigned long long* lds16) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = umax64(v, __shfl_xor(v, o));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) lds16[w] = v;
+  __syncthreads();
+  unsigned long long m = 0ull;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) m = umax64(m, lds16[i]);
+  return m;
+}
+
+__global__ __launch_bounds__(256) void k_topk_blocks(const float* __restrict__ row, int V, int k,
+                                                     unsigned long long* __restrict__ cand) {
+  __shared__ unsigned long long keys[kTopkSlice];
+  __shared__ unsigned long long red[16];
+  const int per = (V + gridDim.x - 1) / gridDim.x;
+  const int lo = blockIdx.x * per, n = min(per, V - lo);
+  for (int i = threadIdx.x; i < kTopkSlice; i += blockDim.x)
+    keys[i] = i < n ? argmax_key(row[lo + i], (uint32_t)(lo + i)) : 0ull;
+  __syncthreads();
+  for (int r = 0; r < k; ++r) {
+    unsigned long long v = 0ull;
+    for (int i = threadIdx.x; i < kTopkSlice; i += blockDim.x) v = umax64(v, keys[i]);
+    const unsigned long long m = block_max_key(v, red);
+    if (threadIdx.x == 0) cand[(size_t)blockIdx.x * k + r] = m;
+    for (int i = threadIdx.x; i < kTopkSlice; i += blockDim.x)
+      if (keys[i] == m && m != 0ull) keys[i] = 0ull;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void k_topk_merge(unsigned long long* __restrict__ cand, int n, int k,
+                                                    unsigned long long* __restrict__ out) {
+  __shared__ unsigned long long red[16];
+  for (int r = 0; r < k; ++r) {
+    unsigned long long v = 0ull;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) v = umax64(v, cand[i]);
+    const unsigned long long m = block_max_key(v, red);
+    if (threadIdx.x == 0) out[r] = m;
+    for (int i = threadIdx.x; i < n; i += blockDim.x)
+      if (cand[i] == m && m != 0ull) cand[i] = 0ull;
+    __syncthreads();
+  }
+}
+
+hipError_t launch_topk(const float* row, int V, int k, unsigned long long* cand, unsigned long long* out,
+                       hipStream_t st) {
+  const int blocks = (V + kTopkSlice - 1) / kTopkSlice;
+  if (k < 1 || k > kTopkMax || blocks > kTopkBlocks) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_topk_blocks, dim3(blocks), dim3(256), 0, st, row, V, k, cand);
+  hipLaunchKernelGGL(k_topk_merge, dim3(1), dim3(256), 0, st, cand, blocks * k, k, out);
+  return hipGetLastError();
+}
+
+// Selected logits: out[i] = row[ids[i]].
+__global__ __launch_bounds__(256) void k_gather(const float* __restrict__ row, const int* __restrict__ ids, int n,
+                                                float* __restrict__ out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = row[ids[i]];
+}
+hipError_t launch_gather(const float* row, const int* ids, int n, float* out, hipStream_t st) {
+  if (n < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_gather, dim3((n + 255) / 256), dim3(256), 0, st, row, ids, n, out);
+  return hipGetLastError();
+}
+
+// Copy the committed KV of one context into another's pool: logical pages
+// [0, n_lp) of every layer, through each context's page table (a page is
+// 2 * n_kv * 16 * dh contiguous fp16 values per layer).
+__global__ __launch_bounds__(256) void k_copy_pages(const uint4* __restrict__ src, const int* __restrict__ src_pt,
+                                                    int src_pages, uint4* __restrict__ dst,
+                                                    const int* __restrict__ dst_pt, int dst_pages, int page_vecs) {
+  const int lp = blockIdx.x, layer = blockIdx.y;
+  const uint4* s = src + ((size_t)layer * src_pages + src_pt[lp]) * page_vecs;
+  uint4* d = dst + ((size_t)layer * dst_pages + dst_pt[lp]) * page_vecs;
+  for (int i = threadIdx.x; i < page_vecs; i += blockDim.x) d[i] = s[i];
+}
+hipError_t launch_copy_pages(const void* src, const int* src_pt, int src_pages, void* dst, const int* dst_pt,
+                             int dst_pages, int n_lp, int n_layers, int page_bytes, hipStream_t st) {
+  if (n_lp < 1 || page_bytes % 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_copy_pages, dim3(n_lp, n_layers), dim3(256), 0, st, (const uint4*)src, src_pt, src_pages,
+                     (uint4*)dst, dst_pt, dst_pages, page_bytes / 16);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------ weight packing
 // Pure permutation into the tile layouts above.  Row i (0..15) of output
 // tile T comes from:

@@ -28,6 +28,7 @@ struct Layout {
   int rows = 0;   // most rows of one forward: 64, or max_prefill_rows when larger
   int max_tiles = 0;   // attention q tiles of a batched forward
   size_t batch = 0, batch_bytes = 0;   // batched-forward tables: rowseq [rows], seqs [kMaxBatch], tiles
+  size_t topk = 0, sel = 0;   // audit mode: top-k scratch keys and results, selected-logit ids and values
   size_t params = 0, x = 0, ss = 0, q = 0, attn_part = 0, uplanes = 0, oplanes = 0, aplanes = 0, best = 0,
          result = 0, logits = 0, rope = 0, prof = 0, total = 0;
   int max_split = 1;
@@ -107,6 +108,8 @@ bool plans_ok(const sv_config& c, const Plans& p) {
   return c.max_k + 1 <= max_rows(c, p);
 }
 
+constexpr int kMaxSelected = 4096;   // ids of one selected-logit read
+
 // Kernel roles the profiler can time (sv_set_profile).
 constexpr int kProfRoles = 6;
 constexpr int kRoleAttn = 5;
@@ -147,6 +150,8 @@ Layout make_layout(const sv_config& c, const Plans& p) {
   L.logits = take(R * (size_t)c.vocab * 4);
   L.rope = take((size_t)c.max_ctx * (c.head_dim / 2) * 8);
   L.prof = take(prof_pairs(c) * 16);
+  L.topk = take((size_t)(kTopkBlocks + 1) * kTopkMax * 8);
+  L.sel = take((size_t)kMaxSelected * 8);
   L.total = off;
   return L;
 }
@@ -681,6 +686,71 @@ sv_status sv_verify_batch(sv_ctx* const* ctxs, int32_t n, const int32_t* prefix_
     if (next_ids) next_ids[i] = nx;
   }
   if (hipStreamSynchronize(c0->stream) != hipSuccess) return SV_EDEVICE;
+  return SV_OK;
+}
+
+// ---- audit mode
+sv_status sv_topk(sv_ctx* c, int32_t row, int32_t k, int32_t* ids, float* vals) {
+  if (!c || !ids || k < 1 || k > kTopkMax || k > c->cfg.vocab) return SV_EINVAL;
+  if (!c->last_stored_logits || c->last_rows == 0) return SV_ESTATE;
+  if (row < 0 || row >= c->last_rows) return SV_EINVAL;
+  const float* src = c->at<float>(c->lay.logits) + (size_t)row * c->cfg.vocab;
+  unsigned long long* cand = c->at<unsigned long long>(c->lay.topk);
+  unsigned long long* out = cand + (size_t)kTopkBlocks * kTopkMax;
+  std::vector<unsigned long long> h(k);
+  if (launch_topk(src, c->cfg.vocab, k, cand, out, c->stream) != hipSuccess ||
+      hipMemcpyAsync(h.data(), out, sizeof(unsigned long long) * k, hipMemcpyDeviceToHost, c->stream) != hipSuccess ||
+      hipStreamSynchronize(c->stream) != hipSuccess)
+    return SV_EDEVICE;
+  for (int i = 0; i < k; ++i) {
+    // key = (orderable logit bits, ~id): undo both maps
+    const uint32_t lo = (uint32_t)(h[i] & 0xffffffffu), hi = (uint32_t)(h[i] >> 32);
+    ids[i] = (int32_t)(0xffffffffu - lo);
+    const uint32_t u = (hi & 0x80000000u) ? (hi & 0x7fffffffu) : ~hi;
+    float f;
+    std::memcpy(&f, &u, 4);
+    if (vals) vals[i] = f;
+  }
+  return SV_OK;
+}
+
+sv_status sv_selected_logits(sv_ctx* c, int32_t row, const int32_t* ids, int32_t n, float* vals) {
+  if (!c || !ids || !vals || n < 1 || n > kMaxSelected) return SV_EINVAL;
+  if (!c->last_stored_logits || c->last_rows == 0) return SV_ESTATE;
+  if (row < 0 || row >= c->last_rows) return SV_EINVAL;
+  if (!ids_ok(c, ids, n)) return SV_EINVAL;
+  int* d_ids = c->at<int>(c->lay.sel);
+  float* d_out = reinterpret_cast<float*>(d_ids + kMaxSelected);
+  const float* src = c->at<float>(c->lay.logits) + (size_t)row * c->cfg.vocab;
+  if (hipMemcpyAsync(d_ids, ids, sizeof(int) * n, hipMemcpyHostToDevice, c->stream) != hipSuccess ||
+      launch_gather(src, d_ids, n, d_out, c->stream) != hipSuccess ||
+      hipMemcpyAsync(vals, d_out, sizeof(float) * n, hipMemcpyDeviceToHost, c->stream) != hipSuccess ||
+      hipStreamSynchronize(c->stream) != hipSuccess)
+    return SV_EDEVICE;
+  return SV_OK;
+}
+
+sv_status sv_clone_state(sv_ctx* dst, const sv_ctx* src) {
+  if (!dst || !src || dst == src) return SV_EINVAL;
+  sv_config a = dst->cfg, b = src->cfg;
+  a.max_prefill_rows = b.max_prefill_rows = 0;
+  if (std::memcmp(&a, &b, sizeof(sv_config)) != 0) return SV_EINVAL;
+  if (src->kv_len > 0) {
+    const sv_config& cfg = src->cfg;
+    const int n_lp = (src->kv_len + kPage - 1) / kPage;
+    const int page_bytes = 2 * cfg.n_kv_heads * kPage * cfg.head_dim * 2;
+    if (hipStreamSynchronize(src->stream) != hipSuccess ||
+        launch_copy_pages(src->buf.kv_pool, src->buf.page_table, src->buf.n_pages, dst->buf.kv_pool,
+                          dst->buf.page_table, dst->buf.n_pages, n_lp, cfg.n_layers, page_bytes,
+                          dst->stream) != hipSuccess ||
+        hipStreamSynchronize(dst->stream) != hipSuccess)
+      return SV_EDEVICE;
+  }
+  dst->kv_len = src->kv_len;
+  dst->next_id = src->next_id;
+  dst->hist = src->hist;
+  dst->last_rows = 0;
+  dst->last_stored_logits = 0;
   return SV_OK;
 }
 

@@ -220,6 +220,33 @@ sv_status sv_get_logits(sv_ctx *ctx, int32_t row, float *host_dst, int32_t vocab
  * *m receives M.  dst must hold max(64, max_prefill_rows) entries. */
 sv_status sv_last_argmax(const sv_ctx *ctx, int32_t *dst, int32_t *m);
 
+/* Audit mode (the diagnostics of "Phase 23: Speculative Verify Parity",
+ * section 4 -- dump the top candidates where verify and decode disagree,
+ * audit sampled steps against one-token decode -- and the selected-logit
+ * reads of "Shape and cache history in Gemma block verification", section
+ * "Next discriminating tests", which must leave the argmax bits alone: they
+ * only read the logits observer mode stored, on the device).
+ *
+ * sv_topk: the k largest logits of row `row` of the last forward, in the
+ * argmax order (larger logit first, the lower id first among equal logits;
+ * -0.0 counts as +0.0), so ids[0] is that row's argmax.  ids: host int32 [k],
+ * vals: host float [k] or NULL; 1 <= k <= 64.  SV_ESTATE if the last forward
+ * stored no logits (sv_set_debug), SV_EINVAL for a bad row or k. */
+sv_status sv_topk(sv_ctx *ctx, int32_t row, int32_t k, int32_t *ids, float *vals);
+
+/* sv_selected_logits: vals[i] = logit of ids[i] in row `row` of the last
+ * forward, gathered on the device.  ids: host int32 [n], each in
+ * [0, vocab); vals: host float [n]; 1 <= n <= 4096.  Errors as sv_topk. */
+sv_status sv_selected_logits(sv_ctx *ctx, int32_t row, const int32_t *ids, int32_t n, float *vals);
+
+/* sv_clone_state: make dst hold src's committed state -- the KV of positions
+ * [0, kv_len) (whole pages, copied on the device through both page tables),
+ * the greedy history, kv_len and next_id -- so a decode audit can replay a
+ * step of src on dst.  Both contexts must have the same sv_config apart from
+ * max_prefill_rows (SV_EINVAL otherwise, or if dst == src).  dst's observer
+ * logits are dropped. */
+sv_status sv_clone_state(sv_ctx *dst, const sv_ctx *src);
+
 /* Measurement (the per-kernel timing a roofline figure needs): every launch
  * of an enabled kernel role stamps the device's constant-rate wall clock
  * (hipDeviceAttributeWallClockRate) when its first workgroup starts and when
