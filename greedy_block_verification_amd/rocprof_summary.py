@@ -62,10 +62,12 @@ def stats(args):
     lines = [f"# rocprofv3 kernel trace: {args.title}", "", "Command:", "", "```", args.command, "```", ""]
     sel = [v for k, v in per.items() if _matches(k, args.kernel)]
     if sel:
-        d = sorted(sel[0], key=lambda t: t[0])[-args.last:]
+        d = sorted(sel[0], key=lambda t: t[0])
+        d = d[len(d) - args.skip - args.last: len(d) - args.skip]
         durs = sorted((e - s) / 1000.0 for s, e in d)
         mean = sum(durs) / len(durs)
-        lines += [f"Timed region: last {len(durs)} dispatches of `{args.kernel}`: mean {mean:.2f} us, "
+        tail = f" (before the final {args.skip})" if args.skip else ""
+        lines += [f"Timed region: last {len(durs)} dispatches{tail} of `{args.kernel}`: mean {mean:.2f} us, "
                   f"median {durs[len(durs) // 2]:.2f} us, min {durs[0]:.2f} us, max {durs[-1]:.2f} us.", ""]
     lines += ["All dispatches of the run (warm-up, prefill and baseline decode included):", "",
               "| kernel | calls | mean us | total ms | share |", "|---|---|---|---|---|"]
@@ -76,17 +78,18 @@ def stats(args):
     print("\n".join(lines))
 
 
-def _counter(path, kernel, last):
+def _counter(path, kernel, last, skip=0):
     rows = list(csv.DictReader(open(path)))
     copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
     vals = [(int(r["Dispatch_Id"]), float(r["Counter_Value"])) for r in rows if _matches(r["Kernel_Name"], kernel)]
-    vals = [v for _, v in sorted(vals)][-last:]
+    vals = [v for _, v in sorted(vals)]
+    vals = vals[len(vals) - skip - last: len(vals) - skip]
     return max(copies), sum(vals) / len(vals), len(vals), rows[0]["Counter_Name"]
 
 
 def traffic(args):
-    cf, f_kib, nf, name_f = _counter(args.fetch, args.kernel, args.last)
-    cw, w_kib, nw, name_w = _counter(args.write, args.kernel, args.last)
+    cf, f_kib, nf, name_f = _counter(args.fetch, args.kernel, args.last, args.skip)
+    cw, w_kib, nw, name_w = _counter(args.write, args.kernel, args.last, args.skip)
     assert name_f == "FETCH_SIZE" and name_w == "WRITE_SIZE", (name_f, name_w)
     scale_f = args.copy_bytes / (cf * 1024.0)
     scale_w = args.copy_bytes / (cw * 1024.0)
@@ -180,6 +183,7 @@ def main():
     s.add_argument("--trace", required=True)
     s.add_argument("--kernel", required=True)
     s.add_argument("--last", type=int, required=True)
+    s.add_argument("--skip", type=int, default=0, help="dispatches after the timed region (bench.py's profiling pass)")
     s.add_argument("--top", type=int, default=16)
     s.add_argument("--title", default="")
     s.add_argument("--command", required=True)
@@ -189,6 +193,7 @@ def main():
     t.add_argument("--write", required=True)
     t.add_argument("--kernel", required=True)
     t.add_argument("--last", type=int, required=True)
+    t.add_argument("--skip", type=int, default=0)
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--algorithmic-bytes", type=int, default=0)
     t.add_argument("--command", required=True)

@@ -9,7 +9,9 @@ bits -- whatever else the batch holds and in whatever order:
   patterns, against one-at-a-time verifies; the same batch reversed and
   regrouped; a batch of 9 sequences (81 rows) through the row-tiled kernels;
   argument errors that leave every context untouched;
-* 8B shape: 8 sequences x K = 4 (40 rows) against one-at-a-time verifies.
+* 8B shape: 8 sequences x K = 4 (40 rows) against one-at-a-time verifies;
+* Gemma-style int4 layers (GeGLU, 6 q heads per KV head): 4 sequences,
+  19 rows, against one-at-a-time verifies.
 """
 import numpy as np
 import pytest
@@ -189,5 +191,25 @@ def test_q8b_batch_of_8_equals_one_at_a_time(q8b_device):
     got = _run_batch(ss, snaps, drafts)
     for s, g, ref in zip(ss, got, refs):
         _check(s, g, ref, 5)
+    for s in ss:
+        s.close()
+
+
+def test_int4_gemma_layers_batch_equals_one_at_a_time():
+    import torch
+    from greedy_block_verification_amd.session import DeviceModel
+    from seeded_inputs import generate_weights
+    from seeded_inputs.configs import layer_variant
+    assert torch.cuda.is_available()
+    cfg = layer_variant("gemma_int4", n_layers=3, vocab=1024)
+    dm = DeviceModel(generate_weights(cfg))
+    lens = [87, 40, 12, 66]
+    ks = [4, 3, 2, 6]
+    ss, snaps = _contexts(dm, cfg, lens, seed=24)
+    drafts = _drafts(dm, cfg, snaps, ks, seed=4)
+    refs = [_alone(dm, cfg, snap, d) for snap, d in zip(snaps, drafts)]
+    got = _run_batch(ss, snaps, drafts)
+    for s, g, ref, k in zip(ss, got, refs, ks):
+        _check(s, g, ref, k + 1)
     for s in ss:
         s.close()
