@@ -1134,6 +1134,70 @@ struct TileRegs {   // one step of this thread's loads (plain members: they stay
   uint4 h0, h1, l0, l1, w0, w1;
 };
 
+// Workgroup -> (row block, column block) of the tiled GEMMs.  Workgroups
+// are dealt to the 8 XCDs round-robin; each XCD gets a contiguous range of
+// the column-major (column block, row block) order, so the row blocks of one
+// column block run side by side on one XCD and read its weight tiles through
+// one L2.
+__device__ __forceinline__ void tiled_block(int M, int n_items, int& r0, int& T0) {
+  const int n_rb = (M + kTileRows - 1) / kTileRows;
+  const int n_cb = (n_items + kTileItems - 1) / kTileItems;
+  const int nblk = n_rb * n_cb;
+  const int q8 = nblk >> 3, rem = nblk & 7, xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+  const int lin = (xcd < rem ? xcd * (q8 + 1) : rem * (q8 + 1) + (xcd - rem) * q8) + loc;
+  r0 = (lin % n_rb) * kTileRows;
+  T0 = (lin / n_rb) * kTileItems;
+}
+
+// Epilogue of a tiled workgroup, two items per wave at a time: the wave's
+// finished sums go to its own LDS slice [64 rows][2 items][16] (lds: at
+// least 4 x 8 KiB, free once the K loop's last barrier has passed), then
+// 16-lane groups run the shared element epilogue row by row.
+template <int ROLE>
+__device__ __forceinline__ void tiled_epilogue(const GemmArgs& a, TileShared& sh, float* lds, const f32x4 (&y)[4][4],
+                                               int r0, int T0, int wave, int lane) {
+  const int wr = wave >> 1, wc = wave & 1;
+  const int n_items = a.N >> 4;
+  float* ys = lds + wave * 2048;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const f32x4 v = y[rt][2 * p + c2];
+        *reinterpret_cast<float4*>(ys + ((rt * 16 + (lane & 15)) * 2 + c2) * 16 + 4 * (lane >> 4)) =
+            make_float4(v.x, v.y, v.z, v.w);
+      }
+    __syncthreads();
+    for (int it = 0; it < 32; ++it) {
+      const int idx = it * 64 + lane;
+      const int c2 = idx >> 10, rl = (idx >> 4) & 63, cc = idx & 15;
+      const int r = r0 + wr * 64 + rl, T = T0 + wc * 4 + 2 * p + c2;
+      if (r < a.M && T < n_items) {
+        const float* yr = ys + (rl * 2 + c2) * 16;
+        const int rs = wr * 64 + rl;
+        epi_element<ROLE>(a, T, r, cc, epi_load<ROLE>(a, T, r * 16 + cc), sh.inv[rs],
+                          [&](int k) { return yr[k]; }, &sh.best[rs]);
+      }
+    }
+    __syncthreads();
+  }
+  if (ROLE == kRoleLmHead && threadIdx.x < kTileRows && r0 + (int)threadIdx.x < a.M)
+    atomicMax(a.best + r0 + threadIdx.x, sh.best[threadIdx.x]);
+}
+
+// RMS scales of the tile's rows and the LM head's row keys, before the K loop.
+template <int ROLE>
+__device__ __forceinline__ void tiled_prologue(const GemmArgs& a, TileShared& sh, int r0, int wave, int lane) {
+  if (norm_role(ROLE))
+    for (int rl = wave; rl < kTileRows; rl += 4) {
+      const float v = r0 + rl < a.M ? row_inv_rms(a, r0 + rl, lane) : 0.f;
+      if (lane == 0) sh.inv[rl] = v;
+    }
+  if (ROLE == kRoleLmHead && threadIdx.x < kTileRows) sh.best[threadIdx.x] = 0ull;
+}
+
 template <int ROLE>
 __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a) {
   __shared__ TileShared sh;
@@ -1143,17 +1207,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
   const int wr = wave >> 1, wc = wave & 1;
   const int n_items = a.N >> 4;
-  const int n_rb = (a.M + kTileRows - 1) / kTileRows;
-  const int n_cb = (n_items + kTileItems - 1) / kTileItems;
-  // Workgroup -> (row block, column block).  Workgroups are dealt to the 8
-  // XCDs round-robin; each XCD gets a contiguous range of the column-major
-  // (column block, row block) order, so the row blocks of one column block
-  // run side by side on one XCD and read its weight tiles through one L2.
-  const int nblk = n_rb * n_cb;
-  const int q8 = nblk >> 3, rem = nblk & 7, xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
-  const int lin = (xcd < rem ? xcd * (q8 + 1) : rem * (q8 + 1) + (xcd - rem) * q8) + loc;
-  const int cb = lin / n_rb, rb = lin % n_rb;
-  const int r0 = rb * kTileRows, T0 = cb * kTileItems;
+  int r0, T0;
+  tiled_block(a.M, n_items, r0, T0);
   const int KC = a.K >> 5, S = a.S, cpi = KC / S;
 
   // this thread's vectors of a step: activation vector v = t + 256 i (row
@@ -1193,12 +1248,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a) {
   };
 
   put(0, fetch(0));
-  if (norm_role(ROLE))
-    for (int rl = wave; rl < kTileRows; rl += 4) {
-      const float v = r0 + rl < a.M ? row_inv_rms(a, r0 + rl, lane) : 0.f;
-      if (lane == 0) sh.inv[rl] = v;
-    }
-  if (ROLE == kRoleLmHead && t < kTileRows) sh.best[t] = 0ull;
+  tiled_prologue<ROLE>(a, sh, r0, wave, lane);
   __syncthreads();
 
   f32x4 acc[4][4], y[4][4];
@@ -1239,44 +1289,160 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a) {
     c = cn;
   }
 
-  // Epilogue, two items per wave at a time: the wave's finished sums go to
-  // its own LDS slice [64 rows][2 items][16] (the stage buffers are free
-  // after the last barrier), then 16-lane groups run the shared element
-  // epilogue row by row.
-  float* ys = reinterpret_cast<float*>(lds) + wave * 2048;
+  tiled_epilogue<ROLE>(a, sh, reinterpret_cast<float*>(lds), y, r0, T0, wave, lane);
+  prof_end(a.prof);
+}
+
+// The tiled GEMM for int4 weights.  A pipeline step is one scale group (64
+// inputs) of one 128-input tile: per output, chain w runs its tiles w,
+// w + S, ... and within a tile its groups 0, 1, each group summed from zero
+// by MFMA (the hi and lo planes of its two 32-input halves) and added to the
+// chain by fmaf with the column's fp32 scale; chains are summed in chain
+// order: the arithmetic of the weight-streaming int4 kernel.  Per step the
+// workgroup stages the group's activation halves (128 rows x 64 inputs, in
+// MFMA operand order), each item's code half-lanes (8 bytes per lane) and
+// each item's 16 group scales.
+constexpr int kTile4Act = 4 * kTileActVecs;              // hi / lo x two 32-input halves: 2048 vectors
+constexpr int kTile4Step = kTile4Act + kTileItems * 32 + kTileItems * 2;   // + codes (as uint4 pairs) + scales: 2320
+
+struct Tile4Regs {   // one step of this thread's loads
+  uint4 a0, a1, a2, a3, a4, a5, a6, a7;
+  uint2 c0, c1;
+  uint4 s;
+};
+
+template <int ROLE>
+__global__ __launch_bounds__(256, 1) void k_gemm_tiled_int4(GemmArgs a) {
+  __shared__ TileShared sh;
+  __shared__ uint4 lds[2 * kTile4Step];
+  prof_start(a.prof);
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
+  const int wr = wave >> 1, wc = wave & 1, g = lane >> 4;
+  const int n_items = a.N >> 4;
+  int r0, T0;
+  tiled_block(a.M, n_items, r0, T0);
+  const int KT = a.K >> 7, S = a.S, cpi = KT / S;   // 128-input tiles; tiles per chain
+  const int spc = 2 * cpi;                          // steps per chain (two groups per tile)
+
+  // activation vector v = t + 256 u (u < 8) of the step: plane v / 1024, half
+  // (v / 512) % 2, row (v % 512) / 4, 8-input group v % 4
+  auto act_off = [&](int u) {   // element offset inside the group's 64 inputs of the row
+    const int v = t + 256 * u, rr = (v & 511) >> 2;
+    return (size_t)min(r0 + rr, a.M - 1) * a.K + ((v >> 9) & 1) * 32 + (v & 3) * 8;
+  };
+  auto act_dst = [&](int u) {
+    const int v = t + 256 * u, rr = (v & 511) >> 2;
+    return (((v >> 9) & 3) * 8 + (rr >> 4)) * 64 + (v & 3) * 16 + (rr & 15);
+  };
+  const uint2* W2 = reinterpret_cast<const uint2*>(a.W);
+  const uint4* S4 = reinterpret_cast<const uint4*>(a.Wscale);
+  const int it0 = t >> 6, it1 = (t + 256) >> 6;                 // code vectors: item, lane t % 64
+  const size_t cbase0 = (size_t)min(T0 + it0, n_items - 1) * KT;
+  const size_t cbase1 = (size_t)min(T0 + it1, n_items - 1) * KT;
+  const size_t sbase = (size_t)min(T0 + ((t & 15) >> 1), n_items - 1) * KT;   // scale vectors: item (t % 16) / 2
+  auto fetch = [&](int kt, int gq) {
+    Tile4Regs r;
+    const size_t k0 = (size_t)kt * 128 + gq * 64;
+    r.a0 = *reinterpret_cast<const uint4*>(a.bhi + act_off(0) + k0);
+    r.a1 = *reinterpret_cast<const uint4*>(a.bhi + act_off(1) + k0);
+    r.a2 = *reinterpret_cast<const uint4*>(a.bhi + act_off(2) + k0);
+    r.a3 = *reinterpret_cast<const uint4*>(a.bhi + act_off(3) + k0);
+    r.a4 = *reinterpret_cast<const uint4*>(a.blo + act_off(4) + k0);
+    r.a5 = *reinterpret_cast<const uint4*>(a.blo + act_off(5) + k0);
+    r.a6 = *reinterpret_cast<const uint4*>(a.blo + act_off(6) + k0);
+    r.a7 = *reinterpret_cast<const uint4*>(a.blo + act_off(7) + k0);
+    r.c0 = W2[((cbase0 + kt) * 64 + (t & 63)) * 2 + gq];
+    r.c1 = W2[((cbase1 + kt) * 64 + (t & 63)) * 2 + gq];
+    r.s = S4[(sbase + kt) * 4 + gq * 2 + (t & 1)];
+    return r;
+  };
+  auto put = [&](int b, const Tile4Regs& r) {
+    uint4* B = lds + b * kTile4Step;
+    B[act_dst(0)] = r.a0; B[act_dst(1)] = r.a1; B[act_dst(2)] = r.a2; B[act_dst(3)] = r.a3;
+    B[act_dst(4)] = r.a4; B[act_dst(5)] = r.a5; B[act_dst(6)] = r.a6; B[act_dst(7)] = r.a7;
+    uint2* C = reinterpret_cast<uint2*>(B + kTile4Act);
+    C[t] = r.c0;
+    C[t + 256] = r.c1;
+    if (t < 16) B[kTile4Act + kTileItems * 32 + t] = r.s;   // LDS store: no load waits on it
+  };
+
+  put(0, fetch(0, 0));
+  tiled_prologue<ROLE>(a, sh, r0, wave, lane);
+  __syncthreads();
+
+  f32x4 acc[4][4], y[4][4];
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
+  for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int ct = 0; ct < 4; ++ct) {
+      acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      y[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  const int n_steps = 2 * KT;
+  int w = 0, c = 0;   // chain and step inside the chain (tile c / 2, group c % 2)
+  for (int s = 0; s < n_steps; ++s) {
+    const int wn = c + 1 == spc ? w + 1 : w, cn = c + 1 == spc ? 0 : c + 1;
+    const Tile4Regs nx = s + 1 < n_steps ? fetch(wn + S * (cn >> 1), cn & 1) : fetch(w + S * (c >> 1), c & 1);
+    const uint4* B = lds + (s & 1) * kTile4Step;
+    const uint2* C = reinterpret_cast<const uint2*>(B + kTile4Act);
+    const uint2* SC = reinterpret_cast<const uint2*>(B + kTile4Act + kTileItems * 32);
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const f32x4 v = y[rt][2 * p + c2];
-        *reinterpret_cast<float4*>(ys + ((rt * 16 + (lane & 15)) * 2 + c2) * 16 + 4 * (lane >> 4)) =
-            make_float4(v.x, v.y, v.z, v.w);
-      }
-    __syncthreads();
-    for (int it = 0; it < 32; ++it) {
-      const int idx = it * 64 + lane;
-      const int c2 = idx >> 10, rl = (idx >> 4) & 63, cc = idx & 15;
-      const int r = r0 + wr * 64 + rl, T = T0 + wc * 4 + 2 * p + c2;
-      if (r < a.M && T < n_items) {
-        const float* yr = ys + (rl * 2 + c2) * 16;
-        const int rs = wr * 64 + rl;
-        epi_element<ROLE>(a, T, r, cc, epi_load<ROLE>(a, T, r * 16 + cc), sh.inv[rs],
-                          [&](int k) { return yr[k]; }, &sh.best[rs]);
+    for (int rt = 0; rt < 4; ++rt) {
+      const int ro = (wr * 4 + rt) * 64 + lane;
+      const BPair b0{B[ro], B[2 * kTileActVecs + ro]};                          // half 0: hi, lo
+      const BPair b1{B[kTileActVecs + ro], B[3 * kTileActVecs + ro]};           // half 1: hi, lo
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int item = wc * 4 + ct;
+        const uint2 q = C[item * 64 + lane];
+        const uint2 sc = SC[item * 4 + g];           // the item's 16 group scales: 4 per lane group
+        const uint4 A0 = codes8(q.x), A1 = codes8(q.y);
+        f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
+        p = mfma_pair(A0, b0, p);
+        p = mfma_pair(A1, b1, p);
+        const float s0 = bf2f((uint16_t)(sc.x & 0xffffu)), s1 = bf2f((uint16_t)(sc.x >> 16));
+        const float s2 = bf2f((uint16_t)(sc.y & 0xffffu)), s3 = bf2f((uint16_t)(sc.y >> 16));
+        acc[rt][ct].x = fmaf(s0, p.x, acc[rt][ct].x);
+        acc[rt][ct].y = fmaf(s1, p.y, acc[rt][ct].y);
+        acc[rt][ct].z = fmaf(s2, p.z, acc[rt][ct].z);
+        acc[rt][ct].w = fmaf(s3, p.w, acc[rt][ct].w);
       }
     }
+    if (c + 1 == spc) {   // chain w complete: add it to the running sum in chain order
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          y[rt][ct] = w == 0 ? acc[rt][ct] : y[rt][ct] + acc[rt][ct];
+          acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    put((s + 1) & 1, nx);
     __syncthreads();
+    w = wn;
+    c = cn;
   }
-  if (ROLE == kRoleLmHead && t < kTileRows && r0 + t < a.M) atomicMax(a.best + r0 + t, sh.best[t]);
+  tiled_epilogue<ROLE>(a, sh, reinterpret_cast<float*>(lds), y, r0, T0, wave, lane);
   prof_end(a.prof);
 }
 
 hipError_t launch_gemm_tiled(const GemmArgs& a, int role, hipStream_t st) {
-  if (a.M < 1 || a.S < 1 || a.N % 16 || a.fmt != 0 || a.K % (32 * a.S)) return hipErrorInvalidValue;
+  if (a.M < 1 || a.S < 1 || a.N % 16 || (a.fmt != 0 && a.fmt != 1) || a.K % ((a.fmt ? 128 : 32) * a.S))
+    return hipErrorInvalidValue;
   const int n_items = a.N >> 4;
   const int nblk = ((a.M + kTileRows - 1) / kTileRows) * ((n_items + kTileItems - 1) / kTileItems);
   const dim3 grid(nblk), block(256);
+  if (a.fmt == 1) {
+    switch (role) {
+      case kRoleQkv: hipLaunchKernelGGL(k_gemm_tiled_int4<kRoleQkv>, grid, block, 0, st, a); break;
+      case kRoleO: hipLaunchKernelGGL(k_gemm_tiled_int4<kRoleO>, grid, block, 0, st, a); break;
+      case kRoleGateUp: hipLaunchKernelGGL(k_gemm_tiled_int4<kRoleGateUp>, grid, block, 0, st, a); break;
+      case kRoleDown: hipLaunchKernelGGL(k_gemm_tiled_int4<kRoleDown>, grid, block, 0, st, a); break;
+      default: return hipErrorInvalidValue;   // the LM head is bf16
+    }
+    return hipGetLastError();
+  }
   switch (role) {
     case kRoleQkv: hipLaunchKernelGGL(k_gemm_tiled<kRoleQkv>, grid, block, 0, st, a); break;
     case kRoleO: hipLaunchKernelGGL(k_gemm_tiled<kRoleO>, grid, block, 0, st, a); break;

@@ -104,7 +104,6 @@ int max_rows(const sv_config& c, const Plans& p) {
 bool plans_ok(const sv_config& c, const Plans& p) {
   for (const GemmPlan* g : {&p.qkv, &p.o, &p.gu, &p.d, &p.lm})
     if (g->S < 1) return false;
-  if (c.max_prefill_rows > 0 && c.weight_fmt != 0) return false;   // tiled kernels: bf16 weights only
   return c.max_k + 1 <= max_rows(c, p);
 }
 

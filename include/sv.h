@@ -53,10 +53,10 @@ typedef struct {
   int32_t max_k;        /* most drafts per verify, 0..63 */
   int32_t max_prefill_rows; /* 0: sv_prefill runs forwards of at most 64 rows
                                (the weight-streaming kernels of decode and verify);
-                               65..16384 (bf16 weights only, else SV_EUNSUPPORTED):
-                               while more than 64 ids remain, forwards of up to this
-                               many rows through row-tiled kernels with the same
-                               per-row arithmetic.  The workspace grows with it. */
+                               65..16384: while more than 64 ids remain, forwards
+                               of up to this many rows through row-tiled kernels
+                               (bf16 and int4) with the same per-row arithmetic.
+                               The workspace grows with it. */
 } sv_config;
 
 /* One layer's weights, all device pointers in the packed layouts that

@@ -10,7 +10,9 @@ them must give every row the bits a one-token decode gives it:
   64-row forwards only give the same history, KV bits and next logits;
 * 8B shape: a 700-id prefill in tiled chunks (512 + 188) vs 64-row chunks:
   equal history, equal KV bits at sampled positions of every layer, equal
-  logits of the last 60 rows, and an identical decode step afterwards.
+  logits of the last 60 rows, and an identical decode step afterwards;
+* Gemma-style int4 layers (int4 tiled GEMM, GeGLU, 6 q heads per KV head):
+  every row of a 150-row tiled forward vs the one-token decode of that row.
 """
 import numpy as np
 import pytest
@@ -125,5 +127,30 @@ def test_q8b_tiled_prefill_equals_small_forwards(q8b_device):
     t = int(rng.integers(0, cfg.vocab))
     assert a.decode_step(t) == b.decode_step(t)
     np.testing.assert_array_equal(_bits(a.logits(0)), _bits(b.logits(0)))
+    a.close()
+    b.close()
+
+
+def test_int4_tiled_prefill_rows_equal_decode_rows():
+    import torch
+    from greedy_block_verification_amd.session import DeviceModel, Session
+    from seeded_inputs import generate_weights
+    from seeded_inputs.configs import layer_variant
+    assert torch.cuda.is_available()
+    cfg = layer_variant("gemma_int4", n_layers=3, vocab=1024)
+    dm = DeviceModel(generate_weights(cfg))
+    ids = _ids(150, 5, cfg.vocab)
+    a = Session(dm, cfg=cfg, prefill_rows=256)
+    a.set_debug(True)
+    nxt = a.prefill(ids)
+    arg = a.last_argmax()
+    assert len(arg) == 150 and arg[-1] == nxt
+    got = [_bits(a.logits(r)) for r in range(150)]
+    b = Session(dm, cfg=cfg)
+    b.set_debug(True)
+    for r, t in enumerate(ids):
+        assert b.decode_step(t) == arg[r]
+        np.testing.assert_array_equal(got[r], _bits(b.logits(0)))
+    np.testing.assert_array_equal(a.kv_positions(150), b.kv_positions(150))
     a.close()
     b.close()
