@@ -819,7 +819,7 @@ __global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
   prof_end(a.prof);
 }
 
-// bf16 items in groups, stages outermost (17..33 rows whose activation planes
+// bf16 items in groups, stages outermost (17..64 rows whose activation planes
 // do not fit one LDS stage): a workgroup takes its items IG at a time and,
 // for each stage of one chunk per wave (two LDS buffers; the next stage's
 // planes come to registers while this one computes), runs that stage for all
@@ -830,16 +830,25 @@ __global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
 // kernel's sums.  Ring slot ig streams item ig of the group; the slots of a
 // partial last group re-read the workgroup's last item, and those items are
 // not finished.
-constexpr int kGrpStageRegs = 5;
+// Stages of up to 33 rows are double-buffered (the next stage is stored
+// while this one is read, one barrier per stage); 34..64 rows fit one buffer,
+// so the next stage waits in registers until every wave is done with the
+// current one (two barriers per stage).  NREG 16-byte vectors per thread
+// carry a stage (M / 8 of them with 16 waves).
 struct GrpStageRegs {   // plain members: they stay in registers
-  uint4 v0, v1, v2, v3, v4;
+  uint4 v0, v1, v2, v3, v4, v5, v6, v7;
 };
-__host__ __device__ __forceinline__ bool grp_fits(int M, int waves) {
-  return 2 * (size_t)M * (waves * 32 + 8) * 4 <= (size_t)kStageBytes && 2 * M * 4 <= kGrpStageRegs * 64;
+// 0: the grouped kernel does not apply; 1: double-buffered; 2: single-buffered
+__host__ __device__ __forceinline__ int grp_mode(int M, int waves) {
+  const size_t one = (size_t)M * (waves * 32 + 8) * 4;
+  if (2 * one <= (size_t)kStageBytes && 2 * M * 4 <= 5 * 64) return 1;
+  if (one <= (size_t)kStageBytes && 2 * M * 4 <= 8 * 64) return 2;
+  return 0;
 }
 
-template <int TM, int ROLE, int IG>
+template <int TM, int ROLE, int IG, bool DB>
 __global__ __launch_bounds__(1024) void k_gemm_grp(GemmArgs a) {
+  constexpr int NREG = DB ? 5 : 8;
   __shared__ GemmShared sh;
   __shared__ __align__(16) uint16_t stage_mem[kStageBytes / 2];
   prof_start(a.prof);
@@ -858,12 +867,17 @@ __global__ __launch_bounds__(1024) void k_gemm_grp(GemmArgs a) {
     return x;
   };
   auto fetch = [&](int s) {                     // planes of stage s into registers (unconditional loads)
-    GrpStageRegs r;
+    GrpStageRegs r{};
     r.v0 = *reinterpret_cast<const uint4*>(stage_src(a, s * nw, nw, 32, 0, nthr));
     r.v1 = *reinterpret_cast<const uint4*>(stage_src(a, s * nw, nw, 32, 1, nthr));
     r.v2 = *reinterpret_cast<const uint4*>(stage_src(a, s * nw, nw, 32, 2, nthr));
     r.v3 = *reinterpret_cast<const uint4*>(stage_src(a, s * nw, nw, 32, 3, nthr));
     r.v4 = *reinterpret_cast<const uint4*>(stage_src(a, s * nw, nw, 32, 4, nthr));
+    if constexpr (NREG > 5) {
+      r.v5 = *reinterpret_cast<const uint4*>(stage_src(a, s * nw, nw, 32, 5, nthr));
+      r.v6 = *reinterpret_cast<const uint4*>(stage_src(a, s * nw, nw, 32, 6, nthr));
+      r.v7 = *reinterpret_cast<const uint4*>(stage_src(a, s * nw, nw, 32, 7, nthr));
+    }
     return r;
   };
   auto store = [&](const Stage& st, const GrpStageRegs& r) {
@@ -872,6 +886,11 @@ __global__ __launch_bounds__(1024) void k_gemm_grp(GemmArgs a) {
     stage_put(a, st, nw, 32, 2, r.v2, &sh.dummy, nthr);
     stage_put(a, st, nw, 32, 3, r.v3, &sh.dummy, nthr);
     stage_put(a, st, nw, 32, 4, r.v4, &sh.dummy, nthr);
+    if constexpr (NREG > 5) {
+      stage_put(a, st, nw, 32, 5, r.v5, &sh.dummy, nthr);
+      stage_put(a, st, nw, 32, 6, r.v6, &sh.dummy, nthr);
+      stage_put(a, st, nw, 32, 7, r.v7, &sh.dummy, nthr);
+    }
   };
   const int n_items = a.N >> 4;
   const int n_my = (n_items - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;   // items of this workgroup (>= 1)
@@ -916,7 +935,7 @@ __global__ __launch_bounds__(1024) void k_gemm_grp(GemmArgs a) {
         }
       }
       sr = fetch(s + 1 < n_st ? s + 1 : 0);
-      const Stage st = stage_buf(buf);
+      const Stage st = stage_buf(DB ? buf : 0);
       const int kl = wave * 32 + g * 8;         // this wave's chunk inside the stage
 #pragma unroll
       for (int ig = 0; ig < IG; ++ig) {
@@ -925,11 +944,17 @@ __global__ __launch_bounds__(1024) void k_gemm_grp(GemmArgs a) {
           acc[ig][rt] = mfma_pair(A[ig], lds_pair(st, row_of(rt * 16 + j, a.M), kl), acc[ig][rt]);
         A[ig] = chunk(gn, sn, ig);
       }
-      // the other buffer was last read in the previous stage, before the
-      // previous barrier; after this barrier every wave reads the new one
-      store(stage_buf(buf ^ 1), sr);
-      __syncthreads();
-      buf ^= 1;
+      if constexpr (DB) {
+        // the other buffer was last read in the previous stage, before the
+        // previous barrier; after this barrier every wave reads the new one
+        store(stage_buf(buf ^ 1), sr);
+        __syncthreads();
+        buf ^= 1;
+      } else {
+        __syncthreads();                        // every wave is done with the stage
+        store(stage_buf(0), sr);
+        __syncthreads();
+      }
     }
 #pragma unroll
     for (int ig = 0; ig < IG; ++ig)
@@ -947,22 +972,32 @@ template <int TM, int ROLE>
 constexpr int grp_max_items() {
   return TM == 1 ? (ROLE == kRoleQkv ? 2 : 4) : (TM == 2 ? 2 : (ROLE == kRoleQkv ? 1 : 2));
 }
-template <int TM, int ROLE>
+template <int TM, int ROLE, bool DB>
 static void launch_grp(const GemmArgs& a, int grid, int per, hipStream_t st) {
-  constexpr int IGM = grp_max_items<TM, ROLE>();
+  // single-buffered stages hold 8 registers of planes: groups of two fit the LM head's three row tiles only
+  constexpr int IGM = DB ? grp_max_items<TM, ROLE>() : (TM == 3 && ROLE == kRoleLmHead ? 2 : 1);
   const dim3 block(64 * a.S), g(grid);
-  if (IGM >= 4 && per >= 4) hipLaunchKernelGGL((k_gemm_grp<TM, ROLE, (IGM >= 4 ? 4 : 1)>), g, block, 0, st, a);
-  else if (IGM >= 2 && per >= 2) hipLaunchKernelGGL((k_gemm_grp<TM, ROLE, (IGM >= 2 ? 2 : 1)>), g, block, 0, st, a);
-  else hipLaunchKernelGGL((k_gemm_grp<TM, ROLE, 1>), g, block, 0, st, a);
+  if (IGM >= 4 && per >= 4) hipLaunchKernelGGL((k_gemm_grp<TM, ROLE, (IGM >= 4 ? 4 : 1), DB>), g, block, 0, st, a);
+  else if (IGM >= 2 && per >= 2) hipLaunchKernelGGL((k_gemm_grp<TM, ROLE, (IGM >= 2 ? 2 : 1), DB>), g, block, 0, st, a);
+  else hipLaunchKernelGGL((k_gemm_grp<TM, ROLE, 1, DB>), g, block, 0, st, a);
 }
 template <int ROLE>
 static hipError_t gemm_dispatch_grp(const GemmArgs& a, int grid, hipStream_t st) {
   const int tm = (a.M + 15) / 16;
   const int per = ((a.N >> 4) + grid - 1) / grid;   // most items of one workgroup
-  if (tm == 1) launch_grp<1, ROLE>(a, grid, per, st);
-  else if (tm == 2) launch_grp<2, ROLE>(a, grid, per, st);
-  else if (tm == 3) launch_grp<3, ROLE>(a, grid, per, st);
-  else return hipErrorInvalidValue;
+  if (grp_mode(a.M, a.S) == 1) {
+    if (tm == 2) launch_grp<2, ROLE, true>(a, grid, per, st);
+    else if (tm == 3) launch_grp<3, ROLE, true>(a, grid, per, st);
+    else return hipErrorInvalidValue;
+  } else {
+    if (tm == 4) launch_grp<4, ROLE, false>(a, grid, per, st);
+    else if constexpr (ROLE == kRoleLmHead) {
+      if (tm == 3) launch_grp<3, ROLE, false>(a, grid, per, st);
+      else return hipErrorInvalidValue;
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   return hipGetLastError();
 }
 
@@ -1076,9 +1111,12 @@ hipError_t launch_gemm(const GemmArgs& a, int role, int grid, hipStream_t st) {
   if (a.M > gemm_max_rows(a.fmt == 1 ? 128 : 32, a.S)) return hipErrorInvalidValue;
   grid = grid > (a.N >> 4) ? (a.N >> 4) : grid;
   const bool i4 = a.fmt == 1;
-  // 17..33 rows whose bf16 planes do not fit one stage: items in groups,
-  // stages outermost (for 9..16 rows the restaging kernel is faster)
-  if (!i4 && a.M >= 17 && grp_fits(a.M, a.S) && stage_chunks(a.K >> 5, a.S, a.M, 32, 1) < (a.K >> 5)) {
+  // 17..64 rows whose bf16 planes do not fit one stage: items in groups,
+  // stages outermost.  Measured on the 8B shapes: the restaging kernel is
+  // faster for 9..16 rows, and for 34..48 rows except on the LM head.
+  const int mode = grp_mode(a.M, a.S);
+  const bool grp = mode == 1 || (mode == 2 && (a.M > 48 || role == kRoleLmHead));
+  if (!i4 && a.M >= 17 && grp && stage_chunks(a.K >> 5, a.S, a.M, 32, 1) < (a.K >> 5)) {
     switch (role) {
       case kRoleQkv: return gemm_dispatch_grp<kRoleQkv>(a, grid, st);
       case kRoleO: return gemm_dispatch_grp<kRoleO>(a, grid, st);
