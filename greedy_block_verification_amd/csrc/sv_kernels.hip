@@ -1168,6 +1168,15 @@ struct TileShared {
   unsigned long long best[kTileRows];
 };
 
+// Slot of activation vector (row tile row `row`, 8-input group q) inside its
+// 64-vector row tile.  An MFMA operand read has lane l take group l / 16 of
+// row l % 16; a staging store has 4 neighbouring lanes take the 4 groups of
+// one row.  XORing the row with a per-group constant keeps every aligned run
+// of 8 (and of 16) lanes on distinct 16-byte bank groups in both patterns.
+__device__ __forceinline__ int act_slot(int q, int row) {
+  return q * 16 + (row ^ ((q & 1 ? 10 : 0) ^ (q & 2 ? 4 : 0)));
+}
+
 struct TileRegs {   // one step of this thread's loads (plain members: they stay in registers)
   uint4 h0, h1, l0, l1, w0, w1;
 };
@@ -1188,15 +1197,17 @@ __device__ __forceinline__ void tiled_block(int M, int n_items, int& r0, int& T0
 }
 
 // Epilogue of a tiled workgroup, two items per wave at a time: the wave's
-// finished sums go to its own LDS slice [64 rows][2 items][16] (lds: at
-// least 4 x 8 KiB, free once the K loop's last barrier has passed), then
-// 16-lane groups run the shared element epilogue row by row.
+// finished sums go to its own LDS slice of 64 rows x (2 items x 16 + 4 pad)
+// floats (lds: at least 4 x 9 KiB, free once the K loop's last barrier has
+// passed; the pad spreads the 16 rows of one MFMA store over distinct
+// banks), then 16-lane groups run the shared element epilogue row by row.
 template <int ROLE>
 __device__ __forceinline__ void tiled_epilogue(const GemmArgs& a, TileShared& sh, float* lds, const f32x4 (&y)[4][4],
                                                int r0, int T0, int wave, int lane) {
   const int wr = wave >> 1, wc = wave & 1;
   const int n_items = a.N >> 4;
-  float* ys = lds + wave * 2048;
+  constexpr int kRowF = 2 * 16 + 4;
+  float* ys = lds + wave * 64 * kRowF;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
 #pragma unroll
@@ -1204,7 +1215,7 @@ __device__ __forceinline__ void tiled_epilogue(const GemmArgs& a, TileShared& sh
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
         const f32x4 v = y[rt][2 * p + c2];
-        *reinterpret_cast<float4*>(ys + ((rt * 16 + (lane & 15)) * 2 + c2) * 16 + 4 * (lane >> 4)) =
+        *reinterpret_cast<float4*>(ys + (rt * 16 + (lane & 15)) * kRowF + c2 * 16 + 4 * (lane >> 4)) =
             make_float4(v.x, v.y, v.z, v.w);
       }
     __syncthreads();
@@ -1213,7 +1224,7 @@ __device__ __forceinline__ void tiled_epilogue(const GemmArgs& a, TileShared& sh
       const int c2 = idx >> 10, rl = (idx >> 4) & 63, cc = idx & 15;
       const int r = r0 + wr * 64 + rl, T = T0 + wc * 4 + 2 * p + c2;
       if (r < a.M && T < n_items) {
-        const float* yr = ys + (rl * 2 + c2) * 16;
+        const float* yr = ys + rl * kRowF + c2 * 16;
         const int rs = wr * 64 + rl;
         epi_element<ROLE>(a, T, r, cc, epi_load<ROLE>(a, T, r * 16 + cc), sh.inv[rs],
                           [&](int k) { return yr[k]; }, &sh.best[rs]);
@@ -1258,8 +1269,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a) {
     const int rr0 = v0 >> 2, rr1 = v1 >> 2;
     asrc0 = (size_t)min(r0 + rr0, a.M - 1) * a.K + (v0 & 3) * 8;
     asrc1 = (size_t)min(r0 + rr1, a.M - 1) * a.K + (v1 & 3) * 8;
-    adst0 = (rr0 >> 4) * 64 + (v0 & 3) * 16 + (rr0 & 15);
-    adst1 = (rr1 >> 4) * 64 + (v1 & 3) * 16 + (rr1 & 15);
+    adst0 = (rr0 >> 4) * 64 + act_slot(v0 & 3, rr0 & 15);
+    adst1 = (rr1 >> 4) * 64 + act_slot(v1 & 3, rr1 & 15);
   }
   const uint4* W4 = reinterpret_cast<const uint4*>(a.W);
   const size_t wsrc0 = (size_t)min(T0 + (t >> 6), n_items - 1) * KC * 64 + (t & 63);
@@ -1285,7 +1296,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a) {
     B[2 * kTileActVecs + 256 + t] = g.w1;
   };
 
-  put(0, fetch(0));
+  // step s runs chunk (s / cpi) + S (s % cpi): chain s / cpi, position s % cpi
+  // (steps past the end fetch the last chunk again: the loads stay unconditional)
+  auto chunk_of = [&](int s) {
+    s = min(s, KC - 1);
+    return s / cpi + S * (s % cpi);
+  };
+  put(0, fetch(chunk_of(0)));
+  TileRegs g1 = fetch(chunk_of(1));
   tiled_prologue<ROLE>(a, sh, r0, wave, lane);
   __syncthreads();
 
@@ -1297,34 +1315,43 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a) {
       acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
       y[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  int w = 0, c = 0;   // chain and position of the current step
-  for (int s = 0; s < KC; ++s) {
-    // next step's chunk (the last step fetches its own again: the loads stay unconditional)
-    const int wn = c + 1 == cpi ? w + 1 : w, cn = c + 1 == cpi ? 0 : c + 1;
-    const TileRegs g = fetch(s + 1 < KC ? wn + S * cn : w + S * c);
+  const int aslot = act_slot(lane >> 4, lane & 15);
+  auto compute = [&](int s) {
     const uint4* B = lds + (s & 1) * kTileStepVecs;
     uint4 A[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) A[ct] = B[2 * kTileActVecs + (wc * 4 + ct) * 64 + lane];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      const BPair bp{B[(wr * 4 + rt) * 64 + lane], B[kTileActVecs + (wr * 4 + rt) * 64 + lane]};
+      const BPair bp{B[(wr * 4 + rt) * 64 + aslot], B[kTileActVecs + (wr * 4 + rt) * 64 + aslot]};
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = mfma_pair(A[ct], bp, acc[rt][ct]);
     }
-    if (c + 1 == cpi) {   // chain w complete: add it to the running sum in chain order
+    if (s % cpi == cpi - 1) {   // chain s / cpi complete: add it to the running sum in chain order
+      const bool first = s < cpi;
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-          y[rt][ct] = w == 0 ? acc[rt][ct] : y[rt][ct] + acc[rt][ct];
+          y[rt][ct] = first ? acc[rt][ct] : y[rt][ct] + acc[rt][ct];
           acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
-    put((s + 1) & 1, g);
+  };
+  // Two steps in flight: while step s computes from LDS buffer s % 2, the
+  // loads of step s + 2 are issued and those of step s + 1 (issued one step
+  // earlier) are stored to the other buffer; one barrier per step.
+  for (int s = 0; s < KC; s += 2) {
+    const TileRegs g0 = fetch(chunk_of(s + 2));
+    compute(s);
+    put(1, g1);
     __syncthreads();
-    w = wn;
-    c = cn;
+    if (s + 1 < KC) {
+      g1 = fetch(chunk_of(s + 3));
+      compute(s + 1);
+      put(0, g0);
+      __syncthreads();
+    }
   }
 
   tiled_epilogue<ROLE>(a, sh, reinterpret_cast<float*>(lds), y, r0, T0, wave, lane);
@@ -1342,6 +1369,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a) {
 // each item's 16 group scales.
 constexpr int kTile4Act = 4 * kTileActVecs;              // hi / lo x two 32-input halves: 2048 vectors
 constexpr int kTile4Step = kTile4Act + kTileItems * 32 + kTileItems * 2;   // + codes (as uint4 pairs) + scales: 2320
+static_assert(4 * 64 * (2 * 16 + 4) <= 2 * kTileStepVecs * 4, "epilogue slices fit the staging buffers");
 
 struct Tile4Regs {   // one step of this thread's loads
   uint4 a0, a1, a2, a3, a4, a5, a6, a7;
@@ -1371,7 +1399,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_tiled_int4(GemmArgs a) {
   };
   auto act_dst = [&](int u) {
     const int v = t + 256 * u, rr = (v & 511) >> 2;
-    return (((v >> 9) & 3) * 8 + (rr >> 4)) * 64 + (v & 3) * 16 + (rr & 15);
+    return (((v >> 9) & 3) * 8 + (rr >> 4)) * 64 + act_slot(v & 3, rr & 15);
   };
   const uint2* W2 = reinterpret_cast<const uint2*>(a.W);
   const uint4* S4 = reinterpret_cast<const uint4*>(a.Wscale);
@@ -1418,6 +1446,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_tiled_int4(GemmArgs a) {
       y[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   const int n_steps = 2 * KT;
+  const int aslot = act_slot(lane >> 4, lane & 15);
   int w = 0, c = 0;   // chain and step inside the chain (tile c / 2, group c % 2)
   for (int s = 0; s < n_steps; ++s) {
     const int wn = c + 1 == spc ? w + 1 : w, cn = c + 1 == spc ? 0 : c + 1;
@@ -1427,7 +1456,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_tiled_int4(GemmArgs a) {
     const uint2* SC = reinterpret_cast<const uint2*>(B + kTile4Act + kTileItems * 32);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      const int ro = (wr * 4 + rt) * 64 + lane;
+      const int ro = (wr * 4 + rt) * 64 + aslot;
       const BPair b0{B[ro], B[2 * kTileActVecs + ro]};                          // half 0: hi, lo
       const BPair b1{B[kTileActVecs + ro], B[3 * kTileActVecs + ro]};           // half 1: hi, lo
 #pragma unroll
@@ -1560,8 +1589,7 @@ struct Fold {
 // final_fold (spw covers every split) the partials go to LDS and the
 // workgroup folds each row's splits and writes its output planes; otherwise
 // they go to the global partial buffer for the combine kernel.
-constexpr int kAttnLdsUnits = 16;
-constexpr int kAttnSplitWaves = 4;   // waves (one split each) per workgroup when splits go to the combine pass
+constexpr int kAttnFoldSplits = 3;   // up to this many splits a row is folded in LDS by one workgroup
 
 template <int DH>
 struct AttnUnitLds {
@@ -1749,7 +1777,7 @@ template <int DH, bool FOLD>
 __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   constexpr int DC = DH / 32;            // d chunks of the score MFMA
   constexpr int DT = DH / 16;            // d tiles of the P.V MFMA
-  __shared__ AttnUnitLds<DH> ul[FOLD ? kAttnLdsUnits : 1];
+  __shared__ AttnUnitLds<DH> ul[FOLD ? kAttnFoldSplits : 1];
 
   prof_start(a.prof);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -2035,15 +2063,19 @@ hipError_t launch_attention(const AttnArgs& a_in, hipStream_t st) {
   const int G = a.nq / a.nkv;
   if ((a.seqs == nullptr && a.M * G > kAttnQRows) || a.n_split < 1 || a.n_split > kAttnMaxSplits || a.n_lpages < 1 ||
       (a.seqs != nullptr && (a.n_tiles < 1 || a.rowseq == nullptr)) ||
-      (a.n_split > kAttnLdsUnits && a.n_split > a.part_splits))
+      (a.n_split > kAttnFoldSplits && a.n_split > a.part_splits))
     return hipErrorInvalidValue;
   const int n_qt = a.seqs != nullptr ? a.n_tiles : (a.M * G + 15) / 16;
-  // up to 16 splits: one workgroup of 8 waves per (q tile, KV head) folds
-  // them in LDS; more: workgroups of kAttnSplitWaves waves, one split each,
-  // and the combine pass
-  a.final_fold = a.n_split <= kAttnLdsUnits ? 1 : 0;
-  a.spw = a.final_fold ? a.n_split : kAttnSplitWaves;
-  a.wpb = a.final_fold ? 8 : kAttnSplitWaves;
+  // up to kAttnFoldSplits splits: one workgroup of 8 waves per (q tile, KV
+  // head) runs them and folds them in LDS; more: one single-wave workgroup
+  // per (q tile, split, KV head), then the combine pass.  Measured on MI355X
+  // (8 KV heads, 1-5 rows): the LDS fold is 0.6 us faster at 2 splits, even
+  // at 3, and falls behind from 5 (15.6 against 10.3 us at 10 splits), as
+  // its few workgroups leave most of the chip idle; single-wave split
+  // workgroups match or beat 2- and 4-wave ones at every context up to 32K.
+  a.final_fold = a.n_split <= kAttnFoldSplits ? 1 : 0;
+  a.spw = a.final_fold ? a.n_split : 1;
+  a.wpb = a.final_fold ? 8 : 1;
   const int n_wg = n_qt * ((a.n_split + a.spw - 1) / a.spw);
   const dim3 grid(n_wg, a.nkv), block(64 * a.wpb);
   if (a.dh == 128) {
