@@ -1929,8 +1929,12 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnArgs a) {
   const int j = lane & 15, g = lane >> 4;
   const int G = a.nq / a.nkv;
   const int n_qt = attn_n_tiles(a);
-  const int h = blockIdx.y;
-  const int qt = blockIdx.x * 4 + wave;
+  // Workgroups are dealt to the 8 XCDs round-robin in launch order; with the
+  // KV head varying fastest, each XCD runs one head's q tiles (with 8 KV
+  // heads), which walk that head's K/V in step and share it through the
+  // XCD's L2 instead of each reading it from the memory-side cache.
+  const int h = blockIdx.x % a.nkv;
+  const int qt = (blockIdx.x / a.nkv) * 4 + wave;
   if (qt < n_qt) {   // wave-uniform
     const AttnView V = attn_view(a, qt);
     const AttnArgs& av = V.av;
@@ -2095,7 +2099,7 @@ hipError_t launch_attention(const AttnArgs& a_in, hipStream_t st) {
 hipError_t launch_attention_rows(const AttnArgs& a, hipStream_t st) {
   if (a.M < 1 || a.n_lpages < 1 || a.nkv < 1 || a.nq % a.nkv) return hipErrorInvalidValue;
   const int n_qt = a.seqs != nullptr ? a.n_tiles : (a.M * (a.nq / a.nkv) + 15) / 16;
-  const dim3 grid((n_qt + 3) / 4, a.nkv), block(256);
+  const dim3 grid(((n_qt + 3) / 4) * a.nkv), block(256);
   if (a.dh == 128) hipLaunchKernelGGL(k_attn_rows<128>, grid, block, 0, st, a);
   else if (a.dh == 64) hipLaunchKernelGGL(k_attn_rows<64>, grid, block, 0, st, a);
   else return hipErrorInvalidValue;
