@@ -30,6 +30,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -74,7 +76,7 @@ def run_spec(sessions, truth, prompt_len, gen, k, srcs, n_steps, profile_mask=0)
     from greedy_block_verification_amd import binding as B
     import torch
     st = {"tokens": 0, "accepted": 0, "proposed": 0, "mism": 0, "matched": 0, "finished": 0,
-          "rows": 0, "bytes": 0, "gu_bytes": 0, "steps": []}
+          "rows": 0, "bytes": 0, "gu_bytes": 0, "steps": [], "step_s": []}
     p = 0
     done = [0] * len(sessions)
     for s in sessions:
@@ -88,7 +90,9 @@ def run_spec(sessions, truth, prompt_len, gen, k, srcs, n_steps, profile_mask=0)
         drafts = srcs[p].window(window, k_eff) if k_eff > 0 else []
         cur = s.next_id
         kv = s.kv_len
-        n, _ = B.sv_verify(s.ctx, kv, drafts)
+        t_step = time.perf_counter()
+        n, _ = B.sv_verify(s.ctx, kv, drafts)   # returns once the step's result is on the host
+        st["step_s"].append(time.perf_counter() - t_step)
         new = [cur] + drafts[:n]
         st["mism"] += sum(int(a != b) for a, b in zip(new, truth[p][c: c + n + 1]))
         st["tokens"] += n + 1
@@ -242,18 +246,35 @@ def run_draft_loop(args, cfg, sessions, truth, prompts, L, G, decode_tpot_ms):
     return out
 
 
-def cpu_baseline(weights, ids, n_tokens, steps):
-    """The fp64 oracle's per-token decoder on this host (bounded sample)."""
+def cpu_baseline(weights, ids, n_tokens, steps, gpu_logits, tol):
+    """The fp64 oracle's per-token decoder on this host (bounded sample).
+
+    Its logits at the sampled positions are also compared with the GPU's
+    (observer-mode logits of the same ids): the largest |difference|, the
+    rows whose oracle top-2 gap is within 2 tol (near ties, where either id
+    may legitimately win), how many of those the GPU resolved differently,
+    and argmax differences outside near ties (which would be a failure)."""
     import numpy as np
     from threadpoolctl import threadpool_info
     from oracle import Fp64Model, TokenDecoder
     threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     m = Fp64Model(weights, cache=False)
     dec = TokenDecoder(m)
+    ref = []
     t0 = time.perf_counter()
     for t in ids[:n_tokens]:
-        dec.decode(int(t))
+        ref.append(dec.decode(int(t)))
     s_per_decode = (time.perf_counter() - t0) / n_tokens
+    max_d, flags, flips, hard = 0.0, 0, 0, 0
+    for o, g in zip(ref, gpu_logits):
+        g = np.asarray(g, dtype=np.float64)
+        max_d = max(max_d, float(np.max(np.abs(g - o))))
+        top2 = np.partition(o, -2)[-2:]
+        near = float(top2[1] - top2[0]) <= 2 * tol
+        differ = int(np.argmax(g)) != int(np.argmax(o))
+        flags += int(near)
+        flips += int(near and differ)
+        hard += int(differ and not near)
     # the oracle verifies a window of k_eff drafts with k_eff + 1 per-token decodes
     tok = sum(n + 1 for _, n, _ in steps)
     decodes = sum(k + 1 for k, _, _ in steps)
@@ -262,7 +283,9 @@ def cpu_baseline(weights, ids, n_tokens, steps):
             "sample": f"{n_tokens} fp64 per-token decode(s) of the full model at positions 0..{n_tokens - 1} "
                       f"({s_per_decode:.2f} s each); verified tokens/s = committed tokens / ((k+1) decodes per "
                       f"verify x s per decode) over the GPU run's own windows",
-            "s_per_decode": s_per_decode, "affinity_cpus": len(os.sched_getaffinity(0))}
+            "s_per_decode": s_per_decode, "affinity_cpus": len(os.sched_getaffinity(0)),
+            "oracle_rows": len(ref), "oracle_max_abs_dlogit": max_d, "oracle_tolerance": tol,
+            "near_tie_flags": flags, "near_tie_flips": flips, "oracle_argmax_mismatches": hard}
 
 
 # Per-workload defaults: the headline is q8b; the others are the remaining
@@ -418,6 +441,9 @@ def main():
     extra = {
         "acceptance_rate": round(metrics.acceptance_rate(st["accepted"], st["proposed"]), 4),
         "tokens_per_verify": round(st["tokens"] / args.steps, 4),
+        "step_ms_median": round(1000.0 * float(np.median(st["step_s"])), 4),
+        "step_ms_p90": round(1000.0 * float(np.percentile(st["step_s"], 90)), 4),
+        "verify_steps": args.steps, "decode_steps": P * G,
         "rows_scored_per_s": round(st["rows"] / st["seconds"], 1),
         "step_hbm_gbs": round(step_bytes / st["seconds"] / 1e9, 1),
         "step_hbm_frac": round(step_bytes / st["seconds"] / 1e9 / PEAK_HBM_GBS, 4),
@@ -473,9 +499,19 @@ def main():
         extra["cpu_baseline_note"] = (f"not run: the oracle's decoder would first have to decode the {L}-id "
                                       "prompt one position at a time in fp64")
     elif not args.no_cpu_baseline:
+        n_cpu = min(args.cpu_tokens, L)
+        obs = Session(dm)
+        obs.set_debug(True)
+        obs.prefill(prompts[0][:n_cpu])
+        gpu_logits = [obs.logits(r) for r in range(n_cpu)]
+        obs.close()
         t = time.perf_counter()
-        cpu = cpu_baseline(weights, prompts[0], args.cpu_tokens, st["steps"])
-        log(f"[bench] cpu baseline {cpu['value']:.4f} tok/s in {time.perf_counter() - t:.1f} s")
+        cpu = cpu_baseline(weights, prompts[0], n_cpu, st["steps"], gpu_logits,
+                           6e-2 if cfg.weight_fmt == "int4" else 3e-2)
+        log(f"[bench] cpu baseline {cpu['value']:.4f} tok/s in {time.perf_counter() - t:.1f} s; oracle max "
+            f"|dlogit| {cpu['oracle_max_abs_dlogit']:.3g} over {cpu['oracle_rows']} rows, near ties "
+            f"{cpu['near_tie_flags']} (flipped {cpu['near_tie_flips']}), argmax mismatches "
+            f"{cpu['oracle_argmax_mismatches']}")
 
     prompt_desc = f"{P} prompt(s) x {L} ids"
     out = {
