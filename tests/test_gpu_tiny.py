@@ -6,7 +6,8 @@
 * Cache histories (one-token commits, 9-row block commits, one prefill): equal
   KV bits and equal verify logits.
 * Rollback at every index, observer mode, NaN-poisoned pool, permuted pages,
-  and argument errors.
+  argument errors, and a verify that fills the context exactly to capacity
+  (then SV_ENOSPACE for every further commit).
 """
 import copy
 
@@ -284,3 +285,53 @@ def test_argument_errors_leave_state_untouched(dev):
         s.decode_step(-1)
     assert e.value.status == B.SV_EINVAL
     assert s.kv_len == kv and s.next_id == nx
+
+
+def test_verify_fills_the_context_to_capacity(dev):
+    """The largest verify that fits (kv_len + K + 1 == max_ctx: the last page
+    and the last page-table entry) equals one-token decode bit for bit; past
+    capacity every call fails with SV_ENOSPACE and changes nothing; empty and
+    out-of-range inputs fail with SV_EINVAL."""
+    from greedy_block_verification_amd import binding as B
+    from seeded_inputs import get_config
+    cap, K = get_config("tiny").max_ctx, 8
+    ids = _prompt(cap - K - 1, 11)
+    a, b = _sess(dev), _sess(dev)
+    a.set_debug(True)
+    b.set_debug(True)
+    nx = a.prefill(ids)
+    assert b.prefill(ids) == nx
+    truth, dec = [nx], []
+    for _ in range(K + 1):
+        t = truth[-1]
+        truth.append(b.decode_step(t))
+        dec.append(b.logits(0))
+    n, _ = a.verify(truth[1:K + 1])
+    assert n == K and a.kv_len == cap == b.kv_len and a.next_id == b.next_id
+    for r in range(K + 1):
+        np.testing.assert_array_equal(_bits(a.logits(r)), _bits(dec[r]))
+    np.testing.assert_array_equal(a.kv_positions(cap), b.kv_positions(cap))
+    for call in (lambda: a.decode_step(truth[-1]), lambda: a.verify([]), lambda: a.prefill([1])):
+        with pytest.raises(B.SvError) as e:
+            call()
+        assert e.value.status == B.SV_ENOSPACE
+    assert a.kv_len == cap and a.next_id == b.next_id
+    with pytest.raises(B.SvError) as e:
+        B.sv_prefill(a.ctx, [])
+    assert e.value.status == B.SV_EINVAL
+    # roll back into the last pages and verify to capacity again (K = 5)
+    a.truncate(cap - 6)
+    b.truncate(cap - 6)
+    t = b.next_id
+    assert a.next_id == t
+    truth, dec = [t], []
+    for _ in range(6):
+        t = b.decode_step(t)
+        truth.append(t)
+        dec.append(b.logits(0))
+    n, _ = a.verify(truth[1:6])
+    assert n == 5 and a.kv_len == cap
+    for r in range(6):
+        np.testing.assert_array_equal(_bits(a.logits(r)), _bits(dec[r]))
+    a.close()
+    b.close()
