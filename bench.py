@@ -440,7 +440,7 @@ def main():
     step_bytes = sum(algorithmic_step_bytes(cfg, k_eff + 1, kv) for k_eff, _, kv in st["steps"])
     extra = {
         "acceptance_rate": round(metrics.acceptance_rate(st["accepted"], st["proposed"]), 4),
-        "tokens_per_verify": round(st["tokens"] / args.steps, 4),
+        "tokens_per_target_step": round(st["tokens"] / args.steps, 4),
         "step_ms_median": round(1000.0 * float(np.median(st["step_s"])), 4),
         "step_ms_p90": round(1000.0 * float(np.percentile(st["step_s"], 90)), 4),
         "verify_steps": args.steps, "decode_steps": P * G,
