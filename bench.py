@@ -455,6 +455,8 @@ def main():
         "prefill_ms_per_prompt": round(1000.0 * t_prefill / P, 3),
         "prefill_tok_s": round(P * L / t_prefill, 1),
         "prefill_rows_per_forward": wl["prefill_rows"] or 64,
+        # per prompt: its prefill, then its G tokens at the verified rate
+        "e2e_tok_s_incl_prefill": round(G / (t_prefill / P + G / value), 2),
         "kernel_us_per_step": {name: round(1000.0 * ms / n_prof, 1) for name, (ms, n) in prof.items()},
         "kernel_launches_per_step": {name: round(n / n_prof, 2) for name, (ms, n) in prof.items()},
     }
