@@ -2019,6 +2019,145 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnArgs a) {
   prof_end(a.prof);
 }
 
+// Two q tiles per wave (single-sequence forwards, whose
+// adjacent tiles share one page table): each block's K/V operands are loaded
+// once and used for every tile of the wave, halving the load bytes per
+// q-row; the block range of a split is the union over the wave's tiles, and
+// blocks outside a row's own range are exact no-ops for it, so every row
+// keeps the arithmetic of the split kernels.
+template <int DH>
+__global__ __launch_bounds__(256) void k_attn_rows2(AttnArgs a) {
+  constexpr int TPW = 2;
+  // the running fold of each tile's rows, per lane: [wave][tile][dt][lane]
+  __shared__ f32x4 fo_lds[4 * TPW * (DH / 16) * 64];
+  constexpr int DC = DH / 32, DT = DH / 16;
+  prof_start(a.prof);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int j = lane & 15, g = lane >> 4;
+  const int G = a.nq / a.nkv;
+  const int n_qt = attn_n_tiles(a);
+  // Workgroups are dealt to the 8 XCDs round-robin in launch order; with the
+  // KV head varying fastest, each XCD runs one head's q tiles (with 8 KV
+  // heads), which walk that head's K/V in step and share it through the
+  // XCD's L2 instead of each reading it from the memory-side cache.
+  const int h = blockIdx.x % a.nkv;
+  const int qt0 = ((blockIdx.x / a.nkv) * 4 + wave) * TPW;
+  if (qt0 < n_qt) {   // wave-uniform
+    const AttnView V = attn_view(a, qt0);
+    const AttnArgs& av = V.av;
+    const int n_qr = V.m * G;
+    const int kv_len = attn_kv_len(a, qt0);
+    const int ctx_max = kv_len + V.m;
+    bool have[TPW];
+    int r[TPW], head[TPW], ctx[TPW], ns_row[TPW];
+    BPair qop[TPW][DC];
+    int rlo = V.m, rhi = 0;   // rows of the wave's tiles
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int qbase = V.qbase + 16 * u;
+      const int qr = qbase + j;
+      have[u] = qt0 + u < n_qt && qr < n_qr;
+      r[u] = have[u] ? qr / G : 0;
+      head[u] = h * G + (have[u] ? qr % G : 0);
+      const float4* qp = reinterpret_cast<const float4*>(a.q + ((size_t)(V.row0 + r[u]) * a.nq + head[u]) * DH + g * 8);
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        const float4 q0 = qp[c * 8], q1 = qp[c * 8 + 1];
+        const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        qop[u][c] = have[u] ? split8_f16(qv) : bzero();
+      }
+      ctx[u] = kv_len + r[u] + 1;
+      ns_row[u] = attn_ns(ctx[u]);
+      if (qt0 + u < n_qt && qbase < n_qr) {
+        int r0, r1;
+        attn_tile_rows(qbase, G, V.m, r0, r1);
+        rlo = min(rlo, r0);
+        rhi = max(rhi, r1);
+      }
+    }
+    int ns_max = 1;
+    for (int rr = rlo; rr <= rhi; ++rr) ns_max = max(ns_max, attn_ns(kv_len + rr + 1));
+
+    float fm[TPW], fl[TPW];
+    auto fo = [&](int u, int dt) -> f32x4& { return fo_lds[((wave * TPW + u) * DT + dt) * 64 + lane]; };
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      fm[u] = 0.f;
+      fl[u] = 0.f;
+    }
+    for (int sp = 0; sp < ns_max; ++sp) {
+      int lo[TPW], hi[TPW];
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        lo[u] = 0;
+        hi[u] = 0;
+        if (have[u] && sp < ns_row[u]) {
+          const int bps = attn_bps(ctx[u]);
+          lo[u] = sp * bps * kAttnBlock;
+          hi[u] = min((sp + 1) * bps * kAttnBlock, ctx[u]);
+        }
+      }
+      int b_lo, b_hi;
+      attn_split_union(kv_len, rlo, rhi, sp, b_lo, b_hi);
+      f32x4 o[TPW][DT];
+      float m[TPW], l[TPW];
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        m[u] = -INFINITY;
+        l[u] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      int4 pq = attn_block_pages(av, b_lo < b_hi ? b_lo : 0);
+      for (int b = b_lo; b < b_hi; ++b) {
+        AttnKV<DH> kv;
+        attn_load_kv<DH>(av, h, j, g, pq, kv);
+        pq = attn_block_pages(av, b + 1 < b_hi ? b + 1 : b);
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) attn_block_step<DH>(av, kv, qop[u], b, g, lo[u], hi[u], ctx_max, m[u], l[u], o[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        if (sp == 0) {
+          fm[u] = m[u];
+          fl[u] = l[u];
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) fo(u, dt) = o[u][dt];
+        } else if (sp < ns_row[u]) {
+          const float mn = fmaxf(fm[u], m[u]);
+          const float wa = exp2f(fm[u] - mn), wb = exp2f(m[u] - mn);
+          fl[u] = fl[u] * wa + l[u] * wb;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            f32x4 f = fo(u, dt);
+            f.x = f.x * wa + o[u][dt].x * wb; f.y = f.y * wa + o[u][dt].y * wb;
+            f.z = f.z * wa + o[u][dt].z * wb; f.w = f.w * wa + o[u][dt].w * wb;
+            fo(u, dt) = f;
+          }
+          fm[u] = mn;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      if (have[u]) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const f32x4 f = fo(u, dt);
+          const float ov[4] = {f.x, f.y, f.z, f.w};
+          uint16_t hb[4], lb[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) split1(ov[e] / fl[u], hb[e], lb[e]);
+          const size_t oi = ((size_t)(V.row0 + r[u]) * a.nq + head[u]) * DH + dt * 16 + 4 * g;
+          *reinterpret_cast<uint2*>(a.ohi + oi) = make_uint2(pack2(hb[0], hb[1]), pack2(hb[2], hb[3]));
+          *reinterpret_cast<uint2*>(a.olo + oi) = make_uint2(pack2(lb[0], lb[1]), pack2(lb[2], lb[3]));
+        }
+      }
+    }
+  }
+  prof_end(a.prof);
+}
+
 // Fold of the global partials of row r, query head j (record [m, l, -, -, o[dh]]):
 // the row's records are staged in LDS with coalesced 16-byte loads (a long
 // context has up to 128 of them), then thread d folds output d in split order.
@@ -2099,10 +2238,18 @@ hipError_t launch_attention(const AttnArgs& a_in, hipStream_t st) {
 hipError_t launch_attention_rows(const AttnArgs& a, hipStream_t st) {
   if (a.M < 1 || a.n_lpages < 1 || a.nkv < 1 || a.nq % a.nkv) return hipErrorInvalidValue;
   const int n_qt = a.seqs != nullptr ? a.n_tiles : (a.M * (a.nq / a.nkv) + 15) / 16;
-  const dim3 grid(((n_qt + 3) / 4) * a.nkv), block(256);
-  if (a.dh == 128) hipLaunchKernelGGL(k_attn_rows<128>, grid, block, 0, st, a);
-  else if (a.dh == 64) hipLaunchKernelGGL(k_attn_rows<64>, grid, block, 0, st, a);
-  else return hipErrorInvalidValue;
+  // two q tiles per wave where the tiles share one sequence
+  const int tpw = a.seqs == nullptr ? 2 : 1;
+  const dim3 grid(((n_qt + 4 * tpw - 1) / (4 * tpw)) * a.nkv), block(256);
+  if (a.dh == 128) {
+    if (tpw == 2) hipLaunchKernelGGL(k_attn_rows2<128>, grid, block, 0, st, a);
+    else hipLaunchKernelGGL(k_attn_rows<128>, grid, block, 0, st, a);
+  } else if (a.dh == 64) {
+    if (tpw == 2) hipLaunchKernelGGL(k_attn_rows2<64>, grid, block, 0, st, a);
+    else hipLaunchKernelGGL(k_attn_rows<64>, grid, block, 0, st, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
