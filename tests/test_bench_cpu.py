@@ -47,3 +47,13 @@ def test_cpu_baseline_oracle_comparison_counts():
     tied[2][lo] = o[hi] + 1e-9
     t = bench.cpu_baseline(w, ids, 3, steps, tied, tol2)
     assert t["near_tie_flags"] >= 1 and t["near_tie_flips"] == 1 and t["oracle_argmax_mismatches"] == 0
+
+
+def test_more_than_one_gpu_is_refused_before_any_gpu_work():
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 2 and "one GPU only" in r.stdout + r.stderr and r.stdout.strip() == ""
