@@ -8,6 +8,8 @@
 * Rollback at every index, observer mode, NaN-poisoned pool, permuted pages,
   argument errors, and a verify that fills the context exactly to capacity
   (then SV_ENOSPACE for every further commit).
+* Seeded random sequences of verifies, rollbacks and decodes, each state
+  checked against a context rebuilt from one-token decodes alone.
 """
 import copy
 
@@ -335,3 +337,72 @@ def test_verify_fills_the_context_to_capacity(dev):
         np.testing.assert_array_equal(_bits(a.logits(r)), _bits(dec[r]))
     a.close()
     b.close()
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_random_operation_sequences_match_one_token_decodes(dev, seed):
+    """A seeded random sequence of verifies (random K, drafts right up to a
+    random index), rollbacks to random lengths and one-token decodes.  After
+    every operation the context equals a reference rebuilt only from
+    one-token decodes of its committed ids: kv_len, next_id, the greedy
+    history, the last forward's logits rows and the KV bits of every
+    committed position (the reference uses its own permuted page table)."""
+    from seeded_inputs import get_config
+    cfg = get_config("tiny")
+    rng = np.random.default_rng(100 + seed)
+    perm = rng.permutation(cfg.max_ctx // 16)
+    s = _sess(dev)
+    s.set_debug(True)
+    ids = _prompt(int(rng.integers(1, 40)), 20 + seed)
+    s.prefill(ids)
+    committed = list(ids)
+
+    def reference(n):
+        """A fresh context built by one-token decodes of committed[:n]."""
+        r = _sess(dev, page_perm=perm)
+        r.set_debug(True)
+        logits = []
+        for t in committed[:n]:
+            r.decode_step(t)
+            logits.append(r.logits(0))
+        return r, logits
+
+    for step in range(30):
+        op = rng.choice(["verify", "verify", "truncate", "decode"])
+        kv0 = s.kv_len
+        if op == "verify" and kv0 + cfg.max_k + 1 <= cfg.max_ctx:
+            k = int(rng.integers(0, cfg.max_k + 1))
+            # the greedy continuation from a scratch copy, wrong from a random index on
+            probe, _ = reference(kv0)
+            truth, t = [], s.next_id
+            for _ in range(k):
+                t = probe.decode_step(t)
+                truth.append(t)
+            probe.close()
+            wrong_at = int(rng.integers(0, k + 1))
+            drafts = truth[:wrong_at] + [(x + 1) % cfg.vocab for x in truth[wrong_at:]]
+            rows = [s.next_id] + drafts
+            n, _ = s.verify(drafts)
+            assert n == wrong_at
+            committed[kv0:] = rows[:n + 1]
+            last_rows = k + 1
+        elif op == "truncate" and kv0 > 1:
+            s.truncate(int(rng.integers(1, kv0)))
+            del committed[s.kv_len:]
+            last_rows = 0
+        elif kv0 + 1 <= cfg.max_ctx:
+            t = s.next_id
+            s.decode_step(t)
+            committed[kv0:] = [t]
+            last_rows = 1
+        else:
+            continue
+        assert s.kv_len == len(committed)
+        ref, logits = reference(s.kv_len)
+        assert s.next_id == ref.next_id and s.history() == ref.history()
+        np.testing.assert_array_equal(s.kv_positions(s.kv_len), ref.kv_positions(ref.kv_len))
+        # the last forward's rows were the positions kv0 .. kv0 + last_rows - 1
+        for r in range(min(last_rows, s.kv_len - kv0)):
+            np.testing.assert_array_equal(_bits(s.logits(r)), _bits(logits[kv0 + r]))
+        ref.close()
+    s.close()
