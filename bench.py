@@ -118,6 +118,28 @@ def run_spec(sessions, truth, prompt_len, gen, k, srcs, n_steps, profile_mask=0)
     return st
 
 
+def warm_walks(sessions, truth, prompt_len, gen, k, srcs, profile_mask=0):
+    """Untimed: walk every prompt's speculative loop once at window size k.
+
+    A context captures one HIP graph per (rows, split count, profiling mask)
+    it meets, the first time it meets it; walking each prompt once with the
+    timed run's mask lets the timed steps replay cached graphs, as a serving
+    loop does after its first requests."""
+    from greedy_block_verification_amd import binding as B
+    for s in sessions:
+        B.sv_set_profile(s.ctx, profile_mask)
+    for s, tr, src in zip(sessions, truth, srcs):
+        c = 0
+        while c < gen:
+            k_eff = min(k, gen - c - 1)
+            drafts = src.window(tr[c + 1: c + 1 + k_eff], k_eff) if k_eff > 0 else []
+            n, _ = B.sv_verify(s.ctx, s.kv_len, drafts)
+            c += n + 1
+        s.truncate(prompt_len)
+    for s in sessions:
+        B.sv_set_profile(s.ctx, 0)
+
+
 def run_spec_batch(sessions, truth, prompt_len, gen, k, srcs, n_steps):
     """Batched verify: the B sessions advance together, one sv_verify_batch
     per step; a session that finishes its continuation restarts at its prompt."""
@@ -190,47 +212,53 @@ def run_draft_loop(args, cfg, sessions, truth, prompts, L, G, decode_tpot_ms):
     out = {"draft": f"{dcfg.name}: {dcfg.n_layers} layers, d {dcfg.d_model}"}
     # the draft's own one-token decode rate
     d0 = dsess[0]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    x = d0.next_id
-    for _ in range(32):
-        x = d0.decode_step(x)
-    torch.cuda.synchronize()
-    draft_tpot_ms = 1000.0 * (time.perf_counter() - t0) / 32
-    d0.truncate(L)
+    for timed in (False, True):   # the first pass captures the context's graphs
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        x = d0.next_id
+        for _ in range(32):
+            x = d0.decode_step(x)
+        torch.cuda.synchronize()
+        draft_tpot_ms = 1000.0 * (time.perf_counter() - t0) / 32
+        d0.truncate(L)
     out["draft_decode_tpot_ms"] = round(draft_tpot_ms, 4)
     base_tok_s = 1000.0 / decode_tpot_ms
     for k in [int(v) for v in args.draft_ks.split(",") if v.strip()]:
         if k > min(cfg.max_k, dcfg.max_k):
             continue
-        done = [0] * P
-        srcs = [DraftSource(cfg.seed, 40_000 + p, cfg.vocab, p_correct=args.p_correct) for p in range(P)]
+        def walk(seed0):
+            """sweep_steps rounds over the prompts in order; returns (tokens, mismatches, seconds, loops)"""
+            done = [0] * P
+            srcs = [DraftSource(cfg.seed, seed0 + p, cfg.vocab, p_correct=args.p_correct) for p in range(P)]
 
-        def proposer_for(p):
-            return lambda kk: srcs[p].window(truth[p][done[p] + 1: done[p] + 1 + kk], kk)
-        loops = [DraftLoop(sessions[p], dsess[p], proposer_for(p)) for p in range(P)]
-        tokens = mism = 0
-        p = 0
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.sweep_steps):
-            c = done[p]
-            k_eff = min(k, G - c - 1)
-            got = loops[p].step(k_eff)
-            mism += sum(int(a != b) for a, b in zip(got, truth[p][c: c + len(got)]))
-            tokens += len(got)
-            done[p] = c + len(got)
-            if done[p] >= G:
-                sessions[p].truncate(L)
-                dsess[p].truncate(L)
-                done[p] = 0
-                p = (p + 1) % P
-        torch.cuda.synchronize()
-        sec = time.perf_counter() - t0
-        for q in range(P):
-            if sessions[q].kv_len != L:
-                sessions[q].truncate(L)
-                dsess[q].truncate(L)
+            def proposer_for(p):
+                return lambda kk: srcs[p].window(truth[p][done[p] + 1: done[p] + 1 + kk], kk)
+            loops = [DraftLoop(sessions[p], dsess[p], proposer_for(p)) for p in range(P)]
+            tokens = mism = 0
+            p = 0
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.sweep_steps):
+                c = done[p]
+                k_eff = min(k, G - c - 1)
+                got = loops[p].step(k_eff)
+                mism += sum(int(a != b) for a, b in zip(got, truth[p][c: c + len(got)]))
+                tokens += len(got)
+                done[p] = c + len(got)
+                if done[p] >= G:
+                    sessions[p].truncate(L)
+                    dsess[p].truncate(L)
+                    done[p] = 0
+                    p = (p + 1) % P
+            torch.cuda.synchronize()
+            sec = time.perf_counter() - t0
+            for q in range(P):
+                if sessions[q].kv_len != L:
+                    sessions[q].truncate(L)
+                    dsess[q].truncate(L)
+            return tokens, mism, sec, loops
+        walk(45_000)   # untimed: the same prompts' graphs, target and draft
+        tokens, mism, sec, loops = walk(40_000)
         acc = sum(lp.accepted for lp in loops)
         prop = sum(lp.proposed for lp in loops)
         e2e = tokens / sec
@@ -376,16 +404,26 @@ def main():
         torch.cuda.synchronize()
         t_prefill += time.perf_counter() - t
         seq = [nx]
-        t = time.perf_counter()
         for _ in range(G):
             seq.append(s.decode_step(seq[-1]))
-        t_decode += time.perf_counter() - t
         s.truncate(L)
         assert s.next_id == nx
         sessions.append(s)
         truth.append(seq)
         prompts.append(ids)
-    decode_tpot_ms = 1000.0 * t_decode / (P * G)
+    # the plain-decode baseline, timed on contexts whose graphs the pass above
+    # captured (as the verify steps are timed on warm contexts)
+    n_dec = min(P, 8)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for p in range(n_dec):
+        x = truth[p][0]
+        for _ in range(G):
+            x = sessions[p].decode_step(x)
+        sessions[p].truncate(L)
+    torch.cuda.synchronize()
+    t_decode = time.perf_counter() - t
+    decode_tpot_ms = 1000.0 * t_decode / (n_dec * G)
     log(f"[bench] {P} prompts ready; baseline decode {decode_tpot_ms:.3f} ms/token")
 
     if args.copy_probe_mib > 0:
@@ -399,6 +437,9 @@ def main():
         del src, dst
 
     srcs = [DraftSource(cfg.seed, p, cfg.vocab, p_correct=args.p_correct) for p in range(P)]
+    warm_walks(sessions, truth, L, G, args.k,
+               [DraftSource(cfg.seed, 10_000 + p, cfg.vocab, p_correct=args.p_correct) for p in range(P)],
+               profile_mask=1 << ROLE_GATE_UP)
     run_spec(sessions[:1], truth[:1], L, G, args.k, [DraftSource(cfg.seed, 10_000, cfg.vocab, p_correct=args.p_correct)],
              args.warmup)
     for s in sessions:
@@ -443,7 +484,7 @@ def main():
         "tokens_per_target_step": round(st["tokens"] / args.steps, 4),
         "step_ms_median": round(1000.0 * float(np.median(st["step_s"])), 4),
         "step_ms_p90": round(1000.0 * float(np.percentile(st["step_s"], 90)), 4),
-        "verify_steps": args.steps, "decode_steps": P * G,
+        "verify_steps": args.steps, "decode_steps": n_dec * G,
         "rows_scored_per_s": round(st["rows"] / st["seconds"], 1),
         "step_hbm_gbs": round(step_bytes / st["seconds"] / 1e9, 1),
         "step_hbm_frac": round(step_bytes / st["seconds"] / 1e9 / PEAK_HBM_GBS, 4),
@@ -464,6 +505,8 @@ def main():
     for k in [int(x) for x in args.k_sweep.split(",") if x.strip()]:
         if k > cfg.max_k:
             continue
+        warm_walks(sessions, truth, L, G, k,
+                   [DraftSource(cfg.seed, 40_000 + p, cfg.vocab, p_correct=args.p_correct) for p in range(P)])
         sk = run_spec(sessions, truth, L, G, k, [DraftSource(cfg.seed, 20_000 + p, cfg.vocab, p_correct=args.p_correct)
                                                  for p in range(P)], args.sweep_steps)
         sb = sum(algorithmic_step_bytes(cfg, ke + 1, kv) for ke, _, kv in sk["steps"])
@@ -478,6 +521,9 @@ def main():
     for b in batches:
         if b > P:
             continue
+        run_spec_batch(sessions[:b], truth[:b], L, G, args.k,   # untimed: the batch's graphs
+                       [DraftSource(cfg.seed, 60_000 + p, cfg.vocab, p_correct=args.p_correct) for p in range(b)],
+                       min(args.sweep_steps, 4 * G))
         sb_ = run_spec_batch(sessions[:b], truth[:b], L, G, args.k,
                              [DraftSource(cfg.seed, 30_000 + p, cfg.vocab, p_correct=args.p_correct) for p in range(b)],
                              args.sweep_steps)
