@@ -19,12 +19,12 @@ Three commands:
 Usage::
 
     python -m greedy_block_verification_amd.rocprof_summary stats \\
-        --trace DIR/q8b_kernel_trace.csv --kernel "sv::k_gemm_bf16<1, 2>" --last 2160 \\
-        --command "..." --out profiles/gate_up_q8b_k4_kernel_trace.md
+        --trace DIR/q8b_kernel_trace.csv --kernel "sv::k_gemm_bf16<1, 2, 8, false>" --last 2160 \\
+        --skip 720 --command "..." --out profiles/verify_q8b_k4_kernel_trace.md
     python -m greedy_block_verification_amd.rocprof_summary traffic \\
         --fetch A/q8b_counter_collection.csv --write B/q8b_counter_collection.csv \\
-        --kernel "sv::k_gemm_bf16<1, 2>" --last 1440 --copy-bytes 1073741824 \\
-        --algorithmic-bytes 201657173 --command "..." --out profiles/gate_up_q8b_traffic.json
+        --kernel "sv::k_gemm_bf16<1, 2, 8, false>" --last 1440 --skip 720 --copy-bytes 1073741824 \\
+        --algorithmic-bytes 201659392 --command "..." --out profiles/gate_up_q8b_traffic.json
 """
 from __future__ import annotations
 
@@ -44,7 +44,7 @@ def _short(name: str) -> str:
 
 
 def _matches(name: str, kernel: str) -> bool:
-    # "void sv::k_gemm_bf16<1, 2>(sv::GemmArgs)" matches "sv::k_gemm_bf16<1, 2>"
+    # "void sv::k_gemm_bf16<1, 2, 8, false>(sv::GemmArgs)" matches "sv::k_gemm_bf16<1, 2, 8, false>"
     n = name[5:] if name.startswith("void ") else name
     return n.startswith(kernel)
 
