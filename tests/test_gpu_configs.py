@@ -331,3 +331,65 @@ def test_q8b_random_operation_sequence(q8b):
             np.testing.assert_array_equal(bits(s.logits(r)), bits(logits[kv0 + r]))
         ref.close()
     s.close()
+
+
+def test_gemma_int4_random_operation_sequence(gemma):
+    """The int4 GeGLU shape (2 KV heads, groups of 6 q heads) under a seeded
+    random sequence of verifies (K up to 16), rollbacks and decodes: each
+    state equals a context rebuilt from one-token decodes alone."""
+    import numpy as np
+    from greedy_block_verification_amd.session import Session
+    from seeded_inputs import prompt_ids
+    dev, w = gemma
+    cfg = w.cfg
+    rng = np.random.default_rng(9)
+    ids = prompt_ids(cfg.seed, 13, 87, cfg.vocab).tolist()
+    s = Session(dev)
+    s.set_debug(True)
+    s.prefill(ids)
+    committed = list(ids)
+    bits = lambda a: np.asarray(a, dtype=np.float32).view(np.uint32)
+
+    def rebuilt(n):
+        r = Session(dev)
+        r.set_debug(True)
+        logits = []
+        for t in committed[:n]:
+            r.decode_step(t)
+            logits.append(r.logits(0))
+        return r, logits
+
+    for _ in range(6):
+        op = rng.choice(["verify", "verify", "verify", "truncate", "decode"])
+        kv0 = s.kv_len
+        if op == "verify":
+            k = int(rng.integers(1, cfg.max_k + 1))
+            probe, _ = rebuilt(kv0)
+            truth, t = [], s.next_id
+            for _ in range(k):
+                t = probe.decode_step(t)
+                truth.append(t)
+            probe.close()
+            wrong_at = int(rng.integers(0, k + 1))
+            drafts = truth[:wrong_at] + [(x + 1) % cfg.vocab for x in truth[wrong_at:]]
+            rows = [s.next_id] + drafts
+            n, _ = s.verify(drafts)
+            assert n == wrong_at
+            committed[kv0:] = rows[:n + 1]
+            fresh = n + 1
+        elif op == "truncate" and kv0 > 81:
+            s.truncate(int(rng.integers(80, kv0)))
+            del committed[s.kv_len:]
+            fresh = 0
+        else:
+            t = s.next_id
+            s.decode_step(t)
+            committed[kv0:] = [t]
+            fresh = 1
+        ref, logits = rebuilt(s.kv_len)
+        assert (s.kv_len, s.next_id) == (ref.kv_len, ref.next_id) and s.history() == ref.history()
+        np.testing.assert_array_equal(s.kv_positions(s.kv_len), ref.kv_positions(ref.kv_len))
+        for r in range(fresh):
+            np.testing.assert_array_equal(bits(s.logits(r)), bits(logits[kv0 + r]))
+        ref.close()
+    s.close()
