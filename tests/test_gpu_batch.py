@@ -11,7 +11,10 @@ bits -- whatever else the batch holds and in whatever order:
   argument errors that leave every context untouched;
 * 8B shape: 8 sequences x K = 4 (40 rows) against one-at-a-time verifies;
 * Gemma-style int4 layers (GeGLU, 6 q heads per KV head): 4 sequences,
-  19 rows, against one-at-a-time verifies.
+  19 rows, against one-at-a-time verifies;
+* tiny, seeded: 10 rounds over 4 sequences with random rollbacks, a random
+  subset and order of sequences per batch and random window sizes 0..8,
+  against mirror contexts verified one at a time.
 """
 import numpy as np
 import pytest
@@ -212,4 +215,44 @@ def test_int4_gemma_layers_batch_equals_one_at_a_time():
     for s, g, ref, k in zip(ss, got, refs, ks):
         _check(s, g, ref, k + 1)
     for s in ss:
+        s.close()
+
+
+def test_random_batches_with_rollbacks_track_one_at_a_time(tiny):
+    """Seeded rounds: a random subset of four sequences, in random order and
+    with random window sizes (0..8) and drafts right up to a random point, is
+    verified in one batch while mirror contexts verify the same windows one
+    at a time; random rollbacks of single sequences come in between.  After
+    every round each batched context equals its mirror: (n, next), kv_len,
+    next_id, history, the logits rows of its window and its KV bits."""
+    from greedy_block_verification_amd import binding as B
+    dm, w, cfg = tiny
+    rng = np.random.default_rng(31)
+    lens = [20, 33, 7, 61]
+    ss, _ = _contexts(dm, cfg, lens, seed=23)
+    ms, _ = _contexts(dm, cfg, lens, seed=23)
+    for rnd in range(10):
+        if rnd % 3 == 2:   # roll one sequence (and its mirror) back
+            i = int(rng.integers(0, 4))
+            if ss[i].kv_len > 1:
+                n = int(rng.integers(1, ss[i].kv_len))
+                ss[i].truncate(n)
+                ms[i].truncate(n)
+        pick = [int(x) for x in rng.permutation(4)[:int(rng.integers(1, 5))]]
+        ks = [int(rng.integers(0, cfg.max_k + 1)) for _ in pick]
+        pick_ks = [(i, k) for i, k in zip(pick, ks) if ss[i].kv_len + k + 1 <= cfg.max_ctx]
+        if not pick_ks:
+            continue
+        drafts = _drafts(dm, cfg, [ss[i].snapshot() for i, _ in pick_ks], [k for _, k in pick_ks], seed=100 + rnd)
+        got = B.sv_verify_batch([ss[i].ctx for i, _ in pick_ks], [ss[i].kv_len for i, _ in pick_ks], drafts)
+        for (i, k), d, g in zip(pick_ks, drafts, got):
+            kv0 = ms[i].kv_len
+            ref = ms[i].verify(d)
+            assert tuple(g) == tuple(ref)
+            s, m = ss[i], ms[i]
+            assert (s.kv_len, s.next_id) == (m.kv_len, m.next_id) and s.history() == m.history()
+            for r in range(k + 1):
+                np.testing.assert_array_equal(_bits(s.logits(r)), _bits(m.logits(r)))
+            np.testing.assert_array_equal(s.kv_positions(s.kv_len), m.kv_positions(m.kv_len))
+    for s in ss + ms:
         s.close()
