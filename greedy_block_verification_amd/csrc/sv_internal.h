@@ -71,6 +71,14 @@ struct GemmArgs {
   unsigned long long* best;   // [M] row argmax keys (orderable logit, ~id), zeroed by the embed kernel
   float* logits;         // optional [M][N] fp32
   unsigned long long* prof;   // optional [2]: (min start, max end) device wall clock
+  // item plan of the one-workgroup-per-CU bf16 kernel (set by launch_gemm):
+  // whole items below n_full, and half items for workgroups below n_half
+  int n_full, n_half;
+  // launch constants of the skinny kernels (set by the host dispatch, so no
+  // division runs before the weight ring starts): chunks per LDS stage,
+  // stages per item, chunks per wave per stage and per item, and whether the
+  // bf16 kernel stages its activations through the register prologue
+  int cs, n_stages, cpws, cpi, pro_fast;
 };
 
 struct AttnArgs {

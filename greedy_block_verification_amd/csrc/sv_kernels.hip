@@ -237,7 +237,11 @@ struct GemmShared {
   unsigned long long best[kMaxRows];   // LM head: this workgroup's row argmax keys
 };
 
-__device__ __forceinline__ constexpr bool norm_role(int role) {
+// Pair index of row i of a QKV tile (the weight packing below): rows i and
+// i ^ 4 are a (dim, RoPE partner) pair.
+__device__ __forceinline__ int pair_of(int i) { return 4 * (i >> 3) + (i & 3); }
+
+__host__ __device__ __forceinline__ constexpr bool norm_role(int role) {
   return role == kRoleQkv || role == kRoleGateUp || role == kRoleLmHead;
 }
 
@@ -296,7 +300,7 @@ __device__ __forceinline__ EpiPre epi_load(const GemmArgs& a, int T, int idx) {
     } else {
       e.pos = a.params[0] + r;
     }
-    if (hh < a.nq + a.nkv) e.cs = a.rope[(size_t)e.pos * half + 8 * sb + (c & 7)];
+    if (hh < a.nq + a.nkv) e.cs = a.rope[(size_t)e.pos * half + 8 * sb + pair_of(c)];
     if (hh >= a.nq) e.page = table[e.pos / kPage];
   }
   return e;
@@ -328,18 +332,18 @@ __device__ __forceinline__ void epi_element(const GemmArgs& a, int T, int r, int
       const size_t ai = (size_t)r * (a.N >> 1) + T * 8 + c;
       split1(act_fn(y, a.act) * up, a.ahi[ai], a.alo[ai]);
     }
-  } else if (ROLE == kRoleQkv) {                  // [dims 8s+i | half + 8s + i], i < 8
+  } else if (ROLE == kRoleQkv) {                  // dim 8s + pair_of(c) at c, its partner at c ^ 4
     const int half = a.dh >> 1;
     const int gph = half >> 3;
     const int hh = T / gph, sb = T % gph;
-    const bool lo = c < 8;
-    const int i = 8 * sb + (c & 7);
+    const bool lo = (c & 4) == 0;
+    const int i = 8 * sb + pair_of(c);
     const int d = lo ? i : half + i;
     const int pos = e.pos;
     float out = y;
     if (hh < a.nq + a.nkv) {
       const float2 cs = e.cs;
-      const float partner = yv(c ^ 8) * invr;
+      const float partner = yv(c ^ 4) * invr;
       out = lo ? (y * cs.x - partner * cs.y) : (y * cs.x + partner * cs.y);
     }
     if (hh < a.nq) {
@@ -363,11 +367,15 @@ __device__ __forceinline__ void epi_element(const GemmArgs& a, int T, int r, int
   }
 }
 
-// Epilogue on the finished 16 columns of item (tile) T.
+// Epilogue on the finished 16 columns of item (tile) T, or on columns
+// [8 hf, 8 hf + 8) only for a half item (hf >= 0: QKV, whose
+// column pairs never cross the halves; the other half's columns then hold
+// copies of these and are not written).
 template <int ROLE>
-__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, GemmShared& sh, int T, const EpiPre& pre) {
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, GemmShared& sh, int T, const EpiPre& pre, int hf) {
   for (int idx = threadIdx.x; idx < a.M * 16; idx += blockDim.x) {
     const int r = idx >> 4, c = idx & 15;
+    if (hf >= 0 && (c >> 3) != hf) continue;
     const EpiPre e = idx == (int)threadIdx.x ? pre : epi_load<ROLE>(a, T, idx);
     epi_element<ROLE>(a, T, r, c, e, sh.inv[r], [&](int cc) { return sh.y[r][cc]; }, &sh.best[r]);
   }
@@ -376,7 +384,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, GemmShared& sh,
 // Wave partials of one item -> LDS -> summed in wave order -> sh.y -> epilogue.
 template <int TM, int ROLE>
 __device__ __forceinline__ void gemm_finish(const GemmArgs& a, GemmShared& sh, f32x4 (&acc)[TM], int T, int wave,
-                                            int lane, int nw, const EpiPre& pre) {
+                                            int lane, int nw, const EpiPre& pre, int hf = -1) {
 #pragma unroll
   for (int rt = 0; rt < TM; ++rt) {
     sh.red[wave][lane] = acc[rt];
@@ -402,7 +410,7 @@ __device__ __forceinline__ void gemm_finish(const GemmArgs& a, GemmShared& sh, f
     }
     __syncthreads();
   }
-  gemm_epilogue<ROLE>(a, sh, T, pre);
+  gemm_epilogue<ROLE>(a, sh, T, pre, hf);
   __syncthreads();
 }
 
@@ -545,27 +553,39 @@ struct ProRegs {   // named members, not arrays: they must stay in registers
   uint4 v0, v1, v2, v3, v4, v5, v6, v7;
   float s0, s1, s2, s3, s4, s5, s6, s7;
 };
-__device__ __forceinline__ bool prologue_fast(const GemmArgs& a, int cs, int unit, int nw, bool norm) {
+__host__ __device__ __forceinline__ bool prologue_fast(const GemmArgs& a, int cs, int unit, int nw, bool norm) {
   const int n_vec = 2 * a.M * ((cs * unit) >> 3);
   if (n_vec > kProRegs * nw * 64) return false;
   return !norm || (a.M <= nw && (a.K >> 4) <= 64 * kSsRegs);
 }
-// vector k of this thread (index i = threadIdx.x + k * nthr of the hi plane, then the lo plane)
-__device__ __forceinline__ uint4 pro_load(const GemmArgs& a, int vpr, int k, int nthr) {
-  const int per_plane = a.M * vpr;
-  const int i = threadIdx.x + k * nthr;
-  if (i >= 2 * per_plane) return make_uint4(0u, 0u, 0u, 0u);
-  const int pl = i >= per_plane, ii = pl ? i - per_plane : i;
-  const int r = ii / vpr, v = ii % vpr;
-  return *reinterpret_cast<const uint4*>((pl ? a.blo : a.bhi) + (size_t)r * a.K + (size_t)v * 8);
+// Vector k of this thread: index i = threadIdx.x + k * nthr over the hi
+// plane's rows, then the lo plane's; q = i / vpr is the plane row (lo plane
+// row q - M from q = M on), m = i % vpr the vector in it.  (q, m) step from
+// k to k + 1 without a division, so the weight ring, requested after these
+// loads, is not held up by per-vector divisions.
+struct ProIdx {
+  int q, m, dq, dm, vpr;
+  __device__ __forceinline__ ProIdx(int vpr_, int nthr) : vpr(vpr_) {
+    q = (int)threadIdx.x / vpr;
+    m = (int)threadIdx.x - q * vpr;
+    dq = nthr / vpr;
+    dm = nthr - dq * vpr;
+  }
+  __device__ __forceinline__ void next() {
+    q += dq;
+    m += dm;
+    if (m >= vpr) { m -= vpr; ++q; }
+  }
+};
+__device__ __forceinline__ uint4 pro_load(const GemmArgs& a, const ProIdx& p) {
+  if (p.q >= 2 * a.M) return make_uint4(0u, 0u, 0u, 0u);
+  const int pl = p.q >= a.M, r = pl ? p.q - a.M : p.q;
+  return *reinterpret_cast<const uint4*>((pl ? a.blo : a.bhi) + (size_t)r * a.K + (size_t)p.m * 8);
 }
-__device__ __forceinline__ void pro_store(const GemmArgs& a, const Stage& st, int vpr, int k, int nthr, uint4 val) {
-  const int per_plane = a.M * vpr;
-  const int i = threadIdx.x + k * nthr;
-  if (i >= 2 * per_plane) return;
-  const int pl = i >= per_plane, ii = pl ? i - per_plane : i;
-  const int r = ii / vpr, v = ii % vpr;
-  *reinterpret_cast<uint4*>((pl ? st.lo : st.hi) + r * st.stride + v * 8) = val;
+__device__ __forceinline__ void pro_store(const GemmArgs& a, const Stage& st, const ProIdx& p, uint4 val) {
+  if (p.q >= 2 * a.M) return;
+  const int pl = p.q >= a.M, r = pl ? p.q - a.M : p.q;
+  *reinterpret_cast<uint4*>((pl ? st.lo : st.hi) + r * st.stride + p.m * 8) = val;
 }
 __device__ __forceinline__ float ss_load(const GemmArgs& a, int wave, int lane, int k) {
   const int nsl = a.K >> 4;
@@ -574,12 +594,12 @@ __device__ __forceinline__ float ss_load(const GemmArgs& a, int wave, int lane, 
 }
 __device__ __forceinline__ ProRegs prologue_issue(const GemmArgs& a, int cs, int unit, int nthr, int wave, int lane,
                                                   bool norm) {
-  const int vpr = (cs * unit) >> 3;
+  ProIdx p((cs * unit) >> 3, nthr);
   ProRegs pr;
-  pr.v0 = pro_load(a, vpr, 0, nthr); pr.v1 = pro_load(a, vpr, 1, nthr);
-  pr.v2 = pro_load(a, vpr, 2, nthr); pr.v3 = pro_load(a, vpr, 3, nthr);
-  pr.v4 = pro_load(a, vpr, 4, nthr); pr.v5 = pro_load(a, vpr, 5, nthr);
-  pr.v6 = pro_load(a, vpr, 6, nthr); pr.v7 = pro_load(a, vpr, 7, nthr);
+  pr.v0 = pro_load(a, p); p.next(); pr.v1 = pro_load(a, p); p.next();
+  pr.v2 = pro_load(a, p); p.next(); pr.v3 = pro_load(a, p); p.next();
+  pr.v4 = pro_load(a, p); p.next(); pr.v5 = pro_load(a, p); p.next();
+  pr.v6 = pro_load(a, p); p.next(); pr.v7 = pro_load(a, p);
   pr.s0 = pr.s1 = pr.s2 = pr.s3 = pr.s4 = pr.s5 = pr.s6 = pr.s7 = 0.f;
   if (norm && wave < a.M) {
     pr.s0 = ss_load(a, wave, lane, 0); pr.s1 = ss_load(a, wave, lane, 1);
@@ -600,11 +620,11 @@ __device__ __forceinline__ void prologue_finish(const GemmArgs& a, const Stage& 
     v = wave_sum(v);
     if (lane == 0) sh.inv[wave] = 1.0f / sqrtf(v / (float)a.K + a.eps);
   }
-  const int vpr = (cs * unit) >> 3;
-  pro_store(a, st, vpr, 0, nthr, pr.v0); pro_store(a, st, vpr, 1, nthr, pr.v1);
-  pro_store(a, st, vpr, 2, nthr, pr.v2); pro_store(a, st, vpr, 3, nthr, pr.v3);
-  pro_store(a, st, vpr, 4, nthr, pr.v4); pro_store(a, st, vpr, 5, nthr, pr.v5);
-  pro_store(a, st, vpr, 6, nthr, pr.v6); pro_store(a, st, vpr, 7, nthr, pr.v7);
+  ProIdx p((cs * unit) >> 3, nthr);
+  pro_store(a, st, p, pr.v0); p.next(); pro_store(a, st, p, pr.v1); p.next();
+  pro_store(a, st, p, pr.v2); p.next(); pro_store(a, st, p, pr.v3); p.next();
+  pro_store(a, st, p, pr.v4); p.next(); pro_store(a, st, p, pr.v5); p.next();
+  pro_store(a, st, p, pr.v6); p.next(); pro_store(a, st, p, pr.v7);
 }
 
 // Weight loads of one wave run as a ring of NB slots: a slot is refilled with
@@ -613,8 +633,40 @@ __device__ __forceinline__ void prologue_finish(const GemmArgs& a, const Stage& 
 // each item.  Position (item T, c) of wave w is chunk kc = w + nw * c of T;
 // the ring changes only when chunks arrive, never the order of any sum.
 struct LoadCursor {
-  int T, c;
-  size_t off;   // uint4 offset of chunk (T, c) for lane 0 of this wave
+  int T, c;     // item (bf16: this workgroup's item ordinal; int4: the tile) and chunk position
+  size_t off;   // chunk (T, c): bf16, this lane's uint4 offset; int4, the chunk index
+};
+
+// Items of one workgroup.  Whole items T = b, b + G, ... below n_full; for
+// QKV, when the r = n_items % G items of the last round would leave
+// workgroups idle (r <= G/2), each of those items is split into its two
+// 8-column halves, one half per workgroup, so every workgroup streams the
+// same bytes (the 8B shape: 384 items on 256 workgroups).  A half item loads
+// only its own rows' weights (lanes of the other half repeat them) and
+// writes only its own columns; every output's sums are those of the whole
+// item.  launch_gemm sets n_full and n_half (2 r, or 0 without a split).
+// Measured on MI355X: the split code path costs a gate/up GEMM more than
+// splitting would gain on these shapes, so only QKV takes it.
+template <int ROLE>
+struct ItemPlan {
+  static constexpr bool kSplits = ROLE == kRoleQkv;
+  int n_full, n_half, G;
+  // item o of this workgroup: tile T and half hf (-1: whole); -1 past its last
+  __device__ __forceinline__ int tile(int o, int& hf) const {
+    const int b = blockIdx.x;
+    const int T = b + o * G;
+    hf = -1;
+    if (T < n_full) return T;
+    if (kSplits && b < n_half && T - G < n_full) {
+      hf = b & 1;
+      return n_full + (b >> 1);
+    }
+    return -1;
+  }
+  // whether item (T, hf) of this workgroup is followed by another
+  __device__ __forceinline__ bool has_next(int T, int hf) const {
+    return hf < 0 && (T + G < n_full || (kSplits && (int)blockIdx.x < n_half));
+  }
 };
 
 // bf16: wave w accumulates chunks w, w + NW, w + 2 NW, ... of each item in
@@ -628,10 +680,10 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int KC = a.K >> 5;
-  const int cs = DBL ? nw * NB : stage_chunks(KC, nw, a.M, 32, NB);
-  const int n_stages = KC / cs;
-  const int cpws = cs / nw;                     // chunks per wave per stage (multiple of NB; DBL: NB)
-  const int cpi = KC / nw;                      // chunks per wave per item (multiple of NB)
+  const int cs = a.cs;                          // DBL: nw * NB
+  const int n_stages = a.n_stages;
+  const int cpws = a.cpws;                      // chunks per wave per stage (multiple of NB; DBL: NB)
+  const int cpi = a.cpi;                        // chunks per wave per item (multiple of NB)
   const int stride = cs * 32 + 8;
   const int buf_elems = 2 * a.M * stride;       // one buffer: hi then lo planes
   // stage buffer b (no array of pointers: a runtime index would put it in scratch)
@@ -642,10 +694,17 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16(GemmArgs a) {
     x.lo = x.hi + (size_t)a.M * stride;
     return x;
   };
-  const int n_items = a.N >> 4;
+  const ItemPlan<ROLE> ip{a.n_full, a.n_half, (int)gridDim.x};
   // packed weights are tile-major: chunk kc of tile T is the KiB at (T * KC + kc)
-  const uint4* W4 = reinterpret_cast<const uint4*>(a.W) + lane;
-  LoadCursor cur{(int)blockIdx.x, 0, ((size_t)blockIdx.x * KC + wave) * 64};
+  const uint4* W4 = reinterpret_cast<const uint4*>(a.W);
+  // this lane's uint4 inside chunk 0 of item o (a half item's other lanes load its own rows)
+  auto item_off = [&](int o) {                 // (past the last item: computed, never loaded)
+    int hf;
+    const int T = max(ip.tile(o, hf), 0);
+    const int ln = hf < 0 ? lane : ((lane & ~8) | (hf << 3));
+    return ((size_t)T * KC + wave) * 64 + ln;
+  };
+  LoadCursor cur{0, 0, item_off(0)};
   // Unconditional: the caller never refills past this workgroup's last item
   // (loads that may or may not be issued would leave the compiler unable to
   // count outstanding loads, and every wait would drain them all).
@@ -654,11 +713,11 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16(GemmArgs a) {
     cur.off += (size_t)nw * 64;
     if (++cur.c == cpi) {
       cur.c = 0;
-      cur.T += gridDim.x;
-      cur.off = ((size_t)cur.T * KC + wave) * 64;
+      cur.T += 1;                               // next item ordinal of this workgroup
+      cur.off = item_off(cur.T);
     }
   };
-  const bool fast = (n_stages == 1 || DBL) && prologue_fast(a, cs, 32, nw, norm_role(ROLE));
+  const bool fast = a.pro_fast != 0;
   ProRegs pr{};
   if (fast) pr = prologue_issue(a, cs, 32, nw * 64, wave, lane, norm_role(ROLE));
   uint4 A[NB];
@@ -677,21 +736,24 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16(GemmArgs a) {
   }
   int buf = 0;                                  // DBL: buffer of the current stage
 
-  for (int T = blockIdx.x; T < n_items; T += gridDim.x) {
+  for (int o = 0;; ++o) {
+    int hf;
+    const int T = ip.tile(o, hf);
+    if (T < 0) break;
     const EpiPre pre = epi_load<ROLE>(a, T, threadIdx.x);
     f32x4 acc[TM];
 #pragma unroll
     for (int rt = 0; rt < TM; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int cl0 = 0, si = 0;                        // position inside the current stage, and its index
     for (int c0 = 0; c0 < cpi; c0 += NB) {
-      const int cl0 = c0 % cpws;                // position inside the current stage
       if (!DBL && n_stages > 1 && cl0 == 0) {
         __syncthreads();
-        stage_planes(a, stage_buf(0), (c0 / cpws) * cs, cs, 32);
+        stage_planes(a, stage_buf(0), si * cs, cs, 32);
         __syncthreads();
       }
       StageRegs sreg{};
       if (DBL) {                                // next stage (cyclically: the next item restarts at 0)
-        const int s_next = c0 / cpws + 1;
+        const int s_next = si + 1;
         sreg = stage_fetch(a, s_next < n_stages ? s_next * cs : 0, cs, 32, nw * 64);
       }
       const Stage st = stage_buf(DBL ? buf : 0);
@@ -713,11 +775,13 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16(GemmArgs a) {
           __syncthreads();
         }
       };
-      if (T + (int)gridDim.x < n_items || c0 + NB < cpi) group(true);
+      if (ip.has_next(T, hf) || c0 + NB < cpi) group(true);
       else group(false);                        // the last NB chunks of this workgroup
       if (DBL) buf ^= 1;
+      cl0 += NB;
+      if (cl0 == cpws) { cl0 = 0; ++si; }
     }
-    gemm_finish<TM, ROLE>(a, sh, acc, T, wave, lane, nw, pre);
+    gemm_finish<TM, ROLE>(a, sh, acc, T, wave, lane, nw, pre, hf);
   }
   row_best_publish<ROLE>(a, sh);
   prof_end(a.prof);
@@ -742,10 +806,10 @@ __global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int KT = a.K >> 7;                 // 128-input tiles
-  const int cs = stage_chunks(KT, nw, a.M, 128, NB);
-  const int n_stages = KT / cs;
-  const int cpws = cs / nw;
-  const int cpi = KT / nw;
+  const int cs = a.cs;
+  const int n_stages = a.n_stages;
+  const int cpws = a.cpws;
+  const int cpi = a.cpi;
   Stage st;
   st.stride = cs * 128 + 8;
   st.hi = stage_mem;
@@ -779,11 +843,11 @@ __global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
     f32x4 acc[TM];
 #pragma unroll
     for (int rt = 0; rt < TM; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int cl0 = 0, si = 0;                    // position inside the current stage, and its index
     for (int c0 = 0; c0 < cpi; c0 += NB) {
-      const int cl0 = c0 % cpws;
       if (n_stages > 1 && cl0 == 0) {
         __syncthreads();
-        stage_planes(a, st, (c0 / cpws) * cs, cs, 128);
+        stage_planes(a, st, si * cs, cs, 128);
         __syncthreads();
       }
       auto group = [&](bool refills) {
@@ -813,6 +877,8 @@ __global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
       };
       if (T + (int)gridDim.x < n_items || c0 + NB < cpi) group(true);
       else group(false);
+      cl0 += NB;
+      if (cl0 == cpws) { cl0 = 0; ++si; }
     }
     gemm_finish<TM, ROLE>(a, sh, acc, T, wave, lane, nw, pre);
   }
@@ -1089,9 +1155,18 @@ int gemm_ring_depth(int n_chunks, int waves, int M, int unit, bool* dbl) {
 }
 
 template <int ROLE, bool INT4>
-static hipError_t gemm_dispatch(const GemmArgs& a, int grid, hipStream_t st) {
+static hipError_t gemm_dispatch(const GemmArgs& a_in, int grid, hipStream_t st) {
   bool dbl = false;
-  switch (gemm_ring_depth(a.K / (INT4 ? 128 : 32), a.S, a.M, INT4 ? 128 : 32, &dbl)) {
+  const int unit = INT4 ? 128 : 32, n_chunks = a_in.K / unit, nw = a_in.S;
+  const int nb = gemm_ring_depth(n_chunks, nw, a_in.M, unit, &dbl);
+  if (nb < 1) return hipErrorInvalidValue;
+  GemmArgs a = a_in;
+  a.cs = dbl ? nw * nb : stage_chunks(n_chunks, nw, a.M, unit, nb);
+  a.n_stages = n_chunks / a.cs;
+  a.cpws = a.cs / nw;
+  a.cpi = n_chunks / nw;
+  a.pro_fast = !INT4 && (a.n_stages == 1 || dbl) && prologue_fast(a, a.cs, unit, nw, norm_role(ROLE));
+  switch (nb) {
     case 8:
       if constexpr (INT4) return hipErrorInvalidValue;
       else return gemm_dispatch_nb<ROLE, INT4, 8>(a, grid, st, dbl);
@@ -1111,6 +1186,13 @@ hipError_t launch_gemm(const GemmArgs& a, int role, int grid, hipStream_t st) {
   if (a.M > gemm_max_rows(a.fmt == 1 ? 128 : 32, a.S)) return hipErrorInvalidValue;
   grid = grid > (a.N >> 4) ? (a.N >> 4) : grid;
   const bool i4 = a.fmt == 1;
+  // item plan of k_gemm_bf16 (QKV splits the last round's items into halves
+  // when that spreads them over at most every workgroup)
+  GemmArgs b = a;
+  const int n_items = a.N >> 4, r = n_items % grid;
+  const bool split = role == kRoleQkv && r > 0 && 2 * r <= grid;
+  b.n_full = split ? n_items - r : n_items;
+  b.n_half = split ? 2 * r : 0;
   // 17..64 rows whose bf16 planes do not fit one stage: items in groups,
   // stages outermost.  Measured on the 8B shapes: the restaging kernel is
   // faster for 9..16 rows, and for 34..48 rows except on the LM head.
@@ -1118,23 +1200,23 @@ hipError_t launch_gemm(const GemmArgs& a, int role, int grid, hipStream_t st) {
   const bool grp = mode == 1 || (mode == 2 && (a.M > 48 || role == kRoleLmHead));
   if (!i4 && a.M >= 17 && grp && stage_chunks(a.K >> 5, a.S, a.M, 32, 1) < (a.K >> 5)) {
     switch (role) {
-      case kRoleQkv: return gemm_dispatch_grp<kRoleQkv>(a, grid, st);
-      case kRoleO: return gemm_dispatch_grp<kRoleO>(a, grid, st);
-      case kRoleGateUp: return gemm_dispatch_grp<kRoleGateUp>(a, grid, st);
-      case kRoleDown: return gemm_dispatch_grp<kRoleDown>(a, grid, st);
-      case kRoleLmHead: return gemm_dispatch_grp<kRoleLmHead>(a, grid, st);
+      case kRoleQkv: return gemm_dispatch_grp<kRoleQkv>(b, grid, st);
+      case kRoleO: return gemm_dispatch_grp<kRoleO>(b, grid, st);
+      case kRoleGateUp: return gemm_dispatch_grp<kRoleGateUp>(b, grid, st);
+      case kRoleDown: return gemm_dispatch_grp<kRoleDown>(b, grid, st);
+      case kRoleLmHead: return gemm_dispatch_grp<kRoleLmHead>(b, grid, st);
       default: return hipErrorInvalidValue;
     }
   }
   switch (role) {
-    case kRoleQkv: return i4 ? gemm_dispatch<kRoleQkv, true>(a, grid, st) : gemm_dispatch<kRoleQkv, false>(a, grid, st);
-    case kRoleO: return i4 ? gemm_dispatch<kRoleO, true>(a, grid, st) : gemm_dispatch<kRoleO, false>(a, grid, st);
+    case kRoleQkv: return i4 ? gemm_dispatch<kRoleQkv, true>(b, grid, st) : gemm_dispatch<kRoleQkv, false>(b, grid, st);
+    case kRoleO: return i4 ? gemm_dispatch<kRoleO, true>(b, grid, st) : gemm_dispatch<kRoleO, false>(b, grid, st);
     case kRoleGateUp:
-      return i4 ? gemm_dispatch<kRoleGateUp, true>(a, grid, st) : gemm_dispatch<kRoleGateUp, false>(a, grid, st);
-    case kRoleDown: return i4 ? gemm_dispatch<kRoleDown, true>(a, grid, st) : gemm_dispatch<kRoleDown, false>(a, grid, st);
+      return i4 ? gemm_dispatch<kRoleGateUp, true>(b, grid, st) : gemm_dispatch<kRoleGateUp, false>(b, grid, st);
+    case kRoleDown: return i4 ? gemm_dispatch<kRoleDown, true>(b, grid, st) : gemm_dispatch<kRoleDown, false>(b, grid, st);
     case kRoleLmHead:
       if (i4) return hipErrorInvalidValue;
-      return gemm_dispatch<kRoleLmHead, false>(a, grid, st);
+      return gemm_dispatch<kRoleLmHead, false>(b, grid, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -2442,8 +2524,9 @@ hipError_t launch_copy_pages(const void* src, const int* src_pt, int src_pages, 
 //   layout 0: src0 row 16T + i
 //   layout 1 (gate/up): i < 8: src0 (gate) row 8T + i; else src1 (up) row 8T + i - 8
 //   layout 2 (QKV, per head of head_dim rows, gph = head_dim/16 tiles per
-//            head): tile (head h, s) holds dims 8s + i (i < 8) and their
-//            RoPE partners dh/2 + 8s + (i - 8)
+//            head): tile (head h, s) holds, for f = pair_of(i), dim 8s + f
+//            in row i when i & 4 == 0 and its RoPE partner dh/2 + 8s + f in
+//            row i ^ 4, so either 8-row half of the tile holds whole pairs
 __device__ __forceinline__ int pack_src_row(int layout, int T, int i, int dh, int& which) {
   which = 0;
   if (layout == 1) {
@@ -2453,7 +2536,7 @@ __device__ __forceinline__ int pack_src_row(int layout, int T, int i, int dh, in
   if (layout == 2) {
     const int half = dh >> 1, gph = half >> 3;
     const int hh = T / gph, sb = T % gph;
-    return hh * dh + (i < 8 ? 0 : half) + 8 * sb + (i & 7);
+    return hh * dh + ((i & 4) ? half : 0) + 8 * sb + pair_of(i);
   }
   return T * 16 + i;
 }

@@ -67,10 +67,10 @@ struct Plans {
   GemmPlan qkv, o, gu, d, lm;
 };
 
-// Workgroups per GEMM: enough to cover two per compute unit, never more
-// than there are 16-output items.  Any grid gives the same bits.
-// One persistent workgroup per CU (a GEMM workgroup holds a whole CU's
-// worth of waves and LDS); the LM head's many items take two per CU.
+// Persistent workgroups per GEMM: per_cu per compute unit, never more than
+// there are 16-output items.  A GEMM workgroup holds a whole CU's worth of
+// waves and LDS, so the layer GEMMs take one per CU; the LM head's many
+// items take two.  Any grid gives the same bits.
 int grid_for(int N, int per_cu, int n_cu) { return std::max(1, std::min(N / 16, per_cu * n_cu)); }
 
 Plans make_plans(const sv_config& c, int n_cu) {
