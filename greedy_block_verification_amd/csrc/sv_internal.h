@@ -104,6 +104,11 @@ struct AttnArgs {
   int spw;               // splits per workgroup
   int wpb;               // waves per workgroup
   int final_fold;        // 1: one workgroup per KV head folds its splits in LDS and writes the output
+  // set by the launchers: q heads per KV head, q tiles and split groups, and
+  // for each the multiplier that divides by it (n / d as the high word of
+  // n * magic), so the kernels run no integer division before their loads
+  int G, n_qt, n_sg;
+  unsigned g_magic, qt_magic, sg_magic;
 };
 
 hipError_t launch_gemm(const GemmArgs& a, int role, int grid, hipStream_t st);

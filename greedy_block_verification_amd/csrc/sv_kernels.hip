@@ -1617,7 +1617,18 @@ __host__ __device__ __forceinline__ int attn_bps(int ctx) {
 __host__ __device__ __forceinline__ int attn_ns(int ctx) {
   const int nb = (ctx + kAttnBlock - 1) / kAttnBlock;
   const int bps = attn_bps(ctx);
-  return (nb + bps - 1) / bps;
+  return bps == 1 ? nb : (nb + bps - 1) / bps;   // (contexts up to 8192 skip the division)
+}
+
+// n / d for n >= 0 and n * d < 2^32, as the high word of n * m with
+// m = ceil(2^32 / d) = (2^32 + e) / d, 0 <= e < d: n m / 2^32 = n / d + n e /
+// (d 2^32), and n e / (d 2^32) < n / 2^32 < 1 / d, which never carries the
+// quotient past the next integer.  d = 1 takes n itself (m would not fit).
+inline unsigned div_magic(int d) {
+  return d <= 1 ? 0u : (unsigned)((0x100000000ull + (unsigned)d - 1u) / (unsigned)d);
+}
+__device__ __forceinline__ int div_m(int n, int d, unsigned magic) {
+  return d == 1 ? n : (int)__umulhi((unsigned)n, magic);
 }
 int attn_splits(int ctx) { return attn_ns(ctx); }
 // The split count is not monotone in ctx (ctx 8192: 128 one-block splits;
@@ -1807,9 +1818,9 @@ __device__ __forceinline__ void attn_block_step(const AttnArgs& a, const AttnKV<
 
 // Rows of the q tile starting at q-row qbase (of a sequence of M rows) whose
 // ranges make up a unit: r0 .. r1.
-__device__ __forceinline__ void attn_tile_rows(int qbase, int G, int M, int& r0, int& r1) {
-  r0 = qbase / G;
-  r1 = min((qbase + 15) / G, M - 1);
+__device__ __forceinline__ void attn_tile_rows(int qbase, int G, unsigned gm, int M, int& r0, int& r1) {
+  r0 = div_m(qbase, G, gm);
+  r1 = min(div_m(qbase + 15, G, gm), M - 1);
 }
 
 // The view of one q tile: its sequence's pool, page table and length, the
@@ -1837,9 +1848,7 @@ __device__ __forceinline__ AttnView attn_view(const AttnArgs& a, int qt) {
 __device__ __forceinline__ int attn_kv_len(const AttnArgs& a, int qt) {
   return a.seqs != nullptr ? a.seqs[a.tiles[qt].x].kv_len : a.params[0];
 }
-__device__ __forceinline__ int attn_n_tiles(const AttnArgs& a) {
-  return a.seqs != nullptr ? a.n_tiles : (a.M * (a.nq / a.nkv) + 15) >> 4;
-}
+__device__ __forceinline__ int attn_n_tiles(const AttnArgs& a) { return a.n_qt; }
 
 // Union of the tile rows' ranges of split sp, in whole blocks [b_lo, b_hi)
 // (wave-uniform; empty when no row of the tile has that split).
@@ -1864,24 +1873,26 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   prof_start(a.prof);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
-  const int G = a.nq / a.nkv;
-  const int n_qt = attn_n_tiles(a);
+  const int G = a.G;
+  const int n_qt = a.n_qt;
   // Workgroup -> (q tile, split group, KV head).  Workgroups are dealt to the
   // 8 XCDs round-robin in launch order; when the (split group, head) units
   // come in multiples of 8, the q tiles of one unit are placed 8 apart so
   // they run on the same XCD and read the unit's K/V through one L2.
-  const int n_sg = (a.n_split + a.spw - 1) / a.spw;
+  const int n_sg = a.n_sg;
   const int n_units = n_sg * a.nkv;
   const int lid = blockIdx.x + n_qt * n_sg * blockIdx.y;
   int qt, sg, h;
   if (n_qt > 1 && (n_units & 7) == 0) {
-    qt = (lid >> 3) % n_qt;
-    const int u = (lid / (8 * n_qt)) * 8 + (lid & 7);
-    sg = u % n_sg;
-    h = u / n_sg;
+    const int l8 = lid >> 3;
+    const int qd = div_m(l8, n_qt, a.qt_magic);   // lid / (8 n_qt)
+    qt = l8 - qd * n_qt;
+    const int u = qd * 8 + (lid & 7);
+    h = div_m(u, n_sg, a.sg_magic);
+    sg = u - h * n_sg;
   } else {
-    qt = blockIdx.x % n_qt;
-    sg = blockIdx.x / n_qt;
+    sg = div_m(blockIdx.x, n_qt, a.qt_magic);
+    qt = blockIdx.x - sg * n_qt;
     h = blockIdx.y;
   }
   const int s_lo = sg * a.spw;
@@ -1893,8 +1904,9 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   // r is the row inside the tile's sequence
   const int qr = V.qbase + j;
   const bool have = qr < n_qr;
-  const int r = have ? qr / G : 0;
-  const int head = h * G + (have ? qr % G : 0);
+  const int rq = div_m(qr, G, a.g_magic);
+  const int r = have ? rq : 0;
+  const int head = h * G + (have ? qr - rq * G : 0);
   float4 qraw[DC][2];
   {
     const float4* qp = reinterpret_cast<const float4*>(a.q + ((size_t)(V.row0 + r) * a.nq + head) * DH + g * 8);
@@ -1928,7 +1940,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     int b_lo, b_hi;
     {
       int r0, r1;
-      attn_tile_rows(V.qbase, G, V.m, r0, r1);
+      attn_tile_rows(V.qbase, G, a.g_magic, V.m, r0, r1);
       attn_split_union(kv_len, r0, r1, sp, b_lo, b_hi);
     }
     f32x4 o[DT];
@@ -1968,7 +1980,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       const int jj = t / TPR, d0 = (t % TPR) * 4;
       const int q2 = V.qbase + jj;
       if (q2 >= n_qr) continue;
-      const int r2 = q2 / G, head2 = h * G + q2 % G;
+      const int r2 = div_m(q2, G, a.g_magic), head2 = h * G + (q2 - r2 * G);
       const int ns = attn_ns(kv_len + r2 + 1);
       // the Fold arithmetic, with the weights of a split shared by the 4 outputs
       float fm = ul[0].m[jj], fl = ul[0].l[jj];
@@ -2009,7 +2021,7 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnArgs a) {
   prof_start(a.prof);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
-  const int G = a.nq / a.nkv;
+  const int G = a.G;
   const int n_qt = attn_n_tiles(a);
   // Workgroups are dealt to the 8 XCDs round-robin in launch order; with the
   // KV head varying fastest, each XCD runs one head's q tiles (with 8 KV
@@ -2023,8 +2035,9 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnArgs a) {
     const int n_qr = V.m * G;
     const int qr = V.qbase + j;
     const bool have = qr < n_qr;
-    const int r = have ? qr / G : 0;
-    const int head = h * G + (have ? qr % G : 0);
+    const int rq = div_m(qr, G, a.g_magic);
+    const int r = have ? rq : 0;
+    const int head = h * G + (have ? qr - rq * G : 0);
     BPair qop[DC];
     {
       const float4* qp = reinterpret_cast<const float4*>(a.q + ((size_t)(V.row0 + r) * a.nq + head) * DH + g * 8);
@@ -2040,7 +2053,7 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnArgs a) {
     const int ctx = kv_len + r + 1;
     const int ns_row = attn_ns(ctx);
     int r0, r1;
-    attn_tile_rows(V.qbase, G, V.m, r0, r1);
+    attn_tile_rows(V.qbase, G, a.g_magic, V.m, r0, r1);
     int ns_max = 1;
     for (int rr = r0; rr <= r1; ++rr) ns_max = max(ns_max, attn_ns(kv_len + rr + 1));
 
@@ -2116,7 +2129,7 @@ __global__ __launch_bounds__(256) void k_attn_rows2(AttnArgs a) {
   prof_start(a.prof);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
-  const int G = a.nq / a.nkv;
+  const int G = a.G;
   const int n_qt = attn_n_tiles(a);
   // Workgroups are dealt to the 8 XCDs round-robin in launch order; with the
   // KV head varying fastest, each XCD runs one head's q tiles (with 8 KV
@@ -2139,8 +2152,9 @@ __global__ __launch_bounds__(256) void k_attn_rows2(AttnArgs a) {
       const int qbase = V.qbase + 16 * u;
       const int qr = qbase + j;
       have[u] = qt0 + u < n_qt && qr < n_qr;
-      r[u] = have[u] ? qr / G : 0;
-      head[u] = h * G + (have[u] ? qr % G : 0);
+      const int rq = div_m(qr, G, a.g_magic);
+      r[u] = have[u] ? rq : 0;
+      head[u] = h * G + (have[u] ? qr - rq * G : 0);
       const float4* qp = reinterpret_cast<const float4*>(a.q + ((size_t)(V.row0 + r[u]) * a.nq + head[u]) * DH + g * 8);
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
@@ -2152,7 +2166,7 @@ __global__ __launch_bounds__(256) void k_attn_rows2(AttnArgs a) {
       ns_row[u] = attn_ns(ctx[u]);
       if (qt0 + u < n_qt && qbase < n_qr) {
         int r0, r1;
-        attn_tile_rows(qbase, G, V.m, r0, r1);
+        attn_tile_rows(qbase, G, a.g_magic, V.m, r0, r1);
         rlo = min(rlo, r0);
         rhi = max(rhi, r1);
       }
@@ -2301,7 +2315,13 @@ hipError_t launch_attention(const AttnArgs& a_in, hipStream_t st) {
   a.final_fold = a.n_split <= kAttnFoldSplits ? 1 : 0;
   a.spw = a.final_fold ? a.n_split : 1;
   a.wpb = a.final_fold ? 8 : 1;
-  const int n_wg = n_qt * ((a.n_split + a.spw - 1) / a.spw);
+  a.G = G;
+  a.n_qt = n_qt;
+  a.n_sg = (a.n_split + a.spw - 1) / a.spw;
+  a.g_magic = div_magic(G);
+  a.qt_magic = div_magic(n_qt);
+  a.sg_magic = div_magic(a.n_sg);
+  const int n_wg = n_qt * a.n_sg;
   const dim3 grid(n_wg, a.nkv), block(64 * a.wpb);
   if (a.dh == 128) {
     if (a.final_fold) hipLaunchKernelGGL((k_attn_mfma<128, true>), grid, block, 0, st, a);
@@ -2317,9 +2337,16 @@ hipError_t launch_attention(const AttnArgs& a_in, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_attention_rows(const AttnArgs& a, hipStream_t st) {
-  if (a.M < 1 || a.n_lpages < 1 || a.nkv < 1 || a.nq % a.nkv) return hipErrorInvalidValue;
+hipError_t launch_attention_rows(const AttnArgs& a_in, hipStream_t st) {
+  if (a_in.M < 1 || a_in.n_lpages < 1 || a_in.nkv < 1 || a_in.nq % a_in.nkv) return hipErrorInvalidValue;
+  AttnArgs a = a_in;
   const int n_qt = a.seqs != nullptr ? a.n_tiles : (a.M * (a.nq / a.nkv) + 15) / 16;
+  a.G = a.nq / a.nkv;
+  a.n_qt = n_qt;
+  a.n_sg = 1;
+  a.g_magic = div_magic(a.G);
+  a.qt_magic = div_magic(n_qt);
+  a.sg_magic = 0u;
   // two q tiles per wave where the tiles share one sequence
   const int tpw = a.seqs == nullptr ? 2 : 1;
   const dim3 grid(((n_qt + 4 * tpw - 1) / (4 * tpw)) * a.nkv), block(256);
