@@ -129,8 +129,10 @@ int attn_splits(int ctx);
 // rows attend to kv_len + 1 .. kv_len + M positions).
 int attn_splits_max(int kv_len, int M);
 // Embedding rows of the forward's ids; also clears the M row-argmax keys.
-hipError_t launch_embed(const int* params, int M, const void* embed, int vocab, int d, float* x, float* ss,
-                        const uint16_t* g0, uint16_t* uhi, uint16_t* ulo, unsigned long long* best,
+// hparams: the forward's [kv_len, M, ids] in pinned host memory (device
+// address); params: their device copy, which k_embed writes for the later kernels
+hipError_t launch_embed(const int* hparams, int* params, int M, const void* embed, int vocab, int d, float* x,
+                        float* ss, const uint16_t* g0, uint16_t* uhi, uint16_t* ulo, unsigned long long* best,
                         hipStream_t st);
 hipError_t launch_accept(const int* params, int M, int verify, const unsigned long long* best, int* result,
                          hipStream_t st);

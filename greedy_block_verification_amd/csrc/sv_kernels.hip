@@ -2368,16 +2368,24 @@ hipError_t launch_attention_rows(const AttnArgs& a_in, hipStream_t st) {
 // the planes of x * g_attn of layer 0.
 // One thread per (row, feature): x = E[id] (exact bf16 -> fp32), the row's
 // per-16-column sums of squares (16 consecutive lanes), planes of x * g0.
-// Block (r, 0) also clears row r's argmax key for the LM head.
-__global__ __launch_bounds__(256) void k_embed(const int* __restrict__ params, const uint16_t* __restrict__ E, int d,
-                                               float* __restrict__ x, float* __restrict__ ss,
-                                               const uint16_t* __restrict__ g0, uint16_t* __restrict__ uhi,
-                                               uint16_t* __restrict__ ulo, unsigned long long* __restrict__ best) {
+// Block (r, 0) also clears row r's argmax key for the LM head.  The forward's
+// parameters [kv_len, M, ids] come straight from the caller's pinned host
+// buffer (hparams, read over the bus); block (r, 0) stores id r, and block
+// (0, 0) kv_len and M, into the device copy (params) the later kernels read.
+__global__ __launch_bounds__(256) void k_embed(const int* __restrict__ hparams, int* __restrict__ params,
+                                               const uint16_t* __restrict__ E, int d, float* __restrict__ x,
+                                               float* __restrict__ ss, const uint16_t* __restrict__ g0,
+                                               uint16_t* __restrict__ uhi, uint16_t* __restrict__ ulo,
+                                               unsigned long long* __restrict__ best) {
   const int r = blockIdx.y;
   const int k = blockIdx.x * 256 + threadIdx.x;
-  if (blockIdx.x == 0 && threadIdx.x == 0) best[r] = 0ull;
+  const int id = hparams[2 + r];
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    best[r] = 0ull;
+    params[2 + r] = id;
+    if (r == 0) { params[0] = hparams[0]; params[1] = hparams[1]; }
+  }
   if (k >= d) return;   // d is a multiple of 16, so whole 16-lane groups exit together
-  const int id = params[2 + r];
   // the embedding is packed like a bf16 weight matrix: 16-row tiles of 32-input chunks
   const size_t off = ((size_t)(id >> 4) * (d >> 5) + (k >> 5)) * 512 + (size_t)(((k & 31) >> 3) * 16 + (id & 15)) * 8 + (k & 7);
   const float v = bf2f(E[off]);
@@ -2389,11 +2397,12 @@ __global__ __launch_bounds__(256) void k_embed(const int* __restrict__ params, c
   split1(v * bf2f(g0[k]), uhi[(size_t)r * d + k], ulo[(size_t)r * d + k]);
 }
 
-hipError_t launch_embed(const int* params, int M, const void* embed, int vocab, int d, float* x, float* ss,
-                        const uint16_t* g0, uint16_t* uhi, uint16_t* ulo, unsigned long long* best, hipStream_t st) {
+hipError_t launch_embed(const int* hparams, int* params, int M, const void* embed, int vocab, int d, float* x,
+                        float* ss, const uint16_t* g0, uint16_t* uhi, uint16_t* ulo, unsigned long long* best,
+                        hipStream_t st) {
   (void)vocab;
-  hipLaunchKernelGGL(k_embed, dim3((d + 255) / 256, M), dim3(256), 0, st, params, (const uint16_t*)embed, d, x, ss, g0,
-                     uhi, ulo, best);
+  hipLaunchKernelGGL(k_embed, dim3((d + 255) / 256, M), dim3(256), 0, st, hparams, params, (const uint16_t*)embed, d,
+                     x, ss, g0, uhi, ulo, best);
   return hipGetLastError();
 }
 

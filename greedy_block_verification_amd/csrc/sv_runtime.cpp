@@ -30,7 +30,7 @@ struct Layout {
   size_t batch = 0, batch_bytes = 0;   // batched-forward tables: rowseq [rows], seqs [kMaxBatch], tiles
   size_t topk = 0, sel = 0;   // audit mode: top-k scratch keys and results, selected-logit ids and values
   size_t params = 0, x = 0, ss = 0, q = 0, attn_part = 0, uplanes = 0, oplanes = 0, aplanes = 0, best = 0,
-         result = 0, logits = 0, rope = 0, prof = 0, total = 0;
+         logits = 0, rope = 0, prof = 0, total = 0;
   int max_split = 1;
 };
 
@@ -145,7 +145,6 @@ Layout make_layout(const sv_config& c, const Plans& p) {
   L.oplanes = take(2 * R * qd * 2);          // attention output
   L.aplanes = take(2 * R * c.d_ff * 2);      // act(gate) * up
   L.best = take(R * 8);
-  L.result = take(sizeof(int) * (2 + R + 2 * kMaxBatch));
   L.logits = take(R * (size_t)c.vocab * 4);
   L.rope = take((size_t)c.max_ctx * (c.head_dim / 2) * 8);
   L.prof = take(prof_pairs(c) * 16);
@@ -170,8 +169,10 @@ struct sv_ctx {
   Plans plans;
   Layout lay;
   char* ws = nullptr;
-  int* h_params = nullptr;   // pinned
-  int* h_result = nullptr;   // pinned
+  int* h_params = nullptr;   // pinned, coherent: k_embed reads it over the bus (device address hd_params)
+  int* h_result = nullptr;   // pinned, coherent: k_accept writes it over the bus (device address hd_result)
+  int* hd_params = nullptr;
+  int* hd_result = nullptr;
   char* h_batch = nullptr;   // pinned staging of the batched-forward tables
   unsigned long long* h_prof = nullptr;   // pinned copy of the profiling slots
   int kv_len = 0;
@@ -254,7 +255,7 @@ hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, int logits
   const bool tiled = M > kMaxRows;
   const int R = c->lay.rows;
   const int qd = cfg.n_q_heads * cfg.head_dim;
-  const int* d_params = c->at<int>(c->lay.params);
+  int* d_params = c->at<int>(c->lay.params);
   float* x = c->at<float>(c->lay.x);
   float* ss = c->at<float>(c->lay.ss);
   float* q = c->at<float>(c->lay.q);
@@ -272,8 +273,8 @@ hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, int logits
                                hipSuccess)
     return e;
   unsigned long long* best = c->at<unsigned long long>(c->lay.best);
-  e = launch_embed(d_params, M, c->w.embed, cfg.vocab, cfg.d_model, x, ss, gain(c->layers[0].g_attn), uhi, ulo, best,
-                   st);
+  e = launch_embed(c->hd_params, d_params, M, c->w.embed, cfg.vocab, cfg.d_model, x, ss, gain(c->layers[0].g_attn), uhi,
+                   ulo, best, st);
   if (e != hipSuccess) return e;
 
   GemmArgs g{};
@@ -333,23 +334,23 @@ hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, int logits
   g.best = best;
   g.logits = logits ? c->at<float>(c->lay.logits) : nullptr;
   if ((e = gemm_timed(c, g, kRoleLmHead, c->plans.lm.grid, st, tiled)) != hipSuccess) return e;
-  if (bd.seqs != nullptr) return launch_accept_batch(d_params, M, bd.seqs, bd.n_seq, best, c->at<int>(c->lay.result), st);
-  return launch_accept(d_params, M, verify, best, c->at<int>(c->lay.result), st);
+  if (bd.seqs != nullptr) return launch_accept_batch(d_params, M, bd.seqs, bd.n_seq, best, c->hd_result, st);
+  return launch_accept(d_params, M, verify, best, c->hd_result, st);
 }
 
-// One forward of M rows on c's stream: params (and, for a batched forward of
-// n_seq > 0 sequences, the tables the caller staged in h_batch) go up, the
-// kernels run (a cached HIP graph for up to 64 rows), the result
-// [n, next, a_0 .. a_{M-1}, (n_s, next_s) per sequence] and the profiling
-// slots come back.  kv_len: the params' length (one sequence).
+// One forward of M rows on c's stream: the params go into the pinned buffer
+// the first kernel reads (and, for a batched forward of n_seq > 0 sequences,
+// the tables the caller staged in h_batch go up), the kernels run (a cached
+// HIP graph for up to 64 rows) and write the result [n, next, a_0 .. a_{M-1},
+// (n_s, next_s) per sequence] into pinned memory, and the profiling slots
+// come back.  No copy kernel runs for the params or the result.  kv_len: the
+// params' length (one sequence).  The buffers are rewritten only after the
+// previous forward's synchronisation, so no forward reads another's params.
 sv_status run_forward(sv_ctx* c, int M, const int* ids, int verify, int n_split, int n_seq, int n_tiles, int logits) {
   hipStream_t st = c->stream;
-  int* d_params = c->at<int>(c->lay.params);
   c->h_params[0] = c->kv_len;
   c->h_params[1] = M;
   std::memcpy(c->h_params + 2, ids, sizeof(int) * M);
-  if (hipMemcpyAsync(d_params, c->h_params, sizeof(int) * (2 + M), hipMemcpyHostToDevice, st) != hipSuccess)
-    return SV_EDEVICE;
   if (n_seq > 0 && hipMemcpyAsync(c->at<char>(c->lay.batch), c->h_batch, c->lay.batch_bytes, hipMemcpyHostToDevice,
                                   st) != hipSuccess)
     return SV_EDEVICE;
@@ -374,10 +375,6 @@ sv_status run_forward(sv_ctx* c, int M, const int* ids, int verify, int n_split,
   } else {
     if (enqueue_forward(c, M, verify, n_split, logits, bd, st) != hipSuccess) return SV_EDEVICE;
   }
-  int* d_result = c->at<int>(c->lay.result);
-  if (hipMemcpyAsync(c->h_result, d_result, sizeof(int) * (2 + M + 2 * n_seq), hipMemcpyDeviceToHost, st) !=
-      hipSuccess)
-    return SV_EDEVICE;
   if (c->prof_mask != 0 && hipMemcpyAsync(c->h_prof, c->at<unsigned long long>(c->lay.prof),
                                           16 * (size_t)prof_pairs(c->cfg), hipMemcpyDeviceToHost, st) != hipSuccess)
     return SV_EDEVICE;
@@ -504,9 +501,11 @@ sv_status sv_create(const sv_config* cfg, const sv_weights* w, const sv_buffers*
   c->ws = static_cast<char*>(buf->workspace);
   c->hist.assign(cfg->max_ctx, -1);
   c->last_argmax.assign(lay.rows, 0);
-  if (hipHostMalloc((void**)&c->h_params, sizeof(int) * (2 + lay.rows), hipHostMallocDefault) != hipSuccess ||
-      hipHostMalloc((void**)&c->h_result, sizeof(int) * (2 + lay.rows + 2 * kMaxBatch), hipHostMallocDefault) !=
-          hipSuccess ||
+  const unsigned mapped = hipHostMallocMapped | hipHostMallocCoherent;
+  if (hipHostMalloc((void**)&c->h_params, sizeof(int) * (2 + lay.rows), mapped) != hipSuccess ||
+      hipHostMalloc((void**)&c->h_result, sizeof(int) * (2 + lay.rows + 2 * kMaxBatch), mapped) != hipSuccess ||
+      hipHostGetDevicePointer((void**)&c->hd_params, c->h_params, 0) != hipSuccess ||
+      hipHostGetDevicePointer((void**)&c->hd_result, c->h_result, 0) != hipSuccess ||
       hipHostMalloc((void**)&c->h_batch, lay.batch_bytes, hipHostMallocDefault) != hipSuccess ||
       hipHostMalloc((void**)&c->h_prof, 16 * (size_t)prof_pairs(*cfg), hipHostMallocDefault) != hipSuccess) {
     sv_destroy(c);
