@@ -125,7 +125,11 @@ sv_status sv_pack_linear(int32_t fmt, int32_t layout, const void *src0, const vo
 
 /* Create a context at kv_len = 0.  Validates cfg and buffer sizes, uploads the
  * RoPE table (angle pos * theta^(-2i/head_dim), cos/sin evaluated in double and
- * rounded once to float) into the workspace.  `stream` is a hipStream_t. */
+ * rounded once to float) into the workspace.  `stream` is a hipStream_t.  The
+ * context owns a few small pinned, device-mapped host buffers (the forward's
+ * params, which its first kernel reads over the bus, and the result its last
+ * kernel writes there), freed by sv_destroy.  Errors: SV_EINVAL (bad cfg or
+ * buffer sizes), SV_EUNSUPPORTED, SV_EDEVICE (a HIP allocation or copy). */
 sv_status sv_create(const sv_config *cfg, const sv_weights *w, const sv_buffers *buf,
                     void *stream, sv_ctx **out);
 void sv_destroy(sv_ctx *ctx);
