@@ -8,7 +8,11 @@ bits -- whatever else the batch holds and in whatever order:
 * tiny: 6 sequences of different lengths, window sizes 0..8 and draft
   patterns, against one-at-a-time verifies; the same batch reversed and
   regrouped; a batch of 9 sequences (81 rows) through the row-tiled kernels;
-  argument errors that leave every context untouched;
+  argument errors that leave every context untouched; in both batches every
+  row's logits also against the fp64 oracle's cacheless recompute of its
+  own sequence (|dlogit| <= 3e-2, argmax equal away from flagged near ties),
+  the equality with the plain greedy computation that "Phase 23:
+  Speculative Verify Parity", section 3, reports as matched;
 * 8B shape: 8 sequences x K = 4 (40 rows) against one-at-a-time verifies;
 * Gemma-style int4 layers (GeGLU, 6 q heads per KV head): 4 sequences,
   19 rows, against one-at-a-time verifies;
@@ -108,6 +112,29 @@ def _check(s, got, ref, m):
     np.testing.assert_array_equal(s.kv_positions(ref["kv_len"], ref["kv_len"] - ref["n"] - 1), ref["kv"])
 
 
+def _check_oracle(w, cfg, ss, lens, drafts, seed, label):
+    """Teacher-forced: row r of sequence i scores prompt_i + next_i +
+    drafts_i[:r] in the fp64 oracle (forward_cacheless of that sequence)."""
+    from oracle import Fp64Model, forward_cacheless
+    from oracle.spec import greedy_id, top2_margin
+    tol = 3e-2
+    m = Fp64Model(w)
+    worst, flips, rows = 0.0, 0, 0
+    for i, (s, n, d) in enumerate(zip(ss, lens, drafts)):
+        hist = s.history(n)
+        seq = _ids(n, i, cfg.vocab, seed) + [hist[n - 1]] + list(d)
+        ref = forward_cacheless(m, seq, positions=np.arange(n, n + len(d) + 1))
+        for r in range(len(d) + 1):
+            lg = s.logits(r).astype(np.float64)
+            worst = max(worst, float(np.max(np.abs(lg - ref[r]))))
+            if int(np.argmax(lg)) != greedy_id(ref[r]):
+                assert top2_margin(ref[r]) < tol, f"{label}: sequence {i} row {r} flips away from a near tie"
+                flips += 1
+            rows += 1
+    print(f"{label}: {rows} batched rows vs the oracle, max|dlogit| {worst:.3e}, flagged flips {flips}")
+    assert worst <= tol
+
+
 def _run_batch(ss, snaps, drafts):
     from greedy_block_verification_amd import binding as B
     for s, snap in zip(ss, snaps):
@@ -125,6 +152,7 @@ def test_batch_equals_one_at_a_time(tiny):
     got = _run_batch(ss, snaps, drafts)
     for s, g, ref, k in zip(ss, got, refs, ks):
         _check(s, g, ref, k + 1)
+    _check_oracle(w, cfg, ss, lens, drafts, 21, "tiny batch of 6")
     # reversed, and regrouped into two batches: the same bits
     order = list(reversed(range(len(ss))))
     got = _run_batch([ss[i] for i in order], [snaps[i] for i in order], [drafts[i] for i in order])
@@ -150,6 +178,7 @@ def test_batch_through_row_tiled_kernels(tiny):
     got = _run_batch(ss, snaps, drafts)
     for s, g, ref in zip(ss, got, refs):
         _check(s, g, ref, 9)
+    _check_oracle(w, cfg, ss, lens, drafts, 22, "tiny row-tiled batch of 9")
     for s in ss:
         s.close()
 

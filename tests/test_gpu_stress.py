@@ -7,9 +7,11 @@ GPU-vs-GPU properties that hold at any size:
 * verify == one-token decode bit for bit for K in {1, 2, 4, 8, 16, 32};
 * rollback after a reject at every index 0..K-1 (K = 32), then a re-verify,
   equals the state built by one-token commits (logits and KV bits);
-* planted near-ties in the LM head (a row copied exactly, and a row one
-  bf16 ulp away) resolve identically in verify and decode, and an exact tie
-  goes to the lower id;
+* planted near-ties in the LM head (a row copied exactly, and rows one bf16
+  ulp away at the largest and the smallest |h_j| of the final hidden vector,
+  below and above the argmax id) resolve identically in verify and decode,
+  every other logit keeps its bits, and the lowest id wins among equal
+  maxima;
 * rows straddling a change of the attention split plan, and a 32640-id
   prompt prefilled through the row-tiled kernels, verify == decode bitwise.
 """
@@ -163,42 +165,110 @@ def test_stress_rollback_at_every_index(stress):
         chk.close()
 
 
-def test_stress_planted_near_ties(stress):
-    from greedy_block_verification_amd.session import DeviceModel, Session
+def _planted_model(dev, w, rows):
+    """A device model sharing dev's layer weights whose tied embedding / LM
+    head has the given rows replaced ({id: bf16 row bits})."""
+    from greedy_block_verification_amd.session import DeviceModel
     from seeded_inputs.weights import ModelWeights
-    dev, w, cfg, snap = stress
-    rng = np.random.default_rng(77)
-    drafts = rng.integers(1000, cfg.vocab, 4).tolist()
-    base = _sess(dev, cfg, snap)
-    base.verify(drafts)
-    a = base.last_argmax()[0]
-    base.close()
-    # plant: c = an exact copy of LM-head row a with c < a (exact tie -> lower id),
-    #        b = row a with one element moved by one bf16 ulp (a 1-ulp near-tie)
-    c = a - 1 if a > 0 else a + 1
-    b = a - 2 if a > 1 else a + 2
     emb = w.embed.copy()
-    emb[c] = emb[a]
-    emb[b] = emb[a]
-    emb[b, 0] = np.uint16(int(emb[a, 0]) + 1)
-    planted = DeviceModel(ModelWeights(w.cfg, emb, w.g_final, w.layers), share_layers_with=dev)
-    p1, p2 = _sess(planted, cfg, snap), _sess(planted, cfg, snap)
-    rows = [p1.next_id] + drafts
+    for i, r in rows.items():
+        emb[i] = r
+    return DeviceModel(ModelWeights(w.cfg, emb, w.g_final, w.layers), share_layers_with=dev)
+
+
+def _rows_and_logits(model, cfg, snap, drafts):
+    """(verify logits and argmax, one-token decode logits and argmax) of the window."""
+    p1, p2 = _sess(model, cfg, snap), _sess(model, cfg, snap)
     dec = []
-    for t in rows:
+    for t in [p1.next_id] + drafts:
         p1.decode_step(t)
         dec.append((p1.last_argmax()[0], p1.logits(0)))
     p2.verify(drafts)
-    for r in range(5):
-        np.testing.assert_array_equal(_bits(p2.logits(r)), _bits(dec[r][1]))
-        assert p2.last_argmax()[r] == dec[r][0]
-    lg = p2.logits(0)
-    assert lg[c] == lg[a]                       # exact copy -> exactly equal logits
-    win = p2.last_argmax()[0]
-    top = lg.max()
-    assert lg[win] == top and win == int(np.flatnonzero(lg == top)[0])   # lowest id among the maxima
-    if lg[a] == top:
-        assert win == min(a, c, b if lg[b] == top else a)
-    print(f"planted: a={a} c={c} b={b}; logits a {lg[a]!r} c {lg[c]!r} b {lg[b]!r}; argmax {win}")
+    ver = [(p2.last_argmax()[r], p2.logits(r)) for r in range(len(drafts) + 1)]
     p1.close()
     p2.close()
+    return ver, dec
+
+
+def test_stress_planted_near_ties(stress):
+    """Near ties planted in the LM head as the measurement plan describes:
+    with a the unplanted argmax of row 0, row c is an exact copy of row a,
+    and rows b1..b4 are row a with one element moved by one bf16 ulp -- at
+    the largest |h_j| of the row's final normalised hidden vector (a gap
+    fp32 resolves) and at the smallest (a gap at fp32 rounding level), each
+    once with b below a and once above it.  No planted id is among the
+    window's ids (the head is tied, so planting also changes those ids'
+    embeddings).  h is read through a probe head whose rows 'base + j' are
+    the unit vectors e_j, so that logit = h_j.  Checked unconditionally:
+    verify == decode bits and argmax on every row; every logit of an
+    unplanted id equals the unplanted model's bit for bit; c ties a
+    exactly; the winner of row 0 is the lowest id among its maxima and is
+    one of a, c, b1..b4; at the largest |h_j| each gap has the sign of
+    (row change) x h_j."""
+    from seeded_inputs.weights import f32_from_bf16_bits
+    dev, w, cfg, snap = stress
+    rng = np.random.default_rng(77)
+    drafts = rng.integers(1000, 90000, 4).tolist()
+    base = _sess(dev, cfg, snap)
+    rows = [base.next_id] + drafts
+    base.verify(drafts)
+    a = base.last_argmax()[0]
+    lg0 = base.logits(0)
+    base.close()
+    d = cfg.d_model
+    # probe: unit rows at ids [pb, pb + d), away from the window's ids and from a
+    pb = next(x for x in (100000, 110000, 120000, 130000, 140000)
+              if all(not x <= t < x + d for t in rows + [a]))
+    unit = {pb + j: np.zeros(d, dtype=np.uint16) for j in range(d)}
+    for j in range(d):
+        unit[pb + j][j] = 0x3F80                       # bf16 1.0
+    probe = _planted_model(dev, w, unit)
+    pv, _ = _rows_and_logits(probe, cfg, snap, drafts)
+    del probe
+    h = pv[0][1][pb:pb + d].astype(np.float64)         # row 0's final hidden vector, h_j = logit of e_j
+    ea = w.embed[a]
+    ea_f = f32_from_bf16_bits(ea).astype(np.float64)
+    # largest |h_j| where row a's element is at least 2^-7 in magnitude (one
+    # bf16 ulp there is at least 2^-14, so the gap clears fp32 rounding of
+    # the logit); smallest |h_j| anywhere
+    big_ok = np.abs(ea_f) >= 2.0 ** -7
+    j_big = int(np.argmax(np.where(big_ok, np.abs(h), -1.0)))
+    j_small = int(np.argmin(np.abs(h)))
+    # plant: ids around a (two below, three above; none among the window's ids)
+    taken = set(rows)
+    below = [x for x in range(a - 1, -1, -1) if x not in taken][:2]
+    above = [x for x in range(a + 1, cfg.vocab) if x not in taken][:3]
+    assert len(below) == 2 and len(above) == 3, "a sits too close to an end of the vocabulary"
+    c = above[2]
+    plan = {below[0]: j_big, above[0]: j_big, below[1]: j_small, above[1]: j_small}
+    planted_rows = {c: ea.copy()}
+    for b, j in plan.items():
+        r = ea.copy()
+        r[j] = np.uint16(int(ea[j]) + 1)               # one ulp further from zero
+        planted_rows[b] = r
+    assert not set(planted_rows) & set(rows)
+    model = _planted_model(dev, w, planted_rows)
+    ver, dec = _rows_and_logits(model, cfg, snap, drafts)
+    for r in range(5):
+        np.testing.assert_array_equal(_bits(ver[r][1]), _bits(dec[r][1]))
+        assert ver[r][0] == dec[r][0]
+        lg = ver[r][1]
+        top = lg.max()
+        assert ver[r][0] == int(np.flatnonzero(lg == top)[0])   # lowest id among the maxima
+    lg = ver[0][1]
+    others = np.ones(cfg.vocab, dtype=bool)
+    others[list(planted_rows)] = False
+    np.testing.assert_array_equal(_bits(lg[others]), _bits(lg0[others]))
+    assert _bits(lg[c]) == _bits(lg[a])
+    top = lg.max()
+    cands = [a, c] + list(plan)
+    assert lg[a] == lg0[a] and top == max(lg[x] for x in cands)
+    assert ver[0][0] == min(x for x in cands if lg[x] == top)
+    # the direction of each resolvable gap: row change (one ulp away from zero) times h_j
+    for b in (below[0], above[0]):
+        delta = float(f32_from_bf16_bits(planted_rows[b][j_big:j_big + 1])[0]) - float(ea_f[j_big])
+        gap = float(lg[b]) - float(lg[a])
+        assert gap != 0.0 and np.sign(gap) == np.sign(delta * h[j_big])
+    print(f"planted: a={a} c={c} |h| max {abs(h[j_big]):.3g} at {j_big}, min {abs(h[j_small]):.3g} at {j_small}; "
+          + ", ".join(f"b={b} (j={j}) gap {float(lg[b]) - float(lg[a]):.3g}" for b, j in plan.items())
+          + f"; row-0 argmax {ver[0][0]}")
