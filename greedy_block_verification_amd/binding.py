@@ -13,7 +13,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsv.so")
 
-SV_OK, SV_EINVAL, SV_ESTATE, SV_ENOSPACE, SV_EDEVICE, SV_EUNSUPPORTED = 0, -1, -2, -3, -4, -5
+SV_OK, SV_EINVAL, SV_ESTATE, SV_ENOSPACE, SV_EDEVICE, SV_EUNSUPPORTED, SV_ESCRATCH = 0, -1, -2, -3, -4, -5, -6
 
 
 class SvError(RuntimeError):
@@ -61,6 +61,8 @@ SIGNATURES = {
     "sv_decode_step": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_int32)]),
     "sv_verify": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_int32), C.c_int32, C.POINTER(C.c_int32),
                             C.POINTER(C.c_int32)]),
+    "sv_verify_noalloc": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_int32), C.c_int32, C.POINTER(C.c_int32),
+                                    C.POINTER(C.c_int32)]),
     "sv_verify_batch": (C.c_int, [C.POINTER(C.c_void_p), C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
                                   C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
     "sv_kv_truncate": (C.c_int, [C.c_void_p, C.c_int32]),
@@ -163,6 +165,13 @@ def sv_verify(ctx, prefix_len: int, draft_ids):
     n, nx = C.c_int32(), C.c_int32()
     _check(lib().sv_verify(ctx, int(prefix_len), _i32_array(draft_ids), len(draft_ids), C.byref(n), C.byref(nx)),
            "sv_verify")
+    return n.value, nx.value
+
+
+def sv_verify_noalloc(ctx, prefix_len: int, draft_ids):
+    n, nx = C.c_int32(), C.c_int32()
+    _check(lib().sv_verify_noalloc(ctx, int(prefix_len), _i32_array(draft_ids), len(draft_ids), C.byref(n),
+                                   C.byref(nx)), "sv_verify_noalloc")
     return n.value, nx.value
 
 

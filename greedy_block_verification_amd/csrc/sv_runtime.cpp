@@ -9,6 +9,7 @@
 #include <map>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -160,6 +161,35 @@ size_t kv_pool_bytes_for(const sv_config& c, int n_pages) {
 
 }  // namespace
 
+// Intermediates of sv_verify_noalloc: one array per GPU, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not
+// device memory: its device address on each GPU comes from
+// hipGetSymbolAddress (scratch_address below), and only that address is
+// ever handed to a kernel.  Every sv_verify_noalloc call on a GPU uses that
+// GPU's one copy, so calls that overlap in time on one GPU race.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of `scratch` on GPU `dev`, which must be the current
+// device; looked up once per device and kept.
+sv_status scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return SV_EDEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SV_EDEVICE;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return SV_OK;
+}
+}  // namespace
+
 struct sv_ctx {
   sv_config cfg{};
   sv_weights w{};
@@ -173,6 +203,7 @@ struct sv_ctx {
   int* h_result = nullptr;   // pinned, coherent: k_accept writes it over the bus (device address hd_result)
   int* hd_params = nullptr;
   int* hd_result = nullptr;
+  void* scratch = nullptr;   // device address of this GPU's copy of `scratch` (sv_verify_noalloc)
   char* h_batch = nullptr;   // pinned staging of the batched-forward tables
   unsigned long long* h_prof = nullptr;   // pinned copy of the profiling slots
   int kv_len = 0;
@@ -200,10 +231,79 @@ struct sv_ctx {
 
 namespace {
 
+// Device buffers one forward computes in: the per-forward intermediates
+// (params copy, residual, sums of squares, q, attention partials, activation
+// planes, row argmax keys), the optional logits output, the profiling slots
+// and the RoPE table.  R is the row stride of the plane buffers (lo plane =
+// hi plane + R rows).
+struct FwdBufs {
+  int R = 0;
+  int* params = nullptr;
+  float *x = nullptr, *ss = nullptr, *q = nullptr, *part = nullptr, *logits = nullptr;
+  int part_splits = 0;
+  uint16_t *uplanes = nullptr, *oplanes = nullptr, *aplanes = nullptr;
+  unsigned long long *best = nullptr, *prof = nullptr;
+  const float2* rope = nullptr;
+};
+
+// The context's workspace (every forward of sv_prefill, sv_decode_step,
+// sv_verify and sv_verify_batch).
+FwdBufs ws_bufs(sv_ctx* c) {
+  FwdBufs b;
+  b.R = c->lay.rows;
+  b.params = c->at<int>(c->lay.params);
+  b.x = c->at<float>(c->lay.x);
+  b.ss = c->at<float>(c->lay.ss);
+  b.q = c->at<float>(c->lay.q);
+  b.part = c->at<float>(c->lay.attn_part);
+  b.part_splits = c->lay.max_split;
+  b.uplanes = c->at<uint16_t>(c->lay.uplanes);
+  b.oplanes = c->at<uint16_t>(c->lay.oplanes);
+  b.aplanes = c->at<uint16_t>(c->lay.aplanes);
+  b.best = c->at<unsigned long long>(c->lay.best);
+  b.logits = c->at<float>(c->lay.logits);
+  b.prof = c->at<unsigned long long>(c->lay.prof);
+  b.rope = c->at<const float2>(c->lay.rope);
+  return b;
+}
+
+// sv_verify_noalloc: the per-forward intermediates of M rows whose attention
+// runs n_split splits, carved from `base` (this GPU's scratch address; null
+// only sizes them); the observer logits (an output) and the RoPE table (an
+// input built by sv_create) stay in the context's workspace, and nothing is
+// profiled.  Returns the bytes the intermediates take.
+size_t scratch_bufs(sv_ctx* c, char* base, int M, int n_split, FwdBufs* out) {
+  const sv_config& cfg = c->cfg;
+  const size_t qd = (size_t)cfg.n_q_heads * cfg.head_dim;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base == nullptr ? nullptr : base + off;
+    off = align_up(off + bytes, 256);
+    return p;
+  };
+  FwdBufs b;
+  b.R = M;
+  b.params = reinterpret_cast<int*>(take(sizeof(int) * (2 + (size_t)M)));
+  b.x = reinterpret_cast<float*>(take((size_t)M * cfg.d_model * 4));
+  b.ss = reinterpret_cast<float*>(take((size_t)M * (cfg.d_model / 16) * 4));
+  b.q = reinterpret_cast<float*>(take((size_t)M * qd * 4));
+  b.part_splits = std::max(n_split, 1);
+  b.part = reinterpret_cast<float*>(take((size_t)M * cfg.n_q_heads * b.part_splits * (cfg.head_dim + 4) * 4));
+  b.uplanes = reinterpret_cast<uint16_t*>(take(2 * (size_t)M * cfg.d_model * 2));
+  b.oplanes = reinterpret_cast<uint16_t*>(take(2 * (size_t)M * qd * 2));
+  b.aplanes = reinterpret_cast<uint16_t*>(take(2 * (size_t)M * cfg.d_ff * 2));
+  b.best = reinterpret_cast<unsigned long long*>(take((size_t)M * 8));
+  b.logits = c->at<float>(c->lay.logits);
+  b.prof = nullptr;
+  b.rope = c->at<const float2>(c->lay.rope);
+  if (out) *out = b;
+  return off;
+}
+
 // Profiling slot of (role, layer) when that role is enabled, else null.
-unsigned long long* prof_slot(sv_ctx* c, int role, int layer) {
-  if (!(c->prof_mask & (1 << role))) return nullptr;
-  return c->at<unsigned long long>(c->lay.prof) + 2 * ((size_t)role * c->cfg.n_layers + layer);
+unsigned long long* prof_slot(sv_ctx* c, const FwdBufs& fb, int role, int layer) {
+  if (fb.prof == nullptr || !(c->prof_mask & (1 << role))) return nullptr;
+  return fb.prof + 2 * ((size_t)role * c->cfg.n_layers + layer);
 }
 
 // Add the spans of the last forward's timed launches (slots copied to host).
@@ -222,8 +322,8 @@ void prof_accumulate(sv_ctx* c) {
 
 // tiled: forwards of more than 64 rows run the row-tiled kernels (the same
 // per-row arithmetic as the weight-streaming ones).
-hipError_t gemm_timed(sv_ctx* c, GemmArgs& g, int role, int grid, hipStream_t st, bool tiled) {
-  g.prof = prof_slot(c, role, g.layer);
+hipError_t gemm_timed(sv_ctx* c, const FwdBufs& fb, GemmArgs& g, int role, int grid, hipStream_t st, bool tiled) {
+  g.prof = prof_slot(c, fb, role, g.layer);
   const hipError_t e = tiled ? launch_gemm_tiled(g, role, st) : launch_gemm(g, role, grid, st);
   g.prof = nullptr;
   return e;
@@ -250,29 +350,30 @@ BatchDev batch_dev(sv_ctx* c, int n_seq, int n_tiles) {
   return b;
 }
 
-hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, int logits, const BatchDev& bd, hipStream_t st) {
+hipError_t enqueue_forward(sv_ctx* c, const FwdBufs& fb, int M, int verify, int n_split, int logits,
+                           const BatchDev& bd, hipStream_t st) {
   const sv_config& cfg = c->cfg;
   const bool tiled = M > kMaxRows;
-  const int R = c->lay.rows;
+  const int R = fb.R;
   const int qd = cfg.n_q_heads * cfg.head_dim;
-  int* d_params = c->at<int>(c->lay.params);
-  float* x = c->at<float>(c->lay.x);
-  float* ss = c->at<float>(c->lay.ss);
-  float* q = c->at<float>(c->lay.q);
-  uint16_t* uhi = c->at<uint16_t>(c->lay.uplanes);
+  int* d_params = fb.params;
+  float* x = fb.x;
+  float* ss = fb.ss;
+  float* q = fb.q;
+  uint16_t* uhi = fb.uplanes;
   uint16_t* ulo = uhi + (size_t)R * cfg.d_model;
-  uint16_t* ohi = c->at<uint16_t>(c->lay.oplanes);
+  uint16_t* ohi = fb.oplanes;
   uint16_t* olo = ohi + (size_t)R * qd;
-  uint16_t* ahi = c->at<uint16_t>(c->lay.aplanes);
+  uint16_t* ahi = fb.aplanes;
   uint16_t* alo = ahi + (size_t)R * cfg.d_ff;
   uint16_t* kv = static_cast<uint16_t*>(c->buf.kv_pool);
   auto gain = [](const void* p) { return static_cast<const uint16_t*>(p); };
 
   hipError_t e = hipSuccess;
-  if (c->prof_mask != 0 && (e = launch_prof_reset(c->at<unsigned long long>(c->lay.prof), prof_pairs(cfg), st)) !=
-                               hipSuccess)
+  if (c->prof_mask != 0 && fb.prof != nullptr &&
+      (e = launch_prof_reset(fb.prof, prof_pairs(cfg), st)) != hipSuccess)
     return e;
-  unsigned long long* best = c->at<unsigned long long>(c->lay.best);
+  unsigned long long* best = fb.best;
   e = launch_embed(c->hd_params, d_params, M, c->w.embed, cfg.vocab, cfg.d_model, x, ss, gain(c->layers[0].g_attn), uhi,
                    ulo, best, st);
   if (e != hipSuccess) return e;
@@ -296,7 +397,7 @@ hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, int logits
   g.nq = cfg.n_q_heads;
   g.nkv = cfg.n_kv_heads;
   g.dh = cfg.head_dim;
-  g.rope = c->at<const float2>(c->lay.rope);
+  g.rope = fb.rope;
   g.seqs = bd.seqs;
   g.rowseq = bd.rowseq;
   auto plan = [&](const GemmPlan& p, const void* W, const void* Ws, const uint16_t* bhi, const uint16_t* blo) {
@@ -308,32 +409,32 @@ hipError_t enqueue_forward(sv_ctx* c, int M, int verify, int n_split, int logits
     g.layer = l;
     // attention block: (norm) QKV + RoPE + KV append, attention, O + residual
     plan(c->plans.qkv, L.wqkv, L.wqkv_scales, uhi, ulo);
-    if ((e = gemm_timed(c, g, kRoleQkv, c->plans.qkv.grid, st, tiled)) != hipSuccess) return e;
+    if ((e = gemm_timed(c, fb, g, kRoleQkv, c->plans.qkv.grid, st, tiled)) != hipSuccess) return e;
     AttnArgs at{};
     at.params = d_params; at.q = q; at.kv_pool = kv; at.page_table = c->buf.page_table; at.n_pages = c->buf.n_pages;
     at.layer = l; at.nq = cfg.n_q_heads; at.nkv = cfg.n_kv_heads; at.dh = cfg.head_dim; at.M = M;
     at.n_split = n_split; at.n_lpages = cfg.max_ctx / kPage; at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cfg.head_dim));
-    at.part = c->at<float>(c->lay.attn_part); at.part_splits = c->lay.max_split; at.ohi = ohi; at.olo = olo;
-    at.prof = prof_slot(c, kRoleAttn, l);
+    at.part = fb.part; at.part_splits = fb.part_splits; at.ohi = ohi; at.olo = olo;
+    at.prof = prof_slot(c, fb, kRoleAttn, l);
     at.seqs = bd.seqs; at.rowseq = bd.rowseq; at.tiles = bd.tiles; at.n_tiles = bd.n_tiles;
     if ((e = tiled ? launch_attention_rows(at, st) : launch_attention(at, st)) != hipSuccess) return e;
     plan(c->plans.o, L.wo, L.wo_scales, ohi, olo);
     g.gnext = gain(L.g_mlp);
-    if ((e = gemm_timed(c, g, kRoleO, c->plans.o.grid, st, tiled)) != hipSuccess) return e;
+    if ((e = gemm_timed(c, fb, g, kRoleO, c->plans.o.grid, st, tiled)) != hipSuccess) return e;
     // MLP block: (norm) gate/up + activation, down + residual
     plan(c->plans.gu, L.wgu, L.wgu_scales, uhi, ulo);
-    if ((e = gemm_timed(c, g, kRoleGateUp, c->plans.gu.grid, st, tiled)) != hipSuccess) return e;
+    if ((e = gemm_timed(c, fb, g, kRoleGateUp, c->plans.gu.grid, st, tiled)) != hipSuccess) return e;
     plan(c->plans.d, L.wd, L.wd_scales, ahi, alo);
     g.gnext = l + 1 < cfg.n_layers ? gain(c->layers[l + 1].g_attn) : gain(c->w.g_final);
-    if ((e = gemm_timed(c, g, kRoleDown, c->plans.d.grid, st, tiled)) != hipSuccess) return e;
+    if ((e = gemm_timed(c, fb, g, kRoleDown, c->plans.d.grid, st, tiled)) != hipSuccess) return e;
   }
 
   // (final norm) LM head + per-16-column argmax, then acceptance
   plan(c->plans.lm, c->w.lm_head, nullptr, uhi, ulo);
   g.layer = 0;
   g.best = best;
-  g.logits = logits ? c->at<float>(c->lay.logits) : nullptr;
-  if ((e = gemm_timed(c, g, kRoleLmHead, c->plans.lm.grid, st, tiled)) != hipSuccess) return e;
+  g.logits = logits ? fb.logits : nullptr;
+  if ((e = gemm_timed(c, fb, g, kRoleLmHead, c->plans.lm.grid, st, tiled)) != hipSuccess) return e;
   if (bd.seqs != nullptr) return launch_accept_batch(d_params, M, bd.seqs, bd.n_seq, best, c->hd_result, st);
   return launch_accept(d_params, M, verify, best, c->hd_result, st);
 }
@@ -356,6 +457,7 @@ sv_status run_forward(sv_ctx* c, int M, const int* ids, int verify, int n_split,
     return SV_EDEVICE;
   const BatchDev bd = batch_dev(c, n_seq, n_tiles);
 
+  const FwdBufs fb = ws_bufs(c);
   if (c->use_graphs && M <= kMaxRows) {   // forwards of many rows take milliseconds: launched directly
     const std::array<int, 7> key = {M, n_split, verify, logits, c->prof_mask, n_seq, n_tiles};
     auto it = c->graphs.find(key);
@@ -363,7 +465,7 @@ sv_status run_forward(sv_ctx* c, int M, const int* ids, int verify, int n_split,
       hipGraph_t graph = nullptr;
       hipGraphExec_t exec = nullptr;
       if (hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal) != hipSuccess) return SV_EDEVICE;
-      const hipError_t e = enqueue_forward(c, M, verify, n_split, logits, bd, c->cap_stream);
+      const hipError_t e = enqueue_forward(c, fb, M, verify, n_split, logits, bd, c->cap_stream);
       const hipError_t e2 = hipStreamEndCapture(c->cap_stream, &graph);
       hipError_t e3 = hipErrorUnknown;
       if (e == hipSuccess && e2 == hipSuccess && graph != nullptr) e3 = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
@@ -373,7 +475,7 @@ sv_status run_forward(sv_ctx* c, int M, const int* ids, int verify, int n_split,
     }
     if (hipGraphLaunch(it->second, st) != hipSuccess) return SV_EDEVICE;
   } else {
-    if (enqueue_forward(c, M, verify, n_split, logits, bd, st) != hipSuccess) return SV_EDEVICE;
+    if (enqueue_forward(c, fb, M, verify, n_split, logits, bd, st) != hipSuccess) return SV_EDEVICE;
   }
   if (c->prof_mask != 0 && hipMemcpyAsync(c->h_prof, c->at<unsigned long long>(c->lay.prof),
                                           16 * (size_t)prof_pairs(c->cfg), hipMemcpyDeviceToHost, st) != hipSuccess)
@@ -383,8 +485,27 @@ sv_status run_forward(sv_ctx* c, int M, const int* ids, int verify, int n_split,
   return SV_OK;
 }
 
-sv_status forward(sv_ctx* c, int M, const int* ids, int verify) {
-  const sv_status s = run_forward(c, M, ids, verify, attn_splits_max(c->kv_len, M), 0, 0, c->store_logits);
+// sv_verify_noalloc's forward: the same kernels, launched directly (no HIP
+// graph is instantiated) with the intermediates in this GPU's scratch array
+// (the caller has checked that they fit).  The row argmax keys there are
+// cleared by the first kernel; every other intermediate is written before
+// it is read, so nothing a previous call left behind is used.
+sv_status run_forward_noalloc(sv_ctx* c, int M, const int* ids, int n_split, int logits) {
+  hipStream_t st = c->stream;
+  c->h_params[0] = c->kv_len;
+  c->h_params[1] = M;
+  std::memcpy(c->h_params + 2, ids, sizeof(int) * M);
+  FwdBufs fb;
+  scratch_bufs(c, static_cast<char*>(c->scratch), M, n_split, &fb);
+  if (enqueue_forward(c, fb, M, 1, n_split, logits, BatchDev{}, st) != hipSuccess) return SV_EDEVICE;
+  if (hipStreamSynchronize(st) != hipSuccess) return SV_EDEVICE;
+  return SV_OK;
+}
+
+sv_status forward(sv_ctx* c, int M, const int* ids, int verify, bool noalloc = false) {
+  const int n_split = attn_splits_max(c->kv_len, M);
+  const sv_status s = noalloc ? run_forward_noalloc(c, M, ids, n_split, c->store_logits)
+                              : run_forward(c, M, ids, verify, n_split, 0, 0, c->store_logits);
   if (s != SV_OK) return s;
   c->last_rows = M;
   c->last_stored_logits = c->store_logits;
@@ -398,6 +519,33 @@ bool ids_ok(const sv_ctx* c, const int32_t* ids, int n) {
   return true;
 }
 
+sv_status verify_impl(sv_ctx* c, int32_t prefix_len, const int32_t* draft_ids, int32_t k, int32_t* n_accepted,
+                      int32_t* next_id, bool noalloc) {
+  if (!c) return SV_EINVAL;
+  if (k < 0 || k > c->cfg.max_k || (k > 0 && !draft_ids)) return SV_EINVAL;
+  if (prefix_len != c->kv_len || c->next_id < 0) return SV_ESTATE;
+  if (k > 0 && !ids_ok(c, draft_ids, k)) return SV_EINVAL;
+  if ((int64_t)c->kv_len + k + 1 > c->cfg.max_ctx) return SV_ENOSPACE;
+  if (noalloc) {
+    if (c->scratch == nullptr) return SV_EDEVICE;
+    if (scratch_bufs(c, nullptr, k + 1, attn_splits_max(c->kv_len, k + 1), nullptr) > kScratchBytes)
+      return SV_ESCRATCH;
+  }
+  int rows[kMaxRows];
+  rows[0] = c->next_id;
+  for (int i = 0; i < k; ++i) rows[1 + i] = draft_ids[i];
+  const sv_status s = forward(c, k + 1, rows, 1, noalloc);
+  if (s != SV_OK) return s;
+  const int n = c->h_result[0];
+  for (int r = 0; r <= n; ++r) c->hist[c->kv_len + r] = c->h_result[2 + r];
+  c->kv_len += n + 1;
+  c->next_id = c->h_result[1];
+  if (n_accepted) *n_accepted = n;
+  if (next_id) *next_id = c->next_id;
+  return SV_OK;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -410,6 +558,7 @@ const char* sv_status_str(sv_status s) {
     case SV_ENOSPACE: return "KV capacity exceeded";
     case SV_EDEVICE: return "HIP device error";
     case SV_EUNSUPPORTED: return "unsupported configuration";
+    case SV_ESCRATCH: return "intermediates exceed the library's static scratch array";
   }
   return "unknown status";
 }
@@ -474,6 +623,8 @@ sv_status sv_create(const sv_config* cfg, const sv_weights* w, const sv_buffers*
   const Plans p = make_plans(*cfg, n_cu);
   if (!plans_ok(*cfg, p)) return SV_EUNSUPPORTED;
   const Layout lay = make_layout(*cfg, p);
+  void* scratch_addr = nullptr;
+  if (scratch_address(dev, &scratch_addr) != SV_OK) return SV_EDEVICE;
   if (!buf->kv_pool || !buf->page_table || !buf->workspace) return SV_EINVAL;
   if (reinterpret_cast<uintptr_t>(buf->page_table) % 16 != 0) return SV_EINVAL;   // read 4 entries at a time
   if (buf->n_pages < 1 || buf->kv_pool_bytes < (int64_t)kv_pool_bytes_for(*cfg, buf->n_pages)) return SV_EINVAL;
@@ -499,6 +650,7 @@ sv_status sv_create(const sv_config* cfg, const sv_weights* w, const sv_buffers*
   c->lay = lay;
   c->wall_khz = wall_khz;
   c->ws = static_cast<char*>(buf->workspace);
+  c->scratch = scratch_addr;
   c->hist.assign(cfg->max_ctx, -1);
   c->last_argmax.assign(lay.rows, 0);
   const unsigned mapped = hipHostMallocMapped | hipHostMallocCoherent;
@@ -588,23 +740,12 @@ sv_status sv_decode_step(sv_ctx* c, int32_t token, int32_t* next_id) {
 
 sv_status sv_verify(sv_ctx* c, int32_t prefix_len, const int32_t* draft_ids, int32_t k, int32_t* n_accepted,
                     int32_t* next_id) {
-  if (!c) return SV_EINVAL;
-  if (k < 0 || k > c->cfg.max_k || (k > 0 && !draft_ids)) return SV_EINVAL;
-  if (prefix_len != c->kv_len || c->next_id < 0) return SV_ESTATE;
-  if (k > 0 && !ids_ok(c, draft_ids, k)) return SV_EINVAL;
-  if ((int64_t)c->kv_len + k + 1 > c->cfg.max_ctx) return SV_ENOSPACE;
-  int rows[kMaxRows];
-  rows[0] = c->next_id;
-  for (int i = 0; i < k; ++i) rows[1 + i] = draft_ids[i];
-  const sv_status s = forward(c, k + 1, rows, 1);
-  if (s != SV_OK) return s;
-  const int n = c->h_result[0];
-  for (int r = 0; r <= n; ++r) c->hist[c->kv_len + r] = c->h_result[2 + r];
-  c->kv_len += n + 1;
-  c->next_id = c->h_result[1];
-  if (n_accepted) *n_accepted = n;
-  if (next_id) *next_id = c->next_id;
-  return SV_OK;
+  return verify_impl(c, prefix_len, draft_ids, k, n_accepted, next_id, false);
+}
+
+sv_status sv_verify_noalloc(sv_ctx* c, int32_t prefix_len, const int32_t* draft_ids, int32_t k,
+                            int32_t* n_accepted, int32_t* next_id) {
+  return verify_impl(c, prefix_len, draft_ids, k, n_accepted, next_id, true);
 }
 
 sv_status sv_verify_batch(sv_ctx* const* ctxs, int32_t n, const int32_t* prefix_lens, const int32_t* ks,

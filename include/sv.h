@@ -36,7 +36,8 @@ typedef enum {
   SV_ESTATE = -2,        /* call does not match the context state (prefix_len != kv_len, ...) */
   SV_ENOSPACE = -3,      /* KV capacity (max_ctx or pages) would be exceeded */
   SV_EDEVICE = -4,       /* a HIP call failed */
-  SV_EUNSUPPORTED = -5   /* configuration this build does not implement */
+  SV_EUNSUPPORTED = -5,  /* configuration this build does not implement */
+  SV_ESCRATCH = -6       /* sv_verify_noalloc: the call's intermediates exceed the library's static array */
 } sv_status;
 
 /* Model and capacity description.  Shapes: d_model, n_q_heads*head_dim and
@@ -167,6 +168,35 @@ sv_status sv_decode_step(sv_ctx *ctx, int32_t token, int32_t *next_id);
  * [0, vocab); kv_len + k + 1 <= max_ctx (SV_ENOSPACE).  Outputs are host. */
 sv_status sv_verify(sv_ctx *ctx, int32_t prefix_len, const int32_t *draft_ids, int32_t k,
                     int32_t *n_accepted, int32_t *next_id);
+
+/* sv_verify for callers that cannot allocate (a serving loop or harness in
+ * which no call may reach hipMalloc, hipFree or any other allocating
+ * routine).  Arguments, checks, kernels and results are sv_verify's, bit for
+ * bit: the same (n_accepted, next_id), KV bits, history and observer logits.
+ * What differs: the forward's intermediates (the params copy, residual rows,
+ * sums of squares, q, attention split partials, activation planes and row
+ * argmax keys) live in one static device array of the library instead of the
+ * context's workspace, and the kernels are launched directly, so no HIP graph
+ * is instantiated.  The observer logits still go to the workspace (an
+ * output), the RoPE table is read from it (an input sv_create wrote), and no
+ * profiling stamps are taken.
+ *
+ * The array holds 64 MiB on every GPU the library runs on, for the life of
+ * the process.  A call needs about (k+1) x [d_model x 8.25 + n_q x head_dim x
+ * 8 + d_ff x 4 + n_q x splits x (head_dim + 4) x 4 + 12] bytes (each of nine
+ * buffers rounded up to 256 B), where splits is the most attention splits of
+ * any row of the window (a row at context c has ceil(c / 64) of them up to
+ * 128 and never more than 128); above 64 MiB the call returns SV_ESCRATCH
+ * before any launch (for example the 8B shape at a 32K context with k above
+ * 28).  Every call on one GPU shares that GPU's array: calls
+ * whose execution overlaps on one GPU (other threads, other streams) race
+ * and their results are undefined.  Nothing a previous call left in the
+ * array is read: the row keys are cleared by the first kernel and every
+ * other intermediate is written before it is read.
+ * Errors: as sv_verify, plus SV_ESCRATCH; SV_EDEVICE if the array's device
+ * address could not be obtained at sv_create. */
+sv_status sv_verify_noalloc(sv_ctx *ctx, int32_t prefix_len, const int32_t *draft_ids, int32_t k,
+                            int32_t *n_accepted, int32_t *next_id);
 
 /* Batched greedy block verify: n contexts of one model (identical sv_config
  * apart from max_prefill_rows, identical weight pointers) each verify their

@@ -1,0 +1,136 @@
+"""sv_verify_noalloc, the verify entry point for callers that cannot allocate,
+against sv_verify through the C ABI.
+
+Both run the same kernels; the no-allocation call keeps the forward's
+intermediates in the library's static device array instead of the
+context's workspace and launches without a HIP graph.  Its results must be
+sv_verify's bit for bit -- (n_accepted, next_id), every row's argmax and
+observer logits, the committed history and the KV bits -- on two calls in a
+row, the second with fewer rows than the first (so the array holds the
+first call's larger leftovers), on the tiny and the 8B shape; a call whose
+intermediates exceed the array is refused before any launch, leaving the
+context as it was.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(a):
+    return np.asarray(a, dtype=np.float32).view(np.uint32)
+
+
+def _state(s, n_rows, kv0):
+    return dict(kv_len=s.kv_len, next=s.next_id, hist=s.history(), arg=s.last_argmax(),
+                logits=[_bits(s.logits(r)) for r in range(n_rows)], kv=s.kv_positions(s.kv_len, kv0))
+
+
+def _same(a, b):
+    assert a["kv_len"] == b["kv_len"] and a["next"] == b["next"]
+    assert a["hist"] == b["hist"] and a["arg"] == b["arg"]
+    for x, y in zip(a["logits"], b["logits"]):
+        np.testing.assert_array_equal(x, y)
+    np.testing.assert_array_equal(a["kv"], b["kv"])
+
+
+def _pair_calls(dev, cfg, prompt, windows, label):
+    """Two contexts with the same prompt: one verifies each window with
+    sv_verify, the other with sv_verify_noalloc; states compared after each."""
+    from greedy_block_verification_amd import binding as B
+    from greedy_block_verification_amd.session import Session
+    a, b = Session(dev, cfg=cfg), Session(dev, cfg=cfg)
+    for s in (a, b):
+        s.prefill(prompt)
+        s.set_debug(True)
+    for drafts in windows:
+        print(f"{label}: window of {len(drafts)} drafts at kv_len {a.kv_len}", flush=True)
+        kv0 = a.kv_len
+        ra = B.sv_verify(a.ctx, a.kv_len, drafts)
+        rb = B.sv_verify_noalloc(b.ctx, b.kv_len, drafts)
+        assert ra == rb
+        _same(_state(a, len(drafts) + 1, kv0), _state(b, len(drafts) + 1, kv0))
+    a.close()
+    b.close()
+
+
+def _greedy_windows(dev, cfg, prompt, sizes, seed):
+    """Windows that follow the greedy continuation up to a random point."""
+    from greedy_block_verification_amd.session import Session
+    rng = np.random.default_rng(seed)
+    s = Session(dev, cfg=cfg)
+    s.prefill(prompt)
+    truth = [s.next_id]
+    for _ in range(sum(sizes) + len(sizes)):
+        truth.append(s.decode_step(truth[-1]))
+    s.close()
+    out, c = [], 0
+    for k in sizes:
+        cut = int(rng.integers(0, k + 1))
+        w = truth[c + 1: c + 1 + cut] + rng.integers(0, cfg.vocab, k - cut).tolist()
+        out.append(w)
+        c += cut + 1      # the accepted part plus the correction
+    return out
+
+
+def test_noalloc_equals_verify_tiny():
+    import torch
+    from greedy_block_verification_amd.session import DeviceModel
+    from seeded_inputs import generate_weights, get_config, prompt_ids
+    assert torch.cuda.is_available()
+    cfg = get_config("tiny")
+    dev = DeviceModel(generate_weights(cfg))
+    prompt = prompt_ids(41, 0, 40, cfg.vocab).tolist()
+    _pair_calls(dev, cfg, prompt, _greedy_windows(dev, cfg, prompt, [8, 3, 0, 5], 41), "tiny")
+
+
+def test_noalloc_equals_verify_q8b(q8b_device):
+    from seeded_inputs import get_config, prompt_ids
+    dev, w = q8b_device
+    cfg = get_config("q8b")
+    prompt = prompt_ids(42, 0, 128, cfg.vocab).tolist()
+    _pair_calls(dev, cfg, prompt, _greedy_windows(dev, cfg, prompt, [8, 4], 42), "q8b")
+
+
+def test_noalloc_long_context_and_oversized_window(q8b_device):
+    """At a 32,704-position context (synthetic KV), a K = 16 window (128
+    attention splits, partials in the array) matches sv_verify bit for bit
+    after a K = 20 one; K = 32 needs more than the array holds and is
+    refused with SV_ESCRATCH, leaving the context untouched."""
+    import torch
+    from greedy_block_verification_amd import binding as B
+    from greedy_block_verification_amd.session import Session
+    from seeded_inputs import get_config
+    dev, w = q8b_device
+    cfg = get_config("q8b_stress")
+    prefix = 32704
+    a, b = Session(dev, cfg=cfg), Session(dev, cfg=cfg)
+    g = torch.Generator(device=a.kv.device)
+    g.manual_seed(77)
+    n_pages = cfg.max_ctx // cfg.page_size
+    used = prefix // cfg.page_size
+    for s in (a, b):
+        pool = s.kv.view(cfg.n_layers, n_pages, -1)
+        g.manual_seed(77)
+        for l in range(cfg.n_layers):
+            vals = torch.randn((used, pool.shape[2]), generator=g, device=s.kv.device, dtype=torch.float32)
+            pool[l, :used] = vals.to(torch.float16).view(torch.int16)
+    torch.cuda.synchronize()
+    hist = np.random.default_rng(78).integers(0, cfg.vocab, prefix).tolist()
+    for s in (a, b):
+        B.sv_restore(s.ctx, prefix, hist)
+        s.set_debug(True)
+    rng = np.random.default_rng(79)
+    before = (b.kv_len, b.next_id)
+    with pytest.raises(B.SvError) as e:
+        B.sv_verify_noalloc(b.ctx, b.kv_len, rng.integers(0, cfg.vocab, 32).tolist())
+    assert e.value.status == B.SV_ESCRATCH
+    assert (b.kv_len, b.next_id) == before
+    for k in (20, 16):
+        drafts = rng.integers(0, cfg.vocab, k).tolist()
+        print(f"q8b 32K: window of {k} drafts at kv_len {a.kv_len}", flush=True)
+        kv0 = a.kv_len
+        assert B.sv_verify(a.ctx, a.kv_len, drafts) == B.sv_verify_noalloc(b.ctx, b.kv_len, drafts)
+        _same(_state(a, k + 1, kv0), _state(b, k + 1, kv0))
+    a.close()
+    b.close()
