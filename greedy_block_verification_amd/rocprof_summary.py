@@ -15,6 +15,11 @@ Three commands:
   SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE``: FLOPs = MOPS x 512 over the
   dispatch's own duration, against the dense bf16 / fp16 peak; busy % =
   MFMA busy cycles / (GPU active cycles per XCC x SIMDs).
+* ``counters``: per-kernel means of whatever counters one ``--pmc`` run
+  took, plus the ratios that explain where a kernel's waves spend their time
+  when the run has the counters for them: VALU and MFMA instructions per
+  wave, the share of wave cycles waiting on anything (``SQ_WAIT_ANY``) and
+  waiting to issue (``SQ_WAIT_INST_ANY``), and MFMA busy %.
 
 Usage::
 
@@ -176,6 +181,51 @@ def mfma(args):
     print("\n".join(lines))
 
 
+def counters(args):
+    per = defaultdict(lambda: defaultdict(dict))
+    names = []
+    for r in csv.DictReader(open(args.counters)):
+        if args.kernel and not any(_matches(r["Kernel_Name"], k) for k in args.kernel):
+            continue
+        d = per[r["Kernel_Name"]][int(r["Dispatch_Id"])]
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        if r["Counter_Name"] not in names:
+            names.append(r["Counter_Name"])
+    lines = [f"# Counters per kernel: {args.title}", "", "Command:", "", "```", args.command, "```", "",
+             f"Means per dispatch over the last {args.last} dispatches of each kernel.", ""]
+    derived = []
+    if {"SQ_INSTS_VALU", "SQ_WAVES"} <= set(names):
+        derived.append(("VALU / wave", lambda d: d["SQ_INSTS_VALU"] / d["SQ_WAVES"]))
+    if {"SQ_INSTS_MFMA", "SQ_WAVES"} <= set(names):
+        derived.append(("MFMA / wave", lambda d: d["SQ_INSTS_MFMA"] / d["SQ_WAVES"]))
+    if {"SQ_WAIT_ANY", "SQ_WAVE_CYCLES"} <= set(names):
+        derived.append(("wait any %", lambda d: 100.0 * d["SQ_WAIT_ANY"] / d["SQ_WAVE_CYCLES"]))
+    if {"SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"} <= set(names):
+        derived.append(("wait issue %", lambda d: 100.0 * d["SQ_WAIT_INST_ANY"] / d["SQ_WAVE_CYCLES"]))
+    if {"SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"} <= set(names):
+        derived.append(("MFMA busy %", lambda d: 100.0 * d["SQ_VALU_MFMA_BUSY_CYCLES"] /
+                        (d["GRBM_GUI_ACTIVE"] / args.xcc * args.simds)))
+    head = ["kernel", "dispatches", "mean us"] + names + [n for n, _ in derived]
+    lines += ["| " + " | ".join(head) + " |", "|" + "---|" * len(head)]
+    for k, ds in sorted(per.items(), key=lambda kv: kv[0]):
+        ds = [ds[i] for i in sorted(ds)][-args.last:]
+        ds = [d for d in ds if all(n in d for n in names)]
+        if not ds:
+            continue
+        mean = {n: sum(d[n] for d in ds) / len(ds) for n in names + ["ns"]}
+        cells = [f"`{_short(k)}`", str(len(ds)), f"{mean['ns'] / 1000:.2f}"]
+        cells += [f"{mean[n]:.4g}" for n in names]
+        for _, f in derived:
+            try:
+                cells.append(f"{f(mean):.3g}")
+            except ZeroDivisionError:
+                cells.append("-")
+        lines.append("| " + " | ".join(cells) + " |")
+    open(args.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -209,8 +259,17 @@ def main():
     m.add_argument("--title", default="")
     m.add_argument("--command", required=True)
     m.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--counters", required=True)
+    c.add_argument("--kernel", action="append", default=[], help="keep only kernels whose name starts so")
+    c.add_argument("--last", type=int, default=1000)
+    c.add_argument("--xcc", type=int, default=8)
+    c.add_argument("--simds", type=int, default=1024)
+    c.add_argument("--title", default="")
+    c.add_argument("--command", required=True)
+    c.add_argument("--out", required=True)
     a = ap.parse_args()
-    {"stats": stats, "traffic": traffic, "mfma": mfma}[a.cmd](a)
+    {"stats": stats, "traffic": traffic, "mfma": mfma, "counters": counters}[a.cmd](a)
 
 
 if __name__ == "__main__":

@@ -61,3 +61,26 @@ def test_traffic_scales_counters_by_the_copy_probe(tmp_path):
     assert rec["fetch_bytes_per_launch"] == 204800 and rec["write_bytes_per_launch"] == 10240
     assert rec["traffic_over_algorithmic"] == 1.0
     assert rec["kernel_source_sha256"] == R.kernel_source_sha256()
+
+
+def test_counters_means_and_wait_shares(tmp_path):
+    path = tmp_path / "c.csv"
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
+                                          "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for d in range(1, 4):                     # three dispatches of 2, 4, 6 us
+            vals = {"SQ_WAVES": 100.0, "SQ_INSTS_VALU": 1000.0 * d, "SQ_WAVE_CYCLES": 4000.0,
+                    "SQ_WAIT_ANY": 1000.0 * d, "SQ_WAIT_INST_ANY": 400.0}
+            for n, v in vals.items():
+                w.writerow({"Dispatch_Id": d, "Kernel_Name": K, "Counter_Name": n, "Counter_Value": v,
+                            "Start_Timestamp": 0, "End_Timestamp": 2000 * d})
+    a = argparse.Namespace(counters=str(path), kernel=["sv::k_gemm_bf16"], last=2, xcc=8, simds=1024,
+                           title="synthetic", command="cmd", out=str(tmp_path / "c.md"))
+    R.counters(a)
+    text = open(tmp_path / "c.md").read()
+    # last two dispatches: 4 and 6 us, VALU 2500 per dispatch = 25 per wave, wait any 62.5 %, wait issue 10 %
+    row = [l for l in text.splitlines() if l.startswith("| `void sv::k_gemm_bf16")][0]
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    assert cells[1:3] == ["2", "5.00"]
+    assert cells[-3:] == ["25", "62.5", "10"]
