@@ -192,18 +192,19 @@ __device__ __forceinline__ f32x4 mfma_pair_f16(uint4 a, const BPair& b, f32x4 c)
   return mfma16x16x32_f16(a, b.lo, c);
 }
 
-// int4 nibble -> bf16 bits of the integer code (exact).
-__device__ __forceinline__ uint16_t code_bf16(uint32_t nib) {
-  const int q = (int)(nib ^ 8u) - 8;
-  return f2bf((float)q);
+// 8 int4 codes (one 32-bit word, nibble e = code of element e, two's
+// complement) -> one MFMA operand of 8 bf16 holding the integers exactly.
+// Code e is sign-extended and converted to fp32; an integer of magnitude at
+// most 8 has a zero low half in fp32, so its bf16 is the high half, and
+// v_perm packs the high halves of two fp32 values into one word.
+__device__ __forceinline__ uint32_t code_f32_bits(uint32_t w, int e) {
+  return __float_as_uint((float)(((int)(w << (28 - 4 * e))) >> 28));
 }
-
-// 8 nibbles (one 32-bit word) -> one MFMA operand of 8 bf16.
+__device__ __forceinline__ uint32_t codes2(uint32_t w, int e) {   // elements e (low half) and e + 1
+  return __builtin_amdgcn_perm(code_f32_bits(w, e + 1), code_f32_bits(w, e), 0x07060302u);
+}
 __device__ __forceinline__ uint4 codes8(uint32_t w) {
-  return make_uint4(pack2(code_bf16(w & 15u), code_bf16((w >> 4) & 15u)),
-                    pack2(code_bf16((w >> 8) & 15u), code_bf16((w >> 12) & 15u)),
-                    pack2(code_bf16((w >> 16) & 15u), code_bf16((w >> 20) & 15u)),
-                    pack2(code_bf16((w >> 24) & 15u), code_bf16((w >> 28) & 15u)));
+  return make_uint4(codes2(w, 0), codes2(w, 2), codes2(w, 4), codes2(w, 6));
 }
 
 __device__ __forceinline__ float act_fn(float x, int act) {
@@ -885,6 +886,163 @@ __global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
   prof_end(a.prof);
 }
 
+// int4 weights, one row tile (at most 16 rows), register operands: the
+// small int4 matrices are bound by latency, not bytes (a Gemma-shaped layer
+// streams 1-10 MB per GEMM), so every load a workgroup needs goes out at
+// once -- the codes and scales of all IG items' tiles, then each wave's own
+// activation operands (wave w only ever multiplies the input columns of its
+// chain's tiles, so nothing is staged in LDS and no barrier comes before
+// the MFMAs) -- and the IG items share one reduction.  CPI tiles per wave
+// and item; the activation operands of tiles 0 and 1 load up front, those
+// of tile c + 2 after tile c's MFMAs.  The sums are k_gemm_int4's: chain w
+// runs its tiles in order, per tile the scale groups in order, each group
+// summed from zero over its two 32-input chunks (hi plane before lo plane)
+// and added to the chain sum scaled by the group scale; the chain sums meet
+// in LDS in chain order.
+template <int IG>
+struct Int4rShared {
+  f32x4 red[IG][kMaxWaves][64];
+  float y[IG][16][16];
+  float inv[16];
+};
+
+template <int ROLE, int CPI, int IG>
+__global__ __launch_bounds__(768) void k_gemm_int4r(GemmArgs a) {
+  constexpr int CPA = CPI < 2 ? CPI : 2;   // tiles whose activation operands are held at once
+  __shared__ Int4rShared<IG> sh;
+  prof_start(a.prof);
+  const int nw = a.S, nthr = 64 * a.S;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int j = lane & 15, g = lane >> 4;
+  const int KT = a.K >> 7;
+  const int n_items = a.N >> 4;
+  const int n_my = (n_items - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;   // items of this workgroup, 1..IG
+  int T[IG];
+#pragma unroll
+  for (int i = 0; i < IG; ++i) T[i] = (int)blockIdx.x + (i < n_my ? i : n_my - 1) * (int)gridDim.x;
+  // codes and scales of every (tile position, item): tile kt = wave + nw c of item T_i
+  const uint4* Wq = reinterpret_cast<const uint4*>(a.W) + lane;
+  const uint2* Ws = reinterpret_cast<const uint2*>(a.Wscale) + g;
+  uint4 q[CPI][IG];
+  uint2 s0[CPI][IG], s1[CPI][IG];
+#pragma unroll
+  for (int c = 0; c < CPI; ++c)
+#pragma unroll
+    for (int i = 0; i < IG; ++i) {
+      const size_t off = (size_t)T[i] * KT + wave + (size_t)nw * c;
+      q[c][i] = ld_stream(Wq + off * 64);
+      s0[c][i] = Ws[off * 8];
+      s1[c][i] = Ws[off * 8 + 4];
+    }
+  // this lane's activation operands of a tile: row j (clamped), inputs
+  // kt*128 + 64 gq + 32 h + 8 g .. +7, hi and lo planes
+  const int r = row_of(j, a.M);
+  auto act = [&](int c, BPair (&B)[2][2]) {
+    const int kt = wave + nw * c;
+#pragma unroll
+    for (int gq = 0; gq < 2; ++gq)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) B[gq][h] = load_planes(a, r, kt * 128 + gq * 64 + h * 32 + g * 8);
+  };
+  BPair B[CPA][2][2];
+#pragma unroll
+  for (int c = 0; c < CPA; ++c) act(c, B[c]);
+  if (norm_role(ROLE))
+    for (int rr = wave; rr < a.M; rr += nw) {
+      const float v = row_inv_rms(a, rr, lane);
+      if (lane == 0) sh.inv[rr] = v;
+    }
+  // epilogue operands of element e of item i, for t = threadIdx.x = i M 16 + e
+  const int per_item = a.M * 16;
+  const int i_pre = (int)threadIdx.x / per_item;
+  const EpiPre pre = epi_load<ROLE>(a, T[i_pre < n_my ? i_pre : 0], (int)threadIdx.x - i_pre * per_item);
+  f32x4 acc[IG];
+#pragma unroll
+  for (int i = 0; i < IG; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < CPI; ++c) {
+    BPair (&Bc)[2][2] = B[c % CPA];
+#pragma unroll
+    for (int i = 0; i < IG; ++i)
+#pragma unroll
+      for (int gq = 0; gq < 2; ++gq) {
+        const uint2 SC = gq == 0 ? s0[c][i] : s1[c][i];
+        const uint4 A0 = codes8(gq == 0 ? q[c][i].x : q[c][i].z), A1 = codes8(gq == 0 ? q[c][i].y : q[c][i].w);
+        const float f0 = bf2f((uint16_t)(SC.x & 0xffffu)), f1 = bf2f((uint16_t)(SC.x >> 16));
+        const float f2 = bf2f((uint16_t)(SC.y & 0xffffu)), f3 = bf2f((uint16_t)(SC.y >> 16));
+        f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
+        p = mfma_pair(A0, Bc[gq][0], p);
+        p = mfma_pair(A1, Bc[gq][1], p);
+        acc[i].x = fmaf(f0, p.x, acc[i].x);
+        acc[i].y = fmaf(f1, p.y, acc[i].y);
+        acc[i].z = fmaf(f2, p.z, acc[i].z);
+        acc[i].w = fmaf(f3, p.w, acc[i].w);
+      }
+    if (c + CPA < CPI) act(c + CPA, Bc);
+  }
+  // the IG items' chain sums meet in LDS, in chain order
+#pragma unroll
+  for (int i = 0; i < IG; ++i) sh.red[i][wave][lane] = acc[i];
+  __syncthreads();
+  for (int t = threadIdx.x; t < IG * 256; t += nthr) {
+    const int i = t >> 8, tt = t & 255;
+    const float* red = reinterpret_cast<const float*>(sh.red[i]);
+    float v = 0.f;
+#pragma unroll
+    for (int w0 = 0; w0 < kMaxWaves; w0 += 8) {
+      float part[8];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) part[w] = red[(w0 + w) * 256 + tt];
+#pragma unroll
+      for (int w = 0; w < 8; ++w)
+        if (w0 + w < nw) v = (w0 + w == 0) ? part[w] : v + part[w];
+    }
+    const int l = tt >> 2;
+    const int rr = l & 15;
+    if (rr < a.M) sh.y[i][rr][4 * (l >> 4) + (tt & 3)] = v;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < n_my * per_item; idx += nthr) {
+    const int i = idx / per_item, e = idx - i * per_item;
+    const int rr = e >> 4, cc = e & 15;
+    const EpiPre ep = idx == (int)threadIdx.x ? pre : epi_load<ROLE>(a, T[i], e);
+    epi_element<ROLE>(a, T[i], rr, cc, ep, sh.inv[rr], [&](int c2) { return sh.y[i][rr][c2]; }, nullptr);
+  }
+  prof_end(a.prof);
+}
+
+// Items per workgroup up to MAXIG (the most whose registers fit without
+// spilling at CPI tiles per wave).
+template <int ROLE, int CPI, int MAXIG>
+static hipError_t launch_int4r_ig(const GemmArgs& a, int grid, int ig, hipStream_t st) {
+  const dim3 block(64 * a.S), g(grid);
+  if (ig > MAXIG) return hipErrorNotSupported;
+  switch (ig) {
+    case 1: hipLaunchKernelGGL((k_gemm_int4r<ROLE, CPI, 1>), g, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_gemm_int4r<ROLE, CPI, (MAXIG >= 2 ? 2 : 1)>), g, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_gemm_int4r<ROLE, CPI, (MAXIG >= 3 ? 3 : 1)>), g, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_gemm_int4r<ROLE, CPI, (MAXIG >= 4 ? 4 : 1)>), g, block, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// The register-operand int4 kernel where it applies (at most 16 rows, at
+// most 12 waves, 1, 2 or 4 tiles per wave and item, at most 4 items per
+// workgroup, 2 at 4 tiles); hipErrorNotSupported otherwise.
+template <int ROLE>
+static hipError_t launch_int4r(const GemmArgs& a, int grid, hipStream_t st) {
+  const int cpi = (a.K >> 7) / a.S;
+  const int ig = ((a.N >> 4) + grid - 1) / grid;
+  if (a.M > 16 || a.S > 12) return hipErrorNotSupported;
+  switch (cpi) {
+    case 1: return launch_int4r_ig<ROLE, 1, 4>(a, grid, ig, st);
+    case 2: return launch_int4r_ig<ROLE, 2, 4>(a, grid, ig, st);
+    case 4: return launch_int4r_ig<ROLE, 4, 2>(a, grid, ig, st);
+    default: return hipErrorNotSupported;
+  }
+}
+
 // bf16 items in groups, stages outermost (17..64 rows whose activation planes
 // do not fit one LDS stage): a workgroup takes its items IG at a time and,
 // for each stage of one chunk per wave (two LDS buffers; the next stage's
@@ -1207,6 +1365,17 @@ hipError_t launch_gemm(const GemmArgs& a, int role, int grid, hipStream_t st) {
       case kRoleLmHead: return gemm_dispatch_grp<kRoleLmHead>(b, grid, st);
       default: return hipErrorInvalidValue;
     }
+  }
+  if (i4 && a.M <= 16) {
+    hipError_t e = hipErrorNotSupported;
+    switch (role) {
+      case kRoleQkv: e = launch_int4r<kRoleQkv>(b, grid, st); break;
+      case kRoleO: e = launch_int4r<kRoleO>(b, grid, st); break;
+      case kRoleGateUp: e = launch_int4r<kRoleGateUp>(b, grid, st); break;
+      case kRoleDown: e = launch_int4r<kRoleDown>(b, grid, st); break;
+      default: break;
+    }
+    if (e != hipErrorNotSupported) return e;
   }
   switch (role) {
     case kRoleQkv: return i4 ? gemm_dispatch<kRoleQkv, true>(b, grid, st) : gemm_dispatch<kRoleQkv, false>(b, grid, st);
