@@ -1251,18 +1251,22 @@ static hipError_t gemm_dispatch_nb(const GemmArgs& a, int grid, hipStream_t st, 
     switch (tm) {
       case 1:
         if (dbl) {
-          if constexpr (NB >= 4) hipLaunchKernelGGL((k_gemm_bf16<1, ROLE, NB, true>), dim3(grid), block, 0, st, a);
+          if constexpr (NB == 4 || NB == 8) hipLaunchKernelGGL((k_gemm_bf16<1, ROLE, NB, true>), dim3(grid), block, 0, st, a);
           else return hipErrorInvalidValue;
         } else {
           hipLaunchKernelGGL((k_gemm_bf16<1, ROLE, NB, false>), dim3(grid), block, 0, st, a);
         }
         break;
       case 2:
-        if (dbl) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((k_gemm_bf16<2, ROLE, NB, false>), dim3(grid), block, 0, st, a);
+        if constexpr (NB == 3 || NB == 6) {
+          return hipErrorInvalidValue;
+        } else {
+          if (dbl) return hipErrorInvalidValue;
+          hipLaunchKernelGGL((k_gemm_bf16<2, ROLE, NB, false>), dim3(grid), block, 0, st, a);
+        }
         break;
       case 3:
-        if constexpr (NB <= 4) {
+        if constexpr (NB <= 4 && NB != 3) {
           if (dbl) return hipErrorInvalidValue;
           hipLaunchKernelGGL((k_gemm_bf16<3, ROLE, NB, false>), dim3(grid), block, 0, st, a);
         } else {
@@ -1303,8 +1307,10 @@ int gemm_ring_depth(int n_chunks, int waves, int M, int unit, bool* dbl) {
   // 1; int4 ring slots also hold scales: 4 deep up to 16 rows, 2 up to 32,
   // then 1
   const int cap = unit == 128 ? (M <= 16 ? 4 : (M <= 32 ? 2 : 1)) : (M <= 32 ? 8 : (M <= 48 ? 4 : 1));
-  for (int nb : {8, 4, 2, 1}) {
-    if (nb > cap) continue;
+  // bf16 at one row tile also takes rings of 6 and 3 (chunks per wave that 8
+  // and 4 do not divide: 96 chunks over 16 waves, 48 over 16)
+  for (int nb : {8, 6, 4, 3, 2, 1}) {
+    if (nb > cap || ((nb == 6 || nb == 3) && (unit != 32 || M > 16))) continue;
     if ((n_chunks / waves) % nb) continue;
     const int cs = stage_chunks(n_chunks, waves, M, unit, nb);
     if (cs > 0) return nb;
@@ -1328,6 +1334,12 @@ static hipError_t gemm_dispatch(const GemmArgs& a_in, int grid, hipStream_t st) 
     case 8:
       if constexpr (INT4) return hipErrorInvalidValue;
       else return gemm_dispatch_nb<ROLE, INT4, 8>(a, grid, st, dbl);
+    case 6:
+      if constexpr (INT4) return hipErrorInvalidValue;
+      else return gemm_dispatch_nb<ROLE, INT4, 6>(a, grid, st, dbl);
+    case 3:
+      if constexpr (INT4) return hipErrorInvalidValue;
+      else return gemm_dispatch_nb<ROLE, INT4, 3>(a, grid, st, dbl);
     case 4: return gemm_dispatch_nb<ROLE, INT4, 4>(a, grid, st, dbl);
     case 2: return gemm_dispatch_nb<ROLE, INT4, 2>(a, grid, st, dbl);
     case 1: return gemm_dispatch_nb<ROLE, INT4, 1>(a, grid, st, dbl);
