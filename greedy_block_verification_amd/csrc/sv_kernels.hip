@@ -2466,14 +2466,41 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   }
   __syncthreads();
   const float* p = reinterpret_cast<const float*>(rec);
+  // The fold's running maximum is a prefix maximum of the m_i (fmaxf is
+  // exact), so every step's weights 2^(M_{i-1} - M_i) and 2^(m_i - M_i) can
+  // be formed at once from a scan; only the (l, o) updates stay sequential,
+  // two dependent operations per split instead of the whole step.  The
+  // values are those of Fold::add, operation for operation.
+  __shared__ float wab[2][kAttnMaxSplits];
+  if (threadIdx.x < 64) {
+    const int i0 = threadIdx.x, i1 = threadIdx.x + 64;
+    const float m0 = i0 < ns ? p[i0 * (DH + 4)] : -INFINITY;
+    const float m1 = i1 < ns ? p[i1 * (DH + 4)] : -INFINITY;
+    float s0 = m0, s1 = m1;                      // inclusive prefix maxima of splits i0, i1
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float t0 = __shfl_up(s0, o), t1 = __shfl_up(s1, o);
+      if (i0 >= o) { s0 = fmaxf(s0, t0); s1 = fmaxf(s1, t1); }
+    }
+    const float all0 = __shfl(s0, 63);           // M_63
+    s1 = fmaxf(s1, all0);
+    float q0 = __shfl_up(s0, 1), q1 = __shfl_up(s1, 1);   // M_{i-1}
+    if (i0 == 0) q1 = all0;
+    if (i0 >= 1 && i0 < ns) { wab[0][i0] = exp2f(q0 - s0); wab[1][i0] = exp2f(m0 - s0); }
+    if (i1 < ns) { wab[0][i1] = exp2f(q1 - s1); wab[1][i1] = exp2f(m1 - s1); }
+  }
+  __syncthreads();
   const int d = threadIdx.x;
   if (d < DH) {
-    Fold f;
-    f.first(p[0], p[1], p[4 + d]);
+    float l = p[1], o = p[4 + d];
 #pragma unroll 8
-    for (int i = 1; i < ns; ++i) f.add(p[i * (DH + 4)], p[i * (DH + 4) + 1], p[i * (DH + 4) + 4 + d]);
+    for (int i = 1; i < ns; ++i) {
+      const float wa = wab[0][i], wb = wab[1][i];
+      l = l * wa + p[i * (DH + 4) + 1] * wb;
+      o = o * wa + p[i * (DH + 4) + 4 + d] * wb;
+    }
     const size_t oi = (size_t)r * a.nq * DH + (size_t)j * DH + d;
-    split1(f.o / f.l, a.ohi[oi], a.olo[oi]);
+    split1(o / l, a.ohi[oi], a.olo[oi]);
   }
   prof_end(a.prof);
 }
