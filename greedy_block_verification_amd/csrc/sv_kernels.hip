@@ -1043,6 +1043,122 @@ static hipError_t launch_int4r(const GemmArgs& a, int grid, hipStream_t st) {
   }
 }
 
+// bf16 weights of small K (1, 2 or 4 chunks per wave), one row tile, the
+// same register-operand scheme as k_gemm_int4r: the workgroup's IG items'
+// chunks and each wave's own activation operands are requested at once, no
+// LDS stage, one reduction for the IG items.  The sums are k_gemm_bf16's:
+// chain w runs chunks w, w + S, w + 2S, ... in order through one MFMA
+// accumulator (hi plane before lo plane), and the S chain sums meet in LDS
+// in chain order.  Not for the LM head (its many items per workgroup keep
+// the ring kernel).  Measured on MI355X (0.6B shape, K = 4): QKV 7.7 -> 6.0
+// us, gate/up 7.8 -> 6.4 us per layer against the ring kernel; at 6 chunks
+// per wave (0.6B down) and 8 (8B O) it was no faster, so those keep the ring.
+template <int IG>
+struct Bf16rShared {
+  f32x4 red[IG][kMaxWaves][64];
+  float y[IG][16][16];
+  float inv[16];
+};
+
+template <int ROLE, int CPW, int IG>
+__global__ __launch_bounds__(1024) void k_gemm_bf16r(GemmArgs a) {
+  __shared__ Bf16rShared<IG> sh;
+  prof_start(a.prof);
+  const int nw = a.S, nthr = 64 * a.S;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int j = lane & 15, g = lane >> 4;
+  const int KC = a.K >> 5;
+  const int n_items = a.N >> 4;
+  const int n_my = (n_items - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;   // items of this workgroup, 1..IG
+  int T[IG];
+#pragma unroll
+  for (int i = 0; i < IG; ++i) T[i] = (int)blockIdx.x + (i < n_my ? i : n_my - 1) * (int)gridDim.x;
+  const uint4* W4 = reinterpret_cast<const uint4*>(a.W) + lane;
+  uint4 A[CPW][IG];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c)
+#pragma unroll
+    for (int i = 0; i < IG; ++i) A[c][i] = ld_stream(W4 + ((size_t)T[i] * KC + wave + (size_t)nw * c) * 64);
+  const int r = row_of(j, a.M);
+  BPair B[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) B[c] = load_planes(a, r, (wave + nw * c) * 32 + g * 8);
+  if (norm_role(ROLE))
+    for (int rr = wave; rr < a.M; rr += nw) {
+      const float v = row_inv_rms(a, rr, lane);
+      if (lane == 0) sh.inv[rr] = v;
+    }
+  const int per_item = a.M * 16;
+  const int i_pre = (int)threadIdx.x / per_item;
+  const EpiPre pre = epi_load<ROLE>(a, T[i_pre < n_my ? i_pre : 0], (int)threadIdx.x - i_pre * per_item);
+  f32x4 acc[IG];
+#pragma unroll
+  for (int i = 0; i < IG; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < CPW; ++c)
+#pragma unroll
+    for (int i = 0; i < IG; ++i) acc[i] = mfma_pair(A[c][i], B[c], acc[i]);
+#pragma unroll
+  for (int i = 0; i < IG; ++i) sh.red[i][wave][lane] = acc[i];
+  __syncthreads();
+  for (int t = threadIdx.x; t < IG * 256; t += nthr) {
+    const int i = t >> 8, tt = t & 255;
+    const float* red = reinterpret_cast<const float*>(sh.red[i]);
+    float v = 0.f;
+#pragma unroll
+    for (int w0 = 0; w0 < kMaxWaves; w0 += 8) {
+      float part[8];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) part[w] = red[(w0 + w) * 256 + tt];
+#pragma unroll
+      for (int w = 0; w < 8; ++w)
+        if (w0 + w < nw) v = (w0 + w == 0) ? part[w] : v + part[w];
+    }
+    const int l = tt >> 2;
+    const int rr = l & 15;
+    if (rr < a.M) sh.y[i][rr][4 * (l >> 4) + (tt & 3)] = v;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < n_my * per_item; idx += nthr) {
+    const int i = idx / per_item, e = idx - i * per_item;
+    const int rr = e >> 4, cc = e & 15;
+    const EpiPre ep = idx == (int)threadIdx.x ? pre : epi_load<ROLE>(a, T[i], e);
+    epi_element<ROLE>(a, T[i], rr, cc, ep, sh.inv[rr], [&](int c2) { return sh.y[i][rr][c2]; }, nullptr);
+  }
+  prof_end(a.prof);
+}
+
+// Items per workgroup up to MAXIG (the most whose registers fit without
+// spilling at CPW chunks per wave).
+template <int ROLE, int CPW, int MAXIG>
+static hipError_t launch_bf16r_ig(const GemmArgs& a, int grid, int ig, hipStream_t st) {
+  const dim3 block(64 * a.S), g(grid);
+  if (ig > MAXIG) return hipErrorNotSupported;
+  switch (ig) {
+    case 1: hipLaunchKernelGGL((k_gemm_bf16r<ROLE, CPW, 1>), g, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_gemm_bf16r<ROLE, CPW, (MAXIG >= 2 ? 2 : 1)>), g, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_gemm_bf16r<ROLE, CPW, (MAXIG >= 3 ? 3 : 1)>), g, block, 0, st, a); break;
+    default: return hipErrorNotSupported;
+  }
+  return hipGetLastError();
+}
+
+// The register-operand bf16 kernel where it applies (at most 16 rows, 1, 2
+// or 4 chunks per wave and item, at most 3 items per workgroup (2 at 4
+// chunks), not the LM head); hipErrorNotSupported otherwise.
+template <int ROLE>
+static hipError_t launch_bf16r(const GemmArgs& a, int grid, hipStream_t st) {
+  const int cpw = (a.K >> 5) / a.S;
+  const int ig = ((a.N >> 4) + grid - 1) / grid;
+  if (ROLE == kRoleLmHead || a.M > 16) return hipErrorNotSupported;
+  switch (cpw) {
+    case 1: return launch_bf16r_ig<ROLE, 1, 3>(a, grid, ig, st);
+    case 2: return launch_bf16r_ig<ROLE, 2, 3>(a, grid, ig, st);
+    case 4: return launch_bf16r_ig<ROLE, 4, 2>(a, grid, ig, st);
+    default: return hipErrorNotSupported;
+  }
+}
+
 // bf16 items in groups, stages outermost (17..64 rows whose activation planes
 // do not fit one LDS stage): a workgroup takes its items IG at a time and,
 // for each stage of one chunk per wave (two LDS buffers; the next stage's
@@ -1377,6 +1493,17 @@ hipError_t launch_gemm(const GemmArgs& a, int role, int grid, hipStream_t st) {
       case kRoleLmHead: return gemm_dispatch_grp<kRoleLmHead>(b, grid, st);
       default: return hipErrorInvalidValue;
     }
+  }
+  if (!i4 && a.M <= 16) {
+    hipError_t e = hipErrorNotSupported;
+    switch (role) {
+      case kRoleQkv: e = launch_bf16r<kRoleQkv>(b, grid, st); break;
+      case kRoleO: e = launch_bf16r<kRoleO>(b, grid, st); break;
+      case kRoleGateUp: e = launch_bf16r<kRoleGateUp>(b, grid, st); break;
+      case kRoleDown: e = launch_bf16r<kRoleDown>(b, grid, st); break;
+      default: break;
+    }
+    if (e != hipErrorNotSupported) return e;
   }
   if (i4 && a.M <= 16) {
     hipError_t e = hipErrorNotSupported;
