@@ -2172,7 +2172,7 @@ __device__ __forceinline__ void attn_split_union(int kv_len, int r0, int r1, int
   }
 }
 
-template <int DH, bool FOLD>
+template <int DH, bool FOLD, bool EARLY>
 __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   constexpr int DC = DH / 32;            // d chunks of the score MFMA
   constexpr int DT = DH / 16;            // d tiles of the P.V MFMA
@@ -2215,18 +2215,34 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   const int rq = div_m(qr, G, a.g_magic);
   const int r = have ? rq : 0;
   const int head = h * G + (have ? qr - rq * G : 0);
-  float4 qraw[DC][2];
-  {
-    const float4* qp = reinterpret_cast<const float4*>(a.q + ((size_t)(V.row0 + r) * a.nq + head) * DH + g * 8);
-#pragma unroll
-    for (int c = 0; c < DC; ++c) { qraw[c][0] = qp[c * 8]; qraw[c][1] = qp[c * 8 + 1]; }
-  }
   auto block_pages = [&](int b) { return attn_block_pages(av, b); };
   // the first unit's first block is its split index whenever splits are one
   // block (contexts up to 8192): fetch its pages before the context length is known
   const int b_guess = s_lo + wave;
   int4 pq_guess = block_pages(b_guess);
   const int kv_len = attn_kv_len(a, qt);
+  // EARLY (the launcher's choice for the split kernel of at most 64 splits):
+  // every row then has one block per split (a row of two or more blocks per
+  // split has at least 65 splits), so a unit is block b_guess or nothing.
+  // Its K/V go out as soon as the page numbers arrive, ahead of q, which the
+  // previous kernel has just written and which arrives no sooner: loads
+  // complete in issue order, so q issued first would hold the K/V back by
+  // its whole latency.  The pages are clamped into the pool for this load
+  // (a unit past its rows' context never uses it); a used block lies inside
+  // the context, whose pages are valid, so the clamp leaves them unchanged.
+  AttnKV<DH> kv_first;
+  if (EARLY && b_guess < s_hi) {                          // wave-uniform
+    const int np = av.n_pages - 1;
+    const int4 pc = make_int4(min(max(pq_guess.x, 0), np), min(max(pq_guess.y, 0), np),
+                              min(max(pq_guess.z, 0), np), min(max(pq_guess.w, 0), np));
+    attn_load_kv<DH>(av, h, j, g, pc, kv_first);
+  }
+  float4 qraw[DC][2];
+  {
+    const float4* qp = reinterpret_cast<const float4*>(a.q + ((size_t)(V.row0 + r) * a.nq + head) * DH + g * 8);
+#pragma unroll
+    for (int c = 0; c < DC; ++c) { qraw[c][0] = qp[c * 8]; qraw[c][1] = qp[c * 8 + 1]; }
+  }
   const int ctx_max = kv_len + V.m;
   const int ctx = kv_len + r + 1;
   BPair qop[DC];
@@ -2237,7 +2253,11 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     qop[c] = have ? split8_f16(qv) : bzero();
   }
 
-  for (int sp = s_lo + wave; sp < s_hi; sp += a.wpb) {     // wave-uniform
+  // a wave runs at most one split: spw <= wpb (the fold takes at most
+  // kAttnFoldSplits <= 8 splits on 8 waves, the split kernel one on one)
+  static_assert(kAttnFoldSplits <= 8, "one split per wave");
+  const int sp = s_lo + wave;
+  if (sp < s_hi) {     // wave-uniform
     int lo = 0, hi = 0;
     if (have && sp < attn_ns(ctx)) {
       const int bps = attn_bps(ctx);
@@ -2256,12 +2276,16 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, l = 0.f;
 
-    int4 pq = (b_lo == b_guess) ? pq_guess : block_pages(b_lo < b_hi ? b_lo : 0);
-    for (int b = b_lo; b < b_hi; ++b) {
-      AttnKV<DH> kv;
-      attn_load_kv<DH>(av, h, j, g, pq, kv);
-      pq = block_pages(b + 1 < b_hi ? b + 1 : b);   // next block's pages, in flight during this block
-      attn_block_step<DH>(av, kv, qop, b, g, lo, hi, ctx_max, m, l, o);
+    if constexpr (EARLY) {
+      if (b_lo < b_hi) attn_block_step<DH>(av, kv_first, qop, b_guess, g, lo, hi, ctx_max, m, l, o);
+    } else {
+      int4 pq = (b_lo == b_guess) ? pq_guess : block_pages(b_lo < b_hi ? b_lo : 0);
+      for (int b = b_lo; b < b_hi; ++b) {
+        AttnKV<DH> kv;
+        attn_load_kv<DH>(av, h, j, g, pq, kv);
+        pq = block_pages(b + 1 < b_hi ? b + 1 : b);   // next block's pages, in flight during this block
+        attn_block_step<DH>(av, kv, qop, b, g, lo, hi, ctx_max, m, l, o);
+      }
     }
 
     // lane (g, j) holds o of q-row j for d = 16dt + 4g + v
@@ -2658,13 +2682,21 @@ hipError_t launch_attention(const AttnArgs& a_in, hipStream_t st) {
   a.sg_magic = div_magic(a.n_sg);
   const int n_wg = n_qt * a.n_sg;
   const dim3 grid(n_wg, a.nkv), block(64 * a.wpb);
+  // split kernel at most 64 splits: one block per split for every row, so
+  // the unit's K/V can go out ahead of q.  Measured on MI355X: 0.6B shape at
+  // 512-640 positions (10 splits) attention 250.3 -> 246.7 us per K = 4
+  // step; the LDS-fold kernel (2-3 splits) was slower with it (8B 271.5 ->
+  // 275.7, Gemma 239.7 -> 246.1 us), so it keeps its loads in the old order.
+  const bool early = a.n_split <= 64;
   if (a.dh == 128) {
-    if (a.final_fold) hipLaunchKernelGGL((k_attn_mfma<128, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_attn_mfma<128, false>), grid, block, 0, st, a);
+    if (a.final_fold) hipLaunchKernelGGL((k_attn_mfma<128, true, false>), grid, block, 0, st, a);
+    else if (early) hipLaunchKernelGGL((k_attn_mfma<128, false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_attn_mfma<128, false, false>), grid, block, 0, st, a);
     if (!a.final_fold) hipLaunchKernelGGL(k_attn_combine<128>, dim3(a.nq, a.M), dim3(256), 0, st, a);
   } else if (a.dh == 64) {
-    if (a.final_fold) hipLaunchKernelGGL((k_attn_mfma<64, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_attn_mfma<64, false>), grid, block, 0, st, a);
+    if (a.final_fold) hipLaunchKernelGGL((k_attn_mfma<64, true, false>), grid, block, 0, st, a);
+    else if (early) hipLaunchKernelGGL((k_attn_mfma<64, false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_attn_mfma<64, false, false>), grid, block, 0, st, a);
     if (!a.final_fold) hipLaunchKernelGGL(k_attn_combine<64>, dim3(a.nq, a.M), dim3(256), 0, st, a);
   } else {
     return hipErrorInvalidValue;
