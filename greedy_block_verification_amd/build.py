@@ -16,6 +16,9 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",
     "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
+    # the first 14 dwords of a kernel's arguments (pointers and scalars) go
+    # into SGPRs before its waves start
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

@@ -906,20 +906,32 @@ struct Int4rShared {
   float inv[16];
 };
 
+// The register-operand kernels take the fields they need before their first
+// loads as leading scalar arguments (SM packs S | M << 8): the library is
+// built so that the hardware loads the first 14 dwords of a kernel's
+// arguments (pointers and scalars; a struct is never preloaded) into SGPRs
+// before a wave starts, so no wave first waits on a scalar load of its
+// argument block.  G is the grid size.  The other fields stay in GemmArgs.
 template <int ROLE, int CPI, int IG>
-__global__ __launch_bounds__(768) void k_gemm_int4r(GemmArgs a) {
+__global__ __launch_bounds__(768) void k_gemm_int4r(const void* W, const void* Wscale, const uint16_t* bhi,
+                                                    const uint16_t* blo, unsigned long long* prof, int N, int K,
+                                                    int G, int SM, GemmArgs args) {
   constexpr int CPA = CPI < 2 ? CPI : 2;   // tiles whose activation operands are held at once
+  GemmArgs a = args;
+  a.W = W; a.Wscale = Wscale; a.bhi = bhi; a.blo = blo; a.prof = prof;
+  a.N = N; a.K = K; a.S = SM & 0xff; a.M = SM >> 8;
   __shared__ Int4rShared<IG> sh;
-  prof_start(a.prof);
   const int nw = a.S, nthr = 64 * a.S;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int KT = a.K >> 7;
   const int n_items = a.N >> 4;
-  const int n_my = (n_items - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;   // items of this workgroup, 1..IG
+  int n_my = 1;                            // items of this workgroup, 1..IG (compares, no division)
+#pragma unroll
+  for (int i = 1; i < IG; ++i) n_my += ((int)blockIdx.x + i * G < n_items) ? 1 : 0;
   int T[IG];
 #pragma unroll
-  for (int i = 0; i < IG; ++i) T[i] = (int)blockIdx.x + (i < n_my ? i : n_my - 1) * (int)gridDim.x;
+  for (int i = 0; i < IG; ++i) T[i] = (int)blockIdx.x + (i < n_my ? i : n_my - 1) * G;
   // codes and scales of every (tile position, item): tile kt = wave + nw c of item T_i
   const uint4* Wq = reinterpret_cast<const uint4*>(a.W) + lane;
   const uint2* Ws = reinterpret_cast<const uint2*>(a.Wscale) + g;
@@ -947,6 +959,9 @@ __global__ __launch_bounds__(768) void k_gemm_int4r(GemmArgs a) {
   BPair B[CPA][2][2];
 #pragma unroll
   for (int c = 0; c < CPA; ++c) act(c, B[c]);
+  // the start stamp once the loads are out (a few dozen instructions after
+  // entry): taken first, its wait on the clock read would hold them back
+  prof_start(a.prof);
   if (norm_role(ROLE))
     for (int rr = wave; rr < a.M; rr += nw) {
       const float v = row_inv_rms(a, rr, lane);
@@ -1018,10 +1033,10 @@ static hipError_t launch_int4r_ig(const GemmArgs& a, int grid, int ig, hipStream
   const dim3 block(64 * a.S), g(grid);
   if (ig > MAXIG) return hipErrorNotSupported;
   switch (ig) {
-    case 1: hipLaunchKernelGGL((k_gemm_int4r<ROLE, CPI, 1>), g, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_gemm_int4r<ROLE, CPI, (MAXIG >= 2 ? 2 : 1)>), g, block, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((k_gemm_int4r<ROLE, CPI, (MAXIG >= 3 ? 3 : 1)>), g, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_gemm_int4r<ROLE, CPI, (MAXIG >= 4 ? 4 : 1)>), g, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((k_gemm_int4r<ROLE, CPI, 1>), g, block, 0, st, a.W, a.Wscale, a.bhi, a.blo, a.prof, a.N, a.K, grid, a.S | (a.M << 8), a); break;
+    case 2: hipLaunchKernelGGL((k_gemm_int4r<ROLE, CPI, (MAXIG >= 2 ? 2 : 1)>), g, block, 0, st, a.W, a.Wscale, a.bhi, a.blo, a.prof, a.N, a.K, grid, a.S | (a.M << 8), a); break;
+    case 3: hipLaunchKernelGGL((k_gemm_int4r<ROLE, CPI, (MAXIG >= 3 ? 3 : 1)>), g, block, 0, st, a.W, a.Wscale, a.bhi, a.blo, a.prof, a.N, a.K, grid, a.S | (a.M << 8), a); break;
+    case 4: hipLaunchKernelGGL((k_gemm_int4r<ROLE, CPI, (MAXIG >= 4 ? 4 : 1)>), g, block, 0, st, a.W, a.Wscale, a.bhi, a.blo, a.prof, a.N, a.K, grid, a.S | (a.M << 8), a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1061,18 +1076,23 @@ struct Bf16rShared {
 };
 
 template <int ROLE, int CPW, int IG>
-__global__ __launch_bounds__(1024) void k_gemm_bf16r(GemmArgs a) {
+__global__ __launch_bounds__(1024) void k_gemm_bf16r(const void* W, const uint16_t* bhi, const uint16_t* blo,
+                                                     unsigned long long* prof, int N, int K, int S, int M, int G,
+                                                     GemmArgs args) {
+  GemmArgs a = args;
+  a.W = W; a.bhi = bhi; a.blo = blo; a.prof = prof; a.N = N; a.K = K; a.S = S; a.M = M;
   __shared__ Bf16rShared<IG> sh;
-  prof_start(a.prof);
   const int nw = a.S, nthr = 64 * a.S;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int KC = a.K >> 5;
   const int n_items = a.N >> 4;
-  const int n_my = (n_items - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;   // items of this workgroup, 1..IG
+  int n_my = 1;                            // items of this workgroup, 1..IG (compares, no division)
+#pragma unroll
+  for (int i = 1; i < IG; ++i) n_my += ((int)blockIdx.x + i * G < n_items) ? 1 : 0;
   int T[IG];
 #pragma unroll
-  for (int i = 0; i < IG; ++i) T[i] = (int)blockIdx.x + (i < n_my ? i : n_my - 1) * (int)gridDim.x;
+  for (int i = 0; i < IG; ++i) T[i] = (int)blockIdx.x + (i < n_my ? i : n_my - 1) * G;
   const uint4* W4 = reinterpret_cast<const uint4*>(a.W) + lane;
   uint4 A[CPW][IG];
 #pragma unroll
@@ -1083,6 +1103,7 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16r(GemmArgs a) {
   BPair B[CPW];
 #pragma unroll
   for (int c = 0; c < CPW; ++c) B[c] = load_planes(a, r, (wave + nw * c) * 32 + g * 8);
+  prof_start(a.prof);                      // once the loads are out (as in k_gemm_int4r)
   if (norm_role(ROLE))
     for (int rr = wave; rr < a.M; rr += nw) {
       const float v = row_inv_rms(a, rr, lane);
@@ -1135,9 +1156,9 @@ static hipError_t launch_bf16r_ig(const GemmArgs& a, int grid, int ig, hipStream
   const dim3 block(64 * a.S), g(grid);
   if (ig > MAXIG) return hipErrorNotSupported;
   switch (ig) {
-    case 1: hipLaunchKernelGGL((k_gemm_bf16r<ROLE, CPW, 1>), g, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_gemm_bf16r<ROLE, CPW, (MAXIG >= 2 ? 2 : 1)>), g, block, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((k_gemm_bf16r<ROLE, CPW, (MAXIG >= 3 ? 3 : 1)>), g, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((k_gemm_bf16r<ROLE, CPW, 1>), g, block, 0, st, a.W, a.bhi, a.blo, a.prof, a.N, a.K, a.S, a.M, grid, a); break;
+    case 2: hipLaunchKernelGGL((k_gemm_bf16r<ROLE, CPW, (MAXIG >= 2 ? 2 : 1)>), g, block, 0, st, a.W, a.bhi, a.blo, a.prof, a.N, a.K, a.S, a.M, grid, a); break;
+    case 3: hipLaunchKernelGGL((k_gemm_bf16r<ROLE, CPW, (MAXIG >= 3 ? 3 : 1)>), g, block, 0, st, a.W, a.bhi, a.blo, a.prof, a.N, a.K, a.S, a.M, grid, a); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();
