@@ -220,6 +220,12 @@ __device__ __forceinline__ float act_fn(float x, int act) {
 __device__ __forceinline__ void prof_start(unsigned long long* prof) {
   if (prof != nullptr && threadIdx.x == 0) atomicMin(prof, (unsigned long long)wall_clock64());
 }
+// The GEMM kernels read the clock at entry and publish the start once their
+// first loads are out: a wave that publishes first waits on the clock read
+// (and on the scalar load of the slot pointer) before it can issue them.
+__device__ __forceinline__ void prof_publish_start(unsigned long long* prof, unsigned long long t_start) {
+  if (prof != nullptr && threadIdx.x == 0) atomicMin(prof, t_start);
+}
 __device__ __forceinline__ void prof_end(unsigned long long* prof) {
   if (prof != nullptr) {
     __syncthreads();
@@ -672,12 +678,24 @@ struct ItemPlan {
 
 // bf16: wave w accumulates chunks w, w + NW, w + 2 NW, ... of each item in
 // that order (DBL: double-buffered stages of NB chunks per wave).
+// Leading (preloaded) arguments, as for the register-operand kernels: the
+// weights, activation planes and sums of squares, K, the grid size G and
+// three packed words (ring_pack): pA = M | pro_fast << 7 | waves << 8 |
+// cpi << 13 | n_stages << 23, pB = cs | cpws << 16, pC = n_full | n_half << 21.
 template <int TM, int ROLE, int NB, bool DBL>
-__global__ __launch_bounds__(1024) void k_gemm_bf16(GemmArgs a) {
+__global__ __launch_bounds__(1024) void k_gemm_bf16(const void* W, const uint16_t* bhi, const uint16_t* blo,
+                                                    const float* ss, int K, int G, unsigned pA, unsigned pB,
+                                                    unsigned pC, GemmArgs args) {
+  GemmArgs a = args;
+  a.W = W; a.bhi = bhi; a.blo = blo; a.ss = ss; a.K = K;
+  a.M = (int)(pA & 127u); a.pro_fast = (int)((pA >> 7) & 1u); a.cpi = (int)((pA >> 13) & 1023u);
+  a.n_stages = (int)(pA >> 23); a.cs = (int)(pB & 0xffffu); a.cpws = (int)(pB >> 16);
+  a.n_full = (int)(pC & 0x1fffffu); a.n_half = (int)(pC >> 21);
+  const unsigned long long t_start = wall_clock64();
+  __builtin_amdgcn_sched_barrier(0);       // (the clock read stays at entry)
   __shared__ GemmShared sh;
   __shared__ __align__(16) uint16_t stage_mem[kStageBytes / 2];
-  prof_start(a.prof);
-  const int nw = blockDim.x >> 6;
+  const int nw = (int)((pA >> 8) & 31u);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int KC = a.K >> 5;
@@ -695,7 +713,7 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16(GemmArgs a) {
     x.lo = x.hi + (size_t)a.M * stride;
     return x;
   };
-  const ItemPlan<ROLE> ip{a.n_full, a.n_half, (int)gridDim.x};
+  const ItemPlan<ROLE> ip{a.n_full, a.n_half, G};
   // packed weights are tile-major: chunk kc of tile T is the KiB at (T * KC + kc)
   const uint4* W4 = reinterpret_cast<const uint4*>(a.W);
   // this lane's uint4 inside chunk 0 of item o (a half item's other lanes load its own rows)
@@ -724,6 +742,7 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16(GemmArgs a) {
   uint4 A[NB];
 #pragma unroll
   for (int u = 0; u < NB; ++u) refill(A[u]);     // weights stream from here on (NB <= cpi)
+  prof_publish_start(a.prof, t_start);
   row_best_init<ROLE>(a, sh);
   if (fast) {
     prologue_finish(a, stage_buf(0), cs, 32, nw * 64, wave, lane, norm_role(ROLE), pr, sh);
@@ -920,6 +939,8 @@ __global__ __launch_bounds__(768) void k_gemm_int4r(const void* W, const void* W
   GemmArgs a = args;
   a.W = W; a.Wscale = Wscale; a.bhi = bhi; a.blo = blo; a.prof = prof;
   a.N = N; a.K = K; a.S = SM & 0xff; a.M = SM >> 8;
+  const unsigned long long t_start = wall_clock64();
+  __builtin_amdgcn_sched_barrier(0);       // (the clock read stays at entry)
   __shared__ Int4rShared<IG> sh;
   const int nw = a.S, nthr = 64 * a.S;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -959,9 +980,7 @@ __global__ __launch_bounds__(768) void k_gemm_int4r(const void* W, const void* W
   BPair B[CPA][2][2];
 #pragma unroll
   for (int c = 0; c < CPA; ++c) act(c, B[c]);
-  // the start stamp once the loads are out (a few dozen instructions after
-  // entry): taken first, its wait on the clock read would hold them back
-  prof_start(a.prof);
+  prof_publish_start(a.prof, t_start);
   if (norm_role(ROLE))
     for (int rr = wave; rr < a.M; rr += nw) {
       const float v = row_inv_rms(a, rr, lane);
@@ -1081,6 +1100,8 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16r(const void* W, const uint16
                                                      GemmArgs args) {
   GemmArgs a = args;
   a.W = W; a.bhi = bhi; a.blo = blo; a.prof = prof; a.N = N; a.K = K; a.S = S; a.M = M;
+  const unsigned long long t_start = wall_clock64();
+  __builtin_amdgcn_sched_barrier(0);       // (the clock read stays at entry)
   __shared__ Bf16rShared<IG> sh;
   const int nw = a.S, nthr = 64 * a.S;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -1103,7 +1124,7 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16r(const void* W, const uint16
   BPair B[CPW];
 #pragma unroll
   for (int c = 0; c < CPW; ++c) B[c] = load_planes(a, r, (wave + nw * c) * 32 + g * 8);
-  prof_start(a.prof);                      // once the loads are out (as in k_gemm_int4r)
+  prof_publish_start(a.prof, t_start);
   if (norm_role(ROLE))
     for (int rr = wave; rr < a.M; rr += nw) {
       const float v = row_inv_rms(a, rr, lane);
@@ -1342,6 +1363,23 @@ static void launch_grp(const GemmArgs& a, int grid, int per, hipStream_t st) {
   else if (IGM >= 2 && per >= 2) hipLaunchKernelGGL((k_gemm_grp<TM, ROLE, (IGM >= 2 ? 2 : 1), DB>), g, block, 0, st, a);
   else hipLaunchKernelGGL((k_gemm_grp<TM, ROLE, 1, DB>), g, block, 0, st, a);
 }
+// The packed leading arguments of k_gemm_bf16; false if a field does not fit
+// its bits (no supported shape comes near: M <= 64, at most 16 waves).
+struct RingPack {
+  unsigned a = 0, b = 0, c = 0;
+};
+static bool ring_pack(const GemmArgs& a, RingPack& p) {
+  if (a.M < 1 || a.M > 127 || a.S < 1 || a.S > 31 || a.cpi < 0 || a.cpi > 1023 || a.n_stages < 0 ||
+      a.n_stages > 511 || a.cs < 0 || a.cs > 0xffff || a.cpws < 0 || a.cpws > 0xffff || a.n_full < 0 ||
+      a.n_full > 0x1fffff || a.n_half < 0 || a.n_half > 2047 || (a.pro_fast != 0 && a.pro_fast != 1))
+    return false;
+  p.a = (unsigned)a.M | ((unsigned)a.pro_fast << 7) | ((unsigned)a.S << 8) | ((unsigned)a.cpi << 13) |
+        ((unsigned)a.n_stages << 23);
+  p.b = (unsigned)a.cs | ((unsigned)a.cpws << 16);
+  p.c = (unsigned)a.n_full | ((unsigned)a.n_half << 21);
+  return true;
+}
+
 template <int ROLE>
 static hipError_t gemm_dispatch_grp(const GemmArgs& a, int grid, hipStream_t st) {
   const int tm = (a.M + 15) / 16;
@@ -1366,6 +1404,8 @@ template <int ROLE, bool INT4, int NB>
 static hipError_t gemm_dispatch_nb(const GemmArgs& a, int grid, hipStream_t st, bool dbl) {
   const dim3 block(64 * a.S);
   const int tm = (a.M + 15) / 16;
+  RingPack rp;
+  if (!INT4 && !ring_pack(a, rp)) return hipErrorInvalidValue;
   if constexpr (INT4) {
     // only the (rows, ring depth) pairs gemm_ring_depth can pick are built
     switch (tm) {
@@ -1388,10 +1428,10 @@ static hipError_t gemm_dispatch_nb(const GemmArgs& a, int grid, hipStream_t st, 
     switch (tm) {
       case 1:
         if (dbl) {
-          if constexpr (NB == 4 || NB == 8) hipLaunchKernelGGL((k_gemm_bf16<1, ROLE, NB, true>), dim3(grid), block, 0, st, a);
+          if constexpr (NB == 4 || NB == 8) hipLaunchKernelGGL((k_gemm_bf16<1, ROLE, NB, true>), dim3(grid), block, 0, st, a.W, a.bhi, a.blo, a.ss, a.K, grid, rp.a, rp.b, rp.c, a);
           else return hipErrorInvalidValue;
         } else {
-          hipLaunchKernelGGL((k_gemm_bf16<1, ROLE, NB, false>), dim3(grid), block, 0, st, a);
+          hipLaunchKernelGGL((k_gemm_bf16<1, ROLE, NB, false>), dim3(grid), block, 0, st, a.W, a.bhi, a.blo, a.ss, a.K, grid, rp.a, rp.b, rp.c, a);
         }
         break;
       case 2:
@@ -1399,13 +1439,13 @@ static hipError_t gemm_dispatch_nb(const GemmArgs& a, int grid, hipStream_t st, 
           return hipErrorInvalidValue;
         } else {
           if (dbl) return hipErrorInvalidValue;
-          hipLaunchKernelGGL((k_gemm_bf16<2, ROLE, NB, false>), dim3(grid), block, 0, st, a);
+          hipLaunchKernelGGL((k_gemm_bf16<2, ROLE, NB, false>), dim3(grid), block, 0, st, a.W, a.bhi, a.blo, a.ss, a.K, grid, rp.a, rp.b, rp.c, a);
         }
         break;
       case 3:
         if constexpr (NB <= 4 && NB != 3) {
           if (dbl) return hipErrorInvalidValue;
-          hipLaunchKernelGGL((k_gemm_bf16<3, ROLE, NB, false>), dim3(grid), block, 0, st, a);
+          hipLaunchKernelGGL((k_gemm_bf16<3, ROLE, NB, false>), dim3(grid), block, 0, st, a.W, a.bhi, a.blo, a.ss, a.K, grid, rp.a, rp.b, rp.c, a);
         } else {
           return hipErrorInvalidValue;
         }
@@ -1413,7 +1453,7 @@ static hipError_t gemm_dispatch_nb(const GemmArgs& a, int grid, hipStream_t st, 
       case 4:
         if constexpr (NB == 1) {
           if (dbl) return hipErrorInvalidValue;
-          hipLaunchKernelGGL((k_gemm_bf16<4, ROLE, NB, false>), dim3(grid), block, 0, st, a);
+          hipLaunchKernelGGL((k_gemm_bf16<4, ROLE, NB, false>), dim3(grid), block, 0, st, a.W, a.bhi, a.blo, a.ss, a.K, grid, rp.a, rp.b, rp.c, a);
         } else {
           return hipErrorInvalidValue;
         }
@@ -2193,13 +2233,22 @@ __device__ __forceinline__ void attn_split_union(int kv_len, int r0, int r1, int
   }
 }
 
-template <int DH, bool FOLD, bool EARLY>
-__global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
+template <int DH, bool FOLD, bool EARLY, bool BATCH>
+__global__ __launch_bounds__(512) void k_attn_mfma(const float* q, const int* page_table, const int* params,
+                                                   const SeqDev* seqs, unsigned pk1, unsigned pk2, unsigned qt_magic,
+                                                   unsigned sg_magic, unsigned g_magic, AttnArgs args) {
   constexpr int DC = DH / 32;            // d chunks of the score MFMA
   constexpr int DT = DH / 16;            // d tiles of the P.V MFMA
   __shared__ AttnUnitLds<DH> ul[FOLD ? kAttnFoldSplits : 1];
-
-  prof_start(a.prof);
+  // preloaded leading arguments (attn_pack): everything the first loads need
+  AttnArgs a = args;
+  a.q = q; a.page_table = page_table; a.params = params; a.seqs = seqs;
+  a.n_qt = (int)(pk1 & 255u); a.n_sg = (int)((pk1 >> 8) & 255u); a.G = (int)((pk1 >> 16) & 31u);
+  a.spw = (int)((pk1 >> 21) & 7u); a.nkv = (int)(pk1 >> 24); a.nq = a.G * a.nkv;
+  a.M = (int)(pk2 & 127u); a.n_split = (int)((pk2 >> 7) & 255u); a.n_lpages = (int)(pk2 >> 15);
+  a.qt_magic = qt_magic; a.sg_magic = sg_magic; a.g_magic = g_magic;
+  const unsigned long long t_start = wall_clock64();
+  __builtin_amdgcn_sched_barrier(0);     // (the clock read stays at entry)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int G = a.G;
@@ -2226,7 +2275,9 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   }
   const int s_lo = sg * a.spw;
   const int s_hi = min(s_lo + a.spw, a.n_split);
-  const AttnView V = attn_view(a, qt);
+  // (BATCH: the launch has a sequence table; a single sequence takes no
+  // branch on it, so nothing waits on the table fields before the q loads)
+  const AttnView V = BATCH ? attn_view(a, qt) : AttnView{a, qt * 16, 0, a.M};
   const AttnArgs& av = V.av;
   const int n_qr = V.m * G;
   // this lane's q-row (independent of kv_len: its q loads go out first);
@@ -2241,7 +2292,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   // block (contexts up to 8192): fetch its pages before the context length is known
   const int b_guess = s_lo + wave;
   int4 pq_guess = block_pages(b_guess);
-  const int kv_len = attn_kv_len(a, qt);
+  const int kv_len = BATCH ? attn_kv_len(a, qt) : a.params[0];
   // EARLY (the launcher's choice for the split kernel of at most 64 splits):
   // every row then has one block per split (a row of two or more blocks per
   // split has at least 65 splits), so a unit is block b_guess or nothing.
@@ -2264,6 +2315,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
     for (int c = 0; c < DC; ++c) { qraw[c][0] = qp[c * 8]; qraw[c][1] = qp[c * 8 + 1]; }
   }
+  prof_publish_start(a.prof, t_start);
   const int ctx_max = kv_len + V.m;
   const int ctx = kv_len + r + 1;
   BPair qop[DC];
@@ -2612,7 +2664,10 @@ __global__ __launch_bounds__(256) void k_attn_rows2(AttnArgs a) {
 // context has up to 128 of them), then thread d folds output d in split order.
 // Launched with 256 threads.
 template <int DH>
-__global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
+__global__ __launch_bounds__(256) void k_attn_combine(float* part, const int* params, const SeqDev* seqs,
+                                                      const int* rowseq, int nq, int part_splits, AttnArgs args) {
+  AttnArgs a = args;                     // leading arguments preloaded (as in k_attn_mfma)
+  a.part = part; a.params = params; a.seqs = seqs; a.rowseq = rowseq; a.nq = nq; a.part_splits = part_splits;
   __shared__ float4 rec[kAttnMaxSplits * (DH + 4) / 4];
   const int j = blockIdx.x, r = blockIdx.y;
   int ctx = a.params[0] + r + 1;
@@ -2677,6 +2732,44 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   prof_end(a.prof);
 }
 
+// The packed leading arguments of k_attn_mfma: pk1 = n_qt | n_sg << 8 |
+// G << 16 | spw << 21 | nkv << 24, pk2 = M | n_split << 7 | n_lpages << 15;
+// false if a field does not fit its bits.
+static bool attn_pack(const AttnArgs& a, unsigned& pk1, unsigned& pk2) {
+  if (a.n_qt < 1 || a.n_qt > 255 || a.n_sg < 1 || a.n_sg > 255 || a.G < 1 || a.G > 31 || a.spw < 1 ||
+      a.spw > 7 || a.nkv < 1 || a.nkv > 255 || a.nq != a.G * a.nkv || a.M < 1 || a.M > 127 || a.n_split < 1 ||
+      a.n_split > 255 || a.n_lpages < 1 || a.n_lpages > 0x1ffff)
+    return false;
+  pk1 = (unsigned)a.n_qt | ((unsigned)a.n_sg << 8) | ((unsigned)a.G << 16) | ((unsigned)a.spw << 21) |
+        ((unsigned)a.nkv << 24);
+  pk2 = (unsigned)a.M | ((unsigned)a.n_split << 7) | ((unsigned)a.n_lpages << 15);
+  return true;
+}
+
+// The split kernel (LDS fold, early-K/V split or plain split; single sequence
+// or sequence table) and, without the fold, the combine pass.
+template <int DH>
+static bool launch_attn_split(const AttnArgs& a, dim3 grid, dim3 block, bool early, unsigned pk1, unsigned pk2,
+                              hipStream_t st) {
+  const bool batch = a.seqs != nullptr;
+#define SV_ATTN_LEAD a.q, a.page_table, a.params, a.seqs, pk1, pk2, a.qt_magic, a.sg_magic, a.g_magic, a
+  if (a.final_fold) {
+    if (batch) hipLaunchKernelGGL((k_attn_mfma<DH, true, false, true>), grid, block, 0, st, SV_ATTN_LEAD);
+    else hipLaunchKernelGGL((k_attn_mfma<DH, true, false, false>), grid, block, 0, st, SV_ATTN_LEAD);
+  } else if (early) {
+    if (batch) hipLaunchKernelGGL((k_attn_mfma<DH, false, true, true>), grid, block, 0, st, SV_ATTN_LEAD);
+    else hipLaunchKernelGGL((k_attn_mfma<DH, false, true, false>), grid, block, 0, st, SV_ATTN_LEAD);
+  } else {
+    if (batch) hipLaunchKernelGGL((k_attn_mfma<DH, false, false, true>), grid, block, 0, st, SV_ATTN_LEAD);
+    else hipLaunchKernelGGL((k_attn_mfma<DH, false, false, false>), grid, block, 0, st, SV_ATTN_LEAD);
+  }
+#undef SV_ATTN_LEAD
+  if (!a.final_fold)
+    hipLaunchKernelGGL(k_attn_combine<DH>, dim3(a.nq, a.M), dim3(256), 0, st, a.part, a.params, a.seqs, a.rowseq,
+                       a.nq, a.part_splits, a);
+  return true;
+}
+
 hipError_t launch_attention(const AttnArgs& a_in, hipStream_t st) {
   AttnArgs a = a_in;
   const int G = a.nq / a.nkv;
@@ -2709,16 +2802,12 @@ hipError_t launch_attention(const AttnArgs& a_in, hipStream_t st) {
   // step; the LDS-fold kernel (2-3 splits) was slower with it (8B 271.5 ->
   // 275.7, Gemma 239.7 -> 246.1 us), so it keeps its loads in the old order.
   const bool early = a.n_split <= 64;
+  unsigned pk1, pk2;
+  if (!attn_pack(a, pk1, pk2)) return hipErrorInvalidValue;
   if (a.dh == 128) {
-    if (a.final_fold) hipLaunchKernelGGL((k_attn_mfma<128, true, false>), grid, block, 0, st, a);
-    else if (early) hipLaunchKernelGGL((k_attn_mfma<128, false, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_attn_mfma<128, false, false>), grid, block, 0, st, a);
-    if (!a.final_fold) hipLaunchKernelGGL(k_attn_combine<128>, dim3(a.nq, a.M), dim3(256), 0, st, a);
+    if (!launch_attn_split<128>(a, grid, block, early, pk1, pk2, st)) return hipErrorInvalidValue;
   } else if (a.dh == 64) {
-    if (a.final_fold) hipLaunchKernelGGL((k_attn_mfma<64, true, false>), grid, block, 0, st, a);
-    else if (early) hipLaunchKernelGGL((k_attn_mfma<64, false, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_attn_mfma<64, false, false>), grid, block, 0, st, a);
-    if (!a.final_fold) hipLaunchKernelGGL(k_attn_combine<64>, dim3(a.nq, a.M), dim3(256), 0, st, a);
+    if (!launch_attn_split<64>(a, grid, block, early, pk1, pk2, st)) return hipErrorInvalidValue;
   } else {
     return hipErrorInvalidValue;
   }
