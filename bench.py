@@ -24,6 +24,7 @@ loop walks the prompts' speculative loops in order.  ``value`` = committed
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -71,6 +72,28 @@ def load_traffic(config, kernel_src_sha):
     return rec.get("traffic_bytes_per_launch")
 
 
+class GcPaused:
+    """Python's cyclic garbage collector stays out of a timed region: a full
+    pass over the harness's long-lived objects took tens of ms (0.1 ms per
+    step over a 400-step 0.6B run), host time that is not the method's.
+    ``collections`` counts the passes that ran inside anyway (0 expected)."""
+
+    def __enter__(self):
+        gc.collect()
+        gc.freeze()
+        self.was_on = gc.isenabled()
+        gc.disable()
+        self.before = sum(x["collections"] for x in gc.get_stats())
+        return self
+
+    def __exit__(self, *exc):
+        self.collections = sum(x["collections"] for x in gc.get_stats()) - self.before
+        if self.was_on:
+            gc.enable()
+        gc.unfreeze()
+        return False
+
+
 def run_spec(sessions, truth, prompt_len, gen, k, srcs, n_steps, profile_mask=0):
     """Walk the prompts' speculative loops for exactly n_steps verify calls."""
     from greedy_block_verification_amd import binding as B
@@ -81,34 +104,36 @@ def run_spec(sessions, truth, prompt_len, gen, k, srcs, n_steps, profile_mask=0)
     done = [0] * len(sessions)
     for s in sessions:
         B.sv_set_profile(s.ctx, profile_mask)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(n_steps):
-        s, c = sessions[p], done[p]
-        k_eff = min(k, gen - c - 1)
-        window = truth[p][c + 1: c + 1 + k_eff]
-        drafts = srcs[p].window(window, k_eff) if k_eff > 0 else []
-        cur = s.next_id
-        kv = s.kv_len
-        t_step = time.perf_counter()
-        n, _ = B.sv_verify(s.ctx, kv, drafts)   # returns once the step's result is on the host
-        st["step_s"].append(time.perf_counter() - t_step)
-        new = [cur] + drafts[:n]
-        st["mism"] += sum(int(a != b) for a, b in zip(new, truth[p][c: c + n + 1]))
-        st["tokens"] += n + 1
-        st["accepted"] += n
-        st["proposed"] += k_eff
-        st["rows"] += k_eff + 1
-        st["steps"].append((k_eff, n, kv))
-        done[p] = c + n + 1
-        if done[p] >= gen:
-            st["finished"] += 1
-            st["matched"] += int(done[p] == gen)
-            s.truncate(prompt_len)
-            done[p] = 0
-            p = (p + 1) % len(sessions)
-    torch.cuda.synchronize()
-    st["seconds"] = time.perf_counter() - t0
+    with GcPaused() as pause:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n_steps):
+            s, c = sessions[p], done[p]
+            k_eff = min(k, gen - c - 1)
+            window = truth[p][c + 1: c + 1 + k_eff]
+            drafts = srcs[p].window(window, k_eff) if k_eff > 0 else []
+            cur = s.next_id
+            kv = s.kv_len
+            t_step = time.perf_counter()
+            n, _ = B.sv_verify(s.ctx, kv, drafts)   # returns once the step's result is on the host
+            st["step_s"].append(time.perf_counter() - t_step)
+            new = [cur] + drafts[:n]
+            st["mism"] += sum(int(a != b) for a, b in zip(new, truth[p][c: c + n + 1]))
+            st["tokens"] += n + 1
+            st["accepted"] += n
+            st["proposed"] += k_eff
+            st["rows"] += k_eff + 1
+            st["steps"].append((k_eff, n, kv))
+            done[p] = c + n + 1
+            if done[p] >= gen:
+                st["finished"] += 1
+                st["matched"] += int(done[p] == gen)
+                s.truncate(prompt_len)
+                done[p] = 0
+                p = (p + 1) % len(sessions)
+        torch.cuda.synchronize()
+        st["seconds"] = time.perf_counter() - t0
+    st["gc_collections"] = pause.collections
     for s in sessions:
         B.sv_set_profile(s.ctx, 0)
     # leave every session at its prompt for the next run
@@ -167,38 +192,39 @@ def run_spec_batch(sessions, truth, prompt_len, gen, k, srcs, n_steps):
           "rows": 0, "steps": []}
     done = [0] * len(sessions)
     ctxs = [s.ctx for s in sessions]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(n_steps):
-        drafts, kvs, curs = [], [], []
-        for i, s in enumerate(sessions):
-            c = done[i]
-            k_eff = min(k, gen - c - 1)
-            window = truth[i][c + 1: c + 1 + k_eff]
-            drafts.append(srcs[i].window(window, k_eff) if k_eff > 0 else [])
-            kvs.append(s.kv_len)
-            curs.append(s.next_id)
-        res = B.sv_verify_batch(ctxs, kvs, drafts)
-        row_steps = []
-        for i, s in enumerate(sessions):
-            n, _ = res[i]
-            c = done[i]
-            new = [curs[i]] + drafts[i][:n]
-            st["mism"] += sum(int(a != b) for a, b in zip(new, truth[i][c: c + n + 1]))
-            st["tokens"] += n + 1
-            st["accepted"] += n
-            st["proposed"] += len(drafts[i])
-            st["rows"] += len(drafts[i]) + 1
-            row_steps.append((len(drafts[i]), n, kvs[i]))
-            done[i] = c + n + 1
-            if done[i] >= gen:
-                st["finished"] += 1
-                st["matched"] += int(done[i] == gen)
-                s.truncate(prompt_len)
-                done[i] = 0
-        st["steps"].append(row_steps)
-    torch.cuda.synchronize()
-    st["seconds"] = time.perf_counter() - t0
+    with GcPaused() as pause:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n_steps):
+            drafts, kvs, curs = [], [], []
+            for i, s in enumerate(sessions):
+                c = done[i]
+                k_eff = min(k, gen - c - 1)
+                window = truth[i][c + 1: c + 1 + k_eff]
+                drafts.append(srcs[i].window(window, k_eff) if k_eff > 0 else [])
+                kvs.append(s.kv_len)
+                curs.append(s.next_id)
+            res = B.sv_verify_batch(ctxs, kvs, drafts)
+            row_steps = []
+            for i, s in enumerate(sessions):
+                n, _ = res[i]
+                c = done[i]
+                new = [curs[i]] + drafts[i][:n]
+                st["mism"] += sum(int(a != b) for a, b in zip(new, truth[i][c: c + n + 1]))
+                st["tokens"] += n + 1
+                st["accepted"] += n
+                st["proposed"] += len(drafts[i])
+                st["rows"] += len(drafts[i]) + 1
+                row_steps.append((len(drafts[i]), n, kvs[i]))
+                done[i] = c + n + 1
+                if done[i] >= gen:
+                    st["finished"] += 1
+                    st["matched"] += int(done[i] == gen)
+                    s.truncate(prompt_len)
+                    done[i] = 0
+            st["steps"].append(row_steps)
+        torch.cuda.synchronize()
+        st["seconds"] = time.perf_counter() - t0
     for s in sessions:
         if s.kv_len != prompt_len:
             s.truncate(prompt_len)
@@ -254,22 +280,23 @@ def run_draft_loop(args, cfg, sessions, truth, prompts, L, G, decode_tpot_ms):
             loops = [DraftLoop(sessions[p], dsess[p], proposer_for(p)) for p in range(P)]
             tokens = mism = 0
             p = 0
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(args.sweep_steps):
-                c = done[p]
-                k_eff = min(k, G - c - 1)
-                got = loops[p].step(k_eff)
-                mism += sum(int(a != b) for a, b in zip(got, truth[p][c: c + len(got)]))
-                tokens += len(got)
-                done[p] = c + len(got)
-                if done[p] >= G:
-                    sessions[p].truncate(L)
-                    dsess[p].truncate(L)
-                    done[p] = 0
-                    p = (p + 1) % P
-            torch.cuda.synchronize()
-            sec = time.perf_counter() - t0
+            with GcPaused() as pause:
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(args.sweep_steps):
+                    c = done[p]
+                    k_eff = min(k, G - c - 1)
+                    got = loops[p].step(k_eff)
+                    mism += sum(int(a != b) for a, b in zip(got, truth[p][c: c + len(got)]))
+                    tokens += len(got)
+                    done[p] = c + len(got)
+                    if done[p] >= G:
+                        sessions[p].truncate(L)
+                        dsess[p].truncate(L)
+                        done[p] = 0
+                        p = (p + 1) % P
+                torch.cuda.synchronize()
+                sec = time.perf_counter() - t0
             for q in range(P):
                 if sessions[q].kv_len != L:
                     sessions[q].truncate(L)
@@ -445,15 +472,16 @@ def main():
     # the plain-decode baseline, timed on contexts whose graphs the pass above
     # captured (as the verify steps are timed on warm contexts)
     n_dec = min(P, 8)
-    torch.cuda.synchronize()
-    t = time.perf_counter()
-    for p in range(n_dec):
-        x = truth[p][0]
-        for _ in range(G):
-            x = sessions[p].decode_step(x)
-        sessions[p].truncate(L)
-    torch.cuda.synchronize()
-    t_decode = time.perf_counter() - t
+    with GcPaused():
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for p in range(n_dec):
+            x = truth[p][0]
+            for _ in range(G):
+                x = sessions[p].decode_step(x)
+            sessions[p].truncate(L)
+        torch.cuda.synchronize()
+        t_decode = time.perf_counter() - t
     decode_tpot_ms = 1000.0 * t_decode / (n_dec * G)
     log(f"[bench] {P} prompts ready; baseline decode {decode_tpot_ms:.3f} ms/token")
 
@@ -521,6 +549,13 @@ def main():
         "tokens_per_target_step": round(st["tokens"] / args.steps, 4),
         "step_ms_median": round(1000.0 * float(np.median(st["step_s"])), 4),
         "step_ms_p90": round(1000.0 * float(np.percentile(st["step_s"], 90)), 4),
+        "step_ms_max": round(1000.0 * float(np.max(st["step_s"])), 4),
+        # time of the timed region spent outside the verify calls (host loop)
+        "host_ms_per_step": round(1000.0 * (st["seconds"] - float(np.sum(st["step_s"]))) / args.steps, 4),
+        # verify calls over 3x the median (a first-use graph capture shows here)
+        "gc_collections_in_timed_region": st["gc_collections"],
+        "slow_steps": int(np.sum(np.asarray(st["step_s"]) > 3.0 * float(np.median(st["step_s"])))),
+        "slow_steps_ms": round(1000.0 * float(np.sum(np.asarray(st["step_s"])[np.asarray(st["step_s"]) > 3.0 * float(np.median(st["step_s"]))])), 3),
         "verify_steps": args.steps, "decode_steps": n_dec * G,
         "rows_scored_per_s": round(st["rows"] / st["seconds"], 1),
         "step_hbm_gbs": round(step_bytes / st["seconds"] / 1e9, 1),
