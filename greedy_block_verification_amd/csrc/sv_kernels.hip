@@ -233,6 +233,17 @@ __device__ __forceinline__ void prof_end(unsigned long long* prof) {
   }
 }
 
+// n / d for n >= 0 and n * d < 2^32, as the high word of n * m with
+// m = ceil(2^32 / d) = (2^32 + e) / d, 0 <= e < d: n m / 2^32 = n / d + n e /
+// (d 2^32), and n e / (d 2^32) < n / 2^32 < 1 / d, which never carries the
+// quotient past the next integer.  d = 1 takes n itself (m would not fit).
+inline unsigned div_magic(int d) {
+  return d <= 1 ? 0u : (unsigned)((0x100000000ull + (unsigned)d - 1u) / (unsigned)d);
+}
+__device__ __forceinline__ int div_m(int n, int d, unsigned magic) {
+  return d == 1 ? n : (int)__umulhi((unsigned)n, magic);
+}
+
 constexpr int kMaxWaves = 16;
 constexpr int kStageBytes = kGemmStageBytes;   // LDS for staged activation planes (hi + lo)
 
@@ -818,11 +829,18 @@ struct Int4Slot {
 };
 
 template <int TM, int ROLE, int NB>
-__global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
+__global__ __launch_bounds__(1024) void k_gemm_int4(const void* W, const void* Wscale, const uint16_t* bhi,
+                                                    const uint16_t* blo, const float* ss, int K, int G, unsigned pA,
+                                                    unsigned pB, GemmArgs args) {
+  GemmArgs a = args;                    // leading arguments preloaded (ring_pack, as in k_gemm_bf16)
+  a.W = W; a.Wscale = Wscale; a.bhi = bhi; a.blo = blo; a.ss = ss; a.K = K;
+  a.M = (int)(pA & 127u); a.cpi = (int)((pA >> 13) & 1023u); a.n_stages = (int)(pA >> 23);
+  a.cs = (int)(pB & 0xffffu); a.cpws = (int)(pB >> 16);
+  const unsigned long long t_start = wall_clock64();
+  __builtin_amdgcn_sched_barrier(0);       // (the clock read stays at entry)
   __shared__ GemmShared sh;
   __shared__ __align__(16) uint16_t stage_mem[kStageBytes / 2];
-  prof_start(a.prof);
-  const int nw = blockDim.x >> 6;
+  const int nw = (int)((pA >> 8) & 31u);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int KT = a.K >> 7;                 // 128-input tiles
@@ -846,19 +864,20 @@ __global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
     cur.off += nw;
     if (++cur.c == cpi) {
       cur.c = 0;
-      cur.T += gridDim.x;
+      cur.T += G;
       cur.off = (size_t)cur.T * KT + wave;
     }
   };
   Int4Slot Q[NB];
 #pragma unroll
   for (int u = 0; u < NB; ++u) refill(Q[u]);
+  prof_publish_start(a.prof, t_start);
   if (norm_role(ROLE)) rows_inv_rms(a, sh, wave, lane, nw);
   if (n_stages == 1) {
     stage_planes(a, st, 0, cs, 128);
     __syncthreads();
   }
-  for (int T = blockIdx.x; T < n_items; T += gridDim.x) {
+  for (int T = blockIdx.x; T < n_items; T += G) {
     const EpiPre pre = epi_load<ROLE>(a, T, threadIdx.x);
     f32x4 acc[TM];
 #pragma unroll
@@ -895,7 +914,7 @@ __global__ __launch_bounds__(1024) void k_gemm_int4(GemmArgs a) {
         if (refills) refill(Q[u]);
       }
       };
-      if (T + (int)gridDim.x < n_items || c0 + NB < cpi) group(true);
+      if (T + G < n_items || c0 + NB < cpi) group(true);
       else group(false);
       cl0 += NB;
       if (cl0 == cpws) { cl0 = 0; ++si; }
@@ -1229,11 +1248,15 @@ __host__ __device__ __forceinline__ int grp_mode(int M, int waves) {
 }
 
 template <int TM, int ROLE, int IG, bool DB>
-__global__ __launch_bounds__(1024) void k_gemm_grp(GemmArgs a) {
+__global__ __launch_bounds__(1024) void k_gemm_grp(const void* W, const uint16_t* bhi, const uint16_t* blo, int N,
+                                                   int K, int M, int S, int G, unsigned g_magic, GemmArgs args) {
   constexpr int NREG = DB ? 5 : 8;
+  GemmArgs a = args;                    // leading arguments preloaded (as in k_gemm_bf16)
+  a.W = W; a.bhi = bhi; a.blo = blo; a.N = N; a.K = K; a.M = M; a.S = S;
+  const unsigned long long t_start = wall_clock64();
+  __builtin_amdgcn_sched_barrier(0);       // (the clock read stays at entry)
   __shared__ GemmShared sh;
   __shared__ __align__(16) uint16_t stage_mem[kStageBytes / 2];
-  prof_start(a.prof);
   const int nw = a.S, nthr = 64 * a.S;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
@@ -1275,12 +1298,12 @@ __global__ __launch_bounds__(1024) void k_gemm_grp(GemmArgs a) {
     }
   };
   const int n_items = a.N >> 4;
-  const int n_my = (n_items - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;   // items of this workgroup (>= 1)
+  const int n_my = div_m(n_items - 1 - (int)blockIdx.x, G, g_magic) + 1;   // items of this workgroup (>= 1)
   const int n_grp = (n_my + IG - 1) / IG;
   const uint4* W4 = reinterpret_cast<const uint4*>(a.W) + lane;
   auto item_of = [&](int grp, int ig) {
     const int k = grp * IG + ig;
-    return (int)blockIdx.x + (k < n_my ? k : n_my - 1) * (int)gridDim.x;
+    return (int)blockIdx.x + (k < n_my ? k : n_my - 1) * G;
   };
   auto chunk = [&](int grp, int s, int ig) {   // chunk wave + nw s of slot ig's item
     return ld_stream(W4 + ((size_t)item_of(grp, ig) * KC + wave + (size_t)nw * s) * 64);
@@ -1290,6 +1313,7 @@ __global__ __launch_bounds__(1024) void k_gemm_grp(GemmArgs a) {
   uint4 A[IG];
 #pragma unroll
   for (int ig = 0; ig < IG; ++ig) A[ig] = chunk(0, 0, ig);
+  prof_publish_start(a.prof, t_start);
   row_best_init<ROLE>(a, sh);
   if (norm_role(ROLE)) rows_inv_rms(a, sh, wave, lane, nw);   // read only by the epilogue
   store(stage_buf(0), sr);
@@ -1359,9 +1383,9 @@ static void launch_grp(const GemmArgs& a, int grid, int per, hipStream_t st) {
   // single-buffered stages hold 8 registers of planes: groups of two fit the LM head's three row tiles only
   constexpr int IGM = DB ? grp_max_items<TM, ROLE>() : (TM == 3 && ROLE == kRoleLmHead ? 2 : 1);
   const dim3 block(64 * a.S), g(grid);
-  if (IGM >= 4 && per >= 4) hipLaunchKernelGGL((k_gemm_grp<TM, ROLE, (IGM >= 4 ? 4 : 1), DB>), g, block, 0, st, a);
-  else if (IGM >= 2 && per >= 2) hipLaunchKernelGGL((k_gemm_grp<TM, ROLE, (IGM >= 2 ? 2 : 1), DB>), g, block, 0, st, a);
-  else hipLaunchKernelGGL((k_gemm_grp<TM, ROLE, 1, DB>), g, block, 0, st, a);
+  if (IGM >= 4 && per >= 4) hipLaunchKernelGGL((k_gemm_grp<TM, ROLE, (IGM >= 4 ? 4 : 1), DB>), g, block, 0, st, a.W, a.bhi, a.blo, a.N, a.K, a.M, a.S, grid, div_magic(grid), a);
+  else if (IGM >= 2 && per >= 2) hipLaunchKernelGGL((k_gemm_grp<TM, ROLE, (IGM >= 2 ? 2 : 1), DB>), g, block, 0, st, a.W, a.bhi, a.blo, a.N, a.K, a.M, a.S, grid, div_magic(grid), a);
+  else hipLaunchKernelGGL((k_gemm_grp<TM, ROLE, 1, DB>), g, block, 0, st, a.W, a.bhi, a.blo, a.N, a.K, a.M, a.S, grid, div_magic(grid), a);
 }
 // The packed leading arguments of k_gemm_bf16; false if a field does not fit
 // its bits (no supported shape comes near: M <= 64, at most 16 waves).
@@ -1405,21 +1429,21 @@ static hipError_t gemm_dispatch_nb(const GemmArgs& a, int grid, hipStream_t st, 
   const dim3 block(64 * a.S);
   const int tm = (a.M + 15) / 16;
   RingPack rp;
-  if (!INT4 && !ring_pack(a, rp)) return hipErrorInvalidValue;
+  if (!ring_pack(a, rp)) return hipErrorInvalidValue;
   if constexpr (INT4) {
     // only the (rows, ring depth) pairs gemm_ring_depth can pick are built
     switch (tm) {
-      case 1: hipLaunchKernelGGL((k_gemm_int4<1, ROLE, NB>), dim3(grid), block, 0, st, a); break;
+      case 1: hipLaunchKernelGGL((k_gemm_int4<1, ROLE, NB>), dim3(grid), block, 0, st, a.W, a.Wscale, a.bhi, a.blo, a.ss, a.K, grid, rp.a, rp.b, a); break;
       case 2:
-        if constexpr (NB <= 2) hipLaunchKernelGGL((k_gemm_int4<2, ROLE, NB>), dim3(grid), block, 0, st, a);
+        if constexpr (NB <= 2) hipLaunchKernelGGL((k_gemm_int4<2, ROLE, NB>), dim3(grid), block, 0, st, a.W, a.Wscale, a.bhi, a.blo, a.ss, a.K, grid, rp.a, rp.b, a);
         else return hipErrorInvalidValue;
         break;
       case 3:
-        if constexpr (NB == 1) hipLaunchKernelGGL((k_gemm_int4<3, ROLE, NB>), dim3(grid), block, 0, st, a);
+        if constexpr (NB == 1) hipLaunchKernelGGL((k_gemm_int4<3, ROLE, NB>), dim3(grid), block, 0, st, a.W, a.Wscale, a.bhi, a.blo, a.ss, a.K, grid, rp.a, rp.b, a);
         else return hipErrorInvalidValue;
         break;
       case 4:
-        if constexpr (NB == 1) hipLaunchKernelGGL((k_gemm_int4<4, ROLE, NB>), dim3(grid), block, 0, st, a);
+        if constexpr (NB == 1) hipLaunchKernelGGL((k_gemm_int4<4, ROLE, NB>), dim3(grid), block, 0, st, a.W, a.Wscale, a.bhi, a.blo, a.ss, a.K, grid, rp.a, rp.b, a);
         else return hipErrorInvalidValue;
         break;
       default: return hipErrorInvalidValue;
@@ -1989,16 +2013,6 @@ __host__ __device__ __forceinline__ int attn_ns(int ctx) {
   return bps == 1 ? nb : (nb + bps - 1) / bps;   // (contexts up to 8192 skip the division)
 }
 
-// n / d for n >= 0 and n * d < 2^32, as the high word of n * m with
-// m = ceil(2^32 / d) = (2^32 + e) / d, 0 <= e < d: n m / 2^32 = n / d + n e /
-// (d 2^32), and n e / (d 2^32) < n / 2^32 < 1 / d, which never carries the
-// quotient past the next integer.  d = 1 takes n itself (m would not fit).
-inline unsigned div_magic(int d) {
-  return d <= 1 ? 0u : (unsigned)((0x100000000ull + (unsigned)d - 1u) / (unsigned)d);
-}
-__device__ __forceinline__ int div_m(int n, int d, unsigned magic) {
-  return d == 1 ? n : (int)__umulhi((unsigned)n, magic);
-}
 int attn_splits(int ctx) { return attn_ns(ctx); }
 // The split count is not monotone in ctx (ctx 8192: 128 one-block splits;
 // ctx 8193: 65 two-block splits), so a launch covers the most splits of any
