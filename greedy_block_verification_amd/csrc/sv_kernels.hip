@@ -818,6 +818,97 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16(const void* W, const uint16_
   prof_end(a.prof);
 }
 
+// bf16, one row tile, each wave's activation operands held in registers:
+// wave w only multiplies the input columns of its chain's chunks (w, w + S,
+// ...), the same for every item, so it loads those CPW operand pairs once and
+// the weight ring streams the workgroup's items through them, with no LDS
+// stage and no restaging per item (k_gemm_bf16 restages every item once the
+// rows' planes outgrow one stage).  The item plan, the ring, the sums (chain
+// w over its chunks in order, hi plane before lo plane, the chain sums met in
+// LDS in chain order) and the epilogue are k_gemm_bf16's.  Leading arguments
+// as k_gemm_bf16's (pA, pC of ring_pack).
+template <int ROLE, int NB, int CPW>
+__global__ __launch_bounds__(1024) void k_gemm_bf16rb(const void* W, const uint16_t* bhi, const uint16_t* blo,
+                                                      const float* ss, int K, int G, unsigned pA, unsigned pC,
+                                                      GemmArgs args) {
+  static_assert(CPW % NB == 0, "the ring depth divides the chunks per wave");
+  GemmArgs a = args;
+  a.W = W; a.bhi = bhi; a.blo = blo; a.ss = ss; a.K = K;
+  a.M = (int)(pA & 127u); a.n_full = (int)(pC & 0x1fffffu); a.n_half = (int)(pC >> 21);
+  const unsigned long long t_start = wall_clock64();
+  __builtin_amdgcn_sched_barrier(0);       // (the clock read stays at entry)
+  __shared__ GemmShared sh;
+  const int nw = (int)((pA >> 8) & 31u);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int j = lane & 15, g = lane >> 4;
+  const int KC = a.K >> 5;
+  const ItemPlan<ROLE> ip{a.n_full, a.n_half, G};
+  const uint4* W4 = reinterpret_cast<const uint4*>(a.W);
+  auto item_off = [&](int o) {                 // (as in k_gemm_bf16)
+    int hf;
+    const int T = max(ip.tile(o, hf), 0);
+    const int ln = hf < 0 ? lane : ((lane & ~8) | (hf << 3));
+    return ((size_t)T * KC + wave) * 64 + ln;
+  };
+  LoadCursor cur{0, 0, item_off(0)};
+  auto refill = [&](uint4& slot) {
+    slot = ld_stream(W4 + cur.off);
+    cur.off += (size_t)nw * 64;
+    if (++cur.c == CPW) {
+      cur.c = 0;
+      cur.T += 1;
+      cur.off = item_off(cur.T);
+    }
+  };
+  // this wave's activation operands (row j, clamped), then the row sums of
+  // squares (norm roles), then the weights: a wait on the first two never
+  // holds the weight ring
+  const int r = row_of(j, a.M);
+  BPair B[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) B[c] = load_planes(a, r, (wave + nw * c) * 32 + g * 8);
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (norm_role(ROLE) && wave < a.M) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) s[t] = ss_load(a, wave, lane, t);
+  }
+  uint4 A[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) refill(A[u]);
+  prof_publish_start(a.prof, t_start);
+  row_best_init<ROLE>(a, sh);
+  if (norm_role(ROLE) && wave < a.M) {
+    // the same order as rows_inv_rms: each lane adds its slices in order (the
+    // zeros past the row's slices add exactly nothing), then the butterfly
+    float v = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v = v + s[t];
+    v = wave_sum(v);
+    if (lane == 0) sh.inv[wave] = 1.0f / sqrtf(v / (float)a.K + a.eps);
+  }
+  for (int o = 0;; ++o) {
+    int hf;
+    const int T = ip.tile(o, hf);
+    if (T < 0) break;
+    const EpiPre pre = epi_load<ROLE>(a, T, threadIdx.x);
+    f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+    auto group = [&](int c0, bool refills) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        acc[0] = mfma_pair(A[u], B[c0 + u], acc[0]);
+        if (refills) refill(A[u]);
+      }
+    };
+#pragma unroll
+    for (int c0 = 0; c0 + NB < CPW; c0 += NB) group(c0, true);
+    if (ip.has_next(T, hf)) group(CPW - NB, true);
+    else group(CPW - NB, false);                 // the last NB chunks of this workgroup
+    gemm_finish<1, ROLE>(a, sh, acc, T, wave, lane, nw, pre, hf);
+  }
+  row_best_publish<ROLE>(a, sh);
+  prof_end(a.prof);
+}
+
 // int4 weights: wave w takes 128-input tiles w, w + NW, ...; per row tile and
 // per scale group, the MFMAs over the group's 64 inputs (hi and lo planes of
 // each 32-input chunk) start from zero; the group sum is then scaled by the
@@ -937,11 +1028,11 @@ __global__ __launch_bounds__(1024) void k_gemm_int4(const void* W, const void* W
 // summed from zero over its two 32-input chunks (hi plane before lo plane)
 // and added to the chain sum scaled by the group scale; the chain sums meet
 // in LDS in chain order.
-template <int IG>
+template <int IG, int TM>
 struct Int4rShared {
-  f32x4 red[IG][kMaxWaves][64];
-  float y[IG][16][16];
-  float inv[16];
+  f32x4 red[IG * TM][kMaxWaves][64];
+  float y[IG][16 * TM][16];
+  float inv[16 * TM];
 };
 
 // The register-operand kernels take the fields they need before their first
@@ -950,17 +1041,18 @@ struct Int4rShared {
 // arguments (pointers and scalars; a struct is never preloaded) into SGPRs
 // before a wave starts, so no wave first waits on a scalar load of its
 // argument block.  G is the grid size.  The other fields stay in GemmArgs.
-template <int ROLE, int CPI, int IG>
+template <int ROLE, int CPI, int IG, int TM>
 __global__ __launch_bounds__(768) void k_gemm_int4r(const void* W, const void* Wscale, const uint16_t* bhi,
                                                     const uint16_t* blo, unsigned long long* prof, int N, int K,
                                                     int G, int SM, GemmArgs args) {
-  constexpr int CPA = CPI < 2 ? CPI : 2;   // tiles whose activation operands are held at once
+  // tiles whose activation operands are held at once (one with two row tiles)
+  constexpr int CPA = TM == 2 ? 1 : (CPI < 2 ? CPI : 2);
   GemmArgs a = args;
   a.W = W; a.Wscale = Wscale; a.bhi = bhi; a.blo = blo; a.prof = prof;
   a.N = N; a.K = K; a.S = SM & 0xff; a.M = SM >> 8;
   const unsigned long long t_start = wall_clock64();
   __builtin_amdgcn_sched_barrier(0);       // (the clock read stays at entry)
-  __shared__ Int4rShared<IG> sh;
+  __shared__ Int4rShared<IG, TM> sh;
   const int nw = a.S, nthr = 64 * a.S;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
@@ -986,17 +1078,19 @@ __global__ __launch_bounds__(768) void k_gemm_int4r(const void* W, const void* W
       s0[c][i] = Ws[off * 8];
       s1[c][i] = Ws[off * 8 + 4];
     }
-  // this lane's activation operands of a tile: row j (clamped), inputs
+  // this lane's activation operands of a tile: row 16 rt + j (clamped), inputs
   // kt*128 + 64 gq + 32 h + 8 g .. +7, hi and lo planes
-  const int r = row_of(j, a.M);
-  auto act = [&](int c, BPair (&B)[2][2]) {
+  auto act = [&](int c, BPair (&B)[TM][2][2]) {
     const int kt = wave + nw * c;
 #pragma unroll
-    for (int gq = 0; gq < 2; ++gq)
+    for (int rt = 0; rt < TM; ++rt)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) B[gq][h] = load_planes(a, r, kt * 128 + gq * 64 + h * 32 + g * 8);
+      for (int gq = 0; gq < 2; ++gq)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          B[rt][gq][h] = load_planes(a, row_of(rt * 16 + j, a.M), kt * 128 + gq * 64 + h * 32 + g * 8);
   };
-  BPair B[CPA][2][2];
+  BPair B[CPA][TM][2][2];
 #pragma unroll
   for (int c = 0; c < CPA; ++c) act(c, B[c]);
   prof_publish_start(a.prof, t_start);
@@ -1009,12 +1103,14 @@ __global__ __launch_bounds__(768) void k_gemm_int4r(const void* W, const void* W
   const int per_item = a.M * 16;
   const int i_pre = (int)threadIdx.x / per_item;
   const EpiPre pre = epi_load<ROLE>(a, T[i_pre < n_my ? i_pre : 0], (int)threadIdx.x - i_pre * per_item);
-  f32x4 acc[IG];
+  f32x4 acc[IG][TM];
 #pragma unroll
-  for (int i = 0; i < IG; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < IG; ++i)
+#pragma unroll
+    for (int rt = 0; rt < TM; ++rt) acc[i][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < CPI; ++c) {
-    BPair (&Bc)[2][2] = B[c % CPA];
+    BPair (&Bc)[TM][2][2] = B[c % CPA];
 #pragma unroll
     for (int i = 0; i < IG; ++i)
 #pragma unroll
@@ -1023,23 +1119,30 @@ __global__ __launch_bounds__(768) void k_gemm_int4r(const void* W, const void* W
         const uint4 A0 = codes8(gq == 0 ? q[c][i].x : q[c][i].z), A1 = codes8(gq == 0 ? q[c][i].y : q[c][i].w);
         const float f0 = bf2f((uint16_t)(SC.x & 0xffffu)), f1 = bf2f((uint16_t)(SC.x >> 16));
         const float f2 = bf2f((uint16_t)(SC.y & 0xffffu)), f3 = bf2f((uint16_t)(SC.y >> 16));
-        f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
-        p = mfma_pair(A0, Bc[gq][0], p);
-        p = mfma_pair(A1, Bc[gq][1], p);
-        acc[i].x = fmaf(f0, p.x, acc[i].x);
-        acc[i].y = fmaf(f1, p.y, acc[i].y);
-        acc[i].z = fmaf(f2, p.z, acc[i].z);
-        acc[i].w = fmaf(f3, p.w, acc[i].w);
+#pragma unroll
+        for (int rt = 0; rt < TM; ++rt) {
+          f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
+          p = mfma_pair(A0, Bc[rt][gq][0], p);
+          p = mfma_pair(A1, Bc[rt][gq][1], p);
+          acc[i][rt].x = fmaf(f0, p.x, acc[i][rt].x);
+          acc[i][rt].y = fmaf(f1, p.y, acc[i][rt].y);
+          acc[i][rt].z = fmaf(f2, p.z, acc[i][rt].z);
+          acc[i][rt].w = fmaf(f3, p.w, acc[i][rt].w);
+        }
       }
     if (c + CPA < CPI) act(c + CPA, Bc);
   }
-  // the IG items' chain sums meet in LDS, in chain order
+  // the IG items' chain sums meet in LDS, in chain order (one 16-row tile of
+  // one item per 256 threads' pass)
 #pragma unroll
-  for (int i = 0; i < IG; ++i) sh.red[i][wave][lane] = acc[i];
+  for (int i = 0; i < IG; ++i)
+#pragma unroll
+    for (int rt = 0; rt < TM; ++rt) sh.red[i * TM + rt][wave][lane] = acc[i][rt];
   __syncthreads();
-  for (int t = threadIdx.x; t < IG * 256; t += nthr) {
-    const int i = t >> 8, tt = t & 255;
-    const float* red = reinterpret_cast<const float*>(sh.red[i]);
+  for (int t = threadIdx.x; t < IG * TM * 256; t += nthr) {
+    const int it = t >> 8, tt = t & 255;
+    const int i = it / TM, rt = it - i * TM;
+    const float* red = reinterpret_cast<const float*>(sh.red[it]);
     float v = 0.f;
 #pragma unroll
     for (int w0 = 0; w0 < kMaxWaves; w0 += 8) {
@@ -1051,7 +1154,7 @@ __global__ __launch_bounds__(768) void k_gemm_int4r(const void* W, const void* W
         if (w0 + w < nw) v = (w0 + w == 0) ? part[w] : v + part[w];
     }
     const int l = tt >> 2;
-    const int rr = l & 15;
+    const int rr = rt * 16 + (l & 15);
     if (rr < a.M) sh.y[i][rr][4 * (l >> 4) + (tt & 3)] = v;
   }
   __syncthreads();
@@ -1066,34 +1169,38 @@ __global__ __launch_bounds__(768) void k_gemm_int4r(const void* W, const void* W
 
 // Items per workgroup up to MAXIG (the most whose registers fit without
 // spilling at CPI tiles per wave).
-template <int ROLE, int CPI, int MAXIG>
+template <int ROLE, int CPI, int MAXIG, int TM>
 static hipError_t launch_int4r_ig(const GemmArgs& a, int grid, int ig, hipStream_t st) {
   const dim3 block(64 * a.S), g(grid);
   if (ig > MAXIG) return hipErrorNotSupported;
   switch (ig) {
-    case 1: hipLaunchKernelGGL((k_gemm_int4r<ROLE, CPI, 1>), g, block, 0, st, a.W, a.Wscale, a.bhi, a.blo, a.prof, a.N, a.K, grid, a.S | (a.M << 8), a); break;
-    case 2: hipLaunchKernelGGL((k_gemm_int4r<ROLE, CPI, (MAXIG >= 2 ? 2 : 1)>), g, block, 0, st, a.W, a.Wscale, a.bhi, a.blo, a.prof, a.N, a.K, grid, a.S | (a.M << 8), a); break;
-    case 3: hipLaunchKernelGGL((k_gemm_int4r<ROLE, CPI, (MAXIG >= 3 ? 3 : 1)>), g, block, 0, st, a.W, a.Wscale, a.bhi, a.blo, a.prof, a.N, a.K, grid, a.S | (a.M << 8), a); break;
-    case 4: hipLaunchKernelGGL((k_gemm_int4r<ROLE, CPI, (MAXIG >= 4 ? 4 : 1)>), g, block, 0, st, a.W, a.Wscale, a.bhi, a.blo, a.prof, a.N, a.K, grid, a.S | (a.M << 8), a); break;
+    case 1: hipLaunchKernelGGL((k_gemm_int4r<ROLE, CPI, 1, TM>), g, block, 0, st, a.W, a.Wscale, a.bhi, a.blo, a.prof, a.N, a.K, grid, a.S | (a.M << 8), a); break;
+    case 2: hipLaunchKernelGGL((k_gemm_int4r<ROLE, CPI, (MAXIG >= 2 ? 2 : 1), TM>), g, block, 0, st, a.W, a.Wscale, a.bhi, a.blo, a.prof, a.N, a.K, grid, a.S | (a.M << 8), a); break;
+    case 3: hipLaunchKernelGGL((k_gemm_int4r<ROLE, CPI, (MAXIG >= 3 ? 3 : 1), TM>), g, block, 0, st, a.W, a.Wscale, a.bhi, a.blo, a.prof, a.N, a.K, grid, a.S | (a.M << 8), a); break;
+    case 4: hipLaunchKernelGGL((k_gemm_int4r<ROLE, CPI, (MAXIG >= 4 ? 4 : 1), TM>), g, block, 0, st, a.W, a.Wscale, a.bhi, a.blo, a.prof, a.N, a.K, grid, a.S | (a.M << 8), a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-// The register-operand int4 kernel where it applies (at most 16 rows, at
-// most 12 waves, 1, 2 or 4 tiles per wave and item, at most 4 items per
-// workgroup, 2 at 4 tiles); hipErrorNotSupported otherwise.
+// The register-operand int4 kernel where it applies (at most 32 rows in one
+// or two row tiles, at most 12 waves, 1, 2 or 4 tiles per wave and item, at
+// most 4 items per workgroup, 2 at 4 tiles); hipErrorNotSupported otherwise.
+template <int ROLE, int TM>
+static hipError_t launch_int4r_tm(const GemmArgs& a, int grid, int cpi, int ig, hipStream_t st) {
+  switch (cpi) {
+    case 1: return launch_int4r_ig<ROLE, 1, 4, TM>(a, grid, ig, st);
+    case 2: return launch_int4r_ig<ROLE, 2, (TM == 2 ? 3 : 4), TM>(a, grid, ig, st);   // (4 spill at two tiles)
+    case 4: return launch_int4r_ig<ROLE, 4, 2, TM>(a, grid, ig, st);
+    default: return hipErrorNotSupported;
+  }
+}
 template <int ROLE>
 static hipError_t launch_int4r(const GemmArgs& a, int grid, hipStream_t st) {
   const int cpi = (a.K >> 7) / a.S;
   const int ig = ((a.N >> 4) + grid - 1) / grid;
-  if (a.M > 16 || a.S > 12) return hipErrorNotSupported;
-  switch (cpi) {
-    case 1: return launch_int4r_ig<ROLE, 1, 4>(a, grid, ig, st);
-    case 2: return launch_int4r_ig<ROLE, 2, 4>(a, grid, ig, st);
-    case 4: return launch_int4r_ig<ROLE, 4, 2>(a, grid, ig, st);
-    default: return hipErrorNotSupported;
-  }
+  if (a.M > 32 || a.S > 12) return hipErrorNotSupported;
+  return a.M > 16 ? launch_int4r_tm<ROLE, 2>(a, grid, cpi, ig, st) : launch_int4r_tm<ROLE, 1>(a, grid, cpi, ig, st);
 }
 
 // bf16 weights of small K (1, 2 or 4 chunks per wave), one row tile, the
@@ -1519,6 +1626,30 @@ int gemm_ring_depth(int n_chunks, int waves, int M, int unit, bool* dbl) {
   return 0;
 }
 
+// 0: never, 1: when the planes take more than one stage, 2: at one row tile
+constexpr int kRbMode = 1;
+
+template <int ROLE>
+static hipError_t launch_bf16rb(const GemmArgs& a, int grid, int nb, hipStream_t st) {
+  RingPack rp;
+  if (!ring_pack(a, rp)) return hipErrorInvalidValue;
+  const dim3 block(64 * a.S), g(grid);
+#define SV_RB(NB_, CPW_) hipLaunchKernelGGL((k_gemm_bf16rb<ROLE, NB_, CPW_>), g, block, 0, st, a.W, a.bhi, a.blo, a.ss, a.K, grid, rp.a, rp.c, a)
+  (void)nb;                      // the ring holds a wave's whole item (no stage bounds it)
+  switch (a.cpi) {
+    case 8:                      // (QKV: a ring of 4, as 8 leaves its epilogue state too few registers)
+      if constexpr (ROLE == kRoleQkv) SV_RB(4, 8);
+      else SV_RB(8, 8);
+      break;
+    case 4: SV_RB(4, 4); break;
+    case 2: SV_RB(2, 2); break;
+    case 1: SV_RB(1, 1); break;
+    default: return hipErrorNotSupported;
+  }
+#undef SV_RB
+  return hipGetLastError();
+}
+
 template <int ROLE, bool INT4>
 static hipError_t gemm_dispatch(const GemmArgs& a_in, int grid, hipStream_t st) {
   bool dbl = false;
@@ -1531,6 +1662,14 @@ static hipError_t gemm_dispatch(const GemmArgs& a_in, int grid, hipStream_t st) 
   a.cpws = a.cs / nw;
   a.cpi = n_chunks / nw;
   a.pro_fast = !INT4 && (a.n_stages == 1 || dbl) && prologue_fast(a, a.cs, unit, nw, norm_role(ROLE));
+  if constexpr (!INT4) {
+    // one row tile whose planes take more than one stage: the register-operand
+    // ring (at most 8 chunks per wave, the sums of squares of K <= 8192 rows)
+    if (kRbMode > 0 && a.M <= 16 && a.cpi <= 8 && (a.n_stages > 1 || kRbMode > 1) && a.K <= 8192) {
+      const hipError_t e = launch_bf16rb<ROLE>(a, grid, nb, st);
+      if (e != hipErrorNotSupported) return e;
+    }
+  }
   switch (nb) {
     case 8:
       if constexpr (INT4) return hipErrorInvalidValue;
@@ -1566,7 +1705,8 @@ hipError_t launch_gemm(const GemmArgs& a, int role, int grid, hipStream_t st) {
   b.n_half = split ? 2 * r : 0;
   // 17..64 rows whose bf16 planes do not fit one stage: items in groups,
   // stages outermost.  Measured on the 8B shapes: the restaging kernel is
-  // faster for 9..16 rows, and for 34..48 rows except on the LM head.
+  // faster for 34..48 rows except on the LM head (9..16 rows whose planes
+  // take more than one stage run k_gemm_bf16rb).
   const int mode = grp_mode(a.M, a.S);
   const bool grp = mode == 1 || (mode == 2 && (a.M > 48 || role == kRoleLmHead));
   if (!i4 && a.M >= 17 && grp && stage_chunks(a.K >> 5, a.S, a.M, 32, 1) < (a.K >> 5)) {
@@ -1590,7 +1730,7 @@ hipError_t launch_gemm(const GemmArgs& a, int role, int grid, hipStream_t st) {
     }
     if (e != hipErrorNotSupported) return e;
   }
-  if (i4 && a.M <= 16) {
+  if (i4 && a.M <= 32) {
     hipError_t e = hipErrorNotSupported;
     switch (role) {
       case kRoleQkv: e = launch_int4r<kRoleQkv>(b, grid, st); break;

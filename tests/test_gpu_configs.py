@@ -143,6 +143,15 @@ def test_gemma_int4_rows_match_oracle(gemma):
     _check_rows_vs_oracle(Session(dev), w, ids[:15], ids[15:23], "gemma_int4")
 
 
+def test_gemma_int4_seventeen_rows_match_oracle(gemma):
+    """17 rows: the int4 register-operand kernel's two-row-tile form."""
+    from greedy_block_verification_amd.session import Session
+    from seeded_inputs import prompt_ids
+    dev, w = gemma
+    ids = prompt_ids(w.cfg.seed, 4, 24, w.cfg.vocab).tolist()
+    _check_rows_vs_oracle(Session(dev), w, ids[:8], ids[8:24], "gemma_int4 17 rows")
+
+
 def test_gemma_int4_cache_histories_and_row_decode(gemma):
     from greedy_block_verification_amd.session import Session
     from seeded_inputs import prompt_ids
@@ -190,6 +199,16 @@ def test_q8b_rows_match_oracle(q8b):
     dev, w = q8b
     ids = prompt_ids(w.cfg.seed, 9, 12, w.cfg.vocab).tolist()
     _check_rows_vs_oracle(Session(dev), w, ids[:6], ids[6:10], "q8b")
+
+
+def test_q8b_thirteen_rows_match_oracle(q8b):
+    """13 rows: the activation planes of 9-16 rows outgrow one LDS stage, so
+    these forwards run the register-operand ring kernel."""
+    from greedy_block_verification_amd.session import Session
+    from seeded_inputs import prompt_ids
+    dev, w = q8b
+    ids = prompt_ids(w.cfg.seed, 10, 18, w.cfg.vocab).tolist()
+    _check_rows_vs_oracle(Session(dev), w, ids[:6], ids[6:18], "q8b 13 rows")
 
 
 def test_q8b_verify_equals_decode(q8b):
