@@ -384,7 +384,7 @@ WORKLOADS = {
                  steps=400, sweep_steps=300, prefill_rows=512, roofline_kernel="sv::k_gemm_bf16r<2, 2, 2>",
                  what="Qwen3-0.6B-shaped target"),
     "gemma_int4": dict(k=8, k_sweep="16", prompts=16, prompt_len=87, gen_tokens=64, p_correct=0.66,
-                       steps=300, sweep_steps=200, prefill_rows=0, roofline_kernel="sv::k_gemm_int4r<2, 1, 3>",
+                       steps=300, sweep_steps=200, prefill_rows=0, roofline_kernel="sv::k_gemm_int4r<2, 1, 3, 1>",
                        what="Gemma-style int4 (group 64, bf16 scales) GeGLU target"),
     "q8b_stress": dict(k=4, k_sweep="1,2,8,16,32", prompts=1, prompt_len=32640, gen_tokens=64, p_correct=0.66,
                        steps=150, sweep_steps=60, prefill_rows=2048, roofline_kernel="sv::k_gemm_bf16<1, 2>",

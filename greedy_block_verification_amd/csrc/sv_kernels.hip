@@ -825,24 +825,41 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16(const void* W, const uint16_
 // stage and no restaging per item (k_gemm_bf16 restages every item once the
 // rows' planes outgrow one stage).  The item plan, the ring, the sums (chain
 // w over its chunks in order, hi plane before lo plane, the chain sums met in
-// LDS in chain order) and the epilogue are k_gemm_bf16's.  Leading arguments
-// as k_gemm_bf16's (pA, pC of ring_pack).
-template <int ROLE, int NB, int CPW>
+// LDS in chain order) and the epilogue are k_gemm_bf16's.  TM = 2 (17..24
+// rows of K <= 4096): rows 16.. are staged once into LDS, whole K, and the
+// second row tile reads them there.  Leading arguments as k_gemm_bf16's
+// (pA, pC of ring_pack).
+template <int ROLE, int NB, int CPW, int TM>
 __global__ __launch_bounds__(1024) void k_gemm_bf16rb(const void* W, const uint16_t* bhi, const uint16_t* blo,
                                                       const float* ss, int K, int G, unsigned pA, unsigned pC,
                                                       GemmArgs args) {
   static_assert(CPW % NB == 0, "the ring depth divides the chunks per wave");
+  static_assert(TM == 1 || TM == 2, "one or two row tiles");
   GemmArgs a = args;
   a.W = W; a.bhi = bhi; a.blo = blo; a.ss = ss; a.K = K;
   a.M = (int)(pA & 127u); a.n_full = (int)(pC & 0x1fffffu); a.n_half = (int)(pC >> 21);
   const unsigned long long t_start = wall_clock64();
   __builtin_amdgcn_sched_barrier(0);       // (the clock read stays at entry)
   __shared__ GemmShared sh;
+  __shared__ __align__(16) uint16_t stage_mem[TM == 2 ? kStageBytes / 2 : 8];
   const int nw = (int)((pA >> 8) & 31u);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int KC = a.K >> 5;
   const ItemPlan<ROLE> ip{a.n_full, a.n_half, G};
+  // TM = 2: rows 16.. (a2), whole K, one LDS stage
+  GemmArgs a2 = a;
+  Stage st2{};
+  ProRegs pr{};
+  if constexpr (TM == 2) {
+    a2.bhi = a.bhi + (size_t)16 * a.K;
+    a2.blo = a.blo + (size_t)16 * a.K;
+    a2.M = a.M - 16;
+    st2.stride = KC * 32 + 8;
+    st2.hi = stage_mem;
+    st2.lo = stage_mem + (size_t)a2.M * st2.stride;
+    pr = prologue_issue(a2, KC, 32, nw * 64, wave, lane, false);
+  }
   const uint4* W4 = reinterpret_cast<const uint4*>(a.W);
   auto item_off = [&](int o) {                 // (as in k_gemm_bf16)
     int hf;
@@ -867,35 +884,64 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16rb(const void* W, const uint1
   BPair B[CPW];
 #pragma unroll
   for (int c = 0; c < CPW; ++c) B[c] = load_planes(a, r, (wave + nw * c) * 32 + g * 8);
-  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (norm_role(ROLE) && wave < a.M) {
+  if constexpr (TM == 2) {
+    // the staged rows go to LDS before the weight ring starts (their loads
+    // were issued first, so this waits on them alone): held across the ring
+    // they would push the registers past the limit
+    prologue_finish(a2, st2, KC, 32, nw * 64, wave, lane, false, pr, sh);
+  }
+  // slices of sums of squares per lane and row: K <= 8192 (two row tiles: K <= 4096)
+  constexpr int SSL = TM == 2 ? 4 : 8;
+  float s[TM][SSL];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) s[t] = ss_load(a, wave, lane, t);
+  for (int rt = 0; rt < TM; ++rt)
+#pragma unroll
+    for (int t = 0; t < SSL; ++t) s[rt][t] = 0.f;
+  // with 16 waves each wave takes row wave of each row tile, its slices in
+  // registers ahead of the ring; fewer waves take rows_inv_rms's loop instead
+  const bool ss_regs = norm_role(ROLE) && nw == 16;
+  if (ss_regs) {
+#pragma unroll
+    for (int rt = 0; rt < TM; ++rt)
+      if (wave + 16 * rt < a.M) {
+#pragma unroll
+        for (int t = 0; t < SSL; ++t) s[rt][t] = ss_load(a, wave + 16 * rt, lane, t);
+      }
   }
   uint4 A[NB];
 #pragma unroll
   for (int u = 0; u < NB; ++u) refill(A[u]);
   prof_publish_start(a.prof, t_start);
   row_best_init<ROLE>(a, sh);
-  if (norm_role(ROLE) && wave < a.M) {
-    // the same order as rows_inv_rms: each lane adds its slices in order (the
-    // zeros past the row's slices add exactly nothing), then the butterfly
-    float v = 0.f;
+  if (norm_role(ROLE) && !ss_regs) rows_inv_rms(a, sh, wave, lane, nw);
+  if (ss_regs) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) v = v + s[t];
-    v = wave_sum(v);
-    if (lane == 0) sh.inv[wave] = 1.0f / sqrtf(v / (float)a.K + a.eps);
+    for (int rt = 0; rt < TM; ++rt)
+      if (wave + 16 * rt < a.M) {
+        // the same order as rows_inv_rms: each lane adds its slices in order
+        // (the zeros past the row's slices add exactly nothing), then the butterfly
+        float v = 0.f;
+#pragma unroll
+        for (int t = 0; t < SSL; ++t) v = v + s[rt][t];
+        v = wave_sum(v);
+        if (lane == 0) sh.inv[wave + 16 * rt] = 1.0f / sqrtf(v / (float)a.K + a.eps);
+      }
   }
+  if constexpr (TM == 2) __syncthreads();
   for (int o = 0;; ++o) {
     int hf;
     const int T = ip.tile(o, hf);
     if (T < 0) break;
     const EpiPre pre = epi_load<ROLE>(a, T, threadIdx.x);
-    f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 acc[TM];
+#pragma unroll
+    for (int rt = 0; rt < TM; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto group = [&](int c0, bool refills) {
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         acc[0] = mfma_pair(A[u], B[c0 + u], acc[0]);
+        if constexpr (TM == 2)
+          acc[1] = mfma_pair(A[u], lds_pair(st2, row_of(j, a2.M), (wave + nw * (c0 + u)) * 32 + g * 8), acc[1]);
         if (refills) refill(A[u]);
       }
     };
@@ -903,7 +949,7 @@ __global__ __launch_bounds__(1024) void k_gemm_bf16rb(const void* W, const uint1
     for (int c0 = 0; c0 + NB < CPW; c0 += NB) group(c0, true);
     if (ip.has_next(T, hf)) group(CPW - NB, true);
     else group(CPW - NB, false);                 // the last NB chunks of this workgroup
-    gemm_finish<1, ROLE>(a, sh, acc, T, wave, lane, nw, pre, hf);
+    gemm_finish<TM, ROLE>(a, sh, acc, T, wave, lane, nw, pre, hf);
   }
   row_best_publish<ROLE>(a, sh);
   prof_end(a.prof);
@@ -1629,16 +1675,17 @@ int gemm_ring_depth(int n_chunks, int waves, int M, int unit, bool* dbl) {
 // 0: never, 1: when the planes take more than one stage, 2: at one row tile
 constexpr int kRbMode = 1;
 
-template <int ROLE>
+template <int ROLE, int TM>
 static hipError_t launch_bf16rb(const GemmArgs& a, int grid, int nb, hipStream_t st) {
   RingPack rp;
   if (!ring_pack(a, rp)) return hipErrorInvalidValue;
   const dim3 block(64 * a.S), g(grid);
-#define SV_RB(NB_, CPW_) hipLaunchKernelGGL((k_gemm_bf16rb<ROLE, NB_, CPW_>), g, block, 0, st, a.W, a.bhi, a.blo, a.ss, a.K, grid, rp.a, rp.c, a)
+#define SV_RB(NB_, CPW_) hipLaunchKernelGGL((k_gemm_bf16rb<ROLE, NB_, CPW_, TM>), g, block, 0, st, a.W, a.bhi, a.blo, a.ss, a.K, grid, rp.a, rp.c, a)
   (void)nb;                      // the ring holds a wave's whole item (no stage bounds it)
   switch (a.cpi) {
-    case 8:                      // (QKV: a ring of 4, as 8 leaves its epilogue state too few registers)
-      if constexpr (ROLE == kRoleQkv) SV_RB(4, 8);
+    case 8:                      // (QKV: a ring of 4, two row tiles: of 2, as deeper ones spill)
+      if constexpr (TM == 2) SV_RB(2, 8);
+      else if constexpr (ROLE == kRoleQkv) SV_RB(4, 8);
       else SV_RB(8, 8);
       break;
     case 4: SV_RB(4, 4); break;
@@ -1666,7 +1713,7 @@ static hipError_t gemm_dispatch(const GemmArgs& a_in, int grid, hipStream_t st) 
     // one row tile whose planes take more than one stage: the register-operand
     // ring (at most 8 chunks per wave, the sums of squares of K <= 8192 rows)
     if (kRbMode > 0 && a.M <= 16 && a.cpi <= 8 && (a.n_stages > 1 || kRbMode > 1) && a.K <= 8192) {
-      const hipError_t e = launch_bf16rb<ROLE>(a, grid, nb, st);
+      const hipError_t e = launch_bf16rb<ROLE, 1>(a, grid, nb, st);
       if (e != hipErrorNotSupported) return e;
     }
   }
@@ -1707,6 +1754,30 @@ hipError_t launch_gemm(const GemmArgs& a, int role, int grid, hipStream_t st) {
   // stages outermost.  Measured on the 8B shapes: the restaging kernel is
   // faster for 34..48 rows except on the LM head (9..16 rows whose planes
   // take more than one stage run k_gemm_bf16rb).
+  // 17..24 rows: the register-operand ring with rows 16.. in one LDS stage
+  // (at most 8 chunks per wave, K <= 4096; the staged rows' planes fit the
+  // stage and the fast prologue).  Measured on the 8B shape at 17 rows: O,
+  // gate/up, down and the LM head gain (K = 16 step 5.556 -> 5.052 ms), QKV
+  // (a ring of 2 and a spill at two tiles) was slower and keeps the grouped
+  // kernel.
+  if (!i4 && kRbMode > 0 && a.M >= 17 && a.M <= 24 && (a.K >> 5) / a.S <= 8 && a.K <= 4096) {
+    GemmArgs c = b;
+    c.cpi = (a.K >> 5) / a.S;
+    c.cs = c.cpws = c.n_stages = c.pro_fast = 0;
+    GemmArgs rest = c;
+    rest.M = a.M - 16;
+    if ((size_t)rest.M * ((size_t)a.K + 8) * 4 <= (size_t)kStageBytes && prologue_fast(rest, a.K >> 5, 32, a.S, false)) {
+      hipError_t e = hipErrorNotSupported;
+      switch (role) {
+        case kRoleO: e = launch_bf16rb<kRoleO, 2>(c, grid, 0, st); break;
+        case kRoleGateUp: e = launch_bf16rb<kRoleGateUp, 2>(c, grid, 0, st); break;
+        case kRoleDown: e = launch_bf16rb<kRoleDown, 2>(c, grid, 0, st); break;
+        case kRoleLmHead: e = launch_bf16rb<kRoleLmHead, 2>(c, grid, 0, st); break;
+        default: break;
+      }
+      if (e != hipErrorNotSupported) return e;
+    }
+  }
   const int mode = grp_mode(a.M, a.S);
   const bool grp = mode == 1 || (mode == 2 && (a.M > 48 || role == kRoleLmHead));
   if (!i4 && a.M >= 17 && grp && stage_chunks(a.K >> 5, a.S, a.M, 32, 1) < (a.K >> 5)) {

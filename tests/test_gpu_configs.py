@@ -211,6 +211,15 @@ def test_q8b_thirteen_rows_match_oracle(q8b):
     _check_rows_vs_oracle(Session(dev), w, ids[:6], ids[6:18], "q8b 13 rows")
 
 
+def test_q8b_seventeen_rows_match_oracle(q8b):
+    """17 rows: the register-operand ring with row 16 staged in LDS."""
+    from greedy_block_verification_amd.session import Session
+    from seeded_inputs import prompt_ids
+    dev, w = q8b
+    ids = prompt_ids(w.cfg.seed, 11, 22, w.cfg.vocab).tolist()
+    _check_rows_vs_oracle(Session(dev), w, ids[:6], ids[6:22], "q8b 17 rows")
+
+
 def test_q8b_verify_equals_decode(q8b):
     from greedy_block_verification_amd.session import Session
     from seeded_inputs import prompt_ids
