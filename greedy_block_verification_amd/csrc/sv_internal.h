@@ -11,7 +11,7 @@ constexpr int kMaxPrefillRows = 16384;   // most rows of one row-tiled (prefill)
 constexpr int kPage = 16;           // positions per KV page
 constexpr int kGemmStageBytes = 136 * 1024;   // LDS a GEMM workgroup stages activation planes in
 constexpr int kAttnBlock = 64;      // positions per online-softmax block (4 pages)
-constexpr int kAttnMaxSplits = 128; // most KV splits of one row (the split plan depends only on its ctx)
+constexpr int kAttnMaxSplits = 64;  // most KV splits of one row (the split plan depends only on its ctx)
 constexpr int kAttnQRows = 256;     // most (row, q head) pairs one attention workgroup holds (16 MFMA tiles)
 constexpr int kColGroup = 64;       // LM-head columns per argmax record (4 MFMA tiles of 16)
 constexpr int kEpiCols = 256;       // columns one epilogue workgroup owns (whole heads, 8 gate/up tiles)
@@ -109,6 +109,9 @@ struct AttnArgs {
   // n * magic), so the kernels run no integer division before their loads
   int G, n_qt, n_sg;
   unsigned g_magic, qt_magic, sg_magic;
+  // set by the caller: blocks per split of the first row, the split
+  // kernel's guess of where a unit starts (checked: speed only; 0 = 1)
+  int bps_guess;
 };
 
 hipError_t launch_gemm(const GemmArgs& a, int role, int grid, hipStream_t st);
@@ -125,6 +128,8 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, int role, hipStream_t st);
 hipError_t launch_attention_rows(const AttnArgs& a, hipStream_t st);
 // Number of KV splits of a row attending to ctx positions.
 int attn_splits(int ctx);
+// Blocks of 64 positions per split for a row of context ctx.
+int attn_blocks_per_split(int ctx);
 // Most splits of any row of a forward of M rows after kv_len positions (the
 // rows attend to kv_len + 1 .. kv_len + M positions).
 int attn_splits_max(int kv_len, int M);

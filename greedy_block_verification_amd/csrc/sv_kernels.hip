@@ -2209,11 +2209,14 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, int role, hipStream_t st) {
 
 // ------------------------------------------------------------ attention
 // Split plan of one row, a function of its own ctx only: nb = ceil(ctx/64)
-// blocks of 64 absolute positions, bps = ceil(nb / 128) blocks per split,
+// blocks of 64 absolute positions, bps = ceil(nb / 64) blocks per split,
 // ns = ceil(nb / bps) splits; split i covers positions
-// [64 i bps, min(64 (i+1) bps, ctx)).  Contexts up to 8192 get one block per
-// split, longer ones at most 128 splits (a 32K context: 128 splits of 4
-// blocks), so a long row still spreads over many waves.
+// [64 i bps, min(64 (i+1) bps, ctx)).  Contexts up to 4096 get one block per
+// split, longer ones at most 64 splits (a 32K context: 64 splits of 8
+// blocks), so a long row still spreads over many waves.  Measured on MI355X
+// (8B shape at 32K, K = 4 step): at most 32 / 48 / 64 / 96 / 128 splits
+// 5.04 / 4.81 / 4.71 / 4.83 / 4.87 ms; more splits shorten each wave's
+// block walk but write and fold more partials.
 __host__ __device__ __forceinline__ int attn_bps(int ctx) {
   const int nb = (ctx + kAttnBlock - 1) / kAttnBlock;
   return (nb + kAttnMaxSplits - 1) / kAttnMaxSplits;
@@ -2221,12 +2224,13 @@ __host__ __device__ __forceinline__ int attn_bps(int ctx) {
 __host__ __device__ __forceinline__ int attn_ns(int ctx) {
   const int nb = (ctx + kAttnBlock - 1) / kAttnBlock;
   const int bps = attn_bps(ctx);
-  return bps == 1 ? nb : (nb + bps - 1) / bps;   // (contexts up to 8192 skip the division)
+  return bps == 1 ? nb : (nb + bps - 1) / bps;   // (contexts up to 4096 skip the division)
 }
 
 int attn_splits(int ctx) { return attn_ns(ctx); }
-// The split count is not monotone in ctx (ctx 8192: 128 one-block splits;
-// ctx 8193: 65 two-block splits), so a launch covers the most splits of any
+int attn_blocks_per_split(int ctx) { return attn_bps(ctx); }
+// The split count is not monotone in ctx (ctx 4096: 64 one-block splits;
+// ctx 4097: 33 two-block splits), so a launch covers the most splits of any
 // of its rows, not those of its longest row.
 int attn_splits_max(int kv_len, int M) {
   int n = 1;
@@ -2461,7 +2465,7 @@ __device__ __forceinline__ void attn_split_union(int kv_len, int r0, int r1, int
 template <int DH, bool FOLD, bool EARLY, bool BATCH>
 __global__ __launch_bounds__(512) void k_attn_mfma(const float* q, const int* page_table, const int* params,
                                                    const SeqDev* seqs, unsigned pk1, unsigned pk2, unsigned qt_magic,
-                                                   unsigned sg_magic, unsigned g_magic, AttnArgs args) {
+                                                   unsigned sg_magic, unsigned g_magic, int bps_g, AttnArgs args) {
   constexpr int DC = DH / 32;            // d chunks of the score MFMA
   constexpr int DT = DH / 16;            // d tiles of the P.V MFMA
   __shared__ AttnUnitLds<DH> ul[FOLD ? kAttnFoldSplits : 1];
@@ -2513,22 +2517,29 @@ __global__ __launch_bounds__(512) void k_attn_mfma(const float* q, const int* pa
   const int r = have ? rq : 0;
   const int head = h * G + (have ? qr - rq * G : 0);
   auto block_pages = [&](int b) { return attn_block_pages(av, b); };
-  // the first unit's first block is its split index whenever splits are one
-  // block (contexts up to 8192): fetch its pages before the context length is known
-  const int b_guess = s_lo + wave;
+  // the first unit's first block is its split index times the blocks per
+  // split, which the caller guesses from the first row (every row of a
+  // context up to 8192 has one block per split): fetch its pages before the
+  // context length is known
+  const int b_guess = EARLY ? s_lo + wave : (s_lo + wave) * bps_g;
   int4 pq_guess = block_pages(b_guess);
   const int kv_len = BATCH ? attn_kv_len(a, qt) : a.params[0];
-  // EARLY (the launcher's choice for the split kernel of at most 64 splits):
-  // every row then has one block per split (a row of two or more blocks per
-  // split has at least 65 splits), so a unit is block b_guess or nothing.
+  // EARLY (the launcher's choice for the split kernel of at most
+  // kAttnMaxSplits / 2 splits): every row then has one block per split (a
+  // row of two or more blocks per split has more than kAttnMaxSplits / 2
+  // splits), so a unit is block b_guess or nothing.
   // Its K/V go out as soon as the page numbers arrive, ahead of q, which the
   // previous kernel has just written and which arrives no sooner: loads
   // complete in issue order, so q issued first would hold the K/V back by
   // its whole latency.  The pages are clamped into the pool for this load
   // (a unit past its rows' context never uses it); a used block lies inside
   // the context, whose pages are valid, so the clamp leaves them unchanged.
+  // The split kernel of more splits (rows of two or more blocks per split:
+  // one unit per workgroup) requests the guessed first block the same way;
+  // its block loop starts from it when the guess holds.
+  constexpr bool kHoist = EARLY || !FOLD;
   AttnKV<DH> kv_first;
-  if (EARLY && b_guess < s_hi) {                          // wave-uniform
+  if (kHoist && (!EARLY || b_guess < s_hi)) {             // wave-uniform
     const int np = av.n_pages - 1;
     const int4 pc = make_int4(min(max(pq_guess.x, 0), np), min(max(pq_guess.y, 0), np),
                               min(max(pq_guess.z, 0), np), min(max(pq_guess.w, 0), np));
@@ -2576,6 +2587,17 @@ __global__ __launch_bounds__(512) void k_attn_mfma(const float* q, const int* pa
 
     if constexpr (EARLY) {
       if (b_lo < b_hi) attn_block_step<DH>(av, kv_first, qop, b_guess, g, lo, hi, ctx_max, m, l, o);
+    } else if constexpr (!FOLD) {
+      if (b_lo < b_hi) {                                   // wave-uniform
+        // (a missed guess reloads: the rows span a change of blocks per split)
+        if (b_lo != b_guess) attn_load_kv<DH>(av, h, j, g, block_pages(b_lo), kv_first);
+        for (int b = b_lo;;) {
+          const int4 pq = block_pages(b + 1 < b_hi ? b + 1 : b);   // in flight during this block
+          attn_block_step<DH>(av, kv_first, qop, b, g, lo, hi, ctx_max, m, l, o);
+          if (++b >= b_hi) break;
+          attn_load_kv<DH>(av, h, j, g, pq, kv_first);
+        }
+      }
     } else {
       int4 pq = (b_lo == b_guess) ? pq_guess : block_pages(b_lo < b_hi ? b_lo : 0);
       for (int b = b_lo; b < b_hi; ++b) {
@@ -2886,11 +2908,14 @@ __global__ __launch_bounds__(256) void k_attn_rows2(AttnArgs a) {
 
 // Fold of the global partials of row r, query head j (record [m, l, -, -, o[dh]]):
 // the row's records are staged in LDS with coalesced 16-byte loads (a long
-// context has up to 128 of them), then thread d folds output d in split order.
-// Launched with 256 threads.
+// context has up to kAttnMaxSplits of them), then thread d folds output d in split order.
+// Launched with 256 threads.  The loads cover the launch's most splits
+// (n_split, at most part_splits) and go out with the context length's, not
+// after it; records past the row's own split count are dropped.
 template <int DH>
 __global__ __launch_bounds__(256) void k_attn_combine(float* part, const int* params, const SeqDev* seqs,
-                                                      const int* rowseq, int nq, int part_splits, AttnArgs args) {
+                                                      const int* rowseq, int nq, int part_splits, int n_split,
+                                                      AttnArgs args) {
   AttnArgs a = args;                     // leading arguments preloaded (as in k_attn_mfma)
   a.part = part; a.params = params; a.seqs = seqs; a.rowseq = rowseq; a.nq = nq; a.part_splits = part_splits;
   __shared__ float4 rec[kAttnMaxSplits * (DH + 4) / 4];
@@ -2900,17 +2925,18 @@ __global__ __launch_bounds__(256) void k_attn_combine(float* part, const int* pa
     const SeqDev& sd = a.seqs[a.rowseq[r]];
     ctx = sd.kv_len + r - sd.row0 + 1;
   }
-  const int ns = attn_ns(ctx);
   const float4* base = reinterpret_cast<const float4*>(a.part + ((size_t)r * a.nq + j) * a.part_splits * (DH + 4));
-  const int n4 = ns * ((DH + 4) / 4);
-  // every record of the row in one round of loads (at most 17 per thread)
+  const int n4_max = n_split * ((DH + 4) / 4);
+  // every record of the row in one round of loads (at most 9 per thread)
   constexpr int U = (kAttnMaxSplits * (DH + 4) / 4 + 255) / 256;
   float4 v[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int i = threadIdx.x + u * 256;
-    v[u] = base[i < n4 ? i : 0];
+    v[u] = base[i < n4_max ? i : 0];
   }
+  const int ns = attn_ns(ctx);
+  const int n4 = ns * ((DH + 4) / 4);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int i = threadIdx.x + u * 256;
@@ -2977,7 +3003,8 @@ template <int DH>
 static bool launch_attn_split(const AttnArgs& a, dim3 grid, dim3 block, bool early, unsigned pk1, unsigned pk2,
                               hipStream_t st) {
   const bool batch = a.seqs != nullptr;
-#define SV_ATTN_LEAD a.q, a.page_table, a.params, a.seqs, pk1, pk2, a.qt_magic, a.sg_magic, a.g_magic, a
+#define SV_ATTN_LEAD a.q, a.page_table, a.params, a.seqs, pk1, pk2, a.qt_magic, a.sg_magic, a.g_magic, \
+                     a.bps_guess > 1 ? a.bps_guess : 1, a
   if (a.final_fold) {
     if (batch) hipLaunchKernelGGL((k_attn_mfma<DH, true, false, true>), grid, block, 0, st, SV_ATTN_LEAD);
     else hipLaunchKernelGGL((k_attn_mfma<DH, true, false, false>), grid, block, 0, st, SV_ATTN_LEAD);
@@ -2991,7 +3018,7 @@ static bool launch_attn_split(const AttnArgs& a, dim3 grid, dim3 block, bool ear
 #undef SV_ATTN_LEAD
   if (!a.final_fold)
     hipLaunchKernelGGL(k_attn_combine<DH>, dim3(a.nq, a.M), dim3(256), 0, st, a.part, a.params, a.seqs, a.rowseq,
-                       a.nq, a.part_splits, a);
+                       a.nq, a.part_splits, a.n_split, a);
   return true;
 }
 
@@ -3021,12 +3048,13 @@ hipError_t launch_attention(const AttnArgs& a_in, hipStream_t st) {
   a.sg_magic = div_magic(a.n_sg);
   const int n_wg = n_qt * a.n_sg;
   const dim3 grid(n_wg, a.nkv), block(64 * a.wpb);
-  // split kernel at most 64 splits: one block per split for every row, so
-  // the unit's K/V can go out ahead of q.  Measured on MI355X: 0.6B shape at
-  // 512-640 positions (10 splits) attention 250.3 -> 246.7 us per K = 4
-  // step; the LDS-fold kernel (2-3 splits) was slower with it (8B 271.5 ->
-  // 275.7, Gemma 239.7 -> 246.1 us), so it keeps its loads in the old order.
-  const bool early = a.n_split <= 64;
+  // split kernel of at most kAttnMaxSplits / 2 splits: one block per split
+  // for every row, so the unit's K/V can go out ahead of q.  Measured on
+  // MI355X: 0.6B shape at 512-640 positions (10 splits) attention 250.3 ->
+  // 246.7 us per K = 4 step; the LDS-fold kernel (2-3 splits) was slower
+  // with it (8B 271.5 -> 275.7, Gemma 239.7 -> 246.1 us), so it keeps its
+  // loads in the old order.
+  const bool early = a.n_split <= kAttnMaxSplits / 2;
   unsigned pk1, pk2;
   if (!attn_pack(a, pk1, pk2)) return hipErrorInvalidValue;
   if (a.dh == 128) {

@@ -167,7 +167,7 @@ size_t kv_pool_bytes_for(const sv_config& c, int n_pages) {
 // hipGetSymbolAddress (scratch_address below), and only that address is
 // ever handed to a kernel.  Every sv_verify_noalloc call on a GPU uses that
 // GPU's one copy, so calls that overlap in time on one GPU race.
-constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr size_t kScratchBytes = size_t(32) << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
@@ -417,6 +417,7 @@ hipError_t enqueue_forward(sv_ctx* c, const FwdBufs& fb, int M, int verify, int 
     at.part = fb.part; at.part_splits = fb.part_splits; at.ohi = ohi; at.olo = olo;
     at.prof = prof_slot(c, fb, kRoleAttn, l);
     at.seqs = bd.seqs; at.rowseq = bd.rowseq; at.tiles = bd.tiles; at.n_tiles = bd.n_tiles;
+    at.bps_guess = bd.seqs != nullptr ? 1 : attn_blocks_per_split(c->kv_len + 1);
     if ((e = tiled ? launch_attention_rows(at, st) : launch_attention(at, st)) != hipSuccess) return e;
     plan(c->plans.o, L.wo, L.wo_scales, ohi, olo);
     g.gnext = gain(L.g_mlp);

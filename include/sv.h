@@ -181,14 +181,14 @@ sv_status sv_verify(sv_ctx *ctx, int32_t prefix_len, const int32_t *draft_ids, i
  * output), the RoPE table is read from it (an input sv_create wrote), and no
  * profiling stamps are taken.
  *
- * The array holds 64 MiB on every GPU the library runs on, for the life of
+ * The array holds 32 MiB on every GPU the library runs on, for the life of
  * the process.  A call needs about (k+1) x [d_model x 8.25 + n_q x head_dim x
  * 8 + d_ff x 4 + n_q x splits x (head_dim + 4) x 4 + 12] bytes (nine buffers,
  * each rounded up to 256 B), where splits is the most attention splits of
  * any row of the window (a row at context c has ceil(c / 64) of them up to
- * 128 and never more than 128); above 64 MiB the call returns SV_ESCRATCH
+ * 64 and never more than 64); above 32 MiB the call returns SV_ESCRATCH
  * before any launch (for example the 8B shape at a 32K context with k above
- * 28).  Every call on one GPU shares that GPU's array: calls whose execution
+ * 27).  Every call on one GPU shares that GPU's array: calls whose execution
  * overlaps on one GPU (other threads, other streams) race and their results
  * are undefined.  Nothing a previous call left in the
  * array is read: the row keys are cleared by the first kernel and every

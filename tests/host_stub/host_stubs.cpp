@@ -58,12 +58,13 @@ namespace sv {
 
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // The split plan (a function of the row's own context): 64-position blocks,
-// at most 128 splits.
+// at most kAttnMaxSplits splits.
 static int ns_of(int ctx) {
   const int nb = ceil_div(ctx, kAttnBlock), bps = ceil_div(nb, kAttnMaxSplits);
   return ceil_div(nb, bps);
 }
 int attn_splits(int ctx) { return ns_of(ctx); }
+int attn_blocks_per_split(int ctx) { return ceil_div(ceil_div(ctx, kAttnBlock), kAttnMaxSplits); }
 int attn_splits_max(int kv_len, int M) {
   int m = 1;
   for (int r = 0; r < M; ++r) m = ns_of(kv_len + r + 1) > m ? ns_of(kv_len + r + 1) : m;

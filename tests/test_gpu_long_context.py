@@ -10,10 +10,13 @@ causal recompute) at contexts where the other attention paths run:
 * 600-id prompt, K = 8 verify (contexts 577..609): more than three KV splits
   per row, so the split kernel writes global partials and the combine pass
   folds them; the last prefill forward's rows take the same path.
+* 4090-id prompt, K = 8 verify (contexts 4091..4099): the split plan changes
+  inside the window, from 64 splits of one 64-position block (context up to
+  4096) to 33 splits of two blocks (4097 on), where the split kernel walks
+  several blocks per unit.
 * 8186-id prompt, K = 8 verify (contexts 8187..8195): the split plan changes
-  inside the window, from 128 splits of one 64-position block (context up
-  to 8192) to 65 splits of two blocks (8193 on); page addressing runs past
-  page 512.
+  inside the window, from 64 splits of two blocks (context up to 8192) to 43
+  splits of three (8193 on); page addressing runs past page 512.
 * Both prompts also go through the row-tiled prefill (forwards of more than
   64 rows, whose attention walks each row's splits in one wave); its rows
   and the verify after it must equal the 64-row path bit for bit.
@@ -135,6 +138,11 @@ def _long_context_case(dev, w, n_prompt, prompt_idx, tiled_rows, label):
 def test_combine_path_context_600_matches_oracle(q06b_l2):
     dev, w = q06b_l2
     _long_context_case(dev, w, 600, 500, 512, "q06b L2 ctx 600")
+
+
+def test_split_plan_change_at_4096_matches_oracle(q06b_l2):
+    dev, w = q06b_l2
+    _long_context_case(dev, w, 4090, 503, 2048, "q06b L2 ctx 4090")
 
 
 def test_split_plan_change_at_8192_matches_oracle(q06b_l2):

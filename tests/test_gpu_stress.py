@@ -80,12 +80,13 @@ def test_stress_verify_equals_decode(stress, k):
     b.close()
 
 
-@pytest.mark.parametrize("kv_len", [184, 1020, 8180])
+@pytest.mark.parametrize("kv_len", [184, 1020, 4084, 8180])
 def test_stress_verify_equals_decode_across_split_plan_changes(stress, kv_len):
     """Rows of one verify that straddle a change of the attention launch or
     split plan: around ctx 192 (3 splits folded in the workgroup vs 4 folded
     by the combine pass, chosen by the verify's longest row), around ctx 1024
-    (16 vs 17 splits) and around ctx 8192 (one block per split vs two)."""
+    (16 vs 17 splits), around ctx 4096 (one block per split vs two) and
+    around ctx 8192 (two blocks per split vs three)."""
     dev, w, cfg, snap = stress
     k = 16
     rng = np.random.default_rng(2000 + kv_len)

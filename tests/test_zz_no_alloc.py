@@ -93,7 +93,7 @@ def test_noalloc_equals_verify_q8b(q8b_device):
 
 
 def test_noalloc_long_context_and_oversized_window(q8b_device):
-    """At a 32,704-position context (synthetic KV), a K = 16 window (128
+    """At a 32,704-position context (synthetic KV), a K = 16 window (64
     attention splits, partials in the array) matches sv_verify bit for bit
     after a K = 20 one; K = 32 needs more than the array holds and is
     refused with SV_ESCRATCH, leaving the context untouched."""
