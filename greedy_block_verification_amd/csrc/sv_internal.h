@@ -110,8 +110,10 @@ struct AttnArgs {
   int G, n_qt, n_sg;
   unsigned g_magic, qt_magic, sg_magic;
   // set by the caller: blocks per split of the first row, the split
-  // kernel's guess of where a unit starts (checked: speed only; 0 = 1)
+  // kernel's guess of where a unit starts (checked: speed only; 0 = 1), and
+  // the device's SIMDs (4 per CU; 0: unknown)
   int bps_guess;
+  int n_simd;
 };
 
 hipError_t launch_gemm(const GemmArgs& a, int role, int grid, hipStream_t st);

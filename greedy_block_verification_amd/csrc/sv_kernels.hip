@@ -2304,6 +2304,19 @@ __device__ __forceinline__ int4 attn_block_pages(const AttnArgs& a, int b) {
 }
 
 // MFMA operands of one block of 64 positions for KV head h.
+// attn_block_pages through the scalar data cache (b and the table are
+// wave-uniform): the entries arrive in SGPRs under lgkmcnt, so waiting for
+// them never waits for the K/V loads in flight.  The table is written
+// before the launch, never during it.
+__device__ __forceinline__ int4 attn_block_pages_s(const AttnArgs& a, int b) {
+  typedef const __attribute__((address_space(4))) int* CInt;
+  const CInt t = (CInt)a.page_table;
+  const int last = a.n_lpages - 1;
+  const int e = 4 * b;
+  if (e + 4 <= a.n_lpages) return make_int4(t[e], t[e + 1], t[e + 2], t[e + 3]);
+  return make_int4(t[min(e, last)], t[min(e + 1, last)], t[min(e + 2, last)], t[min(e + 3, last)]);
+}
+
 template <int DH>
 struct AttnKV {
   uint4 k[4][DH / 32];          // lane (g, j): K[pos = 64b + 16pt + j][32c + 8g .. +7], one page per pt
@@ -2311,21 +2324,30 @@ struct AttnKV {
   uint2 vhi[DH / 16][2];        //                  positions {32ks + 16 + 4g .. +3}
 };
 
+// element offset of (page, w = 0: K / 1: V) of KV head h
+__device__ __forceinline__ size_t attn_page_base(const AttnArgs& a, int h, int page, int w, int dh) {
+  return ((((size_t)a.layer * a.n_pages + page) * 2 + w) * a.nkv + h) * ((size_t)kPage * dh);
+}
+
 template <int DH>
-__device__ __forceinline__ void attn_load_kv(const AttnArgs& a, int h, int j, int g, int4 pq, AttnKV<DH>& kv) {
-  constexpr int DC = DH / 32, DT = DH / 16;
-  const size_t layer_base = (size_t)a.layer * a.n_pages;
-  const size_t page_elems = (size_t)kPage * DH;
-  // element offset of (page, kv) for this KV head
-  auto page_base = [&](int page, int w) { return (((layer_base + page) * 2 + w) * a.nkv + h) * page_elems; };
+__device__ __forceinline__ void attn_load_k(const AttnArgs& a, int h, int j, int g, int4 pq, AttnKV<DH>& kv) {
+  constexpr int DC = DH / 32;
   const int pg[4] = {__builtin_amdgcn_readfirstlane(pq.x), __builtin_amdgcn_readfirstlane(pq.y),
                      __builtin_amdgcn_readfirstlane(pq.z), __builtin_amdgcn_readfirstlane(pq.w)};
 #pragma unroll
   for (int pt = 0; pt < 4; ++pt) {
-    const uint16_t* kb = a.kv_pool + page_base(pg[pt], 0) + (size_t)j * DH + g * 8;
+    const uint16_t* kb = a.kv_pool + attn_page_base(a, h, pg[pt], 0, DH) + (size_t)j * DH + g * 8;
 #pragma unroll
     for (int c = 0; c < DC; ++c) kv.k[pt][c] = *reinterpret_cast<const uint4*>(kb + c * 32);
   }
+}
+
+template <int DH>
+__device__ __forceinline__ void attn_load_v(const AttnArgs& a, int h, int j, int g, int4 pq, AttnKV<DH>& kv) {
+  constexpr int DT = DH / 16;
+  const int pg[4] = {__builtin_amdgcn_readfirstlane(pq.x), __builtin_amdgcn_readfirstlane(pq.y),
+                     __builtin_amdgcn_readfirstlane(pq.z), __builtin_amdgcn_readfirstlane(pq.w)};
+  auto page_base = [&](int page, int w) { return attn_page_base(a, h, page, w, DH); };
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     const uint16_t* va = a.kv_pool + page_base(pg[2 * ks], 1) + g * 4;
@@ -2338,15 +2360,20 @@ __device__ __forceinline__ void attn_load_kv(const AttnArgs& a, int h, int j, in
   }
 }
 
-// One block b of a unit: scores, mask to the lane's row range [lo, hi),
-// online-softmax update of (m, l, o).  Both attention kernels run exactly
-// this sequence of operations.
 template <int DH>
-__device__ __forceinline__ void attn_block_step(const AttnArgs& a, const AttnKV<DH>& kv, const BPair (&qop)[DH / 32],
-                                                int b, int g, int lo, int hi, int ctx_max, float& m, float& l,
-                                                f32x4 (&o)[DH / 16]) {
-  constexpr int DC = DH / 32, DT = DH / 16;
-  f32x4 sc[4];
+__device__ __forceinline__ void attn_load_kv(const AttnArgs& a, int h, int j, int g, int4 pq, AttnKV<DH>& kv) {
+  attn_load_k<DH>(a, h, j, g, pq, kv);
+  attn_load_v<DH>(a, h, j, g, pq, kv);
+}
+
+// One block b of a unit: scores (attn_block_scores, from K only), mask to
+// the lane's row range [lo, hi), online-softmax update of (m, l, o)
+// (attn_block_update, from V).  Every attention kernel runs exactly this
+// sequence of operations (attn_block_step, or the two halves with loads
+// between them).
+template <int DH>
+__device__ __forceinline__ void attn_block_scores(const AttnKV<DH>& kv, const BPair (&qop)[DH / 32], f32x4 (&sc)[4]) {
+  constexpr int DC = DH / 32;
 #pragma unroll
   for (int pt = 0; pt < 4; ++pt) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -2354,6 +2381,13 @@ __device__ __forceinline__ void attn_block_step(const AttnArgs& a, const AttnKV<
     for (int c = 0; c < DC; ++c) acc = mfma_pair_f16(kv.k[pt][c], qop[c], acc);
     sc[pt] = acc;
   }
+}
+
+template <int DH>
+__device__ __forceinline__ void attn_block_update(const AttnArgs& a, const AttnKV<DH>& kv, const f32x4 (&sc)[4], int b,
+                                                  int g, int lo, int hi, int ctx_max, float& m, float& l,
+                                                  f32x4 (&o)[DH / 16]) {
+  constexpr int DT = DH / 16;
   // lane (g, j) holds scores of q-row j at positions 64b + 16pt + 4g + v
   float s[16];
   float bmax = -INFINITY;
@@ -2414,6 +2448,15 @@ __device__ __forceinline__ void attn_block_step(const AttnArgs& a, const AttnKV<
   m = mn;
 }
 
+template <int DH>
+__device__ __forceinline__ void attn_block_step(const AttnArgs& a, const AttnKV<DH>& kv, const BPair (&qop)[DH / 32],
+                                                int b, int g, int lo, int hi, int ctx_max, float& m, float& l,
+                                                f32x4 (&o)[DH / 16]) {
+  f32x4 sc[4];
+  attn_block_scores<DH>(kv, qop, sc);
+  attn_block_update<DH>(a, kv, sc, b, g, lo, hi, ctx_max, m, l, o);
+}
+
 // Rows of the q tile starting at q-row qbase (of a sequence of M rows) whose
 // ranges make up a unit: r0 .. r1.
 __device__ __forceinline__ void attn_tile_rows(int qbase, int G, unsigned gm, int M, int& r0, int& r1) {
@@ -2462,8 +2505,8 @@ __device__ __forceinline__ void attn_split_union(int kv_len, int r0, int r1, int
   }
 }
 
-template <int DH, bool FOLD, bool EARLY, bool BATCH>
-__global__ __launch_bounds__(512) void k_attn_mfma(const float* q, const int* page_table, const int* params,
+template <int DH, bool FOLD, bool EARLY, bool BATCH, bool PIPE = false>
+__global__ __launch_bounds__((FOLD || EARLY || !PIPE) ? 512 : 64) void k_attn_mfma(const float* q, const int* page_table, const int* params,
                                                    const SeqDev* seqs, unsigned pk1, unsigned pk2, unsigned qt_magic,
                                                    unsigned sg_magic, unsigned g_magic, int bps_g, AttnArgs args) {
   constexpr int DC = DH / 32;            // d chunks of the score MFMA
@@ -2522,7 +2565,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(const float* q, const int* pa
   // context up to 8192 has one block per split): fetch its pages before the
   // context length is known
   const int b_guess = EARLY ? s_lo + wave : (s_lo + wave) * bps_g;
-  int4 pq_guess = block_pages(b_guess);
+  int4 pq_guess = (FOLD || EARLY) ? block_pages(b_guess) : attn_block_pages_s(av, b_guess);
   const int kv_len = BATCH ? attn_kv_len(a, qt) : a.params[0];
   // EARLY (the launcher's choice for the split kernel of at most
   // kAttnMaxSplits / 2 splits): every row then has one block per split (a
@@ -2590,12 +2633,31 @@ __global__ __launch_bounds__(512) void k_attn_mfma(const float* q, const int* pa
     } else if constexpr (!FOLD) {
       if (b_lo < b_hi) {                                   // wave-uniform
         // (a missed guess reloads: the rows span a change of blocks per split)
-        if (b_lo != b_guess) attn_load_kv<DH>(av, h, j, g, block_pages(b_lo), kv_first);
-        for (int b = b_lo;;) {
-          const int4 pq = block_pages(b + 1 < b_hi ? b + 1 : b);   // in flight during this block
-          attn_block_step<DH>(av, kv_first, qop, b, g, lo, hi, ctx_max, m, l, o);
-          if (++b >= b_hi) break;
-          attn_load_kv<DH>(av, h, j, g, pq, kv_first);
+        if (b_lo != b_guess) attn_load_kv<DH>(av, h, j, g, attn_block_pages_s(av, b_lo), kv_first);
+        if constexpr (PIPE) {
+          // (one wave per SIMD: registers for a second block's K)  Block
+          // b + 1's K goes out once block b's scores have read K, and its V
+          // once block b's update has read V, so each load runs under the
+          // other half's arithmetic.  The loads are unconditional (the last
+          // block reloads itself), so every wait counts exactly; the page
+          // numbers come through scalar loads, whose waits leave them alone.
+          int4 pn = attn_block_pages_s(av, min(b_lo + 1, b_hi - 1));   // pages of block b + 1
+          for (int b = b_lo; b < b_hi; ++b) {
+            const int4 pn2 = attn_block_pages_s(av, min(b + 2, b_hi - 1));
+            f32x4 sc[4];
+            attn_block_scores<DH>(kv_first, qop, sc);
+            attn_load_k<DH>(av, h, j, g, pn, kv_first);
+            attn_block_update<DH>(av, kv_first, sc, b, g, lo, hi, ctx_max, m, l, o);
+            attn_load_v<DH>(av, h, j, g, pn, kv_first);
+            pn = pn2;
+          }
+        } else {
+          for (int b = b_lo;;) {
+            const int4 pq = attn_block_pages_s(av, b + 1 < b_hi ? b + 1 : b);   // in flight during this block
+            attn_block_step<DH>(av, kv_first, qop, b, g, lo, hi, ctx_max, m, l, o);
+            if (++b >= b_hi) break;
+            attn_load_kv<DH>(av, h, j, g, pq, kv_first);
+          }
         }
       }
     } else {
@@ -3000,8 +3062,8 @@ static bool attn_pack(const AttnArgs& a, unsigned& pk1, unsigned& pk2) {
 // The split kernel (LDS fold, early-K/V split or plain split; single sequence
 // or sequence table) and, without the fold, the combine pass.
 template <int DH>
-static bool launch_attn_split(const AttnArgs& a, dim3 grid, dim3 block, bool early, unsigned pk1, unsigned pk2,
-                              hipStream_t st) {
+static bool launch_attn_split(const AttnArgs& a, dim3 grid, dim3 block, bool early, bool pipe, unsigned pk1,
+                              unsigned pk2, hipStream_t st) {
   const bool batch = a.seqs != nullptr;
 #define SV_ATTN_LEAD a.q, a.page_table, a.params, a.seqs, pk1, pk2, a.qt_magic, a.sg_magic, a.g_magic, \
                      a.bps_guess > 1 ? a.bps_guess : 1, a
@@ -3011,6 +3073,9 @@ static bool launch_attn_split(const AttnArgs& a, dim3 grid, dim3 block, bool ear
   } else if (early) {
     if (batch) hipLaunchKernelGGL((k_attn_mfma<DH, false, true, true>), grid, block, 0, st, SV_ATTN_LEAD);
     else hipLaunchKernelGGL((k_attn_mfma<DH, false, true, false>), grid, block, 0, st, SV_ATTN_LEAD);
+  } else if (pipe) {
+    if (batch) hipLaunchKernelGGL((k_attn_mfma<DH, false, false, true, true>), grid, block, 0, st, SV_ATTN_LEAD);
+    else hipLaunchKernelGGL((k_attn_mfma<DH, false, false, false, true>), grid, block, 0, st, SV_ATTN_LEAD);
   } else {
     if (batch) hipLaunchKernelGGL((k_attn_mfma<DH, false, false, true>), grid, block, 0, st, SV_ATTN_LEAD);
     else hipLaunchKernelGGL((k_attn_mfma<DH, false, false, false>), grid, block, 0, st, SV_ATTN_LEAD);
@@ -3055,12 +3120,19 @@ hipError_t launch_attention(const AttnArgs& a_in, hipStream_t st) {
   // with it (8B 271.5 -> 275.7, Gemma 239.7 -> 246.1 us), so it keeps its
   // loads in the old order.
   const bool early = a.n_split <= kAttnMaxSplits / 2;
+  // the split kernel of several blocks per split, when its waves fit one per
+  // SIMD: the instance that keeps a second block's K in flight (more
+  // registers, one wave per SIMD).  Measured on MI355X, 8B shape at 32K (64
+  // splits of 8 blocks, 2 q tiles = 1024 waves): K = 4 step 4.72 -> 4.65 ms;
+  // at K = 16 / 32 (5 / 9 q tiles) it lost 0.8 / 2.5 % to the two-waves-per-
+  // SIMD kernel, so those keep it.  Both run the same operations on every row.
+  const bool pipe = !a.final_fold && !early && a.n_simd > 0 && n_wg * a.nkv <= a.n_simd;
   unsigned pk1, pk2;
   if (!attn_pack(a, pk1, pk2)) return hipErrorInvalidValue;
   if (a.dh == 128) {
-    if (!launch_attn_split<128>(a, grid, block, early, pk1, pk2, st)) return hipErrorInvalidValue;
+    if (!launch_attn_split<128>(a, grid, block, early, pipe, pk1, pk2, st)) return hipErrorInvalidValue;
   } else if (a.dh == 64) {
-    if (!launch_attn_split<64>(a, grid, block, early, pk1, pk2, st)) return hipErrorInvalidValue;
+    if (!launch_attn_split<64>(a, grid, block, early, pipe, pk1, pk2, st)) return hipErrorInvalidValue;
   } else {
     return hipErrorInvalidValue;
   }

@@ -216,6 +216,7 @@ struct sv_ctx {
   // profiling: wall-clock spans of the enabled kernel roles
   int prof_mask = 0;
   double wall_khz = 0.0;               // device wall-clock rate
+  int n_cu = 0;                        // compute units of the device
   double prof_ms[kProfRoles] = {};
   int64_t prof_n[kProfRoles] = {};
 
@@ -418,6 +419,7 @@ hipError_t enqueue_forward(sv_ctx* c, const FwdBufs& fb, int M, int verify, int 
     at.prof = prof_slot(c, fb, kRoleAttn, l);
     at.seqs = bd.seqs; at.rowseq = bd.rowseq; at.tiles = bd.tiles; at.n_tiles = bd.n_tiles;
     at.bps_guess = bd.seqs != nullptr ? 1 : attn_blocks_per_split(c->kv_len + 1);
+    at.n_simd = 4 * c->n_cu;
     if ((e = tiled ? launch_attention_rows(at, st) : launch_attention(at, st)) != hipSuccess) return e;
     plan(c->plans.o, L.wo, L.wo_scales, ohi, olo);
     g.gnext = gain(L.g_mlp);
@@ -650,6 +652,7 @@ sv_status sv_create(const sv_config* cfg, const sv_weights* w, const sv_buffers*
   c->plans = p;
   c->lay = lay;
   c->wall_khz = wall_khz;
+  c->n_cu = n_cu;
   c->ws = static_cast<char*>(buf->workspace);
   c->scratch = scratch_addr;
   c->hist.assign(cfg->max_ctx, -1);
