@@ -80,15 +80,17 @@ def test_stress_verify_equals_decode(stress, k):
     b.close()
 
 
-@pytest.mark.parametrize("kv_len", [184, 1020, 4084, 8180])
-def test_stress_verify_equals_decode_across_split_plan_changes(stress, kv_len):
+@pytest.mark.parametrize("kv_len,k", [(184, 16), (1020, 16), (4084, 16), (8180, 16), (4094, 4), (8190, 4)])
+def test_stress_verify_equals_decode_across_split_plan_changes(stress, kv_len, k):
     """Rows of one verify that straddle a change of the attention launch or
     split plan: around ctx 192 (3 splits folded in the workgroup vs 4 folded
     by the combine pass, chosen by the verify's longest row), around ctx 1024
     (16 vs 17 splits), around ctx 4096 (one block per split vs two) and
-    around ctx 8192 (two blocks per split vs three)."""
+    around ctx 8192 (two blocks per split vs three).  K = 16 runs the
+    two-waves-per-SIMD block walk; K = 4 (two q tiles) the pipelined one,
+    whose first-block guess (from the first row) misses for the rows past
+    the change; one-token decodes run the pipelined walk."""
     dev, w, cfg, snap = stress
-    k = 16
     rng = np.random.default_rng(2000 + kv_len)
     drafts = rng.integers(0, cfg.vocab, k).tolist()
     a, b = _sess(dev, cfg, snap), _sess(dev, cfg, snap)
