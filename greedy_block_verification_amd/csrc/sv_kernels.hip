@@ -2895,6 +2895,19 @@ __global__ __launch_bounds__(256) void k_attn_rows2(AttnArgs a) {
       fm[u] = 0.f;
       fl[u] = 0.f;
     }
+    // One block stream across the splits: block b + 1's K goes out once both
+    // tiles' scores of block b have read K, and its V once both updates have
+    // read V, so each load runs under the other half's arithmetic (one wave
+    // per SIMD: nothing else hides the latency); the block after a split's
+    // last is the next split's first (every split of the union has a block:
+    // sp < ns_max is a split of one of the rows), the very last reloads
+    // itself.  The loads are unconditional and the page numbers come through
+    // scalar loads, so every wait counts exactly.  Each tile runs
+    // attn_block_step's operations in its order.
+    int b_lo, b_hi;
+    attn_split_union(kv_len, rlo, rhi, 0, b_lo, b_hi);
+    AttnKV<DH> kv;
+    attn_load_kv<DH>(av, h, j, g, attn_block_pages_s(av, b_lo), kv);
     for (int sp = 0; sp < ns_max; ++sp) {
       int lo[TPW], hi[TPW];
 #pragma unroll
@@ -2907,8 +2920,8 @@ __global__ __launch_bounds__(256) void k_attn_rows2(AttnArgs a) {
           hi[u] = min((sp + 1) * bps * kAttnBlock, ctx[u]);
         }
       }
-      int b_lo, b_hi;
-      attn_split_union(kv_len, rlo, rhi, sp, b_lo, b_hi);
+      int nb_lo = b_hi - 1, nb_hi = b_hi;               // (past the last split: reload its last block)
+      if (sp + 1 < ns_max) attn_split_union(kv_len, rlo, rhi, sp + 1, nb_lo, nb_hi);
       f32x4 o[TPW][DT];
       float m[TPW], l[TPW];
 #pragma unroll
@@ -2918,14 +2931,19 @@ __global__ __launch_bounds__(256) void k_attn_rows2(AttnArgs a) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      int4 pq = attn_block_pages(av, b_lo < b_hi ? b_lo : 0);
       for (int b = b_lo; b < b_hi; ++b) {
-        AttnKV<DH> kv;
-        attn_load_kv<DH>(av, h, j, g, pq, kv);
-        pq = attn_block_pages(av, b + 1 < b_hi ? b + 1 : b);
+        const int4 pn = attn_block_pages_s(av, b + 1 < b_hi ? b + 1 : nb_lo);   // the next block's pages
+        f32x4 sc[TPW][4];
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) attn_block_step<DH>(av, kv, qop[u], b, g, lo[u], hi[u], ctx_max, m[u], l[u], o[u]);
+        for (int u = 0; u < TPW; ++u) attn_block_scores<DH>(kv, qop[u], sc[u]);
+        attn_load_k<DH>(av, h, j, g, pn, kv);
+#pragma unroll
+        for (int u = 0; u < TPW; ++u)
+          attn_block_update<DH>(av, kv, sc[u], b, g, lo[u], hi[u], ctx_max, m[u], l[u], o[u]);
+        attn_load_v<DH>(av, h, j, g, pn, kv);
       }
+      b_lo = nb_lo;
+      b_hi = nb_hi;
 #pragma unroll
       for (int u = 0; u < TPW; ++u) {
         if (sp == 0) {
