@@ -1567,12 +1567,8 @@ static hipError_t gemm_dispatch_grp(const GemmArgs& a, int grid, hipStream_t st)
     else return hipErrorInvalidValue;
   } else {
     if (tm == 4) launch_grp<4, ROLE, false>(a, grid, per, st);
-    else if constexpr (ROLE == kRoleLmHead) {
-      if (tm == 3) launch_grp<3, ROLE, false>(a, grid, per, st);
-      else return hipErrorInvalidValue;
-    } else {
-      return hipErrorInvalidValue;
-    }
+    else if (tm == 3) launch_grp<3, ROLE, false>(a, grid, per, st);
+    else return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -1751,9 +1747,10 @@ hipError_t launch_gemm(const GemmArgs& a, int role, int grid, hipStream_t st) {
   b.n_full = split ? n_items - r : n_items;
   b.n_half = split ? 2 * r : 0;
   // 17..64 rows whose bf16 planes do not fit one stage: items in groups,
-  // stages outermost.  Measured on the 8B shapes: the restaging kernel is
-  // faster for 34..48 rows except on the LM head (9..16 rows whose planes
-  // take more than one stage run k_gemm_bf16rb).
+  // stages outermost (9..16 rows whose planes take more than one stage run
+  // k_gemm_bf16rb).  Measured on the 8B shape, batch of 8 sequences (about
+  // 39 rows): the grouped kernel 9.61 against 10.0 ms per step for the
+  // restaging ring kernel, whose ring is one chunk deep at 33..48 rows.
   // 17..24 rows: the register-operand ring with rows 16.. in one LDS stage
   // (at most 8 chunks per wave, K <= 4096; the staged rows' planes fit the
   // stage and the fast prologue).  Measured on the 8B shape at 17 rows: O,
@@ -1779,7 +1776,7 @@ hipError_t launch_gemm(const GemmArgs& a, int role, int grid, hipStream_t st) {
     }
   }
   const int mode = grp_mode(a.M, a.S);
-  const bool grp = mode == 1 || (mode == 2 && (a.M > 48 || role == kRoleLmHead));
+  const bool grp = mode != 0;
   if (!i4 && a.M >= 17 && grp && stage_chunks(a.K >> 5, a.S, a.M, 32, 1) < (a.K >> 5)) {
     switch (role) {
       case kRoleQkv: return gemm_dispatch_grp<kRoleQkv>(b, grid, st);
