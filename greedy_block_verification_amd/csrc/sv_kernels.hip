@@ -1750,7 +1750,7 @@ hipError_t launch_gemm(const GemmArgs& a, int role, int grid, hipStream_t st) {
   // stages outermost (9..16 rows whose planes take more than one stage run
   // k_gemm_bf16rb).  Measured on the 8B shape, batch of 8 sequences (about
   // 39 rows): the grouped kernel 9.61 against 10.0 ms per step for the
-  // restaging ring kernel, whose ring is one chunk deep at 33..48 rows.
+  // restaging ring kernel, whose ring is one chunk deep at 34..48 rows.
   // 17..24 rows: the register-operand ring with rows 16.. in one LDS stage
   // (at most 8 chunks per wave, K <= 4096; the staged rows' planes fit the
   // stage and the fast prologue).  Measured on the 8B shape at 17 rows: O,
