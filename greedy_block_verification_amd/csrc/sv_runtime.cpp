@@ -221,10 +221,11 @@ struct sv_ctx {
   int64_t prof_n[kProfRoles] = {};
 
   // HIP graphs of whole forwards, keyed by (rows, attention splits, mode,
-  // logits, profile mask, batch sequences, batch q tiles)
+  // logits, profile mask, batch sequences, batch q tiles, the split
+  // kernel's blocks-per-split guess)
   hipStream_t cap_stream = nullptr;
   bool use_graphs = true;
-  std::map<std::array<int, 7>, hipGraphExec_t> graphs;
+  std::map<std::array<int, 8>, hipGraphExec_t> graphs;
 
   template <class T>
   T* at(size_t off) { return reinterpret_cast<T*>(ws + off); }
@@ -462,7 +463,10 @@ sv_status run_forward(sv_ctx* c, int M, const int* ids, int verify, int n_split,
 
   const FwdBufs fb = ws_bufs(c);
   if (c->use_graphs && M <= kMaxRows) {   // forwards of many rows take milliseconds: launched directly
-    const std::array<int, 7> key = {M, n_split, verify, logits, c->prof_mask, n_seq, n_tiles};
+    // (the guess is a kernel argument: a graph captured at one blocks-per-split
+    // would otherwise replay it at another, correct but reloading every unit)
+    const int bps_guess = n_seq > 0 ? 1 : attn_blocks_per_split(c->kv_len + 1);
+    const std::array<int, 8> key = {M, n_split, verify, logits, c->prof_mask, n_seq, n_tiles, bps_guess};
     auto it = c->graphs.find(key);
     if (it == c->graphs.end()) {
       hipGraph_t graph = nullptr;
