@@ -2502,6 +2502,14 @@ __device__ __forceinline__ void attn_split_union(int kv_len, int r0, int r1, int
   }
 }
 
+// Instances: FOLD, at most kAttnFoldSplits splits folded in LDS by one
+// 8-wave workgroup per (q tile, KV head); otherwise one single-wave
+// workgroup per (q tile, split, KV head) writing global partials, with
+// EARLY (every row one block per split: the unit's block requested before
+// q) or, for several blocks per split, a block walk whose first block is
+// requested at the caller's guess bps_g of the blocks per split (PIPE: the
+// pipelined walk at one wave per SIMD).  BATCH: the launch has a sequence
+// table.
 template <int DH, bool FOLD, bool EARLY, bool BATCH, bool PIPE = false>
 __global__ __launch_bounds__((FOLD || EARLY || !PIPE) ? 512 : 64) void k_attn_mfma(const float* q, const int* page_table, const int* params,
                                                    const SeqDev* seqs, unsigned pk1, unsigned pk2, unsigned qt_magic,
