@@ -109,6 +109,33 @@ def test_stress_verify_equals_decode_across_split_plan_changes(stress, kv_len, k
     b.close()
 
 
+def test_stress_one_session_across_blocks_per_split(stress):
+    """One context verifies K = 4 windows at 32K, 8186 and 4090 positions in
+    turn: the same row and split counts (64 splits) at 8, 2 and 1 blocks per
+    split.  The forward's captured graphs carry the split kernel's
+    blocks-per-split guess, so each window runs with its own; every window's
+    rows must equal one-token decodes of the same rows bit for bit."""
+    dev, w, cfg, snap = stress
+    b = _sess(dev, cfg, snap)
+    for kv_len in (PREFIX, 8186, 4090):
+        if kv_len < b.kv_len:
+            b.truncate(kv_len)
+        drafts = np.random.default_rng(3000 + kv_len).integers(0, cfg.vocab, 4).tolist()
+        a = _sess(dev, cfg, snap)
+        if kv_len < a.kv_len:
+            a.truncate(kv_len)
+        dec = []
+        for t in [a.next_id] + drafts:
+            a.decode_step(t)
+            dec.append(a.logits(0))
+        a.close()
+        b.verify(drafts)
+        for r in range(5):
+            np.testing.assert_array_equal(_bits(b.logits(r)), _bits(dec[r]))
+        b.truncate(kv_len)
+    b.close()
+
+
 def test_stress_prefilled_32k_context_verify_equals_decode(q8b_device):
     """A 32640-id prompt prefilled through the row-tiled kernels (2048-row
     forwards), then a K = 8 verify at that context: bit-identical to one-token
