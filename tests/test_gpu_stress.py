@@ -136,6 +136,38 @@ def test_stress_one_session_across_blocks_per_split(stress):
     b.close()
 
 
+@pytest.mark.parametrize("lens", [(PREFIX, 8186, 4090), (8186,)])
+def test_stress_long_context_batch_equals_one_at_a_time(stress, lens):
+    """Batched verify at long contexts: each sequence's rows equal its own
+    verify's bit for bit.  Three sequences (6 q tiles) run the two-waves-per-
+    SIMD block walk, one sequence (2 q tiles) the pipelined one, both with
+    the sequence table (page numbers and context lengths per tile) and the
+    batch's first-block guess of one block per split, which misses at 8 and
+    2 blocks per split."""
+    from greedy_block_verification_amd import binding as B
+    dev, w, cfg, snap = stress
+    drafts = [np.random.default_rng(4000 + n).integers(0, cfg.vocab, 4).tolist() for n in lens]
+    ref = []
+    for n, d in zip(lens, drafts):
+        a = _sess(dev, cfg, snap)
+        if n < a.kv_len:
+            a.truncate(n)
+        got = a.verify(d)
+        ref.append((got, [_bits(a.logits(r)) for r in range(5)]))
+        a.close()
+    ss = [_sess(dev, cfg, snap) for _ in lens]
+    for s, n in zip(ss, lens):
+        if n < s.kv_len:
+            s.truncate(n)
+    got = B.sv_verify_batch([s.ctx for s in ss], [s.kv_len for s in ss], drafts)
+    for s, g, (g_ref, lg_ref) in zip(ss, got, ref):
+        assert tuple(g) == tuple(g_ref)
+        for r in range(5):
+            np.testing.assert_array_equal(_bits(s.logits(r)), lg_ref[r])
+    for s in ss:
+        s.close()
+
+
 def test_stress_prefilled_32k_context_verify_equals_decode(q8b_device):
     """A 32640-id prompt prefilled through the row-tiled kernels (2048-row
     forwards), then a K = 8 verify at that context: bit-identical to one-token
