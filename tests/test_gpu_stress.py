@@ -136,14 +136,16 @@ def test_stress_one_session_across_blocks_per_split(stress):
     b.close()
 
 
-@pytest.mark.parametrize("lens", [(PREFIX, 8186, 4090), (8186,)])
+@pytest.mark.parametrize("lens", [(PREFIX, 8186, 4090), (8186,), (1500, 600)])
 def test_stress_long_context_batch_equals_one_at_a_time(stress, lens):
     """Batched verify at long contexts: each sequence's rows equal its own
     verify's bit for bit.  Three sequences (6 q tiles) run the two-waves-per-
     SIMD block walk, one sequence (2 q tiles) the pipelined one, both with
     the sequence table (page numbers and context lengths per tile) and the
     batch's first-block guess of one block per split, which misses at 8 and
-    2 blocks per split."""
+    2 blocks per split; 1500 and 600 positions (24 and 10 one-block splits)
+    run the split kernel that requests its block ahead of q, with the
+    sequence table."""
     from greedy_block_verification_amd import binding as B
     dev, w, cfg, snap = stress
     drafts = [np.random.default_rng(4000 + n).integers(0, cfg.vocab, 4).tolist() for n in lens]
