@@ -22,6 +22,8 @@ causal recompute) at contexts where the other attention paths run:
   and the verify after it must equal the 64-row path bit for bit.
 * The Gemma-style int4 GeGLU layer shape (6 q heads per KV head) at the
   600-id context.
+* The tiny shape (head_dim 64) at the 4090- and 8186-id prompts: the 64-wide
+  instances of the same attention paths.
 
 Models are 2-layer variants of the full layer shapes with a 512-id
 vocabulary and norm gains bf16(1 + 0.1 N(0,1)), so the oracle finishes in
@@ -60,6 +62,11 @@ def q06b_l2():
 @pytest.fixture(scope="module")
 def gemma_l2():
     return _model("gemma_int4", 1024)
+
+
+@pytest.fixture(scope="module")
+def tiny_long():
+    return _model("tiny", 8448)
 
 
 def _oracle_rows(weights, seq, lo, hi):
@@ -153,3 +160,12 @@ def test_split_plan_change_at_8192_matches_oracle(q06b_l2):
 def test_int4_geglu_context_600_matches_oracle(gemma_l2):
     dev, w = gemma_l2
     _long_context_case(dev, w, 600, 502, 512, "gemma int4 L2 ctx 600")
+
+
+@pytest.mark.parametrize("n_prompt,tiled", [(4090, 2048), (8186, 4096)])
+def test_head_dim_64_split_plan_changes_match_oracle(tiny_long, n_prompt, tiled):
+    """The 64-wide head instances of the long-context attention paths (the
+    tiny shape: 4 q heads, 2 KV heads, head_dim 64) across the plan changes
+    at 4096 and 8192 positions, against the oracle."""
+    dev, w = tiny_long
+    _long_context_case(dev, w, n_prompt, 504, tiled, f"tiny L2 ctx {n_prompt}")
