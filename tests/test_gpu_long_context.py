@@ -23,7 +23,8 @@ causal recompute) at contexts where the other attention paths run:
 * The Gemma-style int4 GeGLU layer shape (6 q heads per KV head) at the
   600-id context.
 * The tiny shape (head_dim 64) at the 4090- and 8186-id prompts: the 64-wide
-  instances of the same attention paths.
+  instances of the same attention paths; the Gemma shape at the 4090-id
+  prompt as well.
 
 Models are 2-layer variants of the full layer shapes with a 512-id
 vocabulary and norm gains bf16(1 + 0.1 N(0,1)), so the oracle finishes in
@@ -61,7 +62,7 @@ def q06b_l2():
 
 @pytest.fixture(scope="module")
 def gemma_l2():
-    return _model("gemma_int4", 1024)
+    return _model("gemma_int4", 4352)
 
 
 @pytest.fixture(scope="module")
@@ -169,3 +170,10 @@ def test_head_dim_64_split_plan_changes_match_oracle(tiny_long, n_prompt, tiled)
     at 4096 and 8192 positions, against the oracle."""
     dev, w = tiny_long
     _long_context_case(dev, w, n_prompt, 504, tiled, f"tiny L2 ctx {n_prompt}")
+
+
+def test_int4_geglu_split_plan_change_at_4096_matches_oracle(gemma_l2):
+    """6 q heads per KV head (54 q-rows of a K = 8 window over 4 q tiles)
+    across the plan change at 4096 positions, int4 weights."""
+    dev, w = gemma_l2
+    _long_context_case(dev, w, 4090, 505, 2048, "gemma int4 L2 ctx 4090")
